@@ -1,0 +1,362 @@
+"""Pins of the float64 oracle to facts fixed outside the oracle itself.
+
+Each test checks the oracle against something it does not compute by the same
+formula: IEEE binary16 facts, values already on the INT2 grid, brute-force
+nearest-grid-point search, hand-worked examples, closed forms of softmax on
+one or two keys, exact invariances (key centring, orthogonal rotation), and
+hand-computed byte positions of the cache layout.
+
+Sources: "Output-Aware Rotation for INT2 KV-Cache Quantization" (Pith review
+of arXiv 2608.02691) -- "What carries the argument" (key centring is
+attention-equivalent; rotation, clipping, grouping, rounding, dequantisation
+and inverse rotation), "Core claim" (one rotation per KV head and layer),
+"Assumptions & free parameters" (clip ratios; centring leaves full-precision
+softmax unchanged; exp of a skew-symmetric matrix is orthogonal).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workload import haar_orthogonal, hadamard
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- fp16 rounding
+def test_fp16_rounding_ieee_facts():
+    # binary16: 1/3 -> 0x3555 = 1365/4096; ties to even around 1.0; saturation.
+    assert O.fp16_sat(1 / 3) == 1365 / 4096
+    assert O.fp16_sat(1 + 2 ** -11) == 1.0                 # tie -> even mantissa
+    assert O.fp16_sat(1 + 3 * 2 ** -11) == 1 + 2 ** -9     # tie -> even mantissa
+    assert O.fp16_sat(65519.0) == 65504.0
+    assert O.fp16_sat(1e9) == 65504.0 and O.fp16_sat(-1e9) == -65504.0
+    assert O.fp16_sat(2 ** -24) == 2 ** -24                 # smallest subnormal
+    assert O.fp16_sat(2 ** -26) == 0.0
+
+
+# ----------------------------------------------------------------- quantiser
+def _grid_group(rng, group, s16, z16):
+    q = rng.integers(0, 4, size=group)
+    q[rng.integers(group)] = 0
+    q[(rng.integers(group - 1) + 1 + np.flatnonzero(q == 0)[0]) % group] = 3
+    return q, z16 + s16 * q
+
+
+def test_on_grid_values_round_trip():
+    """Values already on a dyadic fp16 grid re-quantise to themselves (c = 1)."""
+    rng = np.random.default_rng(1)
+    for group in (64, 128):
+        for s16, z16 in [(0.25, -1.5), (2.0, 3.0), (0.0078125, -0.5), (16.0, -24.0)]:
+            rows = []
+            codes = []
+            for _ in range(128 // group):
+                q, x = _grid_group(rng, group, s16, z16)
+                rows.append(x)
+                codes.append(q)
+            x = np.concatenate(rows)
+            s, z, c, _, _ = O.encode_groups(x, group, 1.0)
+            assert np.all(s == s16) and np.all(z == z16)
+            assert np.array_equal(c, np.concatenate(codes))
+
+
+def test_codes_are_nearest_grid_point_brute_force():
+    """RTN + clamp equals the exhaustive argmin over the 4 grid points."""
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((500, 128)) * rng.uniform(0.1, 30, size=(500, 1))
+    for group in (64, 128):
+        for clip in (1.0, 0.9):
+            s, z, c, _, _ = O.encode_groups(x, group, clip)
+            G = 128 // group
+            grid = z.reshape(500, G, 1, 1) + s.reshape(500, G, 1, 1) * np.arange(4).reshape(1, 1, 1, 4)
+            dist = np.abs(x.reshape(500, G, group, 1) - grid)
+            best = dist.argmin(-1).reshape(500, 128)
+            srt = np.sort(dist, axis=-1).reshape(500, 128, 4)
+            clear = srt[..., 1] - srt[..., 0] > 1e-9   # no tie
+            assert clear.mean() > 0.99
+            assert np.array_equal(c[clear], best[clear])
+
+
+def test_clip_scales_end_points_hand_example():
+    """c = 0.5 on a group spanning [-4, 8]: lo = -2, hi = 4, s = 2, z = -2."""
+    x = np.zeros(64)
+    x[:6] = [-4.0, 8.0, 0.0, 1.0, 3.0, 2.5]
+    x[6:] = 2.0
+    s, z, c, s_raw, z_raw = O.encode_groups(x, 64, 0.5)
+    assert s_raw[0] == 2.0 and z_raw[0] == -2.0 and s[0] == 2.0 and z[0] == -2.0
+    # -4 clamps to 0; 8 clamps to 3; 0 -> 1; 1 -> rint(1.5) = 2 (tie to even);
+    # 3 -> rint(2.5) = 2 (tie to even); 2.5 -> rint(2.25) = 2; 2 -> 2
+    assert list(c[:7]) == [0, 3, 1, 2, 2, 2, 2]
+
+
+def test_degenerate_group_stores_zero_codes():
+    x = np.full(128, 3.25)
+    s, z, c, _, _ = O.encode_groups(x, 128, 1.0)
+    assert s[0] == 0.0 and z[0] == 3.25 and not c.any()
+    s, z, c, _, _ = O.encode_groups(np.full(128, 1e-9) + np.arange(128) * 1e-12, 128, 1.0)
+    assert s[0] == 0.0 and not c.any()                   # s underflows fp16
+
+
+def test_scale_zero_are_fp16_rounded():
+    x = np.linspace(-1.0, 2.0 / 3.0 + 1e-3, 128)
+    s, z, c, s_raw, z_raw = O.encode_groups(x, 128, 1.0)
+    assert s_raw[0] != s[0]
+    assert s[0] == float(np.float16(s_raw[0])) and z[0] == float(np.float16(z_raw[0]))
+
+
+# ----------------------------------------------------------------- rotation
+def _signed_perm(rng, d):
+    sigma = rng.permutation(d)
+    while np.all(sigma[sigma] == np.arange(d)):
+        sigma = rng.permutation(d)
+    sign = rng.choice([-1.0, 1.0], size=d)
+    R = np.zeros((d, d))
+    R[np.arange(d), sigma] = sign          # e_i -> sign_i e_sigma(i)
+    return R, sigma, sign
+
+
+def test_rotation_is_row_vector_times_R():
+    """x_rot = x @ R: with R[i, sigma(i)] = sign_i, x_rot[sigma(i)] = sign_i x[i]."""
+    rng = np.random.default_rng(3)
+    R, sigma, sign = _signed_perm(rng, 128)
+    x = rng.standard_normal((3, 1, 128))
+    xr = O.rotate(x, R[None])
+    expect = np.empty_like(x)
+    expect[..., sigma] = x * sign
+    assert np.array_equal(xr, expect)
+
+
+def test_generated_rotations_are_orthogonal_and_preserve_dot_products():
+    rng = np.random.default_rng(4)
+    for R in (haar_orthogonal(rng, 128), hadamard(128) / math.sqrt(128) @ haar_orthogonal(rng, 128)):
+        assert np.abs(R.T @ R - np.eye(128)).max() < 1e-12
+        q, k = rng.standard_normal(128), rng.standard_normal(128)
+        assert abs((q @ R) @ (k @ R) - q @ k) <= 1e-12 * np.abs(q).sum() * np.abs(k).sum()
+    H = hadamard(8)
+    assert np.array_equal(H @ H.T, 8 * np.eye(8))
+
+
+# ----------------------------------------------------------------- attention
+def test_attention_closed_forms():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal(16)
+    k = rng.standard_normal((2, 16))
+    v = rng.standard_normal((2, 16))
+    scale = 0.25
+    # N = 1: the value itself
+    assert np.allclose(O.attend(q, k[:1], v[:1], scale), v[0], rtol=0, atol=0)
+    # N = 2: logistic weights
+    l0, l1 = scale * sum(q[i] * k[0, i] for i in range(16)), scale * sum(q[i] * k[1, i] for i in range(16))
+    p0 = 1.0 / (1.0 + math.exp(l1 - l0))
+    assert np.allclose(O.attend(q, k, v, scale), p0 * v[0] + (1 - p0) * v[1], rtol=1e-14, atol=1e-14)
+    # identical keys: mean of values
+    kk = np.repeat(k[:1], 5, axis=0)
+    vv = rng.standard_normal((5, 16))
+    assert np.allclose(O.attend(q, kk, vv, scale), vv.mean(0), rtol=1e-14, atol=1e-14)
+    # huge logit gap: one-hot, no overflow
+    big = np.stack([k[0] * 0, k[0] * 0])
+    big[0, 0] = 1e4
+    qq = np.zeros(16)
+    qq[0] = 1.0
+    assert np.array_equal(O.attend(qq, big, v, 1.0), v[0])
+    # empty context
+    assert np.array_equal(O.attend(q, k[:0], v[:0], scale), np.zeros(16))
+
+
+def test_key_centring_leaves_softmax_unchanged_exactly():
+    """Subtracting one vector from every key shifts all logits by q.mu; with
+    small integers every dot product is exact, so softmax is bit-identical."""
+    rng = np.random.default_rng(6)
+    q = rng.integers(-4, 5, size=32).astype(float)
+    k = rng.integers(-8, 9, size=(40, 32)).astype(float)
+    v = rng.standard_normal((40, 32))
+    mu = rng.integers(-6, 7, size=32).astype(float)
+    a = O.attend(q, k, v, 1 / 8)
+    b = O.attend(q, k - mu, v, 1 / 8)
+    assert np.array_equal(a, b)
+    # Gaussian inputs: a few ulp
+    qg, kg, mug = rng.standard_normal(32), rng.standard_normal((40, 32)), rng.standard_normal(32) * 3
+    a, b = O.attend(qg, kg, v, 0.2), O.attend(qg, kg - mug, v, 0.2)
+    assert np.abs(a - b).max() <= 1e-13 * np.abs(a).max()
+
+
+# ----------------------------------------------------------------- layout
+def test_layout_golden_examples():
+    lines = [ln.split() for ln in open(os.path.join(GOLDEN, "layout_examples.txt"))
+             if ln.strip() and not ln.startswith("#")]
+    assert len(lines) == 8
+    for kind, t, i, code, byte, value in lines:
+        t, i, code, byte, value = int(t), int(i), int(code), int(byte), int(value, 16)
+        site = O.k_code_site if kind == "k" else O.v_code_site
+        off, sh = site(t, i)
+        assert int(off) == byte and (code << int(sh)) == value
+        # through the page writer: one page, one head, one token with one code
+        enc = {key: np.zeros((1, 128) if "codes" in key else (1, 1)) for key in
+               ("k_codes", "v_codes", "k_s", "k_z", "v_s", "v_z")}
+        enc[kind + "_codes"][0, i] = code
+        cache = np.zeros((1, 1, O.page_bytes(128, 128)), np.uint8)
+        O.write_tokens(cache, np.zeros((1, 1), np.int32), 0, [t], 0, slice(None), enc, 1, 128)
+        nz = np.flatnonzero(cache.reshape(-1))
+        assert list(nz) == [byte] and cache.reshape(-1)[byte] == value
+    # the worked K byte: codes [1, 2, 3, 0] on channels 0..3 -> 0x39
+    enc = {key: np.zeros((1, 128) if "codes" in key else (1, 1)) for key in
+           ("k_codes", "v_codes", "k_s", "k_z", "v_s", "v_z")}
+    enc["k_codes"][0, :4] = [1, 2, 3, 0]
+    cache = np.zeros((1, 1, O.page_bytes()), np.uint8)
+    O.write_tokens(cache, np.zeros((1, 1), np.int32), 0, [0], 0, slice(None), enc, 1, 128)
+    assert cache.reshape(-1)[0] == 0x39
+
+
+def test_scale_zero_sites_and_page_size():
+    assert O.page_bytes(128, 128) == 1152 and O.page_bytes(128, 64) == 1280
+    assert int(O.sz_site(3, 1, 64, "k")) == 1052 and int(O.sz_site(3, 1, 64, "v")) == 1180
+    assert int(O.sz_site(15, 0, 128, "v")) == 1024 + 64 + 60
+    enc = {key: np.zeros((1, 128) if "codes" in key else (1, 2)) for key in
+           ("k_codes", "v_codes", "k_s", "k_z", "v_s", "v_z")}
+    enc["v_s"][0, 1] = 0.75      # fp16 0x3A00
+    enc["v_z"][0, 1] = -2.0      # fp16 0xC000
+    cache = np.zeros((1, 1, O.page_bytes(128, 64)), np.uint8)
+    O.write_tokens(cache, np.zeros((1, 1), np.int32), 0, [3], 0, slice(None), enc, 1, 64)
+    flat = cache.reshape(-1)
+    assert list(flat[1180:1184]) == [0x00, 0x3A, 0x00, 0xC0]
+
+
+def test_pack_unpack_identity_over_all_byte_values():
+    """Every byte value of every code site survives write -> read."""
+    rng = np.random.default_rng(7)
+    for group in (64, 128):
+        cache = np.zeros((3, 2, O.page_bytes(128, group)), np.uint8)
+        table = np.array([[2, 0, 1]], np.int32)
+        pos = np.arange(48)
+        G = 128 // group
+        enc = {"k_codes": rng.integers(0, 4, (48, 128)), "v_codes": rng.integers(0, 4, (48, 128)),
+               "k_s": O.fp16_sat(rng.standard_normal((48, G))), "k_z": O.fp16_sat(rng.standard_normal((48, G))),
+               "v_s": O.fp16_sat(rng.standard_normal((48, G))), "v_z": O.fp16_sat(rng.standard_normal((48, G)))}
+        for h in range(2):
+            O.write_tokens(cache, table, 0, pos, h, slice(None), enc, 2, group)
+        for h in range(2):
+            got = O.read_tokens(cache, table, 0, pos, h, 2, group)
+            for key in enc:
+                assert np.array_equal(got[key], enc[key]), key
+    # every byte value 0..255 at a K byte and at a V byte: the four codes that
+    # share the byte are written (as four tokens/channels) and read back
+    for val in range(256):
+        four = [(val >> (2 * i)) & 3 for i in range(4)]
+        for kind in ("k", "v"):
+            cache = np.zeros((1, 1, O.page_bytes()), np.uint8)
+            table = np.zeros((1, 1), np.int32)
+            if kind == "k":
+                t, chans = val % 16, [4 * (val // 16 % 32) + i for i in range(4)]
+                toks = [t] * 4
+            else:
+                th, half, ch = (val // 2) % 2, val % 2, val % 128
+                toks, chans = [8 * th + 4 * half + e for e in range(4)], [ch] * 4
+            for tok, ch, code in zip(toks, chans, four):
+                enc = {key: np.zeros((1, 128) if "codes" in key else (1, 1)) for key in
+                       ("k_codes", "v_codes", "k_s", "k_z", "v_s", "v_z")}
+                old = O.read_tokens(cache, table, 0, [tok], 0, 1, 128)
+                enc[kind + "_codes"][0] = old[kind + "_codes"][0]
+                enc[kind + "_codes"][0, ch] = code
+                O.write_tokens(cache, table, 0, [tok], 0, slice(None), enc, 1, 128)
+            site = O.k_code_site if kind == "k" else O.v_code_site
+            byte = int(site(toks[0], chans[0])[0])
+            assert cache.reshape(-1)[byte] == val
+            got = O.read_tokens(cache, table, 0, toks, 0, 1, 128)[kind + "_codes"]
+            assert [int(got[n, chans[n]]) for n in range(4)] == four
+    # overwriting one token leaves its neighbours' bits untouched
+    cache = np.full((1, 1, O.page_bytes()), 0xFF, np.uint8)
+    enc = {key: np.zeros((1, 128) if "codes" in key else (1, 1)) for key in
+           ("k_codes", "v_codes", "k_s", "k_z", "v_s", "v_z")}
+    O.write_tokens(cache, np.zeros((1, 1), np.int32), 0, [9], 0, slice(None), enc, 1, 128)
+    got = O.read_tokens(cache, np.zeros((1, 1), np.int32), 0, np.arange(16), 0, 1, 128)
+    assert not got["v_codes"][9].any() and np.all(got["v_codes"][np.arange(16) != 9] == 3)
+    assert not got["k_codes"][9].any() and np.all(got["k_codes"][np.arange(16) != 9] == 3)
+
+
+def test_bits_per_element_closed_form():
+    # group 64 stores 2.5 bits/element (stated for the decode-heavy workload); group 128: 2.25
+    assert O.bits_per_element(128, 64) == 2.5
+    assert O.bits_per_element(128, 128) == 2.25
+
+
+# ----------------------------------------------------------------- end to end
+def _one_layer(rng, Hkv, group, R_k, R_v):
+    cache = np.zeros((4, Hkv, O.page_bytes(128, group)), np.uint8)
+    table = np.array([[3, 1, 0, 2]], np.int32)
+    return cache, table
+
+
+def test_value_path_single_token_returns_value_exactly():
+    """Append v with y = v @ R_V on a dyadic grid, decode with one token: the
+    output is v exactly (p = 1, dequantisation exact, inverse rotation exact for
+    a signed permutation)."""
+    rng = np.random.default_rng(8)
+    R_v, _, _ = _signed_perm(rng, 128)
+    R_k, _, _ = _signed_perm(rng, 128)
+    for group in (64, 128):
+        y = np.concatenate([_grid_group(rng, group, 0.5, -1.0)[1] for _ in range(128 // group)])
+        v = y @ R_v.T
+        k = rng.integers(-3, 4, size=128).astype(float)
+        cache, table = _one_layer(rng, 1, group, R_k, R_v)
+        O.append(cache, table, [37], k[None, None, None], v[None, None, None], np.zeros((1, 128)),
+                 R_k[None], R_v[None], group, 0.9, 1.0)
+        table_full = table
+        q = rng.standard_normal((1, 1, 128))
+        # ctx 38 would include unwritten slots; read the single written token
+        tok = O.read_tokens(cache, table_full, 0, [37], 0, 1, group)
+        v_hat_r = O.dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)[0]
+        assert np.array_equal(v_hat_r, y)
+        o_r = O.attend(q[0, 0] @ R_k, O.dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group), v_hat_r[None], 0.1)
+        assert np.array_equal(o_r @ R_v.T, v)
+        # decode over a context of one token
+        cache2, _ = _one_layer(rng, 1, group, R_k, R_v)
+        O.append(cache2, table, [0], k[None, None, None], v[None, None, None], np.zeros((1, 128)),
+                 R_k[None], R_v[None], group, 0.9, 1.0)
+        o = O.decode(cache2, table, [1], q, R_k[None], R_v[None], 0.1, 1, group)
+        assert np.array_equal(o[0, 0], v)
+
+
+def test_key_centring_is_applied_before_rotation():
+    """k = mu + x with x on the grid (R = I, c = 1): the stored grid is x's."""
+    rng = np.random.default_rng(9)
+    x = _grid_group(rng, 128, 0.25, -0.75)[1]
+    mu = rng.integers(-64, 64, size=128) / 8.0
+    k = mu + x
+    enc = O.encode_tokens(k[None, None], np.zeros((1, 1, 128)), mu[None], np.eye(128)[None],
+                          np.eye(128)[None], 128, 1.0, 1.0)
+    assert enc["k_s"][0, 0, 0] == 0.25 and enc["k_z"][0, 0, 0] == -0.75
+    assert np.array_equal(enc["k_codes"][0, 0], ((x + 0.75) / 0.25).astype(int))
+    # values are not centred
+    assert np.array_equal(enc["y"], np.zeros((1, 1, 128)))
+
+
+def test_decode_scores_with_rotated_query_and_maps_gqa_heads():
+    """Keys on the grid in the rotated basis, R_K a non-involutive signed
+    permutation: decode logits equal sm_scale * q . k (rotation preserved), so
+    two-token outputs follow the logistic closed form; query head hq reads KV
+    head hq // (Hq/Hkv)."""
+    rng = np.random.default_rng(10)
+    Hkv, Hq, group, scale = 2, 4, 128, 0.3
+    Rk = np.stack([_signed_perm(rng, 128)[0] for _ in range(Hkv)])
+    Rv = np.stack([_signed_perm(rng, 128)[0] for _ in range(Hkv)])
+    cache = np.zeros((2, Hkv, O.page_bytes(128, group)), np.uint8)
+    table = np.array([[1]], np.int32)
+    ys_k = np.stack([[_grid_group(rng, 128, 0.5, -1.0)[1] for _ in range(Hkv)] for _ in range(2)])
+    ys_v = np.stack([[_grid_group(rng, 128, 0.25, -0.5)[1] for _ in range(Hkv)] for _ in range(2)])
+    k = np.einsum("thj,hij->thi", ys_k, Rk)   # k = y_k @ R_K^T
+    v = np.einsum("thj,hij->thi", ys_v, Rv)
+    O.append(cache, table, [0], k[None], v[None], np.zeros((Hkv, 128)), Rk, Rv, group, 1.0, 1.0)
+    q = rng.standard_normal((1, Hq, 128))
+    o = O.decode(cache, table, [2], q, Rk, Rv, scale, Hkv, group)
+    for hq in range(Hq):
+        h = hq // (Hq // Hkv)
+        l0 = scale * float(np.dot(q[0, hq], k[0, h]))
+        l1 = scale * float(np.dot(q[0, hq], k[1, h]))
+        p0 = 1.0 / (1.0 + math.exp(l1 - l0))
+        expect = p0 * v[0, h] + (1 - p0) * v[1, h]
+        assert np.allclose(o[0, hq], expect, rtol=1e-12, atol=1e-12)
+    # empty context -> zeros
+    o0 = O.decode(cache, table, [0], q, Rk, Rv, scale, Hkv, group)
+    assert np.array_equal(o0, np.zeros_like(o0))
