@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated INT2 KV-cache hot path on one MI355X.
+
+One step runs the whole hot path once per layer: kvq_append encodes one new
+bf16 key/value token per sequence (centre, rotate, clip, INT2 group RTN,
+pack into the paged cache) and kvq_decode_attn runs single-token attention
+over the updated INT2 cache (rotated query, split-K online softmax,
+log-sum-exp merge, inverse value rotation).
+
+Default workload: 36 layers x batch 16 of Qwen3-8B-shaped attention (32
+query / 8 KV heads, head_dim 128), 16K tokens of prior context per sequence,
+paged blocks of 16, group 128, clip 0.9.  All inputs are seeded synthetic
+data resident in HBM before timing starts.  Each step is captured once as a
+HIP graph and replayed.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT2 decode-attention cache GB/s (% of HBM peak) and tokens/s; append Mtok/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_36l_b16_ctx16k_stream")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="bound on the oracle's CPU time for the cpu_baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    return ap.parse_args()
+
+
+def cache_bytes_per_token_head(group: int) -> int:
+    """Algorithmic INT2 cache bytes decode reads per (token, KV head):
+    K and V codes (2 x 32 B) plus one fp16 (scale, zero) pair per group for each."""
+    return 2 * (128 // 4) + 2 * (128 // group) * 4
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rotated_int2_kv_kvq_amd as kvq
+    from workload import WORKLOADS, key_mean, kv_for_sequence, make_static, query_for, scaled
+
+    dev = "cuda"
+    kvq.lib()
+    total_steps = args.warmup + args.steps
+    w0 = WORKLOADS[args.workload]
+    w = scaled(w0, steps=max(w0.steps, total_steps))
+    st = make_static(w)
+    L, B, Hq, Hkv, d = w.layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    pb = kvq.page_bytes(d, w.group)
+    table = torch.from_numpy(st.block_table).to(dev)
+    ctx0 = st.ctx_lens.astype(np.int64)
+
+    # ---------------------------------------------------------------- build the cache
+    pages, mus, rks, rvs = [], [], [], []
+    t_bulk = 0.0
+    n_bulk = 0
+    for layer in range(L):
+        pages.append(torch.empty(st.num_blocks, Hkv, pb, dtype=torch.uint8, device=dev))
+        mus.append(key_mean(w, st, layer, device=dev).contiguous())
+        rks.append(torch.from_numpy(st.rot_k[layer]).to(dev).contiguous())
+        rvs.append(torch.from_numpy(st.rot_v[layer]).to(dev).contiguous())
+        by_len = {}
+        for b, n in enumerate(ctx0):
+            by_len.setdefault(int(n), []).append(b)
+        for n, seqs in by_len.items():
+            kv = [kv_for_sequence(w, st, layer, b, 0, n, dev) for b in seqs]
+            k = torch.stack([x[0] for x in kv]).contiguous()
+            v = torch.stack([x[1] for x in kv]).contiguous()
+            del kv
+            tab = table.index_select(0, torch.as_tensor(seqs, device=dev)).contiguous()
+            sp = torch.zeros(len(seqs), dtype=torch.int32, device=dev)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            kvq.append(pages[layer], tab, sp, k, v, mus[layer], rks[layer], rvs[layer], w.group,
+                       w.clip_k, w.clip_v)
+            torch.cuda.synchronize()
+            t_bulk += time.perf_counter() - t0
+            n_bulk += len(seqs) * n
+            del k, v
+        print(f"[bench] layer {layer} cache built", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- per-step inputs
+    qs, kn, vn, spos, ctxs, maxc = [], [], [], [], [], []
+    new_kv = []  # [layer] -> (k, v) of shape [B][total_steps][Hkv][d]
+    for layer in range(L):
+        kv = [kv_for_sequence(w, st, layer, b, int(ctx0[b]), total_steps, dev) for b in range(B)]
+        new_kv.append((torch.stack([x[0] for x in kv]), torch.stack([x[1] for x in kv])))
+    for step in range(total_steps):
+        qs.append([query_for(w, layer, step, dev).contiguous() for layer in range(L)])
+        kn.append([new_kv[layer][0][:, step:step + 1].contiguous() for layer in range(L)])
+        vn.append([new_kv[layer][1][:, step:step + 1].contiguous() for layer in range(L)])
+        spos.append(torch.from_numpy((ctx0 + step).astype(np.int32)).to(dev))
+        ctxs.append(torch.from_numpy((ctx0 + step + 1).astype(np.int32)).to(dev))
+        maxc.append(int(ctx0.max()) + step + 1)
+    max_ctx_all = maxc[-1]
+    ws = torch.empty(kvq.decode_workspace_bytes(B, Hq, Hkv, max_ctx_all, d), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty(B, Hq, d, dtype=torch.float32, device=dev) for _ in range(L)]
+    sm_scale = 1.0 / math.sqrt(d)
+
+    def run_step(step):
+        for layer in range(L):
+            kvq.append(pages[layer], table, spos[step], kn[step][layer], vn[step][layer],
+                       mus[layer], rks[layer], rvs[layer], w.group, w.clip_k, w.clip_v)
+            kvq.decode(pages[layer], table, ctxs[step], maxc[step], qs[step][layer], rks[layer],
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws)
+
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        for step in range(total_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                run_step(step)
+            graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        # capture does not execute: the cache still holds only the prior context
+
+    def step_fn(step):
+        if graphs:
+            graphs[step].replay()
+        else:
+            run_step(step)
+
+    # ---------------------------------------------------------------- timed steps
+    for step in range(args.warmup):
+        step_fn(step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for step in range(args.warmup, total_steps):
+        step_fn(step)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    step_ms = gpu_ms / args.steps
+    per_tok_head = cache_bytes_per_token_head(w.group)
+    bytes_steps = sum(int((ctx0 + s + 1).sum()) * Hkv * per_tok_head * L
+                      for s in range(args.warmup, total_steps))
+    value = bytes_steps / (gpu_ms * 1e-3) / 1e9
+    assert all(torch.isfinite(o).all().item() for o in outs)
+
+    # ---------------------------------------------------------------- per-kernel event timing
+    # Queue every launch behind a GPU sleep so that host launch latency never
+    # falls inside an event interval.  Stage boundaries of one decode are
+    # launched separately; the split kernel sits alone between its events.
+    last = total_steps - 1
+    split_ms, app_ms = [], []
+    for rep in range(3):
+        evs = []
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)
+        for layer in range(L):
+            a0, a1, s0, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws,
+                       stages=kvq.STAGE_PREPARE)
+            s0.record()
+            kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws,
+                       stages=kvq.STAGE_SPLITS)
+            s1.record()
+            kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws,
+                       stages=kvq.STAGE_MERGE)
+            a0.record()
+            # re-append the last step's token: same slot, same bytes
+            kvq.append(pages[layer], table, spos[last], kn[last][layer], vn[last][layer],
+                       mus[layer], rks[layer], rvs[layer], w.group, w.clip_k, w.clip_v)
+            a1.record()
+            evs.append((s0, s1, a0, a1))
+        torch.cuda.synchronize()
+        if rep == 0:
+            continue
+        for s0, s1, a0, a1 in evs:
+            split_ms.append(s0.elapsed_time(s1))
+            app_ms.append(a0.elapsed_time(a1))
+    split_avg_ms = float(np.mean(split_ms))
+    app_avg_ms = float(np.mean(app_ms))
+    split_bytes = int((ctx0 + last + 1).sum()) * Hkv * per_tok_head
+    achieved = split_bytes / (split_avg_ms * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, st, pages[0], table, ctxs[last], qs[last][0], per_tok_head,
+                           args.cpu_seconds, sm_scale)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w0.name, "layers": L, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+            "head_dim": d, "prior_ctx": int(ctx0.max()), "group": w.group, "block": 16,
+            "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "clip": w.clip_k,
+            "cache": f"INT2 + fp16 scale/zero per {w.group} ({per_tok_head} B per token-head)",
+            "launch": "eager" if args.no_graph else "hipGraph per step", "parallelism": "none",
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(B * args.steps / (gpu_ms * 1e-3), 1),
+        "append_decode_mtok_s": round(B / (app_avg_ms * 1e-3) / 1e6, 4),
+        "append_bulk_mtok_s": round(n_bulk / t_bulk / 1e6, 3) if t_bulk else None,
+        "append_avg_us": round(app_avg_ms * 1e3, 2),
+        "split_kernel_avg_us": round(split_avg_ms * 1e3, 2),
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "kernel": "split_kernel (decode split-K scan)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s, sm_scale):
+    """The float64 oracle's decode of layer 0 on the host, over as many
+    (sequence, KV head) pairs as fit in the time budget, in cache GB/s."""
+    import numpy as np
+
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _cpu_baseline(O, w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s,
+                             sm_scale)
+
+
+def _cpu_baseline(O, w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s, sm_scale):
+    import numpy as np
+    ctx = ctx_t.cpu().numpy()
+    q = q_l0.float().cpu().double().numpy()
+    Hkv, Hg = w.num_kv_heads, w.num_q_heads // w.num_kv_heads
+    done_bytes = 0
+    pairs = 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        n = int(ctx[b])
+        n_pages = (n + 15) // 16
+        cache = pages_l0.index_select(0, table[b, :n_pages].long()).cpu().numpy()
+        ident = np.arange(n_pages, dtype=np.int32)[None, :]
+        for h in range(Hkv):
+            heads = [(0, hq) for hq in range(h * Hg, (h + 1) * Hg)]
+            O.decode(cache, ident, [n], q[b:b + 1], st.rot_k[0], st.rot_v[0], sm_scale, Hkv,
+                     w.group, pairs=heads)
+            done_bytes += n * per_tok_head
+            pairs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle decode of layer 0, {pairs} (sequence, KV head) pairs "
+                      f"x {Hg} query heads at {int(ctx.max())} tokens, BLAS limited to 1 thread, "
+                      f"{el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

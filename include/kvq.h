@@ -1,0 +1,183 @@
+/*
+ * kvq.h -- C ABI of the rotated INT2 KV-cache library for MI355X (gfx950).
+ *
+ * The library implements the serving hot path of rotation-based INT2 KV-cache
+ * quantisation as described in "Output-Aware Rotation for INT2 KV-Cache
+ * Quantization" (Pith review of arXiv 2608.02691; sections "What carries the
+ * argument", "Core claim", "If this is right", "Assumptions & free
+ * parameters", and the abstract):
+ *
+ *   append  -- subtract a per-channel key mean, rotate keys and values by a
+ *              per-KV-head orthogonal matrix, clip, quantise to 2-bit codes per
+ *              group of channels with an fp16 scale and zero, and pack the
+ *              codes into a paged cache;
+ *   decode  -- single-token attention that reads the paged INT2 cache
+ *              directly, with the query rotated by the key rotation, and the
+ *              inverse value rotation applied to the output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer into memory the caller owns,
+ *    except where a comment says "host".  The library allocates nothing,
+ *    keeps no global state, never synchronises the device, and launches all
+ *    work on the given stream (a hipStream_t passed as void*; NULL = the
+ *    default stream).  Calls on different streams may run concurrently as long
+ *    as they do not write the same cache pages or workspace.
+ *  - Rotations use row vectors: x_rot[j] = sum_i x[i] * R[i][j], R stored
+ *    row-major float32 [head_dim][head_dim] per KV head.  The inverse rotation
+ *    of the output is o = o_rot * R_V^T.
+ *  - head_dim must be 128; group (channels sharing one fp16 scale/zero) is 64
+ *    or 128; a block (page) holds 16 tokens.
+ *  - Return values are kvq_status codes.  Arguments are validated on the host
+ *    before anything is launched; a failing check launches nothing.  A launch
+ *    failure reported by the HIP runtime returns KVQ_ERR_HIP.  Values that
+ *    live in device memory (block-table entries, start positions, context
+ *    lengths) cannot be checked on the host: the kernels never read or write
+ *    outside the cache, table and tensors described here, but a block id
+ *    outside [0, num_blocks) or a position past the block table gives
+ *    unspecified cache contents / outputs for the affected sequence.
+ *
+ * Cache layout (one buffer per layer; pages are [num_blocks][num_kv_heads]
+ * of kvq_page_bytes() bytes each; G = head_dim / group):
+ *   byte [0, 512)           K codes, 16 token rows of 32 bytes; channel i of
+ *                           token t at byte 32*t + i/4, bits 2*(i%4)
+ *   byte [512, 1024)        V codes, 64 little-endian 16-bit chunks; chunk
+ *                           (th, n, j) holds tokens 8*th..8*th+7 of channel
+ *                           16*j + n at byte 512 + 2*((16*th + n)*8 + j),
+ *                           token 8*th + e at bit 2*e
+ *   byte [1024, 1024+64G)   K (scale, zero) fp16 pairs, [token][group]
+ *   byte [.., 1024+128G)    V (scale, zero) fp16 pairs, [token][group]
+ * A cached element decodes as x_hat = scale * code + zero (rotated basis).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad dtype, bad clip   */
+  KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim != 128)   */
+  KVQ_ERR_WORKSPACE = -3,   /* workspace pointer null or too small           */
+  KVQ_ERR_HIP = -4          /* the HIP runtime reported a launch error       */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+/* Human-readable text for a kvq_status value (static storage, never NULL). */
+const char *kvq_status_string(int status);
+
+/* Bytes of one (block, KV head) page: 1024 + 128 * head_dim / group.
+ * Returns 0 for an unsupported (head_dim, group). */
+size_t kvq_page_bytes(int32_t head_dim, int32_t group);
+
+/*
+ * kvq_append -- encode new key/value tokens into the paged INT2 cache.
+ *
+ * Defined by the OptR review page, "What carries the argument": keys are
+ * centred by a per-channel mean before rotation (attention-equivalent), then
+ * rotation, clipping, grouping and rounding; "Core claim": one rotation per
+ * KV head and layer; "Assumptions & free parameters": clipping ratios c_K,
+ * c_V.  For token tau of sequence b and KV head h:
+ *     x = (k - mu[h]) * R_K[h],   y = v * R_V[h]
+ * and for every group of `group` rotated channels (separately for x and y):
+ *     lo = c*min, hi = c*max, scale = fp16((hi - lo)/3), zero = fp16(lo)
+ *     code = clamp(round_half_even((x - zero)/scale), 0, 3)  (0 if scale == 0)
+ * fp16 conversion rounds to nearest even and saturates at +-65504.
+ *
+ *   pages          device  uint8 cache buffer of num_blocks * num_kv_heads
+ *                          * kvq_page_bytes(head_dim, group) bytes (written)
+ *   block_table    device  int32 [batch][max_blocks_per_seq]: physical block
+ *                          of logical block p of sequence b
+ *   start_pos      device  int32 [batch]: position of the first new token of
+ *                          sequence b; tokens go to positions start_pos[b] ..
+ *                          start_pos[b] + num_new - 1 (block pos/16, slot pos%16)
+ *   k, v           device  [batch][num_new][num_kv_heads][head_dim] of kv_dtype
+ *   mu             device  float32 [num_kv_heads][head_dim] key mean
+ *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]
+ *   clip_k, clip_v host    clipping ratios in (0, 1]
+ * Only the written tokens' codes, scales and zeros change; other tokens in the
+ * same pages keep their contents.  Two sequences must not share a physical
+ * block that this call writes.  batch == 0 or num_new == 0 is a no-op.
+ */
+int kvq_append(void *pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+               int32_t group, const int32_t *block_table, int32_t max_blocks_per_seq,
+               const int32_t *start_pos, int32_t batch, int32_t num_new, const void *k,
+               const void *v, int32_t kv_dtype, const float *mu, const float *rot_k,
+               const float *rot_v, float clip_k, float clip_v, void *stream);
+
+/*
+ * Workspace bytes kvq_decode_attn needs for this shape (host query, no device
+ * access).  split_pages as for kvq_decode_attn.  Returns 0 on invalid input.
+ */
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_ctx_len, int32_t split_pages);
+
+/*
+ * kvq_decode_attn -- single-token attention over the paged INT2 cache.
+ *
+ * Defined by the OptR review page ("What carries the argument":
+ * dequantisation and inverse rotation after attention over quantised keys and
+ * values; the abstract: attention over the quantised cache).  For sequence b
+ * and query head hq (KV head h = hq / (num_q_heads / num_kv_heads)):
+ *     q_r = q[b][hq] * R_K[h]
+ *     p_t = softmax_t( sm_scale * q_r . k_hat_t ),  t < ctx_len[b]
+ *     out[b][hq] = ( sum_t p_t v_hat_t ) * R_V[h]^T
+ * with k_hat, v_hat the dequantised cache entries.  ctx_len[b] == 0 gives a
+ * zero output.  The context is processed in splits with an online softmax and
+ * merged by log-sum-exp; the result does not depend on the split size beyond
+ * float32 rounding.
+ *
+ *   pages, block_table     as for kvq_append (pages only read)
+ *   ctx_len        device  int32 [batch], each in [0, max_ctx_len]
+ *   max_ctx_len    host    upper bound of ctx_len; <= 16 * max_blocks_per_seq
+ *   q              device  [batch][num_q_heads][head_dim] of q_dtype
+ *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]
+ *   sm_scale       host    softmax scale (1/sqrt(head_dim) for standard attention)
+ *   out            device  float32 [batch][num_q_heads][head_dim] (written)
+ *   workspace      device  at least kvq_decode_workspace_bytes(...) bytes,
+ *                          256-byte aligned; contents are scratch
+ *   split_pages    host    pages per workgroup split: 0 = automatic, else a
+ *                          positive multiple of 8
+ * num_q_heads must be a multiple of num_kv_heads.
+ */
+int kvq_decode_attn(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t group, const int32_t *block_table,
+                    int32_t max_blocks_per_seq, const int32_t *ctx_len, int32_t max_ctx_len,
+                    int32_t batch, int32_t num_q_heads, const void *q, int32_t q_dtype,
+                    const float *rot_k, const float *rot_v, float sm_scale, float *out,
+                    void *workspace, size_t workspace_bytes, int32_t split_pages,
+                    void *stream);
+
+/*
+ * kvq_decode_attn_staged -- the same computation as kvq_decode_attn, run as
+ * separately launchable stages (for callers that schedule or time them apart).
+ * `stages` is a bit mask of the stages to launch now, in this order:
+ */
+#define KVQ_STAGE_PREPARE 1 /* rotate q by R_K; write its MFMA operand to workspace */
+#define KVQ_STAGE_SPLITS 2  /* stream the cache; write per-split partials           */
+#define KVQ_STAGE_MERGE 4   /* log-sum-exp merge, inverse value rotation, write out */
+#define KVQ_STAGE_ALL 7
+/* A stage reads what the previous stage left in the workspace, so the calls
+ * that make up one decode must pass identical arguments and workspace, on one
+ * stream (or with the caller ordering them).  stages outside 1..7 is
+ * KVQ_ERR_INVALID_ARG.  kvq_decode_attn(...) == kvq_decode_attn_staged(...,
+ * KVQ_STAGE_ALL, stream). */
+int kvq_decode_attn_staged(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t group, const int32_t *block_table,
+                           int32_t max_blocks_per_seq, const int32_t *ctx_len,
+                           int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                           const void *q, int32_t q_dtype, const float *rot_k, const float *rot_v,
+                           float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                           int32_t split_pages, int32_t stages, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -52,7 +52,7 @@ F16_MAX = 65504.0
 
 __all__ = [
     "HEAD_DIM", "BLOCK", "F16_MAX", "fp16_sat", "page_bytes", "bits_per_element",
-    "rotate", "encode_groups", "encode_tokens", "k_code_site", "v_code_site",
+    "rotate", "encode_groups", "quantize_on_grid", "encode_tokens", "k_code_site", "v_code_site",
     "sz_site", "write_tokens", "read_tokens", "dequant", "attend", "decode",
     "append", "plain_attention",
 ]
@@ -114,11 +114,24 @@ def encode_groups(x, group: int, clip: float):
     z_raw = lo
     s16 = fp16_sat(s_raw)
     z16 = fp16_sat(z_raw)
+    codes = quantize_on_grid(x, s16, z16, group)
+    return s16, z16, codes, s_raw, z_raw
+
+
+def quantize_on_grid(x, s16, z16, group: int):
+    """Codes of x [..., d] on the grid z16 + s16*{0..3} of each group
+    ([..., G] each): clamp(rint((x - z16)/s16), 0, 3), 0 where s16 == 0."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    G = d // group
+    xg = x.reshape(x.shape[:-1] + (G, group))
+    s16 = np.asarray(s16, np.float64)[..., None]
+    z16 = np.asarray(z16, np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        t = (xg - z16[..., None]) / s16[..., None]
+        t = (xg - z16) / s16
     codes = np.clip(np.rint(t), 0, 3)
-    codes = np.where(s16[..., None] == 0, 0, codes).astype(np.uint8)
-    return s16, z16, codes.reshape(x.shape), s_raw, z_raw
+    codes = np.where(s16 == 0, 0, codes).astype(np.uint8)
+    return codes.reshape(x.shape)
 
 
 def encode_tokens(k, v, mu, rot_k, rot_v, group: int, clip_k: float, clip_v: float):

@@ -1,0 +1,127 @@
+// extern "C" entry points of libkvq: host-side validation, workspace sizing and
+// kernel launches.  No allocation, no synchronisation, no global state.
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+#include "kvq_common.h"
+
+#include "kvq_launch.h"
+
+#define KVQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_geometry(int32_t head_dim, int32_t group) {
+  return head_dim > 0 && (group == 64 || group == 128) && head_dim % group == 0;
+}
+}  // namespace
+
+KVQ_API const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration (head_dim must be 128)";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+KVQ_API size_t kvq_page_bytes(int32_t head_dim, int32_t group) {
+  if (head_dim != kvq::kHeadDim || !valid_geometry(head_dim, group)) return 0;
+  return static_cast<size_t>(kvq::page_bytes_for_groups(head_dim / group));
+}
+
+KVQ_API int kvq_append(void* pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t group, const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* start_pos, int32_t batch, int32_t num_new, const void* k,
+                       const void* v, int32_t kv_dtype, const float* mu, const float* rot_k,
+                       const float* rot_v, float clip_k, float clip_v, void* stream) {
+  if (!valid_geometry(head_dim, group)) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (batch < 0 || num_new < 0 || num_kv_heads < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
+    return KVQ_ERR_INVALID_ARG;
+  if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_INVALID_ARG;
+  if (kv_dtype != KVQ_F32 && kv_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
+    return KVQ_ERR_INVALID_ARG;
+  if (batch == 0 || num_new == 0) return KVQ_OK;
+  if (!pages || !block_table || !start_pos || !k || !v || !mu || !rot_k || !rot_v)
+    return KVQ_ERR_INVALID_ARG;
+  if (!aligned(pages, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(mu, 16) ||
+      !aligned(rot_k, 16) || !aligned(rot_v, 16))
+    return KVQ_ERR_INVALID_ARG;
+  const int rc = kvq::launch_append(static_cast<uint8_t*>(pages), num_blocks, num_kv_heads,
+                                    head_dim / group, block_table, max_blocks_per_seq, start_pos,
+                                    batch, num_new, k, v, kv_dtype == KVQ_BF16, mu, rot_k, rot_v,
+                                    clip_k, clip_v, static_cast<hipStream_t>(stream));
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+namespace {
+bool valid_decode_shape(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t max_ctx_len, int32_t split_pages) {
+  if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_q_heads < num_kv_heads) return false;
+  if (num_q_heads % num_kv_heads != 0 || max_ctx_len < 0) return false;
+  if (split_pages < 0 || split_pages % 8 != 0) return false;
+  const int qg = (num_q_heads / num_kv_heads + 3) / 4;
+  if (static_cast<int64_t>(num_kv_heads) * qg > 65535) return false;
+  return true;
+}
+}  // namespace
+
+KVQ_API size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_ctx_len, int32_t split_pages) {
+  if (head_dim != kvq::kHeadDim) return 0;
+  if (!valid_decode_shape(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages)) return 0;
+  return kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages).total;
+}
+
+KVQ_API int kvq_decode_attn_staged(const void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t group, const int32_t* block_table,
+                                   int32_t max_blocks_per_seq, const int32_t* ctx_len,
+                                   int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                                   const void* q, int32_t q_dtype, const float* rot_k,
+                                   const float* rot_v, float sm_scale, float* out,
+                                   void* workspace, size_t workspace_bytes, int32_t split_pages,
+                                   int32_t stages, void* stream) {
+  if (stages < 1 || stages > KVQ_STAGE_ALL) return KVQ_ERR_INVALID_ARG;
+  if (!valid_geometry(head_dim, group)) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (!valid_decode_shape(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages))
+    return KVQ_ERR_INVALID_ARG;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_ctx_len) > static_cast<int64_t>(max_blocks_per_seq) * kvq::kBlock)
+    return KVQ_ERR_INVALID_ARG;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KVQ_ERR_INVALID_ARG;
+  if (batch == 0) return KVQ_OK;
+  if (!pages || !block_table || !ctx_len || !q || !rot_k || !rot_v || !out)
+    return KVQ_ERR_INVALID_ARG;
+  if (!aligned(pages, 16) || !aligned(rot_k, 16) || !aligned(rot_v, 16))
+    return KVQ_ERR_INVALID_ARG;
+  const kvq::DecodePlan plan =
+      kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
+  if (!workspace || workspace_bytes < plan.total || !aligned(workspace, 256))
+    return KVQ_ERR_WORKSPACE;
+  const int rc = kvq::launch_decode(
+      static_cast<const uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
+      max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k,
+      rot_v, sm_scale, out, workspace, plan, stages, static_cast<hipStream_t>(stream));
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+KVQ_API int kvq_decode_attn(const void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t group, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* ctx_len,
+                            int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                            const void* q, int32_t q_dtype, const float* rot_k,
+                            const float* rot_v, float sm_scale, float* out, void* workspace,
+                            size_t workspace_bytes, int32_t split_pages, void* stream) {
+  return kvq_decode_attn_staged(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                                max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q,
+                                q_dtype, rot_k, rot_v, sm_scale, out, workspace, workspace_bytes,
+                                split_pages, KVQ_STAGE_ALL, stream);
+}

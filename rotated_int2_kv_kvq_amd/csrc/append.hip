@@ -1,0 +1,246 @@
+// Cache-append quantiser: centre, rotate, clip, group INT2 round-to-nearest
+// with fp16 scale/zero, pack into the paged cache.
+//
+// Method: "Output-Aware Rotation for INT2 KV-Cache Quantization" (Pith review
+// of arXiv 2608.02691), "What carries the argument" (key centring before
+// rotation; rotation, clipping, grouping, rounding) and "Core claim" (one
+// orthogonal rotation per KV head and layer).
+//
+// Work decomposition.  One workgroup (4 waves) owns one (sequence, KV head)
+// and a run of consecutive pages touched by this call; it stages R_K and R_V
+// in LDS (transposed, columns permuted so that each lane ends up holding 8
+// consecutive rotated channels), then waves 0-1 encode keys and waves 2-3
+// values, alternating pages.  A wave encodes one 16-token page at a time:
+// the 16 x 128 x 128 rotation is 256 fp32 MFMAs (16x16x4), whose output
+// gives lane l tokens 4*(l/16)..+3 and channels 8*(l%16)..+7; group min/max
+// is a 16-lane (or 8-lane) butterfly; codes are packed in registers and
+// written to the page.  Because a page is owned by one wave for the whole
+// call, partially filled V-code bytes are updated read-modify-write without
+// races.
+#include "kvq_common.h"
+#include "kvq_launch.h"
+
+namespace kvq {
+
+constexpr int kRStride = 132;  // LDS row stride (floats) of a staged rotation
+
+template <bool kBf16>
+__device__ __forceinline__ void load_row32(const void* src, size_t elem_off, float (&a)[32]) {
+  if constexpr (kBf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + elem_off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint4 u = p[q];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+        a[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + elem_off);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float4 f = p[q];
+      a[4 * q] = f.x;
+      a[4 * q + 1] = f.y;
+      a[4 * q + 2] = f.z;
+      a[4 * q + 3] = f.w;
+    }
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void append_kernel(
+    uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
+    const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
+    int T, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ mu, const float* __restrict__ rot_k,
+    const float* __restrict__ rot_v, float clip_k, float clip_v, int pages_per_wg) {
+  __shared__ float Bt[2][kHeadDim * kRStride];
+
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const int s0 = start_pos[b];
+  if (s0 < 0) return;
+  const int first_page = s0 / kBlock;
+  const int last_page = (s0 + T - 1) / kBlock;
+  const int wg_first = first_page + blockIdx.x * pages_per_wg;
+  if (wg_first > last_page) return;
+  const int wg_last = min(last_page, wg_first + pages_per_wg - 1);
+
+  // Stage R_K and R_V: LDS row r = 16*(c%8) + c/8 holds column c of R, so the
+  // MFMA output column (tile nt, lane n) is rotated channel 8*n + nt.
+  for (int mat = 0; mat < 2; ++mat) {
+    const float* R = (mat ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim;
+    for (int idx = tid; idx < kHeadDim * kHeadDim / 4; idx += 256) {
+      const int krow = idx >> 5;
+      const int c4 = (idx & 31) * 4;
+      const float4 r = *reinterpret_cast<const float4*>(R + krow * kHeadDim + c4);
+      const float rv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c4 + u;
+        Bt[mat][((c & 7) * 16 + (c >> 3)) * kRStride + krow] = rv[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int mat = wave >> 1;  // 0 = keys, 1 = values
+  const float clip = mat ? clip_v : clip_k;
+  const void* src = mat ? v : k;
+  const int PB = page_bytes_for_groups(G);
+  const int n = lane & 15;   // B/D column lane: channels 8n..8n+7
+  const int kg = lane >> 4;  // A/B k-group: input channels 32kg..32kg+31
+  const int t = lane & 15;   // A row: token slot in the page
+  const int r4 = lane >> 4;  // D rows: tokens 4*r4..4*r4+3
+
+  for (int pg = wg_first + (wave & 1); pg <= wg_last; pg += 2) {
+    if (pg >= max_blocks) break;
+    const int blk = block_table[static_cast<size_t>(b) * max_blocks + pg];
+    if (blk < 0 || blk >= num_blocks) continue;
+    uint8_t* page = pages + (static_cast<int64_t>(blk) * Hkv + h) * PB;
+
+    // A operand: this lane's token row, input channels 32kg..32kg+31 (centred keys).
+    float a[32];
+    const int pos = pg * kBlock + t;
+    const bool row_new = pos >= s0 && pos < s0 + T;
+    if (row_new) {
+      const size_t off = (static_cast<size_t>(b) * T + (pos - s0)) * Hkv * kHeadDim +
+                         static_cast<size_t>(h) * kHeadDim + 32 * kg;
+      load_row32<kBf16>(src, off, a);
+      if (mat == 0) {
+        const float4* m4 = reinterpret_cast<const float4*>(mu + h * kHeadDim + 32 * kg);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 m = m4[q];
+          a[4 * q] -= m.x;
+          a[4 * q + 1] -= m.y;
+          a[4 * q + 2] -= m.z;
+          a[4 * q + 3] -= m.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 32; ++s) a[s] = 0.f;
+    }
+
+    floatx4 acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const float* Bm = Bt[mat];
+#pragma unroll
+    for (int sb = 0; sb < 8; ++sb) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const float4 bv =
+            *reinterpret_cast<const float4*>(Bm + (nt * 16 + n) * kRStride + 32 * kg + 4 * sb);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 0], bv.x, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 1], bv.y, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 2], bv.z, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 3], bv.w, acc[nt], 0, 0, 0);
+      }
+    }
+
+    // Quantise: lane holds tokens 4*r4 + i, channels 8n + nt.
+    uint32_t code_bits[4];  // per token: 16 bits, channel 8n+e at bits 2e
+    const int gl = (G == 2) ? 8 : 16;  // lanes per group
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mn = acc[0][i], mx = acc[0][i];
+#pragma unroll
+      for (int nt = 1; nt < 8; ++nt) {
+        mn = fminf(mn, acc[nt][i]);
+        mx = fmaxf(mx, acc[nt][i]);
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        if (m < gl) {
+          mn = fminf(mn, shfl_xor(mn, m));
+          mx = fmaxf(mx, shfl_xor(mx, m));
+        }
+      }
+      const float lo = clip * mn;
+      const float hi = clip * mx;
+      const _Float16 s16 = f16_sat((hi - lo) / 3.0f);
+      const _Float16 z16 = f16_sat(lo);
+      const float sf = static_cast<float>(s16);
+      const float zf = static_cast<float>(z16);
+      uint32_t bits = 0;
+      if (sf != 0.f) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          float qv = rintf((acc[nt][i] - zf) / sf);
+          qv = fminf(fmaxf(qv, 0.f), 3.f);
+          bits |= static_cast<uint32_t>(qv) << (2 * nt);
+        }
+      }
+      code_bits[i] = bits;
+      const int tq = 4 * r4 + i;
+      const int tpos = pg * kBlock + tq;
+      if (tpos >= s0 && tpos < s0 + T) {
+        if (mat == 0) {
+          *reinterpret_cast<uint16_t*>(page + kKCodeOff + 32 * tq + 2 * n) =
+              static_cast<uint16_t>(bits);
+        }
+        if ((n & (gl - 1)) == 0) {
+          const int gidx = n / gl;
+          const uint32_t sz = static_cast<uint32_t>(f16_bits(s16)) |
+                              (static_cast<uint32_t>(f16_bits(z16)) << 16);
+          *reinterpret_cast<uint32_t*>(page + kSzOff + mat * 64 * G + (tq * G + gidx) * 4) = sz;
+        }
+      }
+    }
+
+    if (mat == 1) {
+      // V chunks: byte (r4 % 2) of chunk (th = r4/2, n' = 8(n%2) + e, j = n/2)
+      // holds tokens 4*r4..4*r4+3 of channel 8n + e.
+      uint32_t newmask = 0;  // 2-bit field mask of new tokens in this quad
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tpos = pg * kBlock + 4 * r4 + i;
+        if (tpos >= s0 && tpos < s0 + T) newmask |= 3u << (2 * i);
+      }
+      if (newmask) {
+        const int th = r4 >> 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t byte = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) byte |= ((code_bits[i] >> (2 * e)) & 3u) << (2 * i);
+          const int np = 8 * (n & 1) + e;
+          const int j = n >> 1;
+          uint8_t* dst = page + kVCodeOff + 2 * ((16 * th + np) * 8 + j) + (r4 & 1);
+          if (newmask != 0xffu) byte = (*dst & ~newmask) | (byte & newmask);
+          *dst = static_cast<uint8_t>(byte);
+        }
+      }
+    }
+  }
+}
+
+int launch_append(uint8_t* pages, int64_t num_blocks, int Hkv, int G, const int* block_table,
+                  int max_blocks, const int* start_pos, int B, int T, const void* k,
+                  const void* v, bool bf16, const float* mu, const float* rot_k,
+                  const float* rot_v, float clip_k, float clip_v, hipStream_t stream) {
+  const int max_pages = (T + kBlock - 1) / kBlock + 1;
+  const int ppw = max_pages <= 2 ? 2 : 16;
+  const dim3 grid((max_pages + ppw - 1) / ppw, Hkv, B);
+  if (bf16)
+    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(256), 0, stream, pages, num_blocks, Hkv, G,
+                       block_table, max_blocks, start_pos, T, k, v, mu, rot_k, rot_v, clip_k,
+                       clip_v, ppw);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(256), 0, stream, pages, num_blocks, Hkv,
+                       G, block_table, max_blocks, start_pos, T, k, v, mu, rot_k, rot_v, clip_k,
+                       clip_v, ppw);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace kvq

@@ -1,0 +1,44 @@
+// Device-side constants and helpers shared by the append and decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 16;          // tokens per page
+constexpr int kKCodeOff = 0;        // 16 rows x 32 bytes
+constexpr int kVCodeOff = 512;      // 64 16-bit chunks
+constexpr int kSzOff = 1024;        // K (scale, zero) pairs, then V pairs
+constexpr float kF16Max = 65504.0f;
+
+__host__ __device__ constexpr int page_bytes_for_groups(int G) { return 1024 + 128 * G; }
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// fp16 of x, round to nearest even, saturating at +-65504.
+__device__ __forceinline__ _Float16 f16_sat(float x) {
+  return static_cast<_Float16>(fminf(fmaxf(x, -kF16Max), kF16Max));
+}
+
+__device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+__device__ __forceinline__ float f16_lo_to_f32(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi_to_f32(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+}  // namespace kvq

@@ -1,0 +1,31 @@
+// Host-side launchers shared between the entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+int launch_append(uint8_t* pages, int64_t num_blocks, int Hkv, int G, const int* block_table,
+                  int max_blocks, const int* start_pos, int B, int T, const void* k,
+                  const void* v, bool bf16, const float* mu, const float* rot_k,
+                  const float* rot_v, float clip_k, float clip_v, hipStream_t stream);
+
+// Workspace carve-up of one decode call.
+struct DecodePlan {
+  int QG;    // query-head tiles of 4 per KV head
+  int spw;   // pages per workgroup split
+  int S;     // splits for the longest context
+  size_t qa_off, qf_off, part_off, total;
+};
+
+DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages);
+
+int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
+                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
+                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
+                  hipStream_t stream);
+
+}  // namespace kvq

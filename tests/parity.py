@@ -1,0 +1,77 @@
+"""Parity rules between the HIP path and the float64 oracle.
+
+The rules make the quantiser's parity operational (readings of "bit-exact
+codes except at elements within 1e-6 relative of a rounding boundary"):
+
+P1  fp16 scale/zero: equal bit for bit, except groups whose float64 value
+    before fp16 rounding lies within 1e-6 relative of an fp16 rounding
+    midpoint ("boundary groups").
+P2  codes: equal to the oracle's codes of the float64 rotated value on the
+    GPU's own stored grid, except elements whose float64 value lies within
+    1e-6 * max(|b|, s16) of a code boundary b = z16 + (j + 1/2) s16; the
+    exempt count must be <= 1e-5 of all elements.
+P3  bytes: the cache is read back through the oracle's layout functions; bytes
+    of slots that were not written keep their previous contents.
+P4  attention: the oracle decodes the GPU's own cache in float64; the max over
+    (sequence, query head) of ||o - o_ref||_inf / ||o_ref||_inf is <= 2e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+REL = 1e-6
+EXEMPT_FRACTION = 1e-5
+ATTN_TOL = 2e-3
+
+
+def fp16_midpoint_distance(raw):
+    """Relative distance of float64 values to the nearest fp16 rounding midpoint."""
+    raw = np.asarray(raw, np.float64)
+    r16 = O.fp16_sat(raw)
+    # neighbours of r16 in fp16
+    up = np.nextafter(r16.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(r16.astype(np.float16), np.float16(-np.inf)).astype(np.float64)
+    mid = np.where(raw >= r16, (r16 + up) / 2, (r16 + dn) / 2)
+    scale = np.maximum(np.abs(mid), np.finfo(np.float16).smallest_subnormal)
+    return np.abs(raw - mid) / scale
+
+
+def check_scale_zero(gpu_s, gpu_z, ref_s, ref_z, raw_s, raw_z):
+    """P1.  Returns (mismatches outside boundary groups, boundary groups)."""
+    ms = gpu_s != ref_s
+    mz = gpu_z != ref_z
+    bs = fp16_midpoint_distance(raw_s) <= REL
+    bz = fp16_midpoint_distance(raw_z) <= REL
+    bad = (ms & ~bs) | (mz & ~bz)
+    boundary = (ms & bs) | (mz & bz)
+    return int(bad.sum()), int(boundary.sum())
+
+
+def check_codes(gpu_codes, x, gpu_s, gpu_z, group):
+    """P2.  Returns (mismatches outside exemptions, exempt elements, elements)."""
+    ref = O.quantize_on_grid(x, gpu_s, gpu_z, group)
+    d = x.shape[-1]
+    G = d // group
+    xg = np.asarray(x, np.float64).reshape(x.shape[:-1] + (G, group))
+    s = np.asarray(gpu_s, np.float64)[..., None]
+    z = np.asarray(gpu_z, np.float64)[..., None]
+    near = np.zeros(xg.shape, bool)
+    for j in range(3):
+        bnd = z + (j + 0.5) * s
+        near |= (np.abs(xg - bnd) <= REL * np.maximum(np.abs(bnd), s)) & (s > 0)
+    near = near.reshape(x.shape)
+    mismatch = np.asarray(gpu_codes) != ref
+    return int((mismatch & ~near).sum()), int(near.sum()), int(mismatch.size)
+
+
+def attention_error(o_gpu, o_ref):
+    """P4 metric: max over rows of ||o - o_ref||_inf / ||o_ref||_inf."""
+    o_gpu = np.asarray(o_gpu, np.float64).reshape(-1, o_gpu.shape[-1])
+    o_ref = np.asarray(o_ref, np.float64).reshape(-1, o_ref.shape[-1])
+    den = np.abs(o_ref).max(-1)
+    num = np.abs(o_gpu - o_ref).max(-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(den > 0, num / np.where(den > 0, den, 1), num)
+    return float(rel.max()) if rel.size else 0.0

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before launching anything
+(no GPU needed: every call here returns before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import rotated_int2_kv_kvq_amd as kvq
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return kvq.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted([
+        "kvq_append", "kvq_decode_attn", "kvq_decode_attn_staged", "kvq_decode_workspace_bytes",
+        "kvq_page_bytes", "kvq_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_page_bytes(lib):
+    import rotated_int2_kv_kvq_amd as kvq
+    assert kvq.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, 7):
+        assert kvq.status_string(s)
+    assert kvq.page_bytes(128, 128) == 1152
+    assert kvq.page_bytes(128, 64) == 1280
+    assert kvq.page_bytes(128, 32) == 0
+    assert kvq.page_bytes(64, 64) == 0
+
+
+def test_workspace_bytes(lib):
+    import rotated_int2_kv_kvq_amd as kvq
+    a = kvq.decode_workspace_bytes(4, 32, 8, 8192)
+    b = kvq.decode_workspace_bytes(64, 32, 8, 32768)
+    assert 0 < a < b
+    assert kvq.decode_workspace_bytes(4, 30, 8, 8192) == 0          # Hq % Hkv
+    assert kvq.decode_workspace_bytes(4, 32, 8, 8192, split_pages=12) == 0
+    assert kvq.decode_workspace_bytes(4, 32, 8, 8192, head_dim=64) == 0
+    assert kvq.decode_workspace_bytes(4, 32, 8, 0) > 0
+    # workspace grows with the number of splits
+    assert kvq.decode_workspace_bytes(1, 32, 8, 131072, split_pages=8) > \
+        kvq.decode_workspace_bytes(1, 32, 8, 131072, split_pages=64)
+
+
+def _append(lib, **kw):
+    args = dict(pages=1 << 20, num_blocks=4, hkv=8, d=128, g=128, table=1 << 21, maxb=4,
+                start=1 << 22, B=1, T=1, k=1 << 23, v=1 << 24, dt=1, mu=1 << 25, rk=1 << 26,
+                rv=1 << 27, ck=0.9, cv=0.9)
+    args.update(kw)
+    return lib.kvq_append(args["pages"], args["num_blocks"], args["hkv"], args["d"], args["g"],
+                          args["table"], args["maxb"], args["start"], args["B"], args["T"],
+                          args["k"], args["v"], args["dt"], args["mu"], args["rk"], args["rv"],
+                          args["ck"], args["cv"], None)
+
+
+def test_append_rejects_invalid_arguments(lib):
+    assert _append(lib, g=32) == -1
+    assert _append(lib, d=64, g=64) == -2
+    assert _append(lib, ck=0.0) == -1
+    assert _append(lib, cv=1.5) == -1
+    assert _append(lib, dt=5) == -1
+    assert _append(lib, hkv=0) == -1
+    assert _append(lib, k=None) == -1
+    assert _append(lib, pages=(1 << 20) + 4) == -1          # misaligned
+    assert _append(lib, B=0) == 0 and _append(lib, T=0) == 0  # no-ops
+
+
+def _decode(lib, **kw):
+    args = dict(pages=1 << 20, nb=4, hkv=8, d=128, g=128, table=1 << 21, maxb=4, ctx=1 << 22,
+                maxctx=64, B=1, hq=32, q=1 << 23, qdt=1, rk=1 << 24, rv=1 << 25, scale=0.088,
+                out=1 << 26, ws=1 << 27, wsb=1 << 30, sp=0)
+    args.update(kw)
+    return lib.kvq_decode_attn(args["pages"], args["nb"], args["hkv"], args["d"], args["g"],
+                               args["table"], args["maxb"], args["ctx"], args["maxctx"], args["B"],
+                               args["hq"], args["q"], args["qdt"], args["rk"], args["rv"],
+                               args["scale"], args["out"], args["ws"], args["wsb"], args["sp"], None)
+
+
+def test_decode_rejects_invalid_arguments(lib):
+    assert _decode(lib, hq=30) == -1
+    assert _decode(lib, maxctx=65) == -1                     # beyond the block table
+    assert _decode(lib, maxctx=-1) == -1
+    assert _decode(lib, qdt=3) == -1
+    assert _decode(lib, sp=4) == -1
+    assert _decode(lib, scale=float("nan")) == -1
+    assert _decode(lib, out=None) == -1
+    assert _decode(lib, d=64, g=64) == -2
+    assert _decode(lib, wsb=16) == -3
+    assert _decode(lib, ws=None) == -3
+    assert _decode(lib, ws=(1 << 27) + 16) == -3             # workspace alignment
+    assert _decode(lib, B=0) == 0
+    # staged variant: stage mask is validated first
+    base = [1 << 20, 4, 8, 128, 128, 1 << 21, 4, 1 << 22, 64, 1, 32, 1 << 23, 1, 1 << 24, 1 << 25,
+            0.088, 1 << 26, 1 << 27, 1 << 30, 0]
+    assert lib.kvq_decode_attn_staged(*base, 0, None) == -1
+    assert lib.kvq_decode_attn_staged(*base, 8, None) == -1
+    bad = list(base)
+    bad[10] = 30
+    assert lib.kvq_decode_attn_staged(*bad, 7, None) == -1

@@ -1,0 +1,274 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Parity rules P1-P4 are defined in tests/parity.py.  Cases are seeded
+synthetic workloads shaped like the pages' setting (Qwen3-8B attention: 32
+query / 8 KV heads, head_dim 128) at sizes the oracle finishes in seconds,
+with ragged tails, multi-call appends and empty contexts; the full-size
+workloads are checked on sampled sequences and heads.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workload import WORKLOADS, scaled
+
+from cases import (append_range, decode, fill_context, host_pages, new_case, oracle_decode,
+                   oracle_encode, query)
+from parity import ATTN_TOL, EXEMPT_FRACTION, attention_error, check_codes, check_scale_zero
+
+pytestmark = pytest.mark.gpu
+
+# Derived bound: q is split into fp16 hi + lo parts (2^-22 relative), products
+# with exact 2-bit codes accumulate in fp32, and p = exp2 is fp32; the worst
+# logit error is ~1e-5 absolute for logits O(100), so outputs agree to ~1e-5.
+TIGHT = 5e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotated_int2_kv_kvq_amd as kvq
+    kvq.lib()
+
+
+W0 = WORKLOADS["single_layer_b1_h8x2_ctx1k_f32"]
+W1 = WORKLOADS["qwen3_8b_b4_ctx8k"]
+W2 = WORKLOADS["qwen3_8b_b64_ctx1k_32k_g64"]
+W3 = WORKLOADS["qwen3_8b_b1_ctx128k_sinks"]
+W4 = WORKLOADS["qwen3_8b_36l_b16_ctx16k_stream"]
+
+SMALL = {
+    "cfg0_full": W0,
+    "cfg1_b4_ctx1000": scaled(W1, ctx_min=1000, ctx_max=1000),
+    "cfg2_b6_ragged_g64": scaled(W2, batch=6, ctx_min=1, ctx_max=700),
+    "cfg3_ctx3000_sinks": scaled(W3, ctx_min=3000, ctx_max=3000),
+    "cfg4_b3_layer5": scaled(W4, batch=3, ctx_min=333, ctx_max=333, layers=6, steps=4),
+}
+
+
+def _append_parity(case, b, start, count):
+    enc = oracle_encode(case, b, start, count)
+    cache, table = host_pages(case, b, start + count)
+    w = case.w
+    tot_bad = tot_near = tot_n = tot_bnd = 0
+    for h in range(w.num_kv_heads):
+        got = O.read_tokens(cache, table, 0, np.arange(start, start + count), h,
+                            w.num_kv_heads, w.group)
+        for kind, xkey in (("k", "x"), ("v", "y")):
+            bad_sz, bnd = check_scale_zero(got[kind + "_s"], got[kind + "_z"], enc[kind + "_s"][:, h],
+                                           enc[kind + "_z"][:, h], enc[kind + "_s_raw"][:, h],
+                                           enc[kind + "_z_raw"][:, h])
+            assert bad_sz == 0, f"{kind} scale/zero mismatch outside boundary groups (h={h})"
+            bad, near, n = check_codes(got[kind + "_codes"], enc[xkey][:, h], got[kind + "_s"],
+                                       got[kind + "_z"], w.group)
+            assert bad == 0, f"{kind} code mismatches outside exemptions: {bad} (h={h})"
+            tot_near += near
+            tot_n += n
+            tot_bnd += bnd
+    return tot_near, tot_n, tot_bnd
+
+
+def _unwritten_unchanged(case):
+    """P3: bytes of token slots never written keep their initial contents."""
+    w = case.w
+    pages = case.pages.cpu().numpy()
+    init = case.initial.cpu().numpy()
+    written = np.zeros(pages.shape[:2] + (16,), bool)  # [block][head][slot]
+    table = case.table.cpu().numpy()
+    for b, n in case.written.items():
+        pos = np.arange(n)
+        written[table[b, pos // 16], :, pos % 16] = True
+    changed_blocks = set()
+    for blk in range(pages.shape[0]):
+        for h in range(w.num_kv_heads):
+            if written[blk, h].all() or not (pages[blk, h] != init[blk, h]).any():
+                continue
+            a = O.read_tokens(pages[blk:blk + 1], np.zeros((1, 1), np.int32), 0, np.arange(16), h,
+                              w.num_kv_heads, w.group)
+            c = O.read_tokens(init[blk:blk + 1], np.zeros((1, 1), np.int32), 0, np.arange(16), h,
+                              w.num_kv_heads, w.group)
+            keep = ~written[blk, h]
+            for key in a:
+                x, y = a[key][keep], c[key][keep]
+                same = (x == y) | (np.isnan(x) & np.isnan(y)) if x.dtype.kind == "f" else x == y
+                assert same.all(), f"unwritten slot changed: block {blk} head {h} {key}"
+            changed_blocks.add(blk)
+    return changed_blocks
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_append_parity_small(name):
+    w = SMALL[name]
+    say(f"[append] {name}")
+    case = new_case(w)
+    fill_context(case, pieces=[5, 11, 1, 16, 37, 200, 64, 1000])
+    torch.cuda.synchronize()
+    near = n = bnd = 0
+    for b in range(w.batch):
+        if case.ctx[b] == 0:
+            continue
+        a, c, d = _append_parity(case, b, 0, int(case.ctx[b]))
+        near += a
+        n += c
+        bnd += d
+    say(f"  elements {n}  exempt {near}  boundary groups {bnd}")
+    assert near <= max(EXEMPT_FRACTION * n, 1)
+    _unwritten_unchanged(case)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_parity_small(name):
+    w = SMALL[name]
+    say(f"[decode] {name}")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    out = decode(case, q).cpu().numpy()
+    pairs = [(b, hq) for b in range(w.batch) for hq in range(w.num_q_heads)]
+    ref = oracle_decode(case, q, pairs)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  max rel err {err:.3e}")
+    assert err <= ATTN_TOL
+    assert err <= TIGHT
+    # split-size invariance (float32 round-off) and determinism
+    for sp in (8, 16, 64):
+        o2 = decode(case, q, split_pages=sp).cpu().numpy()
+        assert attention_error(o2, out) <= 1e-5, sp
+    o3 = decode(case, q).cpu().numpy()
+    assert np.array_equal(o3, out)
+
+
+def test_empty_and_tiny_contexts():
+    w = scaled(W1, batch=8, ctx_min=64, ctx_max=64)
+    say("[edge] ctx 0/1/15/16/17/33/47/64")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    ctx = np.array([0, 1, 15, 16, 17, 33, 47, 64], np.int32)
+    out = decode(case, q, ctx=ctx, max_ctx=64).cpu().numpy()
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    pairs = [(b, hq) for b in range(1, 8) for hq in range(0, 32, 5)]
+    ref = oracle_decode(case, q, pairs, ctx=ctx)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  max rel err {err:.3e}")
+    assert err <= TIGHT
+    # every context empty: zeros
+    z = decode(case, q, ctx=np.zeros(8, np.int32), max_ctx=0).cpu().numpy()
+    assert not z.any()
+
+
+@pytest.mark.parametrize("hg", [1, 2, 3, 8])
+def test_gqa_ratios(hg):
+    w = scaled(W1, batch=2, num_kv_heads=2, num_q_heads=2 * hg, ctx_min=200, ctx_max=200)
+    say(f"[gqa] Hg={hg}")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    out = decode(case, q).cpu().numpy()
+    pairs = [(b, hq) for b in range(2) for hq in range(2 * hg)]
+    ref = oracle_decode(case, q, pairs)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  max rel err {err:.3e}")
+    assert err <= TIGHT
+
+
+def test_degenerate_groups_and_no_ops():
+    """Constant rotated groups store scale 0 and codes 0; empty calls are no-ops."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = scaled(W0, ctx_min=32, ctx_max=32, kv_dtype="f32")
+    say("[edge] degenerate groups")
+    case = new_case(w)
+    dev = case.device
+    k = torch.zeros(1, 20, w.num_kv_heads, 128, device=dev)
+    v = torch.zeros_like(k)
+    k += case.mu  # centred keys are exactly zero
+    v[:, :, :, :] = 0.0
+    sp = torch.tensor([3], dtype=torch.int32, device=dev)
+    kvq.append(case.pages, case.table[:1].contiguous(), sp, k, v, case.mu, case.rot_k, case.rot_v,
+               w.group, w.clip_k, w.clip_v)
+    case.written[0] = 23
+    cache, table = host_pages(case, 0, 23)
+    for h in range(w.num_kv_heads):
+        got = O.read_tokens(cache, table, 0, np.arange(3, 23), h, w.num_kv_heads, w.group)
+        for kind in "kv":
+            assert not got[kind + "_codes"].any()
+            assert np.all(got[kind + "_s"] == 0) and np.all(got[kind + "_z"] == 0)
+    before = case.pages.clone()
+    kvq.append(case.pages, case.table[:1].contiguous(), sp, k[:, :0].contiguous(),
+               v[:, :0].contiguous(), case.mu, case.rot_k, case.rot_v, w.group, w.clip_k, w.clip_v)
+    torch.cuda.synchronize()
+    assert torch.equal(before, case.pages)
+    # slots 0..2 and 23.. untouched
+    case.written = {0: 0}
+    init = case.initial.cpu().numpy()
+    pages = case.pages.cpu().numpy()
+    blk = int(case.table[0, 0])
+    a = O.read_tokens(pages, case.table.cpu().numpy(), 0, np.array([0, 1, 2, 23, 24, 31]), 0,
+                      w.num_kv_heads, w.group)
+    c = O.read_tokens(init, case.table.cpu().numpy(), 0, np.array([0, 1, 2, 23, 24, 31]), 0,
+                      w.num_kv_heads, w.group)
+    assert np.array_equal(a["k_codes"], c["k_codes"]) and np.array_equal(a["v_codes"], c["v_codes"])
+    assert blk >= 0
+
+
+def test_stream_append_then_decode():
+    """Append one token per sequence per step and decode over the updated cache."""
+    w = SMALL["cfg4_b3_layer5"]
+    say("[stream] 4 steps, layer 5")
+    case = new_case(w, layer=5, keep_initial=False)
+    fill_context(case)
+    ctx = case.ctx.copy()
+    for step in range(w.steps):
+        append_range(case, list(range(w.batch)), int(ctx[0]), 1)
+        ctx = ctx + 1
+        q = query(case, step)
+        out = decode(case, q, ctx=ctx).cpu().numpy()
+        pairs = [(b, hq) for b in range(w.batch) for hq in (0, 7, 13, 31)]
+        ref = oracle_decode(case, q, pairs, ctx=ctx)
+        err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+        say(f"  step {step} max rel err {err:.3e}")
+        assert err <= TIGHT
+    near, n, _ = _append_parity(case, 1, int(case.ctx[1]), w.steps)
+    assert near <= max(EXEMPT_FRACTION * n, 1)
+
+
+FULL = {
+    "cfg1_full": (W1, [(0, 0), (3, 31), (2, 17)]),
+    "cfg2_full": (W2, [(0, 0), (17, 9), (63, 31), (40, 4)]),
+    "cfg3_full": (W3, [(0, 0), (0, 13), (0, 31)]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    w, pairs = FULL[name]
+    say(f"[full] {name}")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    out = decode(case, q).cpu().numpy()
+    assert np.isfinite(out).all()
+    ref = oracle_decode(case, q, pairs)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  sampled max rel err {err:.3e}")
+    assert err <= TIGHT
+    # append parity on sampled token ranges of the sampled sequences
+    near = n = 0
+    for b, _ in pairs:
+        L = int(case.ctx[b])
+        for s in (0, L // 2, max(L - 40, 0)):
+            a, c, _ = _append_parity(case, b, s, min(40, L - s))
+            near += a
+            n += c
+    say(f"  sampled elements {n} exempt {near}")
+    assert near <= max(EXEMPT_FRACTION * n, 1)
