@@ -169,8 +169,8 @@ def main():
 
     # ---------------------------------------------------------------- per-kernel event timing
     # Queue every launch behind a GPU sleep so that host launch latency never
-    # falls inside an event interval.  Stage boundaries of one decode are
-    # launched separately; the split kernel sits alone between its events.
+    # falls inside an event interval.  The three decode stages are launched
+    # separately; the split kernel sits alone between its events.
     last = total_steps - 1
     split_ms, app_ms = [], []
     for rep in range(3):

@@ -225,10 +225,128 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// One new token per sequence (the decode-step append).  Workgroup = (KV head,
+// sequence), 256 threads: threads 0-127 own rotated key channel j = tid, threads
+// 128-255 rotated value channel j = tid - 128.  Each computes its channel as a
+// 128-term dot product with column j of R (coalesced across threads), reduces
+// group min/max across the channel's group (one wave for group 64, two waves
+// through LDS for group 128), rounds, and writes: key codes are gathered four
+// to a byte by lane shuffles; each value code goes to its own byte of the
+// transposed value block, updated read-modify-write by the owning thread.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void append_one_kernel(
+    uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
+    const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
+    const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ mu,
+    const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
+    float clip_v) {
+  __shared__ float a_s[2][kHeadDim];
+  __shared__ float red[4][2];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int mat = tid >> 7;
+  const int j = tid & 127;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+
+  const int pos = start_pos[b];
+  if (pos < 0 || pos / kBlock >= max_blocks) return;
+  const int blk = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int PB = page_bytes_for_groups(G);
+  uint8_t* page = pages + (static_cast<int64_t>(blk) * Hkv + h) * PB;
+  const int t = pos % kBlock;
+
+  // the value byte this thread will update (read early; only this thread writes it)
+  const int th = t >> 3, e = t & 7;
+  uint8_t* vdst = page + kVCodeOff + 2 * ((16 * th + (j & 15)) * 8 + (j >> 4)) + (e >> 2);
+  const uint32_t vold = mat ? *vdst : 0u;
+
+  {
+    const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim + j;
+    float x;
+    if constexpr (kBf16)
+      x = bf16_to_f32((mat ? static_cast<const uint16_t*>(v) : static_cast<const uint16_t*>(k))[off]);
+    else
+      x = (mat ? static_cast<const float*>(v) : static_cast<const float*>(k))[off];
+    if (mat == 0) x -= mu[h * kHeadDim + j];
+    a_s[mat][j] = x;
+  }
+  __syncthreads();
+
+  const float* R = (mat ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim + j;
+  const float* a = a_s[mat];
+  float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < kHeadDim; i += 4) {
+    x0 = fmaf(a[i], R[i * kHeadDim], x0);
+    x1 = fmaf(a[i + 1], R[(i + 1) * kHeadDim], x1);
+    x2 = fmaf(a[i + 2], R[(i + 2) * kHeadDim], x2);
+    x3 = fmaf(a[i + 3], R[(i + 3) * kHeadDim], x3);
+  }
+  const float x = (x0 + x1) + (x2 + x3);
+
+  float mn = x, mx = x;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    mn = fminf(mn, shfl_xor(mn, m));
+    mx = fmaxf(mx, shfl_xor(mx, m));
+  }
+  if (G == 1) {  // group of 128 channels spans this thread's two waves
+    if (lane == 0) {
+      red[wave][0] = mn;
+      red[wave][1] = mx;
+    }
+    __syncthreads();
+    const int w0 = wave & ~1;
+    mn = fminf(red[w0][0], red[w0 + 1][0]);
+    mx = fmaxf(red[w0][1], red[w0 + 1][1]);
+  }
+  const float clip = mat ? clip_v : clip_k;
+  const float lo = clip * mn;
+  const float hi = clip * mx;
+  const _Float16 s16 = f16_sat((hi - lo) / 3.0f);
+  const _Float16 z16 = f16_sat(lo);
+  const float sf = static_cast<float>(s16);
+  const float zf = static_cast<float>(z16);
+  uint32_t code = 0;
+  if (sf != 0.f) code = static_cast<uint32_t>(fminf(fmaxf(rintf((x - zf) / sf), 0.f), 3.f));
+
+  if (mat == 0) {
+    uint32_t byte = code << (2 * (j & 3));
+    byte |= shfl_xor(byte, 1);
+    byte |= shfl_xor(byte, 2);
+    if ((j & 3) == 0) page[kKCodeOff + 32 * t + (j >> 2)] = static_cast<uint8_t>(byte);
+  } else {
+    const int sh = 2 * (e & 3);
+    *vdst = static_cast<uint8_t>((vold & ~(3u << sh)) | (code << sh));
+  }
+  const int gl = G == 2 ? 64 : 128;
+  if ((j & (gl - 1)) == 0) {
+    const uint32_t sz = static_cast<uint32_t>(f16_bits(s16)) |
+                        (static_cast<uint32_t>(f16_bits(z16)) << 16);
+    *reinterpret_cast<uint32_t*>(page + kSzOff + mat * 64 * G + (t * G + j / gl) * 4) = sz;
+  }
+}
+
 int launch_append(uint8_t* pages, int64_t num_blocks, int Hkv, int G, const int* block_table,
                   int max_blocks, const int* start_pos, int B, int T, const void* k,
                   const void* v, bool bf16, const float* mu, const float* rot_k,
                   const float* rot_v, float clip_k, float clip_v, hipStream_t stream) {
+  if (T == 1) {
+    const dim3 grid(Hkv, B);
+    if (bf16)
+      hipLaunchKernelGGL(append_one_kernel<true>, grid, dim3(256), 0, stream, pages, num_blocks,
+                         Hkv, G, block_table, max_blocks, start_pos, k, v, mu, rot_k, rot_v,
+                         clip_k, clip_v);
+    else
+      hipLaunchKernelGGL(append_one_kernel<false>, grid, dim3(256), 0, stream, pages, num_blocks,
+                         Hkv, G, block_table, max_blocks, start_pos, k, v, mu, rot_k, rot_v,
+                         clip_k, clip_v);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int max_pages = (T + kBlock - 1) / kBlock + 1;
   const int ppw = max_pages <= 2 ? 2 : 16;
   const dim3 grid((max_pages + ppw - 1) / ppw, Hkv, B);

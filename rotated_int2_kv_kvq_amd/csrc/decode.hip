@@ -11,17 +11,21 @@
 //   1. prologue: q_r = q * R_K[h], scaled by sm_scale*log2(e) and a power of
 //      two, split into fp16 hi + 2^11*lo parts laid out as the A operand of the
 //      q.K MFMA (rows = 4 query heads x {hi, lo} x {channel half}).
-//   2. split: each wave streams 2-page chunks of one (sequence, KV head);
-//      q.K and P.V both run on 16x16x32 f16 MFMAs.  Cached 2-bit codes become
-//      MFMA operands through the FP4 (e2m1) to f16 conversion: masking a code
-//      word with 0x33333333 leaves one code in the low bits of every nibble,
-//      and such a nibble decodes to exactly code/2, a normal fp16 value.
-//      (fp16 subnormal operands are not an option: MFMA products with them
-//      accumulate at roughly 2^-16 of the magnitude sum, normal ones at 2^-24.)
-//      The four waves of a workgroup interleave chunks and combine their
-//      (max, sum, output) in LDS, so each workgroup writes one partial per
-//      query head.
-//   3. merge: log-sum-exp merge of the partials, then o = o_r * R_V^T.
+//   2. scan: each wave streams 2-page chunks of one (sequence, KV head) through
+//      an LDS ring filled by global->LDS DMA; q.K and P.V both run on 16x16x32
+//      f16 MFMAs.  Cached 2-bit codes become MFMA operands through the FP4
+//      (e2m1) to f16 conversion: masking a code word with 0x33333333 leaves one
+//      code in the low bits of every nibble, and such a nibble decodes to
+//      exactly code/2, a normal fp16 value.  (fp16 subnormal operands are not
+//      an option: MFMA products with them accumulate at roughly 2^-16 of the
+//      magnitude sum, normal ones at 2^-24.)  The four waves of a workgroup
+//      interleave chunks and combine their (max, sum, output) in LDS; each
+//      workgroup writes one partial per query head.
+//   3. merge: log-sum-exp merge of the partials and the inverse value
+//      rotation o = o_r * R_V^T.  (A separate launch: merging inside the scan
+//      through a last-workgroup counter needs device-scope release/acquire,
+//      i.e. an L2 writeback and invalidate per workgroup on this multi-XCD
+//      part, which costs far more than the launch.)
 #include "kvq_common.h"
 #include "kvq_launch.h"
 
@@ -53,6 +57,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
   const int hl = threadIdx.x >> 6;
   const int hloc = qg * kHT + hl;
   const bool valid = hloc < Hg;
+
   const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + hloc) * kHeadDim;
   float q0 = 0.f, q1 = 0.f;
   if (valid) {
@@ -74,6 +79,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
   const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim;
   float r0 = 0.f, r1 = 0.f;
   if (valid) {
+#pragma unroll 16
     for (int i = 0; i < kHeadDim; ++i) {
       const float qi = qin[hl][i];
       r0 = fmaf(qi, R[i * kHeadDim + lane], r0);
@@ -159,37 +165,112 @@ struct Chunk {
   int pg0;
 };
 
-template <int G>
-__device__ __forceinline__ uint2 load_sz(const uint8_t* p) {
-  if constexpr (G == 2) {
-    return *reinterpret_cast<const uint2*>(p);
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    return make_uint2(w, w);
-  }
+// ---- LDS ring: each wave keeps kDepth 2-page chunks in flight, loaded with
+// global->LDS DMA (no VGPRs held while in flight).  A slot holds the two page
+// images exactly as laid out in the cache: codes [0, 1024) and (scale, zero)
+// pairs [1024, 1024 + 128G).  One chunk is kDmaPerChunk DMA instructions.
+constexpr int kDepth = 3;
+constexpr int kRing = kDepth + 1;
+constexpr int kDmaPerChunk = 4;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
+// The compiler does not track when an LDS DMA lands: waits are explicit, and
+// the memory clobber keeps LDS reads and DMA issues on their side of them.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int G>
-__device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* __restrict__ pages,
-                                           int64_t num_blocks, int Hkv, int h,
-                                           const int* __restrict__ row, int pg0, int p_end,
-                                           int lane) {
+__device__ __forceinline__ void issue_chunk(uint8_t* slot, const uint8_t* __restrict__ pages,
+                                            int64_t num_blocks, int Hkv, int h,
+                                            const int* __restrict__ row, int pg0, int p_end,
+                                            int lane) {
   constexpr int PB = page_bytes_for_groups(G);
-  const int t = lane & 15, kg = lane >> 4;
   int b0 = row[pg0];
   int b1 = (pg0 + 1 < p_end) ? row[pg0 + 1] : b0;
   b0 = static_cast<int>(min(static_cast<int64_t>(static_cast<uint32_t>(b0)), num_blocks - 1));
   b1 = static_cast<int>(min(static_cast<int64_t>(static_cast<uint32_t>(b1)), num_blocks - 1));
   const uint8_t* p0 = pages + (static_cast<int64_t>(b0) * Hkv + h) * PB;
   const uint8_t* p1 = pages + (static_cast<int64_t>(b1) * Hkv + h) * PB;
-  c.kc0 = *reinterpret_cast<const uint2*>(p0 + kKCodeOff + 32 * t + 8 * kg);
-  c.kc1 = *reinterpret_cast<const uint2*>(p1 + kKCodeOff + 32 * t + 8 * kg);
-  const uint8_t* pv = (kg >> 1) ? p1 : p0;
-  c.vc = *reinterpret_cast<const uint4*>(pv + kVCodeOff + 256 * (kg & 1) + 16 * t);
-  c.szk0 = load_sz<G>(p0 + kSzOff + t * 4 * G);
-  c.szk1 = load_sz<G>(p1 + kSzOff + t * 4 * G);
-  c.szv0 = load_sz<G>(p0 + kSzOff + 64 * G + t * 4 * G);
-  c.szv1 = load_sz<G>(p1 + kSzOff + 64 * G + t * 4 * G);
+  dma16(p0 + 16 * lane, slot);
+  dma16(p1 + 16 * lane, slot + PB);
+  if (G == 2 || lane < 32) {
+    dma4(p0 + kSzOff + 4 * lane, slot + kSzOff);
+    dma4(p1 + kSzOff + 4 * lane, slot + PB + kSzOff);
+  }
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
+}
+
+// Read this lane's share of one ring slot.  The reads are inline assembly so
+// that the compiler's wait insertion, which cannot tell ring slots apart and
+// would drain every pending DMA before any LDS read, does not see them; the
+// caller has already waited for this slot's DMAs, and the block ends with
+// lgkmcnt(0) so its results are complete when it returns.
+template <int G>
+__device__ __forceinline__ void read_chunk(Chunk& c, const uint8_t* slot, int pg0, int lane) {
+  constexpr int PB = page_bytes_for_groups(G);
+  const int t = lane & 15, kg = lane >> 4;
+  const uint32_t ak = lds_addr(slot + kKCodeOff + 32 * t + 8 * kg);
+  const uint32_t av = lds_addr(slot + (kg >> 1) * PB + kVCodeOff + 256 * (kg & 1) + 16 * t);
+  const uint32_t as = lds_addr(slot + kSzOff + t * 4 * G);
+  u32x2 k0, k1;
+  u32x4 v;
+  if constexpr (G == 2) {
+    u32x2 s0, s1, s2, s3;
+    asm volatile(
+        "ds_read_b64 %0, %7\n"
+        "ds_read_b64 %1, %7 offset:%10\n"
+        "ds_read_b128 %2, %8\n"
+        "ds_read_b64 %3, %9\n"
+        "ds_read_b64 %4, %9 offset:%10\n"
+        "ds_read_b64 %5, %9 offset:%11\n"
+        "ds_read_b64 %6, %9 offset:%12\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(v), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+        : "v"(ak), "v"(av), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
+        : "memory");
+    c.szk0 = make_uint2(s0.x, s0.y);
+    c.szk1 = make_uint2(s1.x, s1.y);
+    c.szv0 = make_uint2(s2.x, s2.y);
+    c.szv1 = make_uint2(s3.x, s3.y);
+  } else {
+    uint32_t s0, s1, s2, s3;
+    asm volatile(
+        "ds_read_b64 %0, %7\n"
+        "ds_read_b64 %1, %7 offset:%10\n"
+        "ds_read_b128 %2, %8\n"
+        "ds_read_b32 %3, %9\n"
+        "ds_read_b32 %4, %9 offset:%10\n"
+        "ds_read_b32 %5, %9 offset:%11\n"
+        "ds_read_b32 %6, %9 offset:%12\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(v), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+        : "v"(ak), "v"(av), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
+        : "memory");
+    c.szk0 = make_uint2(s0, s0);
+    c.szk1 = make_uint2(s1, s1);
+    c.szv0 = make_uint2(s2, s2);
+    c.szv1 = make_uint2(s3, s3);
+  }
+  c.kc0 = make_uint2(k0.x, k0.y);
+  c.kc1 = make_uint2(k1.x, k1.y);
+  c.vc = make_uint4(v.x, v.y, v.z, v.w);
   c.pg0 = pg0;
 }
 
@@ -198,20 +279,30 @@ struct SoftmaxState {
   floatx4 acc[8];
 };
 
+// Reductions over the 16 lanes of a DPP row (all lanes of one query head):
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, shfl_xor(v, 1));
-  v = fmaxf(v, shfl_xor(v, 2));
-  v = fmaxf(v, shfl_xor(v, 4));
-  v = fmaxf(v, shfl_xor(v, 8));
+  v = fmaxf(v, dpp<0xb1>(v));
+  v = fmaxf(v, dpp<0x4e>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-  v += shfl_xor(v, 1);
-  v += shfl_xor(v, 2);
-  v += shfl_xor(v, 4);
-  v += shfl_xor(v, 8);
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
   return v;
 }
+
+// 2^x on the hardware exp unit; arguments here are <= 0 (or -inf -> 0)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int G>
 __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
@@ -255,7 +346,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
   const float mc = row16_max(fmaxf(l0, l1));
   const float mnew = fmaxf(st.m, mc);
   if (__any(mnew > st.m)) {
-    const float alpha = exp2f(st.m - mnew);
+    const float alpha = exp2_hw(st.m - mnew);
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
     st.l *= alpha;
@@ -263,8 +354,8 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
     st.zs1 *= alpha;
     st.m = mnew;
   }
-  const float p0 = v0 ? exp2f(l0 - st.m) : 0.f;
-  const float p1 = v1 ? exp2f(l1 - st.m) : 0.f;
+  const float p0 = v0 ? exp2_hw(l0 - st.m) : 0.f;
+  const float p1 = v1 ? exp2_hw(l1 - st.m) : 0.f;
   st.l += p0 + p1;
   const float sv00 = f16_lo_to_f32(c.szv0.x), zv00 = f16_hi_to_f32(c.szv0.x);
   const float sv01 = f16_lo_to_f32(c.szv0.y), zv01 = f16_hi_to_f32(c.szv0.y);
@@ -281,21 +372,45 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
   const int kk = 8 * (t >> 3) + 4 * (e >> 2) + 2 * (e & 1) + ((e >> 1) & 1);
   const float w[2][2] = {{v0 ? p0 * sv00 : 0.f, v0 ? p0 * sv01 : 0.f},
                          {v1 ? p1 * sv10 : 0.f, v1 ? p1 * sv11 : 0.f}};
+  uint32_t hv[2][2], lv[2][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const _Float16 hi = static_cast<_Float16>(w[p][g]);
       const _Float16 lo = static_cast<_Float16>((w[p][g] - static_cast<float>(hi)) * kLoScale);
-      const int row = 4 * hl + 2 * g;
-      atile[row * 32 + 16 * p + kk] = hi;
-      atile[(row + 1) * 32 + 16 * p + kk] = lo;
+      hv[p][g] = f16_bits(hi);
+      lv[p][g] = f16_bits(lo);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const half8 aw = *reinterpret_cast<const half8*>(atile + (lane & 15) * 32 + 8 * (lane >> 4));
+  // Tile rows are 64 bytes (32 k slots); row 4hl + 2g + part, column 16p + kk.
+  // Inline assembly keeps the compiler from draining the ring DMAs before
+  // these accesses; LDS operations of one wave execute in order, so the read
+  // sees the writes.
+  const uint32_t wa = lds_addr(reinterpret_cast<const uint8_t*>(atile)) + 256 * hl + 2 * kk;
+  asm volatile(
+      "ds_write_b16 %0, %1\n"
+      "ds_write_b16 %0, %2 offset:64\n"
+      "ds_write_b16 %0, %3 offset:128\n"
+      "ds_write_b16 %0, %4 offset:192\n"
+      "ds_write_b16 %0, %5 offset:32\n"
+      "ds_write_b16 %0, %6 offset:96\n"
+      "ds_write_b16 %0, %7 offset:160\n"
+      "ds_write_b16 %0, %8 offset:224"
+      :
+      : "v"(wa), "v"(hv[0][0]), "v"(lv[0][0]), "v"(hv[0][1]), "v"(lv[0][1]), "v"(hv[1][0]),
+        "v"(lv[1][0]), "v"(hv[1][1]), "v"(lv[1][1])
+      : "memory");
+  const uint32_t ra =
+      lds_addr(reinterpret_cast<const uint8_t*>(atile)) + 64 * (lane & 15) + 16 * (lane >> 4);
+  u32x4 awv;
+  asm volatile(
+      "ds_read_b128 %0, %1\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(awv)
+      : "v"(ra)
+      : "memory");
+  const half8 aw = __builtin_bit_cast(half8, awv);
 
   // ---- P.V: D[m][channel 16j + n]; dword j/2 holds the chunks of MFMAs j
   // (bytes 0-1) and j+1 (bytes 2-3), token e of a chunk at bits 2e.
@@ -310,6 +425,71 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
   }
 }
 
+// ---- merge: log-sum-exp merge of the ns partials of the nh query heads of
+// one head tile, then o = o_r * R_V[h]^T.  grid (Hkv * QG, B), block 256.
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
+                                                    const int* __restrict__ ctx_len, int max_ctx,
+                                                    int Hq, int Hkv, int QG, int spw, int S,
+                                                    const float* __restrict__ rot_v,
+                                                    float* __restrict__ out) {
+  __shared__ float orow[kHT * kHeadDim];
+  const int h = blockIdx.x / QG;
+  const int qg = blockIdx.x % QG;
+  const int b = blockIdx.y;
+  const int Hg = Hq / Hkv;
+  const int nh = min(kHT, Hg - qg * kHT);
+  const int ctx = min(max(ctx_len[b], 0), max_ctx);
+  const int ns = ((ctx + kBlock - 1) / kBlock + spw - 1) / spw;
+  const int u = threadIdx.x >> 6;
+  const int c = threadIdx.x & 63;
+  if (ns == 0) {  // empty context: zero output
+    if (u < nh) {
+      float* o = out + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * kHeadDim;
+      o[c] = 0.f;
+      o[c + 64] = 0.f;
+    }
+    return;
+  }
+  if (u < nh) {
+    const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * S * kPartStride;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * kPartStride]);
+    float W = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float a = exp2_hw(p[s * kPartStride] - M);
+      W += a;
+      a0 = fmaf(a, p[s * kPartStride + 4 + c], a0);
+      a1 = fmaf(a, p[s * kPartStride + 4 + c + 64], a1);
+    }
+    const float inv = 1.0f / W;
+    orow[u * kHeadDim + c] = a0 * inv;
+    orow[u * kHeadDim + c + 64] = a1 * inv;
+  }
+  __syncthreads();
+  // thread -> (output channel j = tid/2, half of the input channels)
+  const int j = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const float4* R = reinterpret_cast<const float4*>(
+      rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim + 64 * half);
+  float o[kHT] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i4 = 0; i4 < 16; ++i4) {
+    const float4 r = R[i4];
+    const int i = 64 * half + 4 * i4;
+#pragma unroll
+    for (int uu = 0; uu < kHT; ++uu) {
+      const float* orr = orow + uu * kHeadDim + i;
+      o[uu] = fmaf(orr[0], r.x, fmaf(orr[1], r.y, fmaf(orr[2], r.z, fmaf(orr[3], r.w, o[uu]))));
+    }
+  }
+#pragma unroll
+  for (int uu = 0; uu < kHT; ++uu) {
+    const float tot = o[uu] + __shfl_xor(o[uu], 1, 64);
+    if (half == 0 && uu < nh)
+      out[(static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + uu) * kHeadDim + j] = tot;
+  }
+}
+
 // grid (S, Hkv * QG, B), block 256: workgroup x covers pages [x*spw, (x+1)*spw).
 template <int G>
 __global__ __launch_bounds__(256) void split_kernel(
@@ -317,16 +497,17 @@ __global__ __launch_bounds__(256) void split_kernel(
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
     int max_ctx, int Hq, int QG, int spw, const uint4* __restrict__ qa,
     const float4* __restrict__ qf, float* __restrict__ part, int S) {
+  constexpr int kSlot = 2 * page_bytes_for_groups(G);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
   __shared__ __attribute__((aligned(16))) _Float16 atile[4][2][16 * 32];
   __shared__ float cm[4][kHT], cl[4][kHT];
-  __shared__ float co[4][kHT][kHeadDim];
 
   const int h = blockIdx.y / QG;
   const int qg = blockIdx.y % QG;
   const int b = blockIdx.z;
   const int wgs = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ctx = min(max(ctx_len[b], 0), max_ctx);
   const int n_pages = (ctx + kBlock - 1) / kBlock;
   const int p_begin = wgs * spw;
@@ -334,7 +515,9 @@ __global__ __launch_bounds__(256) void split_kernel(
   const int p_end = min(p_begin + spw, n_pages);
   const int n_chunks = (p_end - p_begin + 1) >> 1;
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
-
+  // this wave's chunks: c_i = wave + 4i
+  const int nc = wave < n_chunks ? (n_chunks - wave + 3) / 4 : 0;
+  // query operand first: waiting for it must not drain the ring's DMAs
   const size_t hgi = (static_cast<size_t>(b) * Hkv + h) * QG + qg;
   const uint4* qap = qa + (hgi * 64 + lane) * 4;
   half8 qA[4];
@@ -342,6 +525,14 @@ __global__ __launch_bounds__(256) void split_kernel(
   for (int j = 0; j < 4; ++j) qA[j] = __builtin_bit_cast(half8, qap[j]);
   const int hl = lane >> 4;
   const float4 fq = qf[hgi * kHT + hl];
+  // consume them here, so the wait for these loads is placed before the DMAs
+  asm volatile("" ::"v"(qA[0]), "v"(qA[1]), "v"(qA[2]), "v"(qA[3]), "v"(fq.x), "v"(fq.y),
+               "v"(fq.z));
+
+  uint8_t* myring = &ring[wave][0][0];
+  for (int i = 0; i < kDepth && i < nc; ++i)
+    issue_chunk<G>(myring + i * kSlot, pages, num_blocks, Hkv, h, row,
+                   p_begin + 2 * (wave + 4 * i), p_end, lane);
 
   SoftmaxState st;
   st.m = -INFINITY;
@@ -351,20 +542,23 @@ __global__ __launch_bounds__(256) void split_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  Chunk ca, cb;
-  int c = wave;
-  if (c < n_chunks)
-    load_chunk<G>(ca, pages, num_blocks, Hkv, h, row, p_begin + 2 * c, p_end, lane);
-  while (c < n_chunks) {
-    if (c + 4 < n_chunks)
-      load_chunk<G>(cb, pages, num_blocks, Hkv, h, row, p_begin + 2 * (c + 4), p_end, lane);
-    compute_chunk<G>(ca, st, qA, fq.x, fq.y, fq.z, ctx, p_end, lane, atile[wave][0]);
-    c += 4;
-    if (c >= n_chunks) break;
-    if (c + 4 < n_chunks)
-      load_chunk<G>(ca, pages, num_blocks, Hkv, h, row, p_begin + 2 * (c + 4), p_end, lane);
-    compute_chunk<G>(cb, st, qA, fq.x, fq.y, fq.z, ctx, p_end, lane, atile[wave][1]);
-    c += 4;
+  for (int i = 0; i < nc; ++i) {
+    if (i + kDepth < nc)
+      issue_chunk<G>(myring + ((i + kDepth) % kRing) * kSlot, pages, num_blocks, Hkv, h, row,
+                     p_begin + 2 * (wave + 4 * (i + kDepth)), p_end, lane);
+    // chunk i has landed once at most the DMAs of the chunks behind it are pending
+    const int behind = min(kDepth, nc - 1 - i);
+    if (behind >= 3)
+      wait_vmem<3 * kDmaPerChunk>();
+    else if (behind == 2)
+      wait_vmem<2 * kDmaPerChunk>();
+    else if (behind == 1)
+      wait_vmem<kDmaPerChunk>();
+    else
+      wait_vmem<0>();
+    Chunk c;
+    read_chunk<G>(c, myring + (i % kRing) * kSlot, p_begin + 2 * (wave + 4 * i), lane);
+    compute_chunk<G>(c, st, qA, fq.x, fq.y, fq.z, ctx, p_end, lane, atile[wave][i & 1]);
   }
 
   // ---- per-wave finish: reduce row sums, form unnormalised outputs
@@ -372,6 +566,8 @@ __global__ __launch_bounds__(256) void split_kernel(
   const float zs0 = row16_sum(st.zs0);
   const float zs1 = row16_sum(st.zs1);
   const int n = lane & 15;
+  __syncthreads();  // every wave is done with its ring; reuse it for the combine
+  float(*co)[kHT][kHeadDim] = reinterpret_cast<float(*)[kHT][kHeadDim]>(&ring[0][0][0]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int g = j >> 2;
@@ -391,14 +587,15 @@ __global__ __launch_bounds__(256) void split_kernel(
   const int cc = threadIdx.x & 63;
   const int hloc = qg * kHT + ch;
   const int Hg = Hq / Hkv;
-  if (hloc < Hg) {
+  const int nh = min(kHT, Hg - qg * kHT);
+  if (ch < nh) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w][ch]);
     float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float a = (cm[w][ch] == -INFINITY) ? 0.f : exp2f(cm[w][ch] - M);
+      const float a = (cm[w][ch] == -INFINITY) ? 0.f : exp2_hw(cm[w][ch] - M);
       L += a * cl[w][ch];
       o0 += a * co[w][ch][cc];
       o1 += a * co[w][ch][cc + 64];
@@ -411,62 +608,6 @@ __global__ __launch_bounds__(256) void split_kernel(
     if (cc == 0) dst[0] = M + __log2f(L);
   }
 }
-
-// --------------------------------------------------------------------------- merge
-// grid (Hkv, B), block 128: thread j = output channel.
-constexpr int kMergeHeads = 8;
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part,
-                                                    const int* __restrict__ ctx_len, int max_ctx,
-                                                    int Hq, int Hkv, int spw, int S,
-                                                    const float* __restrict__ rot_v,
-                                                    float* __restrict__ out) {
-  __shared__ float orow[kMergeHeads][kHeadDim];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int j = threadIdx.x;
-  const int Hg = Hq / Hkv;
-  const int ctx = min(max(ctx_len[b], 0), max_ctx);
-  const int n_pages = (ctx + kBlock - 1) / kBlock;
-  const int ns = (n_pages + spw - 1) / spw;
-  const float* R = rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim;
-  for (int h0 = 0; h0 < Hg; h0 += kMergeHeads) {
-    const int nh = min(kMergeHeads, Hg - h0);
-    for (int u = 0; u < nh; ++u) {
-      const int hq = h * Hg + h0 + u;
-      const float* p = part + (static_cast<size_t>(b) * Hq + hq) * S * kPartStride;
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * kPartStride]);
-      float W = 0.f, acc = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float a = exp2f(p[s * kPartStride] - M);
-        W += a;
-        acc = fmaf(a, p[s * kPartStride + 4 + j], acc);
-      }
-      orow[u][j] = ns ? acc / W : 0.f;
-    }
-    __syncthreads();
-    // o[j] = sum_i o_r[i] * R_V[j][i]
-    float o[kMergeHeads];
-#pragma unroll
-    for (int u = 0; u < kMergeHeads; ++u) o[u] = 0.f;
-    for (int i = 0; i < kHeadDim; i += 4) {
-      const float4 r = *reinterpret_cast<const float4*>(R + i);
-#pragma unroll
-      for (int u = 0; u < kMergeHeads; ++u) {
-        if (u < nh) {
-          o[u] = fmaf(orow[u][i], r.x, o[u]);
-          o[u] = fmaf(orow[u][i + 1], r.y, o[u]);
-          o[u] = fmaf(orow[u][i + 2], r.z, o[u]);
-          o[u] = fmaf(orow[u][i + 3], r.w, o[u]);
-        }
-      }
-    }
-    for (int u = 0; u < nh; ++u)
-      out[(static_cast<size_t>(b) * Hq + h * Hg + h0 + u) * kHeadDim + j] = o[u];
-    __syncthreads();
-  }
-}
-
 // --------------------------------------------------------------------------- host side
 
 
@@ -529,8 +670,8 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          p.S);
   }
   if (stages & 4)
-    hipLaunchKernelGGL(merge_kernel, dim3(Hkv, B), dim3(128), 0, stream, part, ctx_len, max_ctx,
-                       Hq, Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
+    hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(256), 0, stream, part, ctx_len,
+                       max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
