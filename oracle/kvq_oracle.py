@@ -35,9 +35,11 @@ Cache layout (ours; the pages only say the paged KV-cache format is kept,
 [num_blocks][Hkv][page_bytes], 16 tokens per block, head_dim 128, G = 128/group:
     [0, 512)        K codes, token-row major: token t, channel i at byte
                     32*t + i//4, bits 2*(i%4)
-    [512, 1024)     V codes, 64 little-endian 16-bit chunks; chunk
-                    (th, n, j) = tokens 8*th..8*th+7 of channel 16*j + n, at
-                    byte offset 2*((16*th + n)*8 + j); token 8*th+e at bit 2*e
+    [512, 1024)     V codes, 128 little-endian 32-bit words; word
+                    (th, n, q) holds tokens 8*th..8*th+7 of channels
+                    16*(2q+s) + n, s in {0, 1}, at byte offset
+                    512 + 4*((16*th + n)*4 + q); token 8*th+e of channel tile
+                    2q+s at code position u = (3e + 8s) mod 16 (bits 2u)
     [1024, +64G)    K fp16 (scale, zero) pairs, [token][group]
     [.., +64G)      V fp16 (scale, zero) pairs, [token][group]
 """
@@ -163,8 +165,9 @@ def v_code_site(t, i):
     i = np.asarray(i)
     th, e = t // 8, t % 8
     j, n = i // 16, i % 16
-    chunk = (16 * th + n) * 8 + j
-    return 512 + 2 * chunk + e // 4, 2 * (e % 4)
+    q, s = j // 2, j % 2
+    u = (3 * e + 8 * s) % 16
+    return 512 + 4 * ((16 * th + n) * 4 + q) + u // 4, 2 * (u % 4)
 
 
 def sz_site(t, gidx, group: int, which: str):

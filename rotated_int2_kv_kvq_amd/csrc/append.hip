@@ -15,7 +15,7 @@
 // gives lane l tokens 4*(l/16)..+3 and channels 8*(l%16)..+7; group min/max
 // is a 16-lane (or 8-lane) butterfly; codes are packed in registers and
 // written to the page.  Because a page is owned by one wave for the whole
-// call, partially filled V-code bytes are updated read-modify-write without
+// call, partially filled V-code words are updated read-modify-write without
 // races.
 #include "kvq_common.h"
 #include "kvq_launch.h"
@@ -199,26 +199,38 @@ __global__ __launch_bounds__(256) void append_kernel(
     }
 
     if (mat == 1) {
-      // V chunks: byte (r4 % 2) of chunk (th = r4/2, n' = 8(n%2) + e, j = n/2)
-      // holds tokens 4*r4..4*r4+3 of channel 8n + e.
-      uint32_t newmask = 0;  // 2-bit field mask of new tokens in this quad
+      // V words: word (th, ch16 = c % 16, q = c / 32) holds tokens 8*th..8*th+7 of
+      // channel tiles 2q and 2q+1; token e of tile 2q+s at code position
+      // (3e + 8s) mod 16.  This lane holds tokens e = 4*(r4 % 2) + i of
+      // channels 8n + e' (tile n/2, s = (n/2) % 2); lane ^ 16 holds the other
+      // four tokens and lane ^ 2 the other tile of the same words, so the four
+      // quarters are combined before one lane writes each word.
+      const int th = r4 >> 1;
+      const int s = (n >> 1) & 1;
+      uint32_t newq = 0;  // which of this lane's tokens are new
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tpos = pg * kBlock + 4 * r4 + i;
-        if (tpos >= s0 && tpos < s0 + T) newmask |= 3u << (2 * i);
+        if (tpos >= s0 && tpos < s0 + T) newq |= 1u << i;
       }
-      if (newmask) {
-        const int th = r4 >> 1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t byte = 0;
+      for (int e = 0; e < 8; ++e) {
+        uint32_t word = 0, mask = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) byte |= ((code_bits[i] >> (2 * e)) & 3u) << (2 * i);
-          const int np = 8 * (n & 1) + e;
-          const int j = n >> 1;
-          uint8_t* dst = page + kVCodeOff + 2 * ((16 * th + np) * 8 + j) + (r4 & 1);
-          if (newmask != 0xffu) byte = (*dst & ~newmask) | (byte & newmask);
-          *dst = static_cast<uint8_t>(byte);
+        for (int i = 0; i < 4; ++i) {
+          const int u = (3 * (4 * (r4 & 1) + i) + 8 * s) & 15;
+          word |= ((code_bits[i] >> (2 * e)) & 3u) << (2 * u);
+          if (newq & (1u << i)) mask |= 3u << (2 * u);
+        }
+        word |= shfl_xor(word, 16);
+        mask |= shfl_xor(mask, 16);
+        word |= shfl_xor(word, 2);
+        mask |= shfl_xor(mask, 2);
+        if ((r4 & 1) == 0 && (n & 2) == 0 && mask != 0) {
+          const int ch16 = 8 * (n & 1) + e;
+          uint32_t* dst = reinterpret_cast<uint32_t*>(page + kVCodeOff +
+                                                      4 * ((16 * th + ch16) * 4 + (n >> 2)));
+          *dst = (mask == 0xffffffffu) ? word : ((*dst & ~mask) | (word & mask));
         }
       }
     }
@@ -232,8 +244,8 @@ __global__ __launch_bounds__(256) void append_kernel(
 // 128-term dot product with column j of R (coalesced across threads), reduces
 // group min/max across the channel's group (one wave for group 64, two waves
 // through LDS for group 128), rounds, and writes: key codes are gathered four
-// to a byte by lane shuffles; each value code goes to its own byte of the
-// transposed value block, updated read-modify-write by the owning thread.
+// to a byte by lane shuffles; each value code goes to a byte of the value
+// block that no other thread of the call touches, updated read-modify-write.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void append_one_kernel(
     uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
@@ -259,9 +271,11 @@ __global__ __launch_bounds__(256) void append_one_kernel(
   uint8_t* page = pages + (static_cast<int64_t>(blk) * Hkv + h) * PB;
   const int t = pos % kBlock;
 
-  // the value byte this thread will update (read early; only this thread writes it)
+  // the value byte this thread will update (read early; only this thread writes
+  // it): word (th, j % 16, j / 32), code position (3e + 8*((j / 16) % 2)) mod 16
   const int th = t >> 3, e = t & 7;
-  uint8_t* vdst = page + kVCodeOff + 2 * ((16 * th + (j & 15)) * 8 + (j >> 4)) + (e >> 2);
+  const int u = (3 * e + 8 * ((j >> 4) & 1)) & 15;
+  uint8_t* vdst = page + kVCodeOff + 4 * ((16 * th + (j & 15)) * 4 + (j >> 5)) + (u >> 2);
   const uint32_t vold = mat ? *vdst : 0u;
 
   {
@@ -320,7 +334,7 @@ __global__ __launch_bounds__(256) void append_one_kernel(
     byte |= shfl_xor(byte, 2);
     if ((j & 3) == 0) page[kKCodeOff + 32 * t + (j >> 2)] = static_cast<uint8_t>(byte);
   } else {
-    const int sh = 2 * (e & 3);
+    const int sh = 2 * (u & 3);
     *vdst = static_cast<uint8_t>((vold & ~(3u << sh)) | (code << sh));
   }
   const int gl = G == 2 ? 64 : 128;

@@ -13,12 +13,15 @@
 //      q.K MFMA (rows = 4 query heads x {hi, lo} x {channel half}).
 //   2. scan: each wave streams 2-page chunks of one (sequence, KV head) through
 //      an LDS ring filled by global->LDS DMA; q.K and P.V both run on 16x16x32
-//      f16 MFMAs.  Cached 2-bit codes become MFMA operands through the FP4
-//      (e2m1) to f16 conversion: masking a code word with 0x33333333 leaves one
-//      code in the low bits of every nibble, and such a nibble decodes to
-//      exactly code/2, a normal fp16 value.  (fp16 subnormal operands are not
-//      an option: MFMA products with them accumulate at roughly 2^-16 of the
-//      magnitude sum, normal ones at 2^-24.)  The four waves of a workgroup
+//      f16 MFMAs.  Cached 2-bit codes become MFMA operands through the packed
+//      FP6 (e2m3) to f16 conversion, 32 values per instruction: masking a
+//      32-bit word of 16 codes with 0xC30C30C3, 0x30C30C30 and 0x0C30C30C gives
+//      three dwords of a packed FP6 block in which every 6-bit field holds one
+//      code in its low bits, a subnormal that decodes to exactly code/8, a
+//      normal fp16 value; field k of the block is code (3k mod 16) of word
+//      k/16.  (fp16 subnormal operands are not an option: MFMA products with
+//      them accumulate at roughly 2^-16 of the magnitude sum, normal ones at
+//      2^-24.)  The four waves of a workgroup
 //      interleave chunks and combine their (max, sum, output) in LDS; each
 //      workgroup writes one partial per query head.
 //   3. merge: log-sum-exp merge of the partials and the inverse value
@@ -102,15 +105,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
   qsc[hl][lane] = ldexpf(r0, E);
   qsc[hl][lane + 64] = ldexpf(r1, E);
   if (lane == 0) {
-    // the code operand holds code/2, so sum(q*code) = 2^(1-E) * D
+    // the code operand holds code/8, so sum(q*code) = 2^(3-E) * D
     const size_t fi = ((static_cast<size_t>(b) * Hkv + h) * QG + qg) * kHT + hl;
-    qf[fi] = make_float4(ldexpf(1.0f, 1 - E), s0, s1, 0.f);
+    qf[fi] = make_float4(ldexpf(1.0f, 3 - E), s0, s1, 0.f);
   }
   __syncthreads();
 
   // A operand: lane L (row m = L%16 -> head m/4, half (m/2)%2, part m%2;
   // k-group kg = L/16) for MFMA j, element e holds channel
-  // 32kg + 16(j/2) + 8(j%2) + 4(e/4) + (e/2)%2 + 2(e%2), matching codes_b.
+  // 32kg + 16(j/2) + (3*(8(j%2) + e) mod 16), matching codes_fp6.
   const int tid = threadIdx.x;
   const int L = tid >> 2;
   const int j = tid & 3;
@@ -124,8 +127,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int e = 2 * e2 + hb;
-      const int ch = 32 * kg + 16 * (j >> 1) + 8 * (j & 1) + 4 * (e >> 2) + ((e >> 1) & 1) +
-                     2 * (e & 1);
+      const int ch = 32 * kg + 16 * (j >> 1) + ((3 * (8 * (j & 1) + e)) & 15);
       const float x = (rgam == (kg >> 1)) ? qsc[rh][ch] : 0.f;
       const _Float16 hi = static_cast<_Float16>(x);
       const _Float16 lo = static_cast<_Float16>((x - static_cast<float>(hi)) * kLoScale);
@@ -138,24 +140,21 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
 }
 
 // --------------------------------------------------------------------------- split
-// Code operands.  m0 = w & 0x33333333 holds codes u = 4b, 4b+2 in the two
-// nibbles of byte b, m1 = (w >> 2) & 0x33333333 codes u = 4b+1, 4b+3; each
-// FP4 conversion turns one byte into two fp16 values code/2.
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+// Code operands: two 32-bit code words (u = 0..15 at bits 2u) -> 32 fp16
+// values code/8; value k = code (3*(k%16) mod 16) of word k/16.  The four
+// 8-value slices are the B operands of four MFMAs.
+typedef unsigned u32x6_t __attribute__((ext_vector_type(6)));
+typedef _Float16 half32 __attribute__((ext_vector_type(32)));
 
-template <int kByte>
-__device__ __forceinline__ half2v fp4x2(uint32_t m) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 1.0f, kByte);
+__device__ __forceinline__ half32 codes_fp6(uint32_t w0, uint32_t w1) {
+  const u32x6_t f = {w0 & 0xC30C30C3u, w0 & 0x30C30C30u, w0 & 0x0C30C30Cu,
+                     w1 & 0xC30C30C3u, w1 & 0x30C30C30u, w1 & 0x0C30C30Cu};
+  return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(f, 1.0f);
 }
-
-// B operand from bytes kB and kB+1 of (m0, m1): element e = 2*dd + h holds
-// code u = 4*(kB + dd/2) + dd%2 + 2h, i.e. with u0 = 4*kB:
-// u0 + 4(e/4) + (e/2)%2 + 2(e%2).
-template <int kB>
-__device__ __forceinline__ half8 codes_b(uint32_t m0, uint32_t m1) {
-  const half2v d0 = fp4x2<kB>(m0), d1 = fp4x2<kB>(m1);
-  const half2v d2 = fp4x2<kB + 1>(m0), d3 = fp4x2<kB + 1>(m1);
-  return half8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+template <int kS>
+__device__ __forceinline__ half8 slice8(const half32& v) {
+  return __builtin_shufflevector(v, v, 8 * kS, 8 * kS + 1, 8 * kS + 2, 8 * kS + 3, 8 * kS + 4,
+                                 8 * kS + 5, 8 * kS + 6, 8 * kS + 7);
 }
 
 struct Chunk {
@@ -310,24 +309,20 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
                                               float sq1, int ctx, int p_end, int lane,
                                               _Float16* __restrict__ atile) {
   const int t = lane & 15;
-  // ---- q.K: D[m = 4*hl + 2*gamma + part][token t]; MFMA j takes word j/2,
-  // bytes 2(j%2), 2(j%2)+1 (channels 32kg + 16(j/2) + 8(j%2) + ...)
+  // ---- q.K: D[m = 4*hl + 2*gamma + part][token t]; one FP6 conversion per
+  // page gives the four B operands (channels 32kg + 16(j/2) + ...)
   floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
   {
-    const uint32_t a0 = c.kc0.x & 0x33333333u, a1 = (c.kc0.x >> 2) & 0x33333333u;
-    const uint32_t b0 = c.kc1.x & 0x33333333u, b1 = (c.kc1.x >> 2) & 0x33333333u;
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[0], codes_b<0>(a0, a1), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[0], codes_b<0>(b0, b1), d1, 0, 0, 0);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[1], codes_b<2>(a0, a1), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[1], codes_b<2>(b0, b1), d1, 0, 0, 0);
-  }
-  {
-    const uint32_t a0 = c.kc0.y & 0x33333333u, a1 = (c.kc0.y >> 2) & 0x33333333u;
-    const uint32_t b0 = c.kc1.y & 0x33333333u, b1 = (c.kc1.y >> 2) & 0x33333333u;
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[2], codes_b<0>(a0, a1), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[2], codes_b<0>(b0, b1), d1, 0, 0, 0);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[3], codes_b<2>(a0, a1), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[3], codes_b<2>(b0, b1), d1, 0, 0, 0);
+    const half32 k0 = codes_fp6(c.kc0.x, c.kc0.y);
+    const half32 k1 = codes_fp6(c.kc1.x, c.kc1.y);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[0], slice8<0>(k0), d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[0], slice8<0>(k1), d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[1], slice8<1>(k0), d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[1], slice8<1>(k1), d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[2], slice8<2>(k0), d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[2], slice8<2>(k1), d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[3], slice8<3>(k0), d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[3], slice8<3>(k1), d1, 0, 0, 0);
   }
 
   const int pos0 = c.pg0 * kBlock + t;
@@ -365,11 +360,10 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
   st.zs1 += (v0 ? p0 * zv01 : 0.f) + (v1 ? p1 * zv11 : 0.f);
 
   // ---- P into the A tile of the P.V MFMA: row 4*hl + 2*gamma + part; token
-  // t = 8*th + e of page p sits at k = 16p + 8th + 4(e/4) + 2(e%2) + (e/2)%2,
-  // the slot whose V code codes_b places there.
+  // t of page p sits at k = 16p + t (the V-code word layout puts token e of a
+  // channel tile at conversion slot e).
   const int hl = lane >> 4;
-  const int e = t & 7;
-  const int kk = 8 * (t >> 3) + 4 * (e >> 2) + 2 * (e & 1) + ((e >> 1) & 1);
+  const int kk = t;
   const float w[2][2] = {{v0 ? p0 * sv00 : 0.f, v0 ? p0 * sv01 : 0.f},
                          {v1 ? p1 * sv10 : 0.f, v1 ? p1 * sv11 : 0.f}};
   uint32_t hv[2][2], lv[2][2];
@@ -412,16 +406,19 @@ __device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
       : "memory");
   const half8 aw = __builtin_bit_cast(half8, awv);
 
-  // ---- P.V: D[m][channel 16j + n]; dword j/2 holds the chunks of MFMAs j
-  // (bytes 0-1) and j+1 (bytes 2-3), token e of a chunk at bits 2e.
-  const uint32_t vw[4] = {c.vc.x, c.vc.y, c.vc.z, c.vc.w};
-#pragma unroll
-  for (int q2 = 0; q2 < 4; ++q2) {
-    const uint32_t m0 = vw[q2] & 0x33333333u, m1 = (vw[q2] >> 2) & 0x33333333u;
-    st.acc[2 * q2] =
-        __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, codes_b<0>(m0, m1), st.acc[2 * q2], 0, 0, 0);
-    st.acc[2 * q2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, codes_b<2>(m0, m1),
-                                                                st.acc[2 * q2 + 1], 0, 0, 0);
+  // ---- P.V: D[m][channel 16j + n]; dwords (0, 1) of this lane's V codes
+  // convert to the B operands of channel tiles 0-3, dwords (2, 3) to 4-7
+  {
+    const half32 va = codes_fp6(c.vc.x, c.vc.y);
+    st.acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<0>(va), st.acc[0], 0, 0, 0);
+    st.acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<1>(va), st.acc[1], 0, 0, 0);
+    st.acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<2>(va), st.acc[2], 0, 0, 0);
+    st.acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<3>(va), st.acc[3], 0, 0, 0);
+    const half32 vb = codes_fp6(c.vc.z, c.vc.w);
+    st.acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<0>(vb), st.acc[4], 0, 0, 0);
+    st.acc[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<1>(vb), st.acc[5], 0, 0, 0);
+    st.acc[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<2>(vb), st.acc[6], 0, 0, 0);
+    st.acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<3>(vb), st.acc[7], 0, 0, 0);
   }
 }
 
@@ -571,8 +568,8 @@ __global__ __launch_bounds__(256) void split_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int g = j >> 2;
-    // code operand = code/2: sum(w * code) = 2 * D
-    const float val = 2.0f * fmaf(st.acc[j][2 * g + 1], kLoUnscale, st.acc[j][2 * g]) +
+    // code operand = code/8: sum(w * code) = 8 * D
+    const float val = 8.0f * fmaf(st.acc[j][2 * g + 1], kLoUnscale, st.acc[j][2 * g]) +
                       (g ? zs1 : zs0);
     co[wave][hl][16 * j + n] = val;
   }

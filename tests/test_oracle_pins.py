@@ -247,12 +247,14 @@ def test_pack_unpack_identity_over_all_byte_values():
         for kind in ("k", "v"):
             cache = np.zeros((1, 1, O.page_bytes()), np.uint8)
             table = np.zeros((1, 1), np.int32)
-            if kind == "k":
-                t, chans = val % 16, [4 * (val // 16 % 32) + i for i in range(4)]
-                toks = [t] * 4
-            else:
-                th, half, ch = (val // 2) % 2, val % 2, val % 128
-                toks, chans = [8 * th + 4 * half + e for e in range(4)], [ch] * 4
+            site = O.k_code_site if kind == "k" else O.v_code_site
+            target = (32 * (val % 16) + val // 16) if kind == "k" else 512 + 2 * val + (val % 2)
+            # the four (token, channel) codes stored in byte `target`, ordered by bit
+            sites = sorted((int(site(tt, ii)[1]), tt, ii) for tt in range(16) for ii in range(128)
+                           if int(site(tt, ii)[0]) == target)
+            assert [sh for sh, _, _ in sites] == [0, 2, 4, 6]
+            toks = [tt for _, tt, _ in sites]
+            chans = [ii for _, _, ii in sites]
             for tok, ch, code in zip(toks, chans, four):
                 enc = {key: np.zeros((1, 128) if "codes" in key else (1, 1)) for key in
                        ("k_codes", "v_codes", "k_s", "k_z", "v_s", "v_z")}
@@ -260,9 +262,7 @@ def test_pack_unpack_identity_over_all_byte_values():
                 enc[kind + "_codes"][0] = old[kind + "_codes"][0]
                 enc[kind + "_codes"][0, ch] = code
                 O.write_tokens(cache, table, 0, [tok], 0, slice(None), enc, 1, 128)
-            site = O.k_code_site if kind == "k" else O.v_code_site
-            byte = int(site(toks[0], chans[0])[0])
-            assert cache.reshape(-1)[byte] == val
+            assert cache.reshape(-1)[target] == val
             got = O.read_tokens(cache, table, 0, toks, 0, 1, 128)[kind + "_codes"]
             assert [int(got[n, chans[n]]) for n in range(4)] == four
     # overwriting one token leaves its neighbours' bits untouched
