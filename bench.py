@@ -39,7 +39,27 @@ def parse():
                     help="bound on the oracle's CPU time for the cpu_baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the measurement, run a plain fp32 copy kernel (y = -x) over this "
+                         "many MiB three times: the reference for HBM byte counters")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per scan launch from the committed counter summary, or None if
+    it was taken on another workload or the kernel's sources changed since."""
+    from rotated_int2_kv_kvq_amd.traffic import kernel_source_hash
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return round(float(rec["traffic_bytes"]))
 
 
 def cache_bytes_per_token_head(group: int) -> int:
@@ -168,40 +188,44 @@ def main():
     assert all(torch.isfinite(o).all().item() for o in outs)
 
     # ---------------------------------------------------------------- per-kernel event timing
-    # Queue every launch behind a GPU sleep so that host launch latency never
-    # falls inside an event interval.  The three decode stages are launched
-    # separately; the split kernel sits alone between its events.
+    # The decode stages are launched separately, each layer with its own
+    # workspace; the split kernels of all layers run back to back between one
+    # pair of events, and so do the single-token appends.  Every launch is
+    # queued behind a GPU sleep so that host launch latency never falls inside
+    # an event interval.
     last = total_steps - 1
+    wss = [ws] + [torch.empty_like(ws) for _ in range(L - 1)]
     split_ms, app_ms = [], []
-    for rep in range(3):
-        evs = []
+    for rep in range(4):
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)
+        s0, s1, a0, a1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
         for layer in range(L):
-            a0, a1, s0, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
-                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws,
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
                        stages=kvq.STAGE_PREPARE)
-            s0.record()
+        s0.record()
+        for layer in range(L):
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
-                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws,
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
                        stages=kvq.STAGE_SPLITS)
-            s1.record()
+        s1.record()
+        for layer in range(L):
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
-                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws,
+                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
                        stages=kvq.STAGE_MERGE)
-            a0.record()
+        a0.record()
+        for layer in range(L):
             # re-append the last step's token: same slot, same bytes
             kvq.append(pages[layer], table, spos[last], kn[last][layer], vn[last][layer],
                        mus[layer], rks[layer], rvs[layer], w.group, w.clip_k, w.clip_v)
-            a1.record()
-            evs.append((s0, s1, a0, a1))
+        a1.record()
         torch.cuda.synchronize()
         if rep == 0:
             continue
-        for s0, s1, a0, a1 in evs:
-            split_ms.append(s0.elapsed_time(s1))
-            app_ms.append(a0.elapsed_time(a1))
+        split_ms.append(s0.elapsed_time(s1) / L)
+        app_ms.append(a0.elapsed_time(a1) / L)
+    del wss
     split_avg_ms = float(np.mean(split_ms))
     app_avg_ms = float(np.mean(app_ms))
     split_bytes = int((ctx0 + last + 1).sum()) * Hkv * per_tok_head
@@ -212,6 +236,17 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, st, pages[0], table, ctxs[last], qs[last][0], per_tok_head,
                            args.cpu_seconds, sm_scale)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        x = torch.randn(n, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {4 * n} bytes read and written", file=sys.stderr,
+              flush=True)
+        del x, y
 
     line = {
         "metric": METRIC,
@@ -247,7 +282,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w0.name),
+            "algorithmic_bytes": split_bytes,
         },
         "cpu_baseline": cpu,
     }

@@ -2,7 +2,7 @@
 // kernel launches.  No allocation, no synchronisation, no global state.
 #include <stdint.h>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_common.h"
 
 #include "kvq_launch.h"

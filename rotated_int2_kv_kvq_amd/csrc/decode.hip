@@ -168,7 +168,9 @@ struct Chunk {
 // global->LDS DMA (no VGPRs held while in flight).  A slot holds the two page
 // images exactly as laid out in the cache: codes [0, 1024) and (scale, zero)
 // pairs [1024, 1024 + 128G).  One chunk is kDmaPerChunk DMA instructions.
-constexpr int kDepth = 3;
+// Two chunks in flight per wave keep the workgroup's LDS under 40 KB, so four
+// workgroups (four waves per SIMD) fit on a CU alongside the register cap.
+constexpr int kDepth = 2;
 constexpr int kRing = kDepth + 1;
 constexpr int kDmaPerChunk = 4;
 
@@ -488,15 +490,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 }
 
 // grid (S, Hkv * QG, B), block 256: workgroup x covers pages [x*spw, (x+1)*spw).
+// Capped at 128 VGPRs so that four waves share each SIMD: the scan is bound by
+// the latency of its per-chunk dependency chain more than by issue slots.
 template <int G>
-__global__ __launch_bounds__(256) void split_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void split_kernel(
     const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
     int max_ctx, int Hq, int QG, int spw, const uint4* __restrict__ qa,
     const float4* __restrict__ qf, float* __restrict__ part, int S) {
   constexpr int kSlot = 2 * page_bytes_for_groups(G);
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
-  __shared__ __attribute__((aligned(16))) _Float16 atile[4][2][16 * 32];
+  __shared__ __attribute__((aligned(16))) _Float16 atile[4][16 * 32];
   __shared__ float cm[4][kHT], cl[4][kHT];
 
   const int h = blockIdx.y / QG;
@@ -545,9 +549,7 @@ __global__ __launch_bounds__(256) void split_kernel(
                      p_begin + 2 * (wave + 4 * (i + kDepth)), p_end, lane);
     // chunk i has landed once at most the DMAs of the chunks behind it are pending
     const int behind = min(kDepth, nc - 1 - i);
-    if (behind >= 3)
-      wait_vmem<3 * kDmaPerChunk>();
-    else if (behind == 2)
+    if (behind == 2)
       wait_vmem<2 * kDmaPerChunk>();
     else if (behind == 1)
       wait_vmem<kDmaPerChunk>();
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(256) void split_kernel(
       wait_vmem<0>();
     Chunk c;
     read_chunk<G>(c, myring + (i % kRing) * kSlot, p_begin + 2 * (wave + 4 * i), lane);
-    compute_chunk<G>(c, st, qA, fq.x, fq.y, fq.z, ctx, p_end, lane, atile[wave][i & 1]);
+    compute_chunk<G>(c, st, qA, fq.x, fq.y, fq.z, ctx, p_end, lane, atile[wave]);
   }
 
   // ---- per-wave finish: reduce row sums, form unnormalised outputs
