@@ -41,11 +41,10 @@
  * of kvq_page_bytes() bytes each; G = head_dim / group):
  *   byte [0, 512)           K codes, 16 token rows of 32 bytes; channel i of
  *                           token t at byte 32*t + i/4, bits 2*(i%4)
- *   byte [512, 1024)        V codes, 128 little-endian 32-bit words; word
- *                           (th, n, q) at byte 512 + 4*((16*th + n)*4 + q)
- *                           holds tokens 8*th..8*th+7 of channels 16*(2q+s)+n,
- *                           s in {0, 1}: token 8*th + e of channel tile 2q+s at
- *                           code position u = (3e + 8s) mod 16, bits 2u
+ *   byte [512, 1024)        V codes, 128 little-endian 32-bit words, one per
+ *                           channel: channel i at byte 512 + 4*(8*(i%16) +
+ *                           i/16); token t at code position u = 3t mod 16,
+ *                           bits 2u of the word
  *   byte [1024, 1024+64G)   K (scale, zero) fp16 pairs, [token][group]
  *   byte [.., 1024+128G)    V (scale, zero) fp16 pairs, [token][group]
  * A cached element decodes as x_hat = scale * code + zero (rotated basis).

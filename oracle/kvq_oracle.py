@@ -35,11 +35,10 @@ Cache layout (ours; the pages only say the paged KV-cache format is kept,
 [num_blocks][Hkv][page_bytes], 16 tokens per block, head_dim 128, G = 128/group:
     [0, 512)        K codes, token-row major: token t, channel i at byte
                     32*t + i//4, bits 2*(i%4)
-    [512, 1024)     V codes, 128 little-endian 32-bit words; word
-                    (th, n, q) holds tokens 8*th..8*th+7 of channels
-                    16*(2q+s) + n, s in {0, 1}, at byte offset
-                    512 + 4*((16*th + n)*4 + q); token 8*th+e of channel tile
-                    2q+s at code position u = (3e + 8s) mod 16 (bits 2u)
+    [512, 1024)     V codes, 128 little-endian 32-bit words, one per
+                    channel: channel i at byte 512 + 4*(8*(i%16) + i//16),
+                    its 16 tokens inside the word at code positions
+                    u = 3t mod 16 (bits 2u)
     [1024, +64G)    K fp16 (scale, zero) pairs, [token][group]
     [.., +64G)      V fp16 (scale, zero) pairs, [token][group]
 """
@@ -163,11 +162,9 @@ def v_code_site(t, i):
     """(byte offset in page, bit shift) of V code of token t, channel i."""
     t = np.asarray(t)
     i = np.asarray(i)
-    th, e = t // 8, t % 8
-    j, n = i // 16, i % 16
-    q, s = j // 2, j % 2
-    u = (3 * e + 8 * s) % 16
-    return 512 + 4 * ((16 * th + n) * 4 + q) + u // 4, 2 * (u % 4)
+    word = 8 * (i % 16) + i // 16  # one 32-bit word per channel and page
+    u = (3 * t) % 16               # code position of token t in the word
+    return 512 + 4 * word + u // 4, 2 * (u % 4)
 
 
 def sz_site(t, gidx, group: int, which: str):

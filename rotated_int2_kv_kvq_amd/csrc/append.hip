@@ -199,14 +199,11 @@ __global__ __launch_bounds__(256) void append_kernel(
     }
 
     if (mat == 1) {
-      // V words: word (th, ch16 = c % 16, q = c / 32) holds tokens 8*th..8*th+7 of
-      // channel tiles 2q and 2q+1; token e of tile 2q+s at code position
-      // (3e + 8s) mod 16.  This lane holds tokens e = 4*(r4 % 2) + i of
-      // channels 8n + e' (tile n/2, s = (n/2) % 2); lane ^ 16 holds the other
-      // four tokens and lane ^ 2 the other tile of the same words, so the four
-      // quarters are combined before one lane writes each word.
-      const int th = r4 >> 1;
-      const int s = (n >> 1) & 1;
+      // V words: one per channel c at word 8*(c % 16) + c / 16 of the value
+      // block, token tq at code position (3*tq) mod 16.  This lane holds
+      // tokens 4*r4 + i of channels 8n + e; lanes ^16 and ^32 hold the other
+      // tokens of the same channels, so the four quarters are combined and
+      // each of the four lanes writes two of the eight words.
       uint32_t newq = 0;  // which of this lane's tokens are new
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -218,18 +215,17 @@ __global__ __launch_bounds__(256) void append_kernel(
         uint32_t word = 0, mask = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int u = (3 * (4 * (r4 & 1) + i) + 8 * s) & 15;
+          const int u = (3 * (4 * r4 + i)) & 15;
           word |= ((code_bits[i] >> (2 * e)) & 3u) << (2 * u);
           if (newq & (1u << i)) mask |= 3u << (2 * u);
         }
         word |= shfl_xor(word, 16);
         mask |= shfl_xor(mask, 16);
-        word |= shfl_xor(word, 2);
-        mask |= shfl_xor(mask, 2);
-        if ((r4 & 1) == 0 && (n & 2) == 0 && mask != 0) {
-          const int ch16 = 8 * (n & 1) + e;
+        word |= shfl_xor(word, 32);
+        mask |= shfl_xor(mask, 32);
+        if (r4 == (e & 3) && mask != 0) {
           uint32_t* dst = reinterpret_cast<uint32_t*>(page + kVCodeOff +
-                                                      4 * ((16 * th + ch16) * 4 + (n >> 2)));
+                                                      4 * (64 * (n & 1) + 8 * e + (n >> 1)));
           *dst = (mask == 0xffffffffu) ? word : ((*dst & ~mask) | (word & mask));
         }
       }
@@ -272,10 +268,9 @@ __global__ __launch_bounds__(256) void append_one_kernel(
   const int t = pos % kBlock;
 
   // the value byte this thread will update (read early; only this thread writes
-  // it): word (th, j % 16, j / 32), code position (3e + 8*((j / 16) % 2)) mod 16
-  const int th = t >> 3, e = t & 7;
-  const int u = (3 * e + 8 * ((j >> 4) & 1)) & 15;
-  uint8_t* vdst = page + kVCodeOff + 4 * ((16 * th + (j & 15)) * 4 + (j >> 5)) + (u >> 2);
+  // it): word 8*(j % 16) + j / 16, code position 3t mod 16
+  const int u = (3 * t) & 15;
+  uint8_t* vdst = page + kVCodeOff + 4 * (8 * (j & 15) + (j >> 4)) + (u >> 2);
   const uint32_t vold = mat ? *vdst : 0u;
 
   {

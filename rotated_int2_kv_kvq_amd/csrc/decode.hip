@@ -8,22 +8,27 @@
 // log-sum-exp.
 //
 // Three launches on the caller's stream:
-//   1. prologue: q_r = q * R_K[h], scaled by sm_scale*log2(e) and a power of
-//      two, split into fp16 hi + 2^11*lo parts laid out as the A operand of the
-//      q.K MFMA (rows = 4 query heads x {hi, lo} x {channel half}).
-//   2. scan: each wave streams 2-page chunks of one (sequence, KV head) through
-//      an LDS ring filled by global->LDS DMA; q.K and P.V both run on 16x16x32
-//      f16 MFMAs.  Cached 2-bit codes become MFMA operands through the packed
-//      FP6 (e2m3) to f16 conversion, 32 values per instruction: masking a
-//      32-bit word of 16 codes with 0xC30C30C3, 0x30C30C30 and 0x0C30C30C gives
-//      three dwords of a packed FP6 block in which every 6-bit field holds one
-//      code in its low bits, a subnormal that decodes to exactly code/8, a
-//      normal fp16 value; field k of the block is code (3k mod 16) of word
-//      k/16.  (fp16 subnormal operands are not an option: MFMA products with
-//      them accumulate at roughly 2^-16 of the magnitude sum, normal ones at
-//      2^-24.)  The four waves of a workgroup
-//      interleave chunks and combine their (max, sum, output) in LDS; each
-//      workgroup writes one partial per query head.
+//   1. prologue: q_r = q * R_K, scaled by sm_scale*log2(e), written as the A
+//      operands of the q.K products: each query head's |q_r| is fixed-point
+//      with 32 fraction bits under a per-head power of two, and its 4-bit
+//      digits are MFMA rows (rows = 4 heads x 4 digits per operand), each
+//      digit an FP6 value b/8 with the sign of q_r, each row weighted by its
+//      own E8M0 block scale.
+//   2. scan: each wave streams its 8-page (128-token) blocks of one
+//      (sequence, KV head) through an LDS ring filled by global->LDS DMA.
+//      Cached 2-bit codes are MFMA operands as they stand: masking a 32-bit
+//      word of 16 codes with 0xC30C30C3, 0x30C30C30 and 0x0C30C30C gives three
+//      dwords of a packed FP6 block whose 6-bit fields hold one code each in
+//      their low bits, i.e. the FP6 subnormal code/8 (field k = code 3k mod 16
+//      of the word).  q.K runs as 16x16x128 FP6 x FP6 MFMAs per page (two
+//      digit operands, three for group 64); P.V as two 16x16x128 FP8 x FP6
+//      MFMAs per 16 output channels and block, with the softmax weights p*s_V
+//      again fixed-point (32 bits under a per-head, per-block power of two)
+//      split into eight 4-bit digits, each digit b an FP8 byte worth b*2^-9.
+//      Digits and codes are short enough that the MFMA sums are exact before
+//      the fp32 accumulation.
+//      The four waves of a workgroup combine their (max, sum, output) in LDS;
+//      each workgroup writes one partial per query head.
 //   3. merge: log-sum-exp merge of the partials and the inverse value
 //      rotation o = o_r * R_V^T.  (A separate launch: merging inside the scan
 //      through a last-workgroup counter needs device-scope release/acquire,
@@ -32,26 +37,79 @@
 #include "kvq_common.h"
 #include "kvq_launch.h"
 
+#include <array>
+
 namespace kvq {
 
-constexpr int kHT = 4;          // query heads per MFMA row tile
+constexpr int kHT = 4;            // query heads per MFMA row tile (x 4 digit rows)
 constexpr int kPartStride = 132;  // floats per partial: [0] = lse2, [4..131] = o
 constexpr float kLog2e = 1.4426950408889634f;
-// fp16 "lo" parts are stored scaled by 2^11 (their own MFMA rows) so that they
-// stay clear of the fp16 subnormal range; the row sums are unscaled by 2^-11.
-constexpr float kLoScale = 2048.0f;
-constexpr float kLoUnscale = 1.0f / 2048.0f;
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp2(l - m) is 0, not NaN
+// Per lane of the q.K A operands: [0, 6) and [6, 12) and (group 64) [12, 18)
+// three FP6 operands, [28] and [29] the E8M0 row scales of the high- and
+// low-digit operands.
+constexpr int kQaDwords = 32;
+constexpr int kQaScale = 28;
+constexpr int kFmtFp8 = 0;           // f8f6f4 MFMA operand formats
+constexpr int kFmtFp6 = 2;
+constexpr int kScaleOne = 127;  // E8M0 2^0
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// 16x16x128 MFMA, D = A*B + C with per-lane E8M0 scales (A scale = this lane's
+// row; every lane of a row passes the same value).
+template <int FA, int FB>
+__device__ __forceinline__ floatx4 mfma128(const v8i& a, const v8i& b, const floatx4& c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, kScaleOne);
+}
+
+// FP6 operand from two code words (16 codes each, code u at bits 2u): field j
+// of the 32 holds code (3*(j%16)) mod 16 of word j/16, as the value code/8.
+__device__ __forceinline__ v8i fp6_codes(uint32_t w0, uint32_t w1) {
+  v8i r;
+  r[0] = static_cast<int>(w0 & 0xC30C30C3u);
+  r[1] = static_cast<int>(w0 & 0x30C30C30u);
+  r[2] = static_cast<int>(w0 & 0x0C30C30Cu);
+  r[3] = static_cast<int>(w1 & 0xC30C30C3u);
+  r[4] = static_cast<int>(w1 & 0x30C30C30u);
+  r[5] = static_cast<int>(w1 & 0x0C30C30Cu);
+  r[6] = 0;
+  r[7] = 0;
+  return r;
+}
+
+// 2^x on the hardware exp unit
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exponent e with |x| < 2^e <= 2|x| (0 for x == 0)
+__device__ __forceinline__ int exp_above(float x) { return __builtin_amdgcn_frexp_expf(x); }
 
 // --------------------------------------------------------------------------- prologue
-// grid (Hkv * QG, B), block 256: wave w handles query head 4*qg + w of KV head h.
-template <bool kBf16>
+// grid (Hkv * QG, B), block 256: wave w rotates query head 4*qg + w of KV head
+// h; then 64 threads pack the A operands lane by lane.
+//
+// |x| is fixed-point with 32 fraction bits under 2^e: eight 4-bit digits,
+// digit d (0 = most significant) worth b * 2^(e - 4 - 4d), as the FP6 value
+// b/8 under the row scale 2^(e - 1 - 4d).  In an A operand, lane L has row
+// r = L%16 and lane group g = L/16; FP6 field j (k = 32g + j) is channel
+// 32g + 16(j/16) + (3(j%16) mod 16), the channel order fp6_codes gives the
+// key code words.
+//   group 128: operand 0 rows (head r/4, digit r%4), operand 1 rows
+//              (head r/4, digit 4 + r%4);
+//   group 64:  operand 0 and 1 rows (head r/4, digit r%4) over the channels
+//              of group 0 and 1 (zero in the other lanes), operand 2 rows
+//              (head r/4, group (r/2)%2, digit 4 + r%2) over that group's
+//              channels: 24 bits.
+template <bool kBf16, int G>
 __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ q,
                                                        const float* __restrict__ rot_k, int Hq,
                                                        int Hkv, int QG, float qscale,
-                                                       uint4* __restrict__ qa,
+                                                       uint32_t* __restrict__ qa,
                                                        float4* __restrict__ qf) {
   __shared__ float qin[kHT][kHeadDim];
-  __shared__ float qsc[kHT][kHeadDim];
+  __shared__ uint32_t qw[kHT][kHeadDim];  // |x| fixed-point, 32 fraction bits under 2^e
+  __shared__ uint8_t qs[kHT][kHeadDim];   // sign of x
+  __shared__ int qe[kHT];
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
@@ -78,7 +136,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
   qin[hl][lane + 64] = q1;
   __syncthreads();
 
-  // q_r[j] = sum_i q[i] R_K[i][j]; lane computes j = lane and j = lane + 64.
+  // x[j] = qscale * sum_i q[i] R_K[i][j]; lane computes j = lane and j = lane + 64.
   const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim;
   float r0 = 0.f, r1 = 0.f;
   if (valid) {
@@ -99,80 +157,76 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
     s0 += shfl_xor(s0, m);
     s1 += shfl_xor(s1, m);
   }
-  // Scale by 2^E so that max|q| * 2^E is in [2^14, 2^15): fp16 range.
-  int E = 0;
-  if (amax > 0.f) E = min(max(14 - ilogbf(amax), -100), 100);
-  qsc[hl][lane] = ldexpf(r0, E);
-  qsc[hl][lane + 64] = ldexpf(r1, E);
+  // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest
+  const int e = min(max(exp_above(amax), -100), 100);
+  auto fixed32 = [&](float x) -> uint32_t {
+    return static_cast<uint32_t>(fminf(rintf(ldexpf(fabsf(x), 32 - e)), 4294967040.0f));
+  };
+  qw[hl][lane] = fixed32(r0);
+  qw[hl][lane + 64] = fixed32(r1);
+  qs[hl][lane] = r0 < 0.f;
+  qs[hl][lane + 64] = r1 < 0.f;
   if (lane == 0) {
-    // the code operand holds code/8, so sum(q*code) = 2^(3-E) * D
-    const size_t fi = ((static_cast<size_t>(b) * Hkv + h) * QG + qg) * kHT + hl;
-    qf[fi] = make_float4(ldexpf(1.0f, 3 - E), s0, s1, 0.f);
+    qe[hl] = e;
+    // per-group sums of x for the zero-point term (channels < 64, >= 64)
+    qf[((static_cast<size_t>(b) * Hkv + h) * QG + qg) * kHT + hl] = make_float4(0.f, s0, s1, 0.f);
   }
   __syncthreads();
 
-  // A operand: lane L (row m = L%16 -> head m/4, half (m/2)%2, part m%2;
-  // k-group kg = L/16) for MFMA j, element e holds channel
-  // 32kg + 16(j/2) + (3*(8(j%2) + e) mod 16), matching codes_fp6.
-  const int tid = threadIdx.x;
-  const int L = tid >> 2;
-  const int j = tid & 3;
-  const int m = L & 15;
-  const int rh = m >> 2, rgam = (m >> 1) & 1, rpart = m & 1;
-  const int kg = L >> 4;
-  uint32_t packed[4];
+  if (threadIdx.x < 64) {
+    const int L = threadIdx.x;
+    const int r = L & 15, g = L >> 4;
+    const int head = r >> 2;
+    // FP6 operand: field j = digit dig(j) of channel ch(j), or 0 if !use(j)
+    auto pack = [&](auto digit_of, bool use) {
+      uint64_t bits[3] = {0, 0, 0};
 #pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int e = 2 * e2 + hb;
-      const int ch = 32 * kg + 16 * (j >> 1) + ((3 * (8 * (j & 1) + e)) & 15);
-      const float x = (rgam == (kg >> 1)) ? qsc[rh][ch] : 0.f;
-      const _Float16 hi = static_cast<_Float16>(x);
-      const _Float16 lo = static_cast<_Float16>((x - static_cast<float>(hi)) * kLoScale);
-      word |= static_cast<uint32_t>(f16_bits(rpart ? lo : hi)) << (16 * hb);
+      for (int j = 0; j < 32; ++j) {
+        const int ch = 32 * g + 16 * (j >> 4) + ((3 * (j & 15)) & 15);
+        const uint32_t nib = (qw[head][ch] >> (28 - 4 * digit_of)) & 15u;
+        const uint64_t field = (use && nib) ? (nib | (static_cast<uint32_t>(qs[head][ch]) << 5)) : 0u;
+        const int bit = 6 * j;
+        bits[bit >> 6] |= field << (bit & 63);
+        if ((bit & 63) > 58) bits[(bit >> 6) + 1] |= field >> (64 - (bit & 63));
+      }
+      uint32_t op[6];
+      for (int d = 0; d < 6; ++d) op[d] = static_cast<uint32_t>(bits[d >> 1] >> (32 * (d & 1)));
+      return std::array<uint32_t, 6>{op[0], op[1], op[2], op[3], op[4], op[5]};
+    };
+    uint32_t* dst = qa + (((static_cast<size_t>(b) * Hkv + h) * QG + qg) * 64 + L) * kQaDwords;
+    auto store = [&](int at, const std::array<uint32_t, 6>& op) {
+      for (int d = 0; d < 6; ++d) dst[at + d] = op[d];
+    };
+    const int dhi = r & 3;
+    if constexpr (G == 1) {
+      store(0, pack(dhi, true));
+      store(6, pack(4 + dhi, true));
+      dst[kQaScale + 1] = static_cast<uint32_t>(min(max(kScaleOne + qe[head] - 17 - 4 * dhi, 1), 254));
+    } else {
+      store(0, pack(dhi, g < 2));
+      store(6, pack(dhi, g >= 2));
+      const int gam = (r >> 1) & 1, dlo = 4 + (r & 1);
+      store(12, pack(dlo, (g >> 1) == gam));
+      dst[kQaScale + 1] = static_cast<uint32_t>(min(max(kScaleOne + qe[head] - 1 - 4 * dlo, 1), 254));
     }
-    packed[e2] = word;
+    dst[kQaScale] = static_cast<uint32_t>(min(max(kScaleOne + qe[head] - 1 - 4 * dhi, 1), 254));
   }
-  const size_t qi = (((static_cast<size_t>(b) * Hkv + h) * QG + qg) * 64 + L) * 4 + j;
-  qa[qi] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
-// --------------------------------------------------------------------------- split
-// Code operands: two 32-bit code words (u = 0..15 at bits 2u) -> 32 fp16
-// values code/8; value k = code (3*(k%16) mod 16) of word k/16.  The four
-// 8-value slices are the B operands of four MFMAs.
-typedef unsigned u32x6_t __attribute__((ext_vector_type(6)));
-typedef _Float16 half32 __attribute__((ext_vector_type(32)));
-
-__device__ __forceinline__ half32 codes_fp6(uint32_t w0, uint32_t w1) {
-  const u32x6_t f = {w0 & 0xC30C30C3u, w0 & 0x30C30C30u, w0 & 0x0C30C30Cu,
-                     w1 & 0xC30C30C3u, w1 & 0x30C30C30u, w1 & 0x0C30C30Cu};
-  return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(f, 1.0f);
-}
-template <int kS>
-__device__ __forceinline__ half8 slice8(const half32& v) {
-  return __builtin_shufflevector(v, v, 8 * kS, 8 * kS + 1, 8 * kS + 2, 8 * kS + 3, 8 * kS + 4,
-                                 8 * kS + 5, 8 * kS + 6, 8 * kS + 7);
-}
-
-struct Chunk {
-  uint2 kc0, kc1;  // K codes, pages 0/1: token t, bytes 8kg..8kg+7
-  uint4 vc;        // V codes of page kg/2, token half kg%2, channel lane n
-  uint2 szk0, szk1, szv0, szv1;  // (scale, zero) of token t; .y = group 1 if G == 2
-  int pg0;
-};
-
-// ---- LDS ring: each wave keeps kDepth 2-page chunks in flight, loaded with
+// --------------------------------------------------------------------------- scan
+// ---- LDS ring: each wave keeps kDepth 2-page slices in flight, loaded with
 // global->LDS DMA (no VGPRs held while in flight).  A slot holds the two page
 // images exactly as laid out in the cache: codes [0, 1024) and (scale, zero)
-// pairs [1024, 1024 + 128G).  One chunk is kDmaPerChunk DMA instructions.
-// Two chunks in flight per wave keep the workgroup's LDS under 40 KB, so four
-// workgroups (four waves per SIMD) fit on a CU alongside the register cap.
+// pairs [1024, 1024 + 128G).  One slice is kDmaPerSlice DMA instructions.
 constexpr int kDepth = 2;
 constexpr int kRing = kDepth + 1;
-constexpr int kDmaPerChunk = 4;
+constexpr int kDmaPerSlice = 4;
+// P tile: 16 rows (4 heads x 4 digits) x 8 pages x 16 tokens of FP8 digit
+// bytes; the row stride is padded to 144 bytes so that the A-operand reads
+// (16 rows at one page) and the digit writes spread over all LDS banks.  The
+// four per-head exponents follow the rows.
+constexpr int kPRow = 144;
+constexpr int kPTile = 16 * kPRow + 16;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
@@ -191,8 +245,14 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
+}
+
+// DMA the two pages [pg0, pg0 + 1] of this (sequence, KV head) into a slot; a
+// page past the range is replaced by pg0 (its tokens are masked out).
 template <int G>
-__device__ __forceinline__ void issue_chunk(uint8_t* slot, const uint8_t* __restrict__ pages,
+__device__ __forceinline__ void issue_slice(uint8_t* slot, const uint8_t* __restrict__ pages,
                                             int64_t num_blocks, int Hkv, int h,
                                             const int* __restrict__ row, int pg0, int p_end,
                                             int lane) {
@@ -214,37 +274,32 @@ __device__ __forceinline__ void issue_chunk(uint8_t* slot, const uint8_t* __rest
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
-}
+// This lane's share of one ring slot for the q.K products and the softmax:
+// key codes of token t, channels 32kg..32kg+31, of both pages, and the (scale,
+// zero) words of token t (K then V, each for both pages; .y = group 1).
+// Inline assembly keeps the compiler's wait insertion, which cannot tell
+// ring slots apart and would drain every pending DMA, out of the way; the
+// caller has waited for this slot, and the block ends with lgkmcnt(0).
+struct Slice {
+  u32x2 kc0, kc1;
+  uint2 szk0, szk1, szv0, szv1;
+};
 
-// Read this lane's share of one ring slot.  The reads are inline assembly so
-// that the compiler's wait insertion, which cannot tell ring slots apart and
-// would drain every pending DMA before any LDS read, does not see them; the
-// caller has already waited for this slot's DMAs, and the block ends with
-// lgkmcnt(0) so its results are complete when it returns.
 template <int G>
-__device__ __forceinline__ void read_chunk(Chunk& c, const uint8_t* slot, int pg0, int lane) {
+__device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
   constexpr int PB = page_bytes_for_groups(G);
-  const int t = lane & 15, kg = lane >> 4;
-  const uint32_t ak = lds_addr(slot + kKCodeOff + 32 * t + 8 * kg);
-  const uint32_t av = lds_addr(slot + (kg >> 1) * PB + kVCodeOff + 256 * (kg & 1) + 16 * t);
-  const uint32_t as = lds_addr(slot + kSzOff + t * 4 * G);
-  u32x2 k0, k1;
-  u32x4 v;
   if constexpr (G == 2) {
     u32x2 s0, s1, s2, s3;
     asm volatile(
-        "ds_read_b64 %0, %7\n"
-        "ds_read_b64 %1, %7 offset:%10\n"
-        "ds_read_b128 %2, %8\n"
-        "ds_read_b64 %3, %9\n"
-        "ds_read_b64 %4, %9 offset:%10\n"
-        "ds_read_b64 %5, %9 offset:%11\n"
-        "ds_read_b64 %6, %9 offset:%12\n"
+        "ds_read_b64 %0, %6\n"
+        "ds_read_b64 %1, %6 offset:%8\n"
+        "ds_read_b64 %2, %7\n"
+        "ds_read_b64 %3, %7 offset:%8\n"
+        "ds_read_b64 %4, %7 offset:%9\n"
+        "ds_read_b64 %5, %7 offset:%10\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k0), "=&v"(k1), "=&v"(v), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-        : "v"(ak), "v"(av), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
+        : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+        : "v"(ak), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
         : "memory");
     c.szk0 = make_uint2(s0.x, s0.y);
     c.szk1 = make_uint2(s1.x, s1.y);
@@ -253,32 +308,37 @@ __device__ __forceinline__ void read_chunk(Chunk& c, const uint8_t* slot, int pg
   } else {
     uint32_t s0, s1, s2, s3;
     asm volatile(
-        "ds_read_b64 %0, %7\n"
-        "ds_read_b64 %1, %7 offset:%10\n"
-        "ds_read_b128 %2, %8\n"
-        "ds_read_b32 %3, %9\n"
-        "ds_read_b32 %4, %9 offset:%10\n"
-        "ds_read_b32 %5, %9 offset:%11\n"
-        "ds_read_b32 %6, %9 offset:%12\n"
+        "ds_read_b64 %0, %6\n"
+        "ds_read_b64 %1, %6 offset:%8\n"
+        "ds_read_b32 %2, %7\n"
+        "ds_read_b32 %3, %7 offset:%8\n"
+        "ds_read_b32 %4, %7 offset:%9\n"
+        "ds_read_b32 %5, %7 offset:%10\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k0), "=&v"(k1), "=&v"(v), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-        : "v"(ak), "v"(av), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
+        : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+        : "v"(ak), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
         : "memory");
     c.szk0 = make_uint2(s0, s0);
     c.szk1 = make_uint2(s1, s1);
     c.szv0 = make_uint2(s2, s2);
     c.szv1 = make_uint2(s3, s3);
   }
-  c.kc0 = make_uint2(k0.x, k0.y);
-  c.kc1 = make_uint2(k1.x, k1.y);
-  c.vc = make_uint4(v.x, v.y, v.z, v.w);
-  c.pg0 = pg0;
 }
 
-struct SoftmaxState {
-  float m, l, zs0, zs1;
-  floatx4 acc[8];
-};
+// Value code words of channel 16*tau + n (tau = 0..7) of both pages of a slot:
+// word position 8n + tau, i.e. 32 contiguous bytes per page.
+__device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av, int PB) {
+  const uint32_t av1 = av + PB;
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %4 offset:16\n"
+      "ds_read_b128 %2, %5\n"
+      "ds_read_b128 %3, %5 offset:16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vw[0]), "=&v"(vw[1]), "=&v"(vw[2]), "=&v"(vw[3])
+      : "v"(av), "v"(av1)
+      : "memory");
+}
 
 // Reductions over the 16 lanes of a DPP row (all lanes of one query head):
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
@@ -302,125 +362,342 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// 2^x on the hardware exp unit; arguments here are <= 0 (or -inf -> 0)
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <int G>
-__device__ __forceinline__ void compute_chunk(const Chunk& c, SoftmaxState& st,
-                                              const half8 (&qA)[4], float fac, float sq0,
-                                              float sq1, int ctx, int p_end, int lane,
-                                              _Float16* __restrict__ atile) {
-  const int t = lane & 15;
-  // ---- q.K: D[m = 4*hl + 2*gamma + part][token t]; one FP6 conversion per
-  // page gives the four B operands (channels 32kg + 16(j/2) + ...)
-  floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-  {
-    const half32 k0 = codes_fp6(c.kc0.x, c.kc0.y);
-    const half32 k1 = codes_fp6(c.kc1.x, c.kc1.y);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[0], slice8<0>(k0), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[0], slice8<0>(k1), d1, 0, 0, 0);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[1], slice8<1>(k0), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[1], slice8<1>(k1), d1, 0, 0, 0);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[2], slice8<2>(k0), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[2], slice8<2>(k1), d1, 0, 0, 0);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[3], slice8<3>(k0), d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qA[3], slice8<3>(k1), d1, 0, 0, 0);
-  }
-
-  const int pos0 = c.pg0 * kBlock + t;
-  const bool v0 = pos0 < ctx;
-  const bool v1 = (c.pg0 + 1 < p_end) && (pos0 + kBlock < ctx);
-  float l0 = fac * (f16_lo_to_f32(c.szk0.x) * fmaf(d0[1], kLoUnscale, d0[0]) +
-                    f16_lo_to_f32(c.szk0.y) * fmaf(d0[3], kLoUnscale, d0[2])) +
-             f16_hi_to_f32(c.szk0.x) * sq0 + f16_hi_to_f32(c.szk0.y) * sq1;
-  float l1 = fac * (f16_lo_to_f32(c.szk1.x) * fmaf(d1[1], kLoUnscale, d1[0]) +
-                    f16_lo_to_f32(c.szk1.y) * fmaf(d1[3], kLoUnscale, d1[2])) +
-             f16_hi_to_f32(c.szk1.x) * sq0 + f16_hi_to_f32(c.szk1.y) * sq1;
-  l0 = v0 ? l0 : -INFINITY;
-  l1 = v1 ? l1 : -INFINITY;
-
-  // ---- online softmax (base 2), lazy rescale
-  const float mc = row16_max(fmaxf(l0, l1));
-  const float mnew = fmaxf(st.m, mc);
-  if (__any(mnew > st.m)) {
-    const float alpha = exp2_hw(st.m - mnew);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
-    st.l *= alpha;
-    st.zs0 *= alpha;
-    st.zs1 *= alpha;
-    st.m = mnew;
-  }
-  const float p0 = v0 ? exp2_hw(l0 - st.m) : 0.f;
-  const float p1 = v1 ? exp2_hw(l1 - st.m) : 0.f;
-  st.l += p0 + p1;
-  const float sv00 = f16_lo_to_f32(c.szv0.x), zv00 = f16_hi_to_f32(c.szv0.x);
-  const float sv01 = f16_lo_to_f32(c.szv0.y), zv01 = f16_hi_to_f32(c.szv0.y);
-  const float sv10 = f16_lo_to_f32(c.szv1.x), zv10 = f16_hi_to_f32(c.szv1.x);
-  const float sv11 = f16_lo_to_f32(c.szv1.y), zv11 = f16_hi_to_f32(c.szv1.y);
-  st.zs0 += (v0 ? p0 * zv00 : 0.f) + (v1 ? p1 * zv10 : 0.f);
-  st.zs1 += (v0 ? p0 * zv01 : 0.f) + (v1 ? p1 * zv11 : 0.f);
-
-  // ---- P into the A tile of the P.V MFMA: row 4*hl + 2*gamma + part; token
-  // t of page p sits at k = 16p + t (the V-code word layout puts token e of a
-  // channel tile at conversion slot e).
-  const int hl = lane >> 4;
-  const int kk = t;
-  const float w[2][2] = {{v0 ? p0 * sv00 : 0.f, v0 ? p0 * sv01 : 0.f},
-                         {v1 ? p1 * sv10 : 0.f, v1 ? p1 * sv11 : 0.f}};
-  uint32_t hv[2][2], lv[2][2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const _Float16 hi = static_cast<_Float16>(w[p][g]);
-      const _Float16 lo = static_cast<_Float16>((w[p][g] - static_cast<float>(hi)) * kLoScale);
-      hv[p][g] = f16_bits(hi);
-      lv[p][g] = f16_bits(lo);
-    }
-  }
-  // Tile rows are 64 bytes (32 k slots); row 4hl + 2g + part, column 16p + kk.
-  // Inline assembly keeps the compiler from draining the ring DMAs before
-  // these accesses; LDS operations of one wave execute in order, so the read
-  // sees the writes.
-  const uint32_t wa = lds_addr(reinterpret_cast<const uint8_t*>(atile)) + 256 * hl + 2 * kk;
+// Write the four 4-bit digits of the 16-bit X, most significant first, to
+// rows 4*hl + d of the P tile at this lane's (page, token) column.
+__device__ __forceinline__ void put_digits(uint32_t wbase, uint32_t X) {
+  const uint32_t d0 = (X >> 12) & 15u, d1 = (X >> 8) & 15u, d2 = (X >> 4) & 15u, d3 = X & 15u;
   asm volatile(
-      "ds_write_b16 %0, %1\n"
-      "ds_write_b16 %0, %2 offset:64\n"
-      "ds_write_b16 %0, %3 offset:128\n"
-      "ds_write_b16 %0, %4 offset:192\n"
-      "ds_write_b16 %0, %5 offset:32\n"
-      "ds_write_b16 %0, %6 offset:96\n"
-      "ds_write_b16 %0, %7 offset:160\n"
-      "ds_write_b16 %0, %8 offset:224"
+      "ds_write_b8 %0, %1\n"
+      "ds_write_b8 %0, %2 offset:%5\n"
+      "ds_write_b8 %0, %3 offset:%6\n"
+      "ds_write_b8 %0, %4 offset:%7"
       :
-      : "v"(wa), "v"(hv[0][0]), "v"(lv[0][0]), "v"(hv[0][1]), "v"(lv[0][1]), "v"(hv[1][0]),
-        "v"(lv[1][0]), "v"(hv[1][1]), "v"(lv[1][1])
+      : "v"(wbase), "v"(d0), "v"(d1), "v"(d2), "v"(d3), "i"(kPRow), "i"(2 * kPRow),
+        "i"(3 * kPRow)
       : "memory");
-  const uint32_t ra =
-      lds_addr(reinterpret_cast<const uint8_t*>(atile)) + 64 * (lane & 15) + 16 * (lane >> 4);
-  u32x4 awv;
+}
+
+struct ScanState {
+  float m, l, zs0, zs1;
+  floatx4 acc[8];
+};
+
+// The P.V products of one 128-token block for output channel tiles
+// [kT0, kT1).  w = p * s_V is fixed-point with 32 fraction bits under 2^e
+// (per head and block); digit d (0 = most significant) is worth
+// b * 2^(e - 4 - 4d), an FP8 byte b * 2^-9 under the row scale 2^(e + 5 - 4d).
+// Digits 0-3 then 4-7 go through the one P tile (the second set overwrites
+// rows the first has already read back), each read back as an A operand (row
+// r = lane%16, pages g and g + 4 of lane group g = lane/16); then two MFMAs
+// per 16 output channels.
+template <int kT0, int kT1>
+__device__ __forceinline__ void block_pv(ScanState& st, const float (&w)[8], uint8_t* ptile,
+                                         const u32x4 (&vw)[4], int lane) {
+  const int t = lane & 15, hl = lane >> 4;
+  float wmax = w[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) wmax = fmaxf(wmax, w[j]);
+  wmax = row16_max(wmax);
+  const int e = exp_above(wmax);
+  uint32_t W[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    W[j] = static_cast<uint32_t>(fminf(rintf(ldexpf(w[j], 32 - e)), 4294967040.0f));
+  const uint32_t wbase = lds_addr(ptile) + 4 * hl * kPRow + t;
+  const uint32_t hdr = lds_addr(ptile) + 16 * kPRow;
+  if (t == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(hdr + 4 * hl), "v"(e) : "memory");
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t ra = lds_addr(ptile) + r * kPRow + 16 * g;
+  u32x4 h0, h1, l0, l1;
+  int er;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) put_digits(wbase + 16 * j, W[j] >> 16);
   asm volatile(
-      "ds_read_b128 %0, %1\n"
+      "ds_read_b128 %0, %3\n"
+      "ds_read_b128 %1, %3 offset:64\n"
+      "ds_read_b32 %2, %4\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(awv)
+      : "=&v"(h0), "=&v"(h1), "=&v"(er)
+      : "v"(ra), "v"(hdr + 4 * (r >> 2))
+      : "memory");
+#pragma unroll
+  for (int j = 0; j < 8; ++j) put_digits(wbase + 16 * j, W[j] & 0xFFFFu);
+  const int sa_hi = min(max(kScaleOne + er + 5 - 4 * (r & 3), 1), 254);
+  const int sa_lo = min(max(kScaleOne + er - 11 - 4 * (r & 3), 1), 254);
+  // value words: vw[0..1] = page 2g, tiles 0-7; vw[2..3] = page 2g + 1
+  u32x4 v0 = vw[0], v1 = vw[1], v2 = vw[2], v3 = vw[3];
+  {
+    const v8i A = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
+                   static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
+                   static_cast<int>(h1.z), static_cast<int>(h1.w)};
+    const uint32_t p0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const uint32_t p1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+    for (int tau = kT0; tau < kT1; ++tau)
+      st.acc[tau] = mfma128<kFmtFp8, kFmtFp6>(A, fp6_codes(p0[tau], p1[tau]), st.acc[tau], sa_hi);
+  }
+  asm volatile(
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %2 offset:64\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l0), "=&v"(l1)
       : "v"(ra)
       : "memory");
-  const half8 aw = __builtin_bit_cast(half8, awv);
-
-  // ---- P.V: D[m][channel 16j + n]; dwords (0, 1) of this lane's V codes
-  // convert to the B operands of channel tiles 0-3, dwords (2, 3) to 4-7
+  // the code operands are rebuilt rather than kept live across the two sets
+  asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
   {
-    const half32 va = codes_fp6(c.vc.x, c.vc.y);
-    st.acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<0>(va), st.acc[0], 0, 0, 0);
-    st.acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<1>(va), st.acc[1], 0, 0, 0);
-    st.acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<2>(va), st.acc[2], 0, 0, 0);
-    st.acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<3>(va), st.acc[3], 0, 0, 0);
-    const half32 vb = codes_fp6(c.vc.z, c.vc.w);
-    st.acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<0>(vb), st.acc[4], 0, 0, 0);
-    st.acc[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<1>(vb), st.acc[5], 0, 0, 0);
-    st.acc[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<2>(vb), st.acc[6], 0, 0, 0);
-    st.acc[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, slice8<3>(vb), st.acc[7], 0, 0, 0);
+    const v8i A = {static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
+                   static_cast<int>(l0.w), static_cast<int>(l1.x), static_cast<int>(l1.y),
+                   static_cast<int>(l1.z), static_cast<int>(l1.w)};
+    const uint32_t p0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const uint32_t p1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+    for (int tau = kT0; tau < kT1; ++tau)
+      st.acc[tau] = mfma128<kFmtFp8, kFmtFp6>(A, fp6_codes(p0[tau], p1[tau]), st.acc[tau], sa_lo);
+  }
+}
+
+// grid (S, Hkv * QG, B), block 256: workgroup x covers pages [x*spw, (x+1)*spw),
+// cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
+// 128 VGPRs (four waves per SIMD); group 64, with a third q.K operand and a
+// second value group, is given more registers rather than spill inside the
+// loop (a spill reload waits for every outstanding DMA).
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2, 4))) void
+split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
+             const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
+             int max_ctx, int Hq, int QG, int spw, const uint32_t* __restrict__ qa,
+             const float4* __restrict__ qf, float* __restrict__ part, int S) {
+  constexpr int PB = page_bytes_for_groups(G);
+  constexpr int kSlot = 2 * PB;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ptile[4][kPTile];
+  __shared__ float cm[4][kHT], cl[4][kHT];
+
+  const int h = blockIdx.y / QG;
+  const int qg = blockIdx.y % QG;
+  const int b = blockIdx.z;
+  const int wgs = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ctx = min(max(ctx_len[b], 0), max_ctx);
+  const int n_pages = (ctx + kBlock - 1) / kBlock;
+  const int p_begin = wgs * spw;
+  if (p_begin >= n_pages) return;
+  const int p_end = min(p_begin + spw, n_pages);
+  const int np = p_end - p_begin;
+  const int* row = block_table + static_cast<size_t>(b) * max_blocks;
+  // 8-page blocks of this range; this wave's are wave, wave + 4, ...  Only the
+  // range's last block can be short; its slices past the range are skipped.
+  const int nblk = (np + 7) >> 3;
+  const int nbw = wave < nblk ? (nblk - wave + 3) >> 2 : 0;
+  const bool owns_last = nbw > 0 && ((nblk - 1 - wave) & 3) == 0;
+  const int ns_last = owns_last ? min(4, (np - 8 * (nblk - 1) + 1) >> 1) : 4;
+  const int nsl = nbw > 0 ? 4 * (nbw - 1) + ns_last : 0;
+  auto slice_page = [&](int i) { return p_begin + 8 * (wave + 4 * (i >> 2)) + 2 * (i & 3); };
+
+  // query operand first: waiting for it must not drain the ring's DMAs
+  const size_t hgi = (static_cast<size_t>(b) * Hkv + h) * QG + qg;
+  const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
+  const uint4 q0 = qap[0], q1 = qap[1], q2 = qap[2];
+  const uint4 q3 = G == 2 ? qap[3] : make_uint4(0u, 0u, 0u, 0u);
+  const uint4 q4 = G == 2 ? qap[4] : make_uint4(0u, 0u, 0u, 0u);
+  const uint4 qsv = qap[kQaScale / 4];
+  const int t = lane & 15;
+  const int hl = lane >> 4;
+  const float4 fq = qf[hgi * kHT + hl];
+  asm volatile("" ::"v"(__builtin_bit_cast(u32x4, q0)), "v"(__builtin_bit_cast(u32x4, q1)),
+               "v"(__builtin_bit_cast(u32x4, q2)), "v"(__builtin_bit_cast(u32x4, q3)),
+               "v"(__builtin_bit_cast(u32x4, q4)), "v"(__builtin_bit_cast(u32x4, qsv)),
+               "v"(fq.y), "v"(fq.z));
+  auto op6 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
+    return v8i{static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
+               static_cast<int>(e), static_cast<int>(f), 0, 0};
+  };
+  const v8i qA0 = op6(q0.x, q0.y, q0.z, q0.w, q1.x, q1.y);
+  const v8i qA1 = op6(q1.z, q1.w, q2.x, q2.y, q2.z, q2.w);
+  const v8i qA2 = op6(q3.x, q3.y, q3.z, q3.w, q4.x, q4.y);
+  const int qsc_hi = static_cast<int>(qsv.x);
+  const int qsc_lo = static_cast<int>(qsv.y);
+  const float sq0 = G == 1 ? fq.y + fq.z : fq.y;
+  const float sq1 = fq.z;
+
+  uint8_t* myring = &ring[wave][0][0];
+  for (int i = 0; i < kDepth && i < nsl; ++i)
+    issue_slice<G>(myring + i * kSlot, pages, num_blocks, Hkv, h, row, slice_page(i), p_end,
+                   lane);
+
+  ScanState st;
+  st.m = kNegBig;
+  st.l = 0.f;
+  st.zs0 = 0.f;
+  st.zs1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  u32x4 vw[4] = {};
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int bi = 0; bi < nbw; ++bi) {
+    const int pblk = p_begin + 8 * (wave + 4 * bi);
+    float lg[8];
+    uint2 szv[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = 4 * bi + s;
+      if (i < nsl) {
+        if (i + kDepth < nsl)
+          issue_slice<G>(myring + ((i + kDepth) % kRing) * kSlot, pages, num_blocks, Hkv, h, row,
+                         slice_page(i + kDepth), p_end, lane);
+        // slice i has landed once at most the DMAs of the slices behind it are pending
+        const int behind = min(kDepth, nsl - 1 - i);
+        if (behind == 2)
+          wait_vmem<2 * kDmaPerSlice>();
+        else if (behind == 1)
+          wait_vmem<kDmaPerSlice>();
+        else
+          wait_vmem<0>();
+        // the slot base is wave-uniform; the lane offsets are kept opaque so
+        // that the compiler adds them here instead of holding every
+        // (slot, offset) sum in registers across the loop
+        const uint32_t sbase = lds_addr(myring + (i % kRing) * kSlot);
+        uint32_t ok = kKCodeOff + 32 * t + 8 * hl, os = kSzOff + 4 * G * t;
+        uint32_t ov = kVCodeOff + 32 * t;
+        asm volatile("" : "+v"(ok), "+v"(os), "+v"(ov));
+        Slice c;
+        read_slice<G>(c, sbase + ok, sbase + os);
+        if (hl == s) read_vwords(vw, sbase + ov, PB);
+
+        // q.K: D[4*head + digit][token t]; the digit rows add up in-lane
+        const v8i k0 = fp6_codes(c.kc0.x, c.kc0.y);
+        const v8i k1 = fp6_codes(c.kc1.x, c.kc1.y);
+        float l0, l1;
+        if constexpr (G == 1) {
+          // high digits, then low digits accumulated onto them
+          floatx4 d0 = mfma128<kFmtFp6, kFmtFp6>(qA0, k0, zero4, qsc_hi);
+          floatx4 d1 = mfma128<kFmtFp6, kFmtFp6>(qA0, k1, zero4, qsc_hi);
+          d0 = mfma128<kFmtFp6, kFmtFp6>(qA1, k0, d0, qsc_lo);
+          d1 = mfma128<kFmtFp6, kFmtFp6>(qA1, k1, d1, qsc_lo);
+          const float D0 = (d0[0] + d0[1]) + (d0[2] + d0[3]);
+          const float D1 = (d1[0] + d1[1]) + (d1[2] + d1[3]);
+          // logit = 8 s_K sum(x code/8) + z_K sum(x)
+          l0 = fmaf(8.0f * f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0);
+          l1 = fmaf(8.0f * f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0);
+        } else {
+          const floatx4 a0 = mfma128<kFmtFp6, kFmtFp6>(qA0, k0, zero4, qsc_hi);
+          const floatx4 a1 = mfma128<kFmtFp6, kFmtFp6>(qA0, k1, zero4, qsc_hi);
+          const floatx4 b0 = mfma128<kFmtFp6, kFmtFp6>(qA1, k0, zero4, qsc_hi);
+          const floatx4 b1 = mfma128<kFmtFp6, kFmtFp6>(qA1, k1, zero4, qsc_hi);
+          const floatx4 c0 = mfma128<kFmtFp6, kFmtFp6>(qA2, k0, zero4, qsc_lo);
+          const floatx4 c1 = mfma128<kFmtFp6, kFmtFp6>(qA2, k1, zero4, qsc_lo);
+          // group 0: rows of a plus low rows 0-1 of c; group 1: b plus c rows 2-3
+          const float D0 = ((a0[0] + a0[1]) + (a0[2] + a0[3])) + (c0[0] + c0[1]);
+          const float D1 = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + (c1[0] + c1[1]);
+          const float E0 = ((b0[0] + b0[1]) + (b0[2] + b0[3])) + (c0[2] + c0[3]);
+          const float E1 = ((b1[0] + b1[1]) + (b1[2] + b1[3])) + (c1[2] + c1[3]);
+          l0 = fmaf(8.0f * f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0) +
+               fmaf(8.0f * f16_lo_to_f32(c.szk0.y), E0, f16_hi_to_f32(c.szk0.y) * sq1);
+          l1 = fmaf(8.0f * f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0) +
+               fmaf(8.0f * f16_lo_to_f32(c.szk1.y), E1, f16_hi_to_f32(c.szk1.y) * sq1);
+        }
+        const int pg = pblk + 2 * s;
+        const int pos = pg * kBlock + t;
+        const bool v0 = pos < ctx;
+        const bool v1 = pg + 1 < p_end && pos + kBlock < ctx;
+        lg[2 * s] = v0 ? l0 : -INFINITY;
+        lg[2 * s + 1] = v1 ? l1 : -INFINITY;
+        // slots past the context hold arbitrary bytes (possibly NaN as fp16):
+        // their value scale and zero are replaced, not multiplied by p = 0
+        szv[2 * s] = v0 ? c.szv0 : make_uint2(0u, 0u);
+        szv[2 * s + 1] = v1 ? c.szv1 : make_uint2(0u, 0u);
+      } else {
+        lg[2 * s] = -INFINITY;
+        lg[2 * s + 1] = -INFINITY;
+        szv[2 * s] = make_uint2(0u, 0u);
+        szv[2 * s + 1] = make_uint2(0u, 0u);
+      }
+    }
+
+    // ---- online softmax over the block (base 2), lazy rescale
+    float mb = lg[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mb = fmaxf(mb, lg[j]);
+    const float mnew = fmaxf(st.m, row16_max(mb));
+    if (__any(mnew > st.m)) {
+      const float alpha = exp2_hw(st.m - mnew);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+      st.l *= alpha;
+      st.zs0 *= alpha;
+      st.zs1 *= alpha;
+      st.m = mnew;
+    }
+    float w0[8], w1[8];
+    float lsum = 0.f, z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = exp2_hw(lg[j] - st.m);
+      lsum += p;
+      z0 = fmaf(p, f16_hi_to_f32(szv[j].x), z0);
+      w0[j] = p * f16_lo_to_f32(szv[j].x);
+      if constexpr (G == 2) {
+        z1 = fmaf(p, f16_hi_to_f32(szv[j].y), z1);
+        w1[j] = p * f16_lo_to_f32(szv[j].y);
+      }
+    }
+    st.l += lsum;
+    st.zs0 += z0;
+    st.zs1 += z1;
+    if constexpr (G == 1) {
+      block_pv<0, 8>(st, w0, ptile[wave], vw, lane);
+    } else {
+      block_pv<0, 4>(st, w0, ptile[wave], vw, lane);
+      block_pv<4, 8>(st, w1, ptile[wave], vw, lane);
+    }
+  }
+
+  // ---- per-wave finish: reduce row sums, form unnormalised outputs
+  const float l = row16_sum(st.l);
+  const float zs0 = row16_sum(st.zs0);
+  const float zs1 = G == 2 ? row16_sum(st.zs1) : zs0;
+  const int n = lane & 15;
+  __syncthreads();  // every wave is done with its ring; reuse it for the combine
+  float(*co)[kHT][kHeadDim] = reinterpret_cast<float(*)[kHT][kHeadDim]>(&ring[0][0][0]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // digit rows add up; the code operand is code/8
+    const floatx4 a = st.acc[j];
+    co[wave][hl][16 * j + n] = 8.0f * ((a[0] + a[1]) + (a[2] + a[3])) + (j < 4 ? zs0 : zs1);
+  }
+  if (n == 0) {
+    cm[wave][hl] = st.m;
+    cl[wave][hl] = l;
+  }
+  __syncthreads();
+
+  // ---- combine the 4 waves: thread -> (head tid/64, channels c, c + 64)
+  const int ch = threadIdx.x >> 6;
+  const int cc = threadIdx.x & 63;
+  const int hloc = qg * kHT + ch;
+  const int Hg = Hq / Hkv;
+  const int nh = min(kHT, Hg - qg * kHT);
+  if (ch < nh) {
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w][ch]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = exp2_hw(cm[w][ch] - M);  // 0 for a wave that saw no token
+      L += a * cl[w][ch];
+      o0 += a * co[w][ch][cc];
+      o1 += a * co[w][ch][cc + 64];
+    }
+    const int hq = h * Hg + hloc;
+    float* dst = part + ((static_cast<size_t>(b) * Hq + hq) * S + wgs) * kPartStride;
+    const float inv = 1.0f / L;
+    dst[4 + cc] = o0 * inv;
+    dst[4 + cc + 64] = o1 * inv;
+    if (cc == 0) dst[0] = M + __log2f(L);
   }
 }
 
@@ -489,137 +766,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   }
 }
 
-// grid (S, Hkv * QG, B), block 256: workgroup x covers pages [x*spw, (x+1)*spw).
-// Capped at 128 VGPRs so that four waves share each SIMD: the scan is bound by
-// the latency of its per-chunk dependency chain more than by issue slots.
-template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void split_kernel(
-    const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
-    const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
-    int max_ctx, int Hq, int QG, int spw, const uint4* __restrict__ qa,
-    const float4* __restrict__ qf, float* __restrict__ part, int S) {
-  constexpr int kSlot = 2 * page_bytes_for_groups(G);
-  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
-  __shared__ __attribute__((aligned(16))) _Float16 atile[4][16 * 32];
-  __shared__ float cm[4][kHT], cl[4][kHT];
-
-  const int h = blockIdx.y / QG;
-  const int qg = blockIdx.y % QG;
-  const int b = blockIdx.z;
-  const int wgs = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ctx = min(max(ctx_len[b], 0), max_ctx);
-  const int n_pages = (ctx + kBlock - 1) / kBlock;
-  const int p_begin = wgs * spw;
-  if (p_begin >= n_pages) return;
-  const int p_end = min(p_begin + spw, n_pages);
-  const int n_chunks = (p_end - p_begin + 1) >> 1;
-  const int* row = block_table + static_cast<size_t>(b) * max_blocks;
-  // this wave's chunks: c_i = wave + 4i
-  const int nc = wave < n_chunks ? (n_chunks - wave + 3) / 4 : 0;
-  // query operand first: waiting for it must not drain the ring's DMAs
-  const size_t hgi = (static_cast<size_t>(b) * Hkv + h) * QG + qg;
-  const uint4* qap = qa + (hgi * 64 + lane) * 4;
-  half8 qA[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) qA[j] = __builtin_bit_cast(half8, qap[j]);
-  const int hl = lane >> 4;
-  const float4 fq = qf[hgi * kHT + hl];
-  // consume them here, so the wait for these loads is placed before the DMAs
-  asm volatile("" ::"v"(qA[0]), "v"(qA[1]), "v"(qA[2]), "v"(qA[3]), "v"(fq.x), "v"(fq.y),
-               "v"(fq.z));
-
-  uint8_t* myring = &ring[wave][0][0];
-  for (int i = 0; i < kDepth && i < nc; ++i)
-    issue_chunk<G>(myring + i * kSlot, pages, num_blocks, Hkv, h, row,
-                   p_begin + 2 * (wave + 4 * i), p_end, lane);
-
-  SoftmaxState st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-  st.zs0 = 0.f;
-  st.zs1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) st.acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int i = 0; i < nc; ++i) {
-    if (i + kDepth < nc)
-      issue_chunk<G>(myring + ((i + kDepth) % kRing) * kSlot, pages, num_blocks, Hkv, h, row,
-                     p_begin + 2 * (wave + 4 * (i + kDepth)), p_end, lane);
-    // chunk i has landed once at most the DMAs of the chunks behind it are pending
-    const int behind = min(kDepth, nc - 1 - i);
-    if (behind == 2)
-      wait_vmem<2 * kDmaPerChunk>();
-    else if (behind == 1)
-      wait_vmem<kDmaPerChunk>();
-    else
-      wait_vmem<0>();
-    Chunk c;
-    read_chunk<G>(c, myring + (i % kRing) * kSlot, p_begin + 2 * (wave + 4 * i), lane);
-    compute_chunk<G>(c, st, qA, fq.x, fq.y, fq.z, ctx, p_end, lane, atile[wave]);
-  }
-
-  // ---- per-wave finish: reduce row sums, form unnormalised outputs
-  const float l = row16_sum(st.l);
-  const float zs0 = row16_sum(st.zs0);
-  const float zs1 = row16_sum(st.zs1);
-  const int n = lane & 15;
-  __syncthreads();  // every wave is done with its ring; reuse it for the combine
-  float(*co)[kHT][kHeadDim] = reinterpret_cast<float(*)[kHT][kHeadDim]>(&ring[0][0][0]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int g = j >> 2;
-    // code operand = code/8: sum(w * code) = 8 * D
-    const float val = 8.0f * fmaf(st.acc[j][2 * g + 1], kLoUnscale, st.acc[j][2 * g]) +
-                      (g ? zs1 : zs0);
-    co[wave][hl][16 * j + n] = val;
-  }
-  if (n == 0) {
-    cm[wave][hl] = st.m;
-    cl[wave][hl] = l;
-  }
-  __syncthreads();
-
-  // ---- combine the 4 waves: thread -> (head tid/64, channels c, c + 64)
-  const int ch = threadIdx.x >> 6;
-  const int cc = threadIdx.x & 63;
-  const int hloc = qg * kHT + ch;
-  const int Hg = Hq / Hkv;
-  const int nh = min(kHT, Hg - qg * kHT);
-  if (ch < nh) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w][ch]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = (cm[w][ch] == -INFINITY) ? 0.f : exp2_hw(cm[w][ch] - M);
-      L += a * cl[w][ch];
-      o0 += a * co[w][ch][cc];
-      o1 += a * co[w][ch][cc + 64];
-    }
-    const int hq = h * Hg + hloc;
-    float* dst = part + ((static_cast<size_t>(b) * Hq + hq) * S + wgs) * kPartStride;
-    const float inv = 1.0f / L;
-    dst[4 + cc] = o0 * inv;
-    dst[4 + cc + 64] = o1 * inv;
-    if (cc == 0) dst[0] = M + __log2f(L);
-  }
-}
 // --------------------------------------------------------------------------- host side
-
-
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Pages per split: about 1024 workgroups (four per CU), in whole 32-page
+// steps so that each wave gets whole 8-page blocks.
 int choose_split_pages(int B, int Hkv, int QG, int max_ctx) {
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
   const int64_t total = static_cast<int64_t>(B) * Hkv * QG * max_pages;
-  const int64_t target_wgs = 1024;  // 4 waves each: 16 waves per CU on 256 CUs
-  int64_t spw = (total + target_wgs - 1) / target_wgs;
-  spw = (spw + 7) / 8 * 8;
-  if (spw < 8) spw = 8;
-  if (spw > 256) spw = 256;
+  int64_t spw = (total / 1024 + 16) / 32 * 32;
+  if (spw < 32) spw = 32;
+  if (spw > 512) spw = 512;
   return static_cast<int>(spw);
 }
 
@@ -632,7 +789,7 @@ DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages) {
   p.S = static_cast<int>((max_pages + p.spw - 1) / p.spw);
   const size_t hg = static_cast<size_t>(B) * Hkv * p.QG;
   p.qa_off = 0;
-  p.qf_off = align256(hg * 64 * 64);
+  p.qf_off = align256(hg * 64 * kQaDwords * 4);
   p.part_off = p.qf_off + align256(hg * kHT * 16);
   p.total = p.part_off + align256(static_cast<size_t>(B) * Hq * (p.S ? p.S : 1) * kPartStride * 4);
   return p;
@@ -644,18 +801,27 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                   float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
                   hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint4* qa = reinterpret_cast<uint4*>(ws + p.qa_off);
+  uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
   float* part = reinterpret_cast<float*>(ws + p.part_off);
   const float qscale = sm_scale * kLog2e;
   if (p.S > 0 && (stages & 1)) {
     const dim3 g1(Hkv * p.QG, B);
-    if (q_bf16)
-      hipLaunchKernelGGL(prologue_kernel<true>, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv, p.QG,
-                         qscale, qa, qf);
-    else
-      hipLaunchKernelGGL(prologue_kernel<false>, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv,
-                         p.QG, qscale, qa, qf);
+    if (q_bf16) {
+      if (G == 2)
+        hipLaunchKernelGGL((prologue_kernel<true, 2>), g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv,
+                           p.QG, qscale, qa, qf);
+      else
+        hipLaunchKernelGGL((prologue_kernel<true, 1>), g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv,
+                           p.QG, qscale, qa, qf);
+    } else {
+      if (G == 2)
+        hipLaunchKernelGGL((prologue_kernel<false, 2>), g1, dim3(256), 0, stream, q, rot_k, Hq,
+                           Hkv, p.QG, qscale, qa, qf);
+      else
+        hipLaunchKernelGGL((prologue_kernel<false, 1>), g1, dim3(256), 0, stream, q, rot_k, Hq,
+                           Hkv, p.QG, qscale, qa, qf);
+    }
   }
   if (p.S > 0 && (stages & 2)) {
     const dim3 g2(p.S, Hkv * p.QG, B);

@@ -9,7 +9,7 @@ namespace kvq {
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 16;          // tokens per page
 constexpr int kKCodeOff = 0;        // 16 rows x 32 bytes
-constexpr int kVCodeOff = 512;      // 64 16-bit chunks
+constexpr int kVCodeOff = 512;      // 128 32-bit words, one per channel
 constexpr int kSzOff = 1024;        // K (scale, zero) pairs, then V pairs
 constexpr float kF16Max = 65504.0f;
 

@@ -186,7 +186,7 @@ def test_key_centring_leaves_softmax_unchanged_exactly():
 def test_layout_golden_examples():
     lines = [ln.split() for ln in open(os.path.join(GOLDEN, "layout_examples.txt"))
              if ln.strip() and not ln.startswith("#")]
-    assert len(lines) == 8
+    assert len(lines) == 9
     for kind, t, i, code, byte, value in lines:
         t, i, code, byte, value = int(t), int(i), int(code), int(byte), int(value, 16)
         site = O.k_code_site if kind == "k" else O.v_code_site
