@@ -235,29 +235,28 @@ __global__ __launch_bounds__(256) void append_kernel(
 
 // ---------------------------------------------------------------------------
 // One new token per sequence (the decode-step append).  Workgroup = (KV head,
-// sequence), 256 threads: threads 0-127 own rotated key channel j = tid, threads
-// 128-255 rotated value channel j = tid - 128.  Each computes its channel as a
-// 128-term dot product with column j of R (coalesced across threads), reduces
-// group min/max across the channel's group (one wave for group 64, two waves
-// through LDS for group 128), rounds, and writes: key codes are gathered four
-// to a byte by lane shuffles; each value code goes to a byte of the value
-// block that no other thread of the call touches, updated read-modify-write.
+// sequence), 1024 threads.  The two 128 x 128 rotations are split four ways
+// along the input channel: thread (mat, quarter, j) loads its 32 rows of
+// column j of R_K or R_V (all loads in flight at once, coalesced across j)
+// and forms a partial dot product; the partials meet in LDS.  Threads 0-255
+// then own one rotated channel each (0-127 keys, 128-255 values), reduce group
+// min/max across the channel's group (one wave for group 64, two waves
+// through LDS for group 128), round and write: key codes are gathered four to
+// a byte by lane shuffles; each value code goes to a byte of the value block
+// that no other thread of the call touches, updated read-modify-write.
 template <bool kBf16>
-__global__ __launch_bounds__(256) void append_one_kernel(
+__global__ __launch_bounds__(1024) void append_one_kernel(
     uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
     const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ mu,
     const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
     float clip_v) {
   __shared__ float a_s[2][kHeadDim];
+  __shared__ float part[2][4][kHeadDim];
   __shared__ float red[4][2];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int mat = tid >> 7;
-  const int j = tid & 127;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
 
   const int pos = start_pos[b];
   if (pos < 0 || pos / kBlock >= max_blocks) return;
@@ -267,35 +266,48 @@ __global__ __launch_bounds__(256) void append_one_kernel(
   uint8_t* page = pages + (static_cast<int64_t>(blk) * Hkv + h) * PB;
   const int t = pos % kBlock;
 
+  // split-K partial products: thread -> (mat, quarter kq, column jc)
+  {
+    const int pm = tid >> 9, kq = (tid >> 7) & 3, jc = tid & 127;
+    const float* R = (pm ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim +
+                     32 * kq * kHeadDim + jc;
+    float rcol[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) rcol[i] = R[i * kHeadDim];
+    if (kq == 0) {
+      const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim + jc;
+      float x;
+      if constexpr (kBf16)
+        x = bf16_to_f32((pm ? static_cast<const uint16_t*>(v) : static_cast<const uint16_t*>(k))[off]);
+      else
+        x = (pm ? static_cast<const float*>(v) : static_cast<const float*>(k))[off];
+      if (pm == 0) x -= mu[h * kHeadDim + jc];
+      a_s[pm][jc] = x;
+    }
+    __syncthreads();
+    const float* a = a_s[pm] + 32 * kq;
+    float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      x0 = fmaf(a[i], rcol[i], x0);
+      x1 = fmaf(a[i + 1], rcol[i + 1], x1);
+      x2 = fmaf(a[i + 2], rcol[i + 2], x2);
+      x3 = fmaf(a[i + 3], rcol[i + 3], x3);
+    }
+    part[pm][kq][jc] = (x0 + x1) + (x2 + x3);
+  }
+  __syncthreads();
+
+  const bool own = tid < 256;  // threads 0-255 own one rotated channel each
+  const int mat = (tid >> 7) & 1;
+  const int j = tid & 127;
+  const int wave = (tid >> 6) & 3;
   // the value byte this thread will update (read early; only this thread writes
   // it): word 8*(j % 16) + j / 16, code position 3t mod 16
   const int u = (3 * t) & 15;
   uint8_t* vdst = page + kVCodeOff + 4 * (8 * (j & 15) + (j >> 4)) + (u >> 2);
-  const uint32_t vold = mat ? *vdst : 0u;
-
-  {
-    const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim + j;
-    float x;
-    if constexpr (kBf16)
-      x = bf16_to_f32((mat ? static_cast<const uint16_t*>(v) : static_cast<const uint16_t*>(k))[off]);
-    else
-      x = (mat ? static_cast<const float*>(v) : static_cast<const float*>(k))[off];
-    if (mat == 0) x -= mu[h * kHeadDim + j];
-    a_s[mat][j] = x;
-  }
-  __syncthreads();
-
-  const float* R = (mat ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim + j;
-  const float* a = a_s[mat];
-  float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
-#pragma unroll 8
-  for (int i = 0; i < kHeadDim; i += 4) {
-    x0 = fmaf(a[i], R[i * kHeadDim], x0);
-    x1 = fmaf(a[i + 1], R[(i + 1) * kHeadDim], x1);
-    x2 = fmaf(a[i + 2], R[(i + 2) * kHeadDim], x2);
-    x3 = fmaf(a[i + 3], R[(i + 3) * kHeadDim], x3);
-  }
-  const float x = (x0 + x1) + (x2 + x3);
+  const uint32_t vold = (own && mat) ? *vdst : 0u;
+  const float x = (part[mat][0][j] + part[mat][1][j]) + (part[mat][2][j] + part[mat][3][j]);
 
   float mn = x, mx = x;
 #pragma unroll
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(256) void append_one_kernel(
     mx = fmaxf(mx, shfl_xor(mx, m));
   }
   if (G == 1) {  // group of 128 channels spans this thread's two waves
-    if (lane == 0) {
+    if (own && (tid & 63) == 0) {
       red[wave][0] = mn;
       red[wave][1] = mx;
     }
@@ -313,6 +325,7 @@ __global__ __launch_bounds__(256) void append_one_kernel(
     mn = fminf(red[w0][0], red[w0 + 1][0]);
     mx = fmaxf(red[w0][1], red[w0 + 1][1]);
   }
+  if (!own) return;
   const float clip = mat ? clip_v : clip_k;
   const float lo = clip * mn;
   const float hi = clip * mx;
@@ -347,11 +360,11 @@ int launch_append(uint8_t* pages, int64_t num_blocks, int Hkv, int G, const int*
   if (T == 1) {
     const dim3 grid(Hkv, B);
     if (bf16)
-      hipLaunchKernelGGL(append_one_kernel<true>, grid, dim3(256), 0, stream, pages, num_blocks,
+      hipLaunchKernelGGL(append_one_kernel<true>, grid, dim3(1024), 0, stream, pages, num_blocks,
                          Hkv, G, block_table, max_blocks, start_pos, k, v, mu, rot_k, rot_v,
                          clip_k, clip_v);
     else
-      hipLaunchKernelGGL(append_one_kernel<false>, grid, dim3(256), 0, stream, pages, num_blocks,
+      hipLaunchKernelGGL(append_one_kernel<false>, grid, dim3(1024), 0, stream, pages, num_blocks,
                          Hkv, G, block_table, max_blocks, start_pos, k, v, mu, rot_k, rot_v,
                          clip_k, clip_v);
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -23,8 +23,8 @@
 //      of the word).  q.K runs as 16x16x128 FP6 x FP6 MFMAs per page (two
 //      digit operands, three for group 64); P.V as two 16x16x128 FP8 x FP6
 //      MFMAs per 16 output channels and block, with the softmax weights p*s_V
-//      again fixed-point (32 bits under a per-head, per-block power of two)
-//      split into eight 4-bit digits, each digit b an FP8 byte worth b*2^-9.
+//      again fixed-point (24 bits under a per-head, per-block power of two)
+//      split into six 4-bit digits, each digit b an FP8 byte worth b*2^-9.
 //      Digits and codes are short enough that the MFMA sums are exact before
 //      the fp32 accumulation.
 //      The four waves of a workgroup combine their (max, sum, output) in LDS;
@@ -37,7 +37,6 @@
 #include "kvq_common.h"
 #include "kvq_launch.h"
 
-#include <array>
 
 namespace kvq {
 
@@ -84,13 +83,24 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // exponent e with |x| < 2^e <= 2|x| (0 for x == 0)
 __device__ __forceinline__ int exp_above(float x) { return __builtin_amdgcn_frexp_expf(x); }
 
+// Splits of a context of n_pages pages: round(n_pages / spw) of them (at least
+// one for a non-empty context), spw pages each except the last, which takes
+// the rest (between spw/2 and 3spw/2 pages), so that a context a few pages
+// past a multiple of spw does not start a nearly empty workgroup after all
+// the others.
+__host__ __device__ inline int num_splits(int n_pages, int spw) {
+  if (n_pages <= 0) return 0;
+  return max(1, (n_pages + spw / 2) / spw);
+}
+
 // --------------------------------------------------------------------------- prologue
 // grid (Hkv * QG, B), block 256: wave w rotates query head 4*qg + w of KV head
 // h; then 64 threads pack the A operands lane by lane.
 //
 // |x| is fixed-point with 32 fraction bits under 2^e: eight 4-bit digits,
 // digit d (0 = most significant) worth b * 2^(e - 4 - 4d), as the FP6 value
-// b/8 under the row scale 2^(e - 1 - 4d).  In an A operand, lane L has row
+// b/8 under the row scale 2^(e + 2 - 4d): the extra 8 cancels the code
+// operand's code/8, so the MFMA rows sum to x . code.  In an A operand, lane L has row
 // r = L%16 and lane group g = L/16; FP6 field j (k = 32g + j) is channel
 // 32g + 16(j/16) + (3(j%16) mod 16), the channel order fp6_codes gives the
 // key code words.
@@ -107,46 +117,66 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
                                                        uint32_t* __restrict__ qa,
                                                        float4* __restrict__ qf) {
   __shared__ float qin[kHT][kHeadDim];
-  __shared__ uint32_t qw[kHT][kHeadDim];  // |x| fixed-point, 32 fraction bits under 2^e
-  __shared__ uint8_t qs[kHT][kHeadDim];   // sign of x
+  __shared__ float red[4][kHT][kHeadDim];  // split-K partial products
+  __shared__ uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
   __shared__ int qe[kHT];
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
   const int Hg = Hq / Hkv;
-  const int lane = threadIdx.x & 63;
-  const int hl = threadIdx.x >> 6;
-  const int hloc = qg * kHT + hl;
-  const bool valid = hloc < Hg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int nh = min(kHT, Hg - qg * kHT);
 
-  const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + hloc) * kHeadDim;
-  float q0 = 0.f, q1 = 0.f;
-  if (valid) {
-    if constexpr (kBf16) {
-      const uint16_t* qq = static_cast<const uint16_t*>(q) + qrow;
-      q0 = bf16_to_f32(qq[lane]);
-      q1 = bf16_to_f32(qq[lane + 64]);
-    } else {
-      const float* qq = static_cast<const float*>(q) + qrow;
-      q0 = qq[lane];
-      q1 = qq[lane + 64];
+  // the tile's query rows (zero for rows past the KV head's query heads)
+  {
+    const int hh = tid >> 6, c = (tid & 63) * 2;
+    float v0 = 0.f, v1 = 0.f;
+    if (hh < nh) {
+      const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + hh) * kHeadDim + c;
+      if constexpr (kBf16) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + qrow);
+        v0 = bf16_to_f32(static_cast<uint16_t>(u & 0xffffu));
+        v1 = bf16_to_f32(static_cast<uint16_t>(u >> 16));
+      } else {
+        const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(q) + qrow);
+        v0 = f.x;
+        v1 = f.y;
+      }
     }
+    qin[hh][c] = v0;
+    qin[hh][c + 1] = v1;
   }
-  qin[hl][lane] = q0;
-  qin[hl][lane + 64] = q1;
+  // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
+  // before the products, one pass over R_K for the four heads
+  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
+  float ra[32], rb[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    ra[i] = R[i * kHeadDim + lane];
+    rb[i] = R[i * kHeadDim + lane + 64];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < kHT; ++hh) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float qi = qin[hh][32 * wv + i];
+      a0 = fmaf(qi, ra[i], a0);
+      a1 = fmaf(qi, rb[i], a1);
+    }
+    red[wv][hh][lane] = a0;
+    red[wv][hh][lane + 64] = a1;
+  }
   __syncthreads();
 
-  // x[j] = qscale * sum_i q[i] R_K[i][j]; lane computes j = lane and j = lane + 64.
-  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim;
-  float r0 = 0.f, r1 = 0.f;
-  if (valid) {
-#pragma unroll 16
-    for (int i = 0; i < kHeadDim; ++i) {
-      const float qi = qin[hl][i];
-      r0 = fmaf(qi, R[i * kHeadDim + lane], r0);
-      r1 = fmaf(qi, R[i * kHeadDim + lane + 64], r1);
-    }
-  }
+  // wave hl: x = qscale * q_r of head hl, channels lane and lane + 64
+  const int hl = wv;
+  float r0 = ((red[0][hl][lane] + red[1][hl][lane]) + (red[2][hl][lane] + red[3][hl][lane]));
+  float r1 = ((red[0][hl][lane + 64] + red[1][hl][lane + 64]) +
+              (red[2][hl][lane + 64] + red[3][hl][lane + 64]));
   r0 *= qscale;  // logits in log2 units
   r1 *= qscale;
   float amax = fmaxf(fabsf(r0), fabsf(r1));
@@ -157,15 +187,21 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
     s0 += shfl_xor(s0, m);
     s1 += shfl_xor(s1, m);
   }
-  // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest
+  // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest; digit d
+  // (0 = most significant) as the FP6 field sign | nibble
   const int e = min(max(exp_above(amax), -100), 100);
-  auto fixed32 = [&](float x) -> uint32_t {
-    return static_cast<uint32_t>(fminf(rintf(ldexpf(fabsf(x), 32 - e)), 4294967040.0f));
+  auto digits = [&](float x, int ch) {
+    const uint32_t W =
+        static_cast<uint32_t>(fminf(rintf(ldexpf(fabsf(x), 32 - e)), 4294967040.0f));
+    const uint32_t sg = x < 0.f ? 0x20u : 0u;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t nib = (W >> (28 - 4 * d)) & 15u;
+      dig[hl][ch][d] = static_cast<uint8_t>(nib ? (nib | sg) : 0u);
+    }
   };
-  qw[hl][lane] = fixed32(r0);
-  qw[hl][lane + 64] = fixed32(r1);
-  qs[hl][lane] = r0 < 0.f;
-  qs[hl][lane + 64] = r1 < 0.f;
+  digits(r0, lane);
+  digits(r1, lane + 64);
   if (lane == 0) {
     qe[hl] = e;
     // per-group sums of x for the zero-point term (channels < 64, >= 64)
@@ -173,43 +209,52 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
   }
   __syncthreads();
 
-  if (threadIdx.x < 64) {
-    const int L = threadIdx.x;
+  // thread (operand, lane L): FP6 field j of lane L (row r = L%16, lane group
+  // g = L/16) holds the digit of channel 32g + 16(j/16) + (3(j%16) mod 16)
+  constexpr int kOps = G == 1 ? 2 : 3;
+  const int op = wv;
+  if (op < kOps) {
+    const int L = lane;
     const int r = L & 15, g = L >> 4;
     const int head = r >> 2;
-    // FP6 operand: field j = digit dig(j) of channel ch(j), or 0 if !use(j)
-    auto pack = [&](auto digit_of, bool use) {
-      uint64_t bits[3] = {0, 0, 0};
+    int digit;
+    bool use = true;
+    if (op == 0) {
+      digit = r & 3;
+      if (G == 2) use = g < 2;
+    } else if (op == 1 && G == 1) {
+      digit = 4 + (r & 3);
+    } else if (op == 1) {
+      digit = r & 3;
+      use = g >= 2;
+    } else {
+      digit = 4 + (r & 1);
+      use = (g >> 1) == ((r >> 1) & 1);
+    }
+    uint64_t bits[3] = {0, 0, 0};
+    if (use) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const int ch = 32 * g + 16 * (j >> 4) + ((3 * (j & 15)) & 15);
-        const uint32_t nib = (qw[head][ch] >> (28 - 4 * digit_of)) & 15u;
-        const uint64_t field = (use && nib) ? (nib | (static_cast<uint32_t>(qs[head][ch]) << 5)) : 0u;
+        const uint64_t field = dig[head][ch][digit];
         const int bit = 6 * j;
         bits[bit >> 6] |= field << (bit & 63);
         if ((bit & 63) > 58) bits[(bit >> 6) + 1] |= field >> (64 - (bit & 63));
       }
-      uint32_t op[6];
-      for (int d = 0; d < 6; ++d) op[d] = static_cast<uint32_t>(bits[d >> 1] >> (32 * (d & 1)));
-      return std::array<uint32_t, 6>{op[0], op[1], op[2], op[3], op[4], op[5]};
-    };
-    uint32_t* dst = qa + (((static_cast<size_t>(b) * Hkv + h) * QG + qg) * 64 + L) * kQaDwords;
-    auto store = [&](int at, const std::array<uint32_t, 6>& op) {
-      for (int d = 0; d < 6; ++d) dst[at + d] = op[d];
-    };
-    const int dhi = r & 3;
-    if constexpr (G == 1) {
-      store(0, pack(dhi, true));
-      store(6, pack(4 + dhi, true));
-      dst[kQaScale + 1] = static_cast<uint32_t>(min(max(kScaleOne + qe[head] - 17 - 4 * dhi, 1), 254));
-    } else {
-      store(0, pack(dhi, g < 2));
-      store(6, pack(dhi, g >= 2));
-      const int gam = (r >> 1) & 1, dlo = 4 + (r & 1);
-      store(12, pack(dlo, (g >> 1) == gam));
-      dst[kQaScale + 1] = static_cast<uint32_t>(min(max(kScaleOne + qe[head] - 1 - 4 * dlo, 1), 254));
     }
-    dst[kQaScale] = static_cast<uint32_t>(min(max(kScaleOne + qe[head] - 1 - 4 * dhi, 1), 254));
+    uint32_t* dst = qa + (((static_cast<size_t>(b) * Hkv + h) * QG + qg) * 64 + L) * kQaDwords;
+#pragma unroll
+    for (int d = 0; d < 6; ++d)
+      dst[6 * op + d] = static_cast<uint32_t>(bits[d >> 1] >> (32 * (d & 1)));
+    if (op == 0)
+      dst[kQaScale] =
+          static_cast<uint32_t>(min(max(kScaleOne + qe[head] + 2 - 4 * (r & 3), 1), 254));
+    if (op == kOps - 1) {
+      // low-digit operand: digit 4 + r%4 (group 128) or 4 + r%2 (group 64)
+      const int dlo = G == 1 ? 4 + (r & 3) : 4 + (r & 1);
+      dst[kQaScale + 1] =
+          static_cast<uint32_t>(min(max(kScaleOne + qe[head] + 2 - 4 * dlo, 1), 254));
+    }
   }
 }
 
@@ -218,25 +263,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
 // global->LDS DMA (no VGPRs held while in flight).  A slot holds the two page
 // images exactly as laid out in the cache: codes [0, 1024) and (scale, zero)
 // pairs [1024, 1024 + 128G).  One slice is kDmaPerSlice DMA instructions.
+// Two slices in flight per wave (measured on the 36-layer stream: one is too
+// few, three no better); the P tile lives in a ring slot.
 constexpr int kDepth = 2;
 constexpr int kRing = kDepth + 1;
 constexpr int kDmaPerSlice = 4;
 // P tile: 16 rows (4 heads x 4 digits) x 8 pages x 16 tokens of FP8 digit
 // bytes; the row stride is padded to 144 bytes so that the A-operand reads
-// (16 rows at one page) and the digit writes spread over all LDS banks.  The
-// four per-head exponents follow the rows.
+// (16 rows at one page) and the digit writes spread over all LDS banks.  It
+// lives in the ring slot of the block's last slice, which is free from the
+// moment that slice is read until the next slice's DMA is issued.
 constexpr int kPRow = 144;
-constexpr int kPTile = 16 * kPRow + 16;
+constexpr int kPTile = 16 * kPRow;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef const __attribute__((address_space(1))) void gbl_void_t;
-
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
-}
 
 // The compiler does not track when an LDS DMA lands: waits are explicit, and
 // the memory clobber keeps LDS reads and DMA issues on their side of them.
@@ -249,26 +289,45 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
 }
 
-// DMA the two pages [pg0, pg0 + 1] of this (sequence, KV head) into a slot; a
-// page past the range is replaced by pg0 (its tokens are masked out).
+// Physical blocks of the two pages [pg0, pg0 + 1] of a slice, clamped into
+// the cache (a page past the range repeats pg0; its tokens are masked out).
+// Loaded one slice before their DMAs are issued so that the scalar loads are
+// never waited for on the critical path.
+struct SliceIds {
+  int b0, b1;
+};
+__device__ __forceinline__ SliceIds load_ids(const int* __restrict__ row, int pg0, int p_end,
+                                             int max_block) {
+  const int b0 = row[pg0];
+  const int b1 = (pg0 + 1 < p_end) ? row[pg0 + 1] : b0;
+  return {static_cast<int>(min(static_cast<uint32_t>(b0), static_cast<uint32_t>(max_block))),
+          static_cast<int>(min(static_cast<uint32_t>(b1), static_cast<uint32_t>(max_block)))};
+}
+
+// DMA a slice's two pages into a ring slot.  Each page is a buffer resource
+// built in scalar registers (base = the page, 1 record per byte up to the page
+// size); the per-lane offsets are fixed, so issuing takes no vector ALU work.
+constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
+
+template <int G>
+__device__ __forceinline__ void dma_page(const uint8_t* page, uint8_t* slot, uint32_t off16,
+                                         uint32_t off4, bool sz_lane) {
+  constexpr int PB = page_bytes_for_groups(G);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page), 0, PB, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)slot, 16, off16, 0, 0, 0);
+  if (sz_lane)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSzOff), 4, off4, 0, 0, 0);
+}
+
 template <int G>
 __device__ __forceinline__ void issue_slice(uint8_t* slot, const uint8_t* __restrict__ pages,
-                                            int64_t num_blocks, int Hkv, int h,
-                                            const int* __restrict__ row, int pg0, int p_end,
-                                            int lane) {
+                                            int Hkv, int h, SliceIds ids, uint32_t off16,
+                                            uint32_t off4, bool sz_lane) {
   constexpr int PB = page_bytes_for_groups(G);
-  int b0 = row[pg0];
-  int b1 = (pg0 + 1 < p_end) ? row[pg0 + 1] : b0;
-  b0 = static_cast<int>(min(static_cast<int64_t>(static_cast<uint32_t>(b0)), num_blocks - 1));
-  b1 = static_cast<int>(min(static_cast<int64_t>(static_cast<uint32_t>(b1)), num_blocks - 1));
-  const uint8_t* p0 = pages + (static_cast<int64_t>(b0) * Hkv + h) * PB;
-  const uint8_t* p1 = pages + (static_cast<int64_t>(b1) * Hkv + h) * PB;
-  dma16(p0 + 16 * lane, slot);
-  dma16(p1 + 16 * lane, slot + PB);
-  if (G == 2 || lane < 32) {
-    dma4(p0 + kSzOff + 4 * lane, slot + kSzOff);
-    dma4(p1 + kSzOff + 4 * lane, slot + PB + kSzOff);
-  }
+  dma_page<G>(pages + (static_cast<int64_t>(ids.b0) * Hkv + h) * PB, slot, off16, off4, sz_lane);
+  dma_page<G>(pages + (static_cast<int64_t>(ids.b1) * Hkv + h) * PB, slot + PB, off16, off4,
+              sz_lane);
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -345,7 +404,7 @@ __device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av, int PB)
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp<0xb1>(v));
@@ -362,10 +421,10 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// Write the four 4-bit digits of the 16-bit X, most significant first, to
-// rows 4*hl + d of the P tile at this lane's (page, token) column.
-__device__ __forceinline__ void put_digits(uint32_t wbase, uint32_t X) {
-  const uint32_t d0 = (X >> 12) & 15u, d1 = (X >> 8) & 15u, d2 = (X >> 4) & 15u, d3 = X & 15u;
+// Write four digit bytes to rows 4*hl + 0..3 of the P tile at this lane's
+// (page, token) column.
+__device__ __forceinline__ void put_digits(uint32_t wbase, uint32_t d0, uint32_t d1, uint32_t d2,
+                                           uint32_t d3) {
   asm volatile(
       "ds_write_b8 %0, %1\n"
       "ds_write_b8 %0, %2 offset:%5\n"
@@ -383,35 +442,39 @@ struct ScanState {
 };
 
 // The P.V products of one 128-token block for output channel tiles
-// [kT0, kT1).  w = p * s_V is fixed-point with 32 fraction bits under 2^e
-// (per head and block); digit d (0 = most significant) is worth
-// b * 2^(e - 4 - 4d), an FP8 byte b * 2^-9 under the row scale 2^(e + 5 - 4d).
-// Digits 0-3 then 4-7 go through the one P tile (the second set overwrites
-// rows the first has already read back), each read back as an A operand (row
-// r = lane%16, pages g and g + 4 of lane group g = lane/16); then two MFMAs
-// per 16 output channels.
+// [kT0, kT1).  w = p * s_V is fixed-point with 24 fraction bits under 2^e
+// (per head and block, rounded to nearest); digit d (0 = most significant) is worth
+// b * 2^(e - 4 - 4d), an FP8 byte b * 2^-9 under the row scale
+// 2^(e + 8 - 4d) (which also cancels the code operand's code/8).  Digits 0-3,
+// then 4-5 (rows 2 and 3 of each head zero), go through the one P tile (the
+// second set overwrites rows the first has already read back), each read back
+// as an A operand (row r = lane%16, pages g and g + 4 of lane group
+// g = lane/16); then two MFMAs per 16 output channels on one code operand.
 template <int kT0, int kT1>
 __device__ __forceinline__ void block_pv(ScanState& st, const float (&w)[8], uint8_t* ptile,
-                                         const u32x4 (&vw)[4], int lane) {
+                                         int* pexp, const u32x4 (&vw)[4], int lane) {
   const int t = lane & 15, hl = lane >> 4;
   float wmax = w[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) wmax = fmaxf(wmax, w[j]);
   wmax = row16_max(wmax);
-  const int e = exp_above(wmax);
+  // w < 2^(e-1): w * 2^(24 - e) + 1/2 < 2^23, so rounding never carries out
+  const int e = exp_above(wmax) + 1;
+  const float sc = ldexpf(1.0f, 24 - e);
   uint32_t W[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    W[j] = static_cast<uint32_t>(fminf(rintf(ldexpf(w[j], 32 - e)), 4294967040.0f));
+  for (int j = 0; j < 8; ++j) W[j] = static_cast<uint32_t>(fmaf(w[j], sc, 0.5f));
   const uint32_t wbase = lds_addr(ptile) + 4 * hl * kPRow + t;
-  const uint32_t hdr = lds_addr(ptile) + 16 * kPRow;
+  const uint32_t hdr = lds_addr(reinterpret_cast<const uint8_t*>(pexp));
   if (t == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(hdr + 4 * hl), "v"(e) : "memory");
   const int r = lane & 15, g = lane >> 4;
   const uint32_t ra = lds_addr(ptile) + r * kPRow + 16 * g;
   u32x4 h0, h1, l0, l1;
   int er;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) put_digits(wbase + 16 * j, W[j] >> 16);
+  for (int j = 0; j < 8; ++j)
+    put_digits(wbase + 16 * j, (W[j] >> 20) & 15u, (W[j] >> 16) & 15u, (W[j] >> 12) & 15u,
+               (W[j] >> 8) & 15u);
   asm volatile(
       "ds_read_b128 %0, %3\n"
       "ds_read_b128 %1, %3 offset:64\n"
@@ -421,21 +484,7 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&w)[8], uin
       : "v"(ra), "v"(hdr + 4 * (r >> 2))
       : "memory");
 #pragma unroll
-  for (int j = 0; j < 8; ++j) put_digits(wbase + 16 * j, W[j] & 0xFFFFu);
-  const int sa_hi = min(max(kScaleOne + er + 5 - 4 * (r & 3), 1), 254);
-  const int sa_lo = min(max(kScaleOne + er - 11 - 4 * (r & 3), 1), 254);
-  // value words: vw[0..1] = page 2g, tiles 0-7; vw[2..3] = page 2g + 1
-  u32x4 v0 = vw[0], v1 = vw[1], v2 = vw[2], v3 = vw[3];
-  {
-    const v8i A = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
-                   static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
-                   static_cast<int>(h1.z), static_cast<int>(h1.w)};
-    const uint32_t p0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const uint32_t p1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
-#pragma unroll
-    for (int tau = kT0; tau < kT1; ++tau)
-      st.acc[tau] = mfma128<kFmtFp8, kFmtFp6>(A, fp6_codes(p0[tau], p1[tau]), st.acc[tau], sa_hi);
-  }
+  for (int j = 0; j < 8; ++j) put_digits(wbase + 16 * j, (W[j] >> 4) & 15u, W[j] & 15u, 0u, 0u);
   asm volatile(
       "ds_read_b128 %0, %2\n"
       "ds_read_b128 %1, %2 offset:64\n"
@@ -443,17 +492,22 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&w)[8], uin
       : "=&v"(l0), "=&v"(l1)
       : "v"(ra)
       : "memory");
-  // the code operands are rebuilt rather than kept live across the two sets
-  asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
-  {
-    const v8i A = {static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
+  const int sa_hi = min(max(kScaleOne + er + 8 - 4 * (r & 3), 1), 254);
+  const int sa_lo = min(max(kScaleOne + er - 8 - 4 * (r & 3), 1), 254);
+  const v8i Ahi = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
+                   static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
+                   static_cast<int>(h1.z), static_cast<int>(h1.w)};
+  const v8i Alo = {static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
                    static_cast<int>(l0.w), static_cast<int>(l1.x), static_cast<int>(l1.y),
                    static_cast<int>(l1.z), static_cast<int>(l1.w)};
-    const uint32_t p0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const uint32_t p1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+  // value words: vw[0..1] = page 2g, tiles 0-7; vw[2..3] = page 2g + 1
+  const uint32_t p0[8] = {vw[0].x, vw[0].y, vw[0].z, vw[0].w, vw[1].x, vw[1].y, vw[1].z, vw[1].w};
+  const uint32_t p1[8] = {vw[2].x, vw[2].y, vw[2].z, vw[2].w, vw[3].x, vw[3].y, vw[3].z, vw[3].w};
 #pragma unroll
-    for (int tau = kT0; tau < kT1; ++tau)
-      st.acc[tau] = mfma128<kFmtFp8, kFmtFp6>(A, fp6_codes(p0[tau], p1[tau]), st.acc[tau], sa_lo);
+  for (int tau = kT0; tau < kT1; ++tau) {
+    const v8i B = fp6_codes(p0[tau], p1[tau]);
+    st.acc[tau] = mfma128<kFmtFp8, kFmtFp6>(Ahi, B, st.acc[tau], sa_hi);
+    st.acc[tau] = mfma128<kFmtFp8, kFmtFp6>(Alo, B, st.acc[tau], sa_lo);
   }
 }
 
@@ -470,8 +524,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const float4* __restrict__ qf, float* __restrict__ part, int S) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
+  static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t ptile[4][kPTile];
+  __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
   __shared__ float cm[4][kHT], cl[4][kHT];
 
   const int h = blockIdx.y / QG;
@@ -482,9 +537,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ctx = min(max(ctx_len[b], 0), max_ctx);
   const int n_pages = (ctx + kBlock - 1) / kBlock;
+  const int ns_b = num_splits(n_pages, spw);
+  if (wgs >= ns_b) return;
   const int p_begin = wgs * spw;
   if (p_begin >= n_pages) return;
-  const int p_end = min(p_begin + spw, n_pages);
+  const int p_end = (wgs == ns_b - 1) ? n_pages : p_begin + spw;
   const int np = p_end - p_begin;
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
   // 8-page blocks of this range; this wave's are wave, wave + 4, ...  Only the
@@ -522,10 +579,17 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const float sq0 = G == 1 ? fq.y + fq.z : fq.y;
   const float sq1 = fq.z;
 
+  // block ids past INT32_MAX cannot be addressed by the table anyway
+  const int max_block = static_cast<int>(min(num_blocks, static_cast<int64_t>(0x7fffffff)) - 1);
   uint8_t* myring = &ring[wave][0][0];
+  // DMA lane offsets: 16 code bytes per lane; one (scale, zero) word per lane
+  const uint32_t off16 = 16u * lane, off4 = kSzOff + 4u * lane;
+  const bool sz_lane = G == 2 || lane < 32;
   for (int i = 0; i < kDepth && i < nsl; ++i)
-    issue_slice<G>(myring + i * kSlot, pages, num_blocks, Hkv, h, row, slice_page(i), p_end,
-                   lane);
+    issue_slice<G>(myring + i * kSlot, pages, Hkv, h,
+                   load_ids(row, slice_page(i), p_end, max_block), off16, off4, sz_lane);
+  SliceIds next_ids = {0, 0};  // of slice kDepth, and then of each slice kDepth ahead
+  if (kDepth < nsl) next_ids = load_ids(row, slice_page(kDepth), p_end, max_block);
 
   ScanState st;
   st.m = kNegBig;
@@ -545,12 +609,17 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     for (int s = 0; s < 4; ++s) {
       const int i = 4 * bi + s;
       if (i < nsl) {
-        if (i + kDepth < nsl)
-          issue_slice<G>(myring + ((i + kDepth) % kRing) * kSlot, pages, num_blocks, Hkv, h, row,
-                         slice_page(i + kDepth), p_end, lane);
+        if (i + kDepth < nsl) {
+          issue_slice<G>(myring + ((i + kDepth) % kRing) * kSlot, pages, Hkv, h, next_ids, off16,
+                         off4, sz_lane);
+          if (i + kDepth + 1 < nsl)
+            next_ids = load_ids(row, slice_page(i + kDepth + 1), p_end, max_block);
+        }
         // slice i has landed once at most the DMAs of the slices behind it are pending
         const int behind = min(kDepth, nsl - 1 - i);
-        if (behind == 2)
+        if (kDepth >= 3 && behind == 3)
+          wait_vmem<3 * kDmaPerSlice>();
+        else if (kDepth >= 2 && behind == 2)
           wait_vmem<2 * kDmaPerSlice>();
         else if (behind == 1)
           wait_vmem<kDmaPerSlice>();
@@ -579,9 +648,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
           d1 = mfma128<kFmtFp6, kFmtFp6>(qA1, k1, d1, qsc_lo);
           const float D0 = (d0[0] + d0[1]) + (d0[2] + d0[3]);
           const float D1 = (d1[0] + d1[1]) + (d1[2] + d1[3]);
-          // logit = 8 s_K sum(x code/8) + z_K sum(x)
-          l0 = fmaf(8.0f * f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0);
-          l1 = fmaf(8.0f * f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0);
+          // logit = s_K sum(x code) + z_K sum(x)
+          l0 = fmaf(f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0);
+          l1 = fmaf(f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0);
         } else {
           const floatx4 a0 = mfma128<kFmtFp6, kFmtFp6>(qA0, k0, zero4, qsc_hi);
           const floatx4 a1 = mfma128<kFmtFp6, kFmtFp6>(qA0, k1, zero4, qsc_hi);
@@ -594,10 +663,10 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
           const float D1 = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + (c1[0] + c1[1]);
           const float E0 = ((b0[0] + b0[1]) + (b0[2] + b0[3])) + (c0[2] + c0[3]);
           const float E1 = ((b1[0] + b1[1]) + (b1[2] + b1[3])) + (c1[2] + c1[3]);
-          l0 = fmaf(8.0f * f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0) +
-               fmaf(8.0f * f16_lo_to_f32(c.szk0.y), E0, f16_hi_to_f32(c.szk0.y) * sq1);
-          l1 = fmaf(8.0f * f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0) +
-               fmaf(8.0f * f16_lo_to_f32(c.szk1.y), E1, f16_hi_to_f32(c.szk1.y) * sq1);
+          l0 = fmaf(f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0) +
+               fmaf(f16_lo_to_f32(c.szk0.y), E0, f16_hi_to_f32(c.szk0.y) * sq1);
+          l1 = fmaf(f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0) +
+               fmaf(f16_lo_to_f32(c.szk1.y), E1, f16_hi_to_f32(c.szk1.y) * sq1);
         }
         const int pg = pblk + 2 * s;
         const int pos = pg * kBlock + t;
@@ -647,11 +716,13 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     st.l += lsum;
     st.zs0 += z0;
     st.zs1 += z1;
+    // the slot of the block's last slice (read above; no DMA targets it yet)
+    uint8_t* ptile = myring + ((4 * bi + 3 < nsl ? 4 * bi + 3 : nsl - 1) % kRing) * kSlot;
     if constexpr (G == 1) {
-      block_pv<0, 8>(st, w0, ptile[wave], vw, lane);
+      block_pv<0, 8>(st, w0, ptile, pexp[wave], vw, lane);
     } else {
-      block_pv<0, 4>(st, w0, ptile[wave], vw, lane);
-      block_pv<4, 8>(st, w1, ptile[wave], vw, lane);
+      block_pv<0, 4>(st, w0, ptile, pexp[wave], vw, lane);
+      block_pv<4, 8>(st, w1, ptile, pexp[wave], vw, lane);
     }
   }
 
@@ -664,9 +735,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   float(*co)[kHT][kHeadDim] = reinterpret_cast<float(*)[kHT][kHeadDim]>(&ring[0][0][0]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    // digit rows add up; the code operand is code/8
+    // digit rows add up to sum(w code)
     const floatx4 a = st.acc[j];
-    co[wave][hl][16 * j + n] = 8.0f * ((a[0] + a[1]) + (a[2] + a[3])) + (j < 4 ? zs0 : zs1);
+    co[wave][hl][16 * j + n] = ((a[0] + a[1]) + (a[2] + a[3])) + (j < 4 ? zs0 : zs1);
   }
   if (n == 0) {
     cm[wave][hl] = st.m;
@@ -703,6 +774,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 
 // ---- merge: log-sum-exp merge of the ns partials of the nh query heads of
 // one head tile, then o = o_r * R_V[h]^T.  grid (Hkv * QG, B), block 256.
+// Thread (j = tid/2, half) loads its R_V row half before reading any partial,
+// so the two memory latencies overlap.
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
                                                     const int* __restrict__ ctx_len, int max_ctx,
                                                     int Hq, int Hkv, int QG, int spw, int S,
@@ -715,7 +788,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int Hg = Hq / Hkv;
   const int nh = min(kHT, Hg - qg * kHT);
   const int ctx = min(max(ctx_len[b], 0), max_ctx);
-  const int ns = ((ctx + kBlock - 1) / kBlock + spw - 1) / spw;
+  const int ns = num_splits((ctx + kBlock - 1) / kBlock, spw);
   const int u = threadIdx.x >> 6;
   const int c = threadIdx.x & 63;
   if (ns == 0) {  // empty context: zero output
@@ -726,31 +799,50 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     }
     return;
   }
+  const int j = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const float4* R = reinterpret_cast<const float4*>(
+      rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim + 64 * half);
+  float4 rr[16];
+#pragma unroll
+  for (int i4 = 0; i4 < 16; ++i4) rr[i4] = R[i4];
+
   if (u < nh) {
+    // one pass, online rescale; four splits' loads in flight at a time
     const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * S * kPartStride;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * kPartStride]);
-    float W = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float a = exp2_hw(p[s * kPartStride] - M);
-      W += a;
-      a0 = fmaf(a, p[s * kPartStride + 4 + c], a0);
-      a1 = fmaf(a, p[s * kPartStride + 4 + c + 64], a1);
+    float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+      float l[4], x0[4], x1[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int s = min(s0 + k, ns - 1);
+        l[k] = (s0 + k < ns) ? p[s * kPartStride] : -INFINITY;
+        x0[k] = p[s * kPartStride + 4 + c];
+        x1[k] = p[s * kPartStride + 4 + c + 64];
+      }
+      const float Mn = fmaxf(M, fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+      const float sc = exp2_hw(M - Mn);  // M = -inf at the start: 0
+      W *= sc;
+      a0 *= sc;
+      a1 *= sc;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = exp2_hw(l[k] - Mn);
+        W += a;
+        a0 = fmaf(a, x0[k], a0);
+        a1 = fmaf(a, x1[k], a1);
+      }
+      M = Mn;
     }
     const float inv = 1.0f / W;
     orow[u * kHeadDim + c] = a0 * inv;
     orow[u * kHeadDim + c + 64] = a1 * inv;
   }
   __syncthreads();
-  // thread -> (output channel j = tid/2, half of the input channels)
-  const int j = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
-  const float4* R = reinterpret_cast<const float4*>(
-      rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim + 64 * half);
   float o[kHT] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) {
-    const float4 r = R[i4];
+    const float4 r = rr[i4];
     const int i = 64 * half + 4 * i4;
 #pragma unroll
     for (int uu = 0; uu < kHT; ++uu) {
@@ -786,7 +878,7 @@ DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages) {
   p.QG = (Hg + kHT - 1) / kHT;
   p.spw = split_pages > 0 ? split_pages : choose_split_pages(B, Hkv, p.QG, max_ctx);
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
-  p.S = static_cast<int>((max_pages + p.spw - 1) / p.spw);
+  p.S = num_splits(static_cast<int>(max_pages), p.spw);
   const size_t hg = static_cast<size_t>(B) * Hkv * p.QG;
   p.qa_off = 0;
   p.qf_off = align256(hg * 64 * kQaDwords * 4);
