@@ -258,15 +258,8 @@ __global__ __launch_bounds__(1024) void append_one_kernel(
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
 
-  const int pos = start_pos[b];
-  if (pos < 0 || pos / kBlock >= max_blocks) return;
-  const int blk = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
-  if (blk < 0 || blk >= num_blocks) return;
-  const int PB = page_bytes_for_groups(G);
-  uint8_t* page = pages + (static_cast<int64_t>(blk) * Hkv + h) * PB;
-  const int t = pos % kBlock;
-
-  // split-K partial products: thread -> (mat, quarter kq, column jc)
+  // split-K partial products: thread -> (mat, quarter kq, column jc).  The
+  // rotation loads go out first: nothing they need depends on another load.
   {
     const int pm = tid >> 9, kq = (tid >> 7) & 3, jc = tid & 127;
     const float* R = (pm ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim +
@@ -296,9 +289,18 @@ __global__ __launch_bounds__(1024) void append_one_kernel(
     }
     part[pm][kq][jc] = (x0 + x1) + (x2 + x3);
   }
+  // destination page (a position outside the table, or a block id outside
+  // the cache, writes nothing)
+  const int pos = start_pos[b];
+  int blk = -1;
+  if (pos >= 0 && pos / kBlock < max_blocks) blk = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
+  const bool valid = blk >= 0 && blk < num_blocks;
+  const int PB = page_bytes_for_groups(G);
+  uint8_t* page = pages + (static_cast<int64_t>(valid ? blk : 0) * Hkv + h) * PB;
+  const int t = (pos >= 0 ? pos : 0) % kBlock;
   __syncthreads();
 
-  const bool own = tid < 256;  // threads 0-255 own one rotated channel each
+  const bool own = tid < 256 && valid;  // threads 0-255 own one rotated channel each
   const int mat = (tid >> 7) & 1;
   const int j = tid & 127;
   const int wave = (tid >> 6) & 3;

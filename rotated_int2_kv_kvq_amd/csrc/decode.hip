@@ -787,6 +787,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int b = blockIdx.y;
   const int Hg = Hq / Hkv;
   const int nh = min(kHT, Hg - qg * kHT);
+  const int j = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const float4* R = reinterpret_cast<const float4*>(
+      rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim + 64 * half);
+  float4 rr[16];
+#pragma unroll
+  for (int i4 = 0; i4 < 16; ++i4) rr[i4] = R[i4];
   const int ctx = min(max(ctx_len[b], 0), max_ctx);
   const int ns = num_splits((ctx + kBlock - 1) / kBlock, spw);
   const int u = threadIdx.x >> 6;
@@ -799,34 +806,29 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     }
     return;
   }
-  const int j = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
-  const float4* R = reinterpret_cast<const float4*>(
-      rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim + 64 * half);
-  float4 rr[16];
-#pragma unroll
-  for (int i4 = 0; i4 < 16; ++i4) rr[i4] = R[i4];
 
   if (u < nh) {
-    // one pass, online rescale; four splits' loads in flight at a time
+    // one pass, online rescale; eight splits' loads in flight at a time
     const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * S * kPartStride;
     float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 4) {
-      float l[4], x0[4], x1[4];
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float l[8], x0[8], x1[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const int s = min(s0 + k, ns - 1);
         l[k] = (s0 + k < ns) ? p[s * kPartStride] : -INFINITY;
         x0[k] = p[s * kPartStride + 4 + c];
         x1[k] = p[s * kPartStride + 4 + c + 64];
       }
-      const float Mn = fmaxf(M, fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, l[k]);
       const float sc = exp2_hw(M - Mn);  // M = -inf at the start: 0
       W *= sc;
       a0 *= sc;
       a1 *= sc;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const float a = exp2_hw(l[k] - Mn);
         W += a;
         a0 = fmaf(a, x0[k], a0);
