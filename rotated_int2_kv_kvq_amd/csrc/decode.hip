@@ -451,9 +451,13 @@ struct ScanState {
 // as an A operand (row r = lane%16, pages g and g + 4 of lane group
 // g = lane/16); then two MFMAs per 16 output channels on one code operand.
 template <int kT0, int kT1>
-__device__ __forceinline__ void block_pv(ScanState& st, const float (&w)[8], uint8_t* ptile,
-                                         int* pexp, const u32x4 (&vw)[4], int lane) {
+__device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
+                                         const uint32_t (&szv)[8], uint8_t* ptile, int* pexp,
+                                         const u32x4 (&vw)[4], int lane) {
   const int t = lane & 15, hl = lane >> 4;
+  float w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = p[j] * f16_lo_to_f32(szv[j]);
   float wmax = w[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) wmax = fmaxf(wmax, w[j]);
@@ -514,10 +518,10 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&w)[8], uin
 // grid (S, Hkv * QG, B), block 256: workgroup x covers pages [x*spw, (x+1)*spw),
 // cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
 // 128 VGPRs (four waves per SIMD); group 64, with a third q.K operand and a
-// second value group, is given more registers rather than spill inside the
-// loop (a spill reload waits for every outstanding DMA).
+// second value group, gets up to 168 (three waves per SIMD) rather than spill
+// inside the loop (a spill reload waits for every outstanding DMA).
 template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2, 4))) void
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
              int max_ctx, int Hq, int QG, int spw, const uint32_t* __restrict__ qa,
@@ -652,21 +656,19 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
           l0 = fmaf(f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0);
           l1 = fmaf(f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0);
         } else {
-          const floatx4 a0 = mfma128<kFmtFp6, kFmtFp6>(qA0, k0, zero4, qsc_hi);
-          const floatx4 a1 = mfma128<kFmtFp6, kFmtFp6>(qA0, k1, zero4, qsc_hi);
-          const floatx4 b0 = mfma128<kFmtFp6, kFmtFp6>(qA1, k0, zero4, qsc_hi);
-          const floatx4 b1 = mfma128<kFmtFp6, kFmtFp6>(qA1, k1, zero4, qsc_hi);
-          const floatx4 c0 = mfma128<kFmtFp6, kFmtFp6>(qA2, k0, zero4, qsc_lo);
-          const floatx4 c1 = mfma128<kFmtFp6, kFmtFp6>(qA2, k1, zero4, qsc_lo);
-          // group 0: rows of a plus low rows 0-1 of c; group 1: b plus c rows 2-3
-          const float D0 = ((a0[0] + a0[1]) + (a0[2] + a0[3])) + (c0[0] + c0[1]);
-          const float D1 = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + (c1[0] + c1[1]);
-          const float E0 = ((b0[0] + b0[1]) + (b0[2] + b0[3])) + (c0[2] + c0[3]);
-          const float E1 = ((b1[0] + b1[1]) + (b1[2] + b1[3])) + (c1[2] + c1[3]);
-          l0 = fmaf(f16_lo_to_f32(c.szk0.x), D0, f16_hi_to_f32(c.szk0.x) * sq0) +
-               fmaf(f16_lo_to_f32(c.szk0.y), E0, f16_hi_to_f32(c.szk0.y) * sq1);
-          l1 = fmaf(f16_lo_to_f32(c.szk1.x), D1, f16_hi_to_f32(c.szk1.x) * sq0) +
-               fmaf(f16_lo_to_f32(c.szk1.y), E1, f16_hi_to_f32(c.szk1.y) * sq1);
+          // group 0: high rows of qA0 plus low rows 0-1 of qA2; group 1: qA1
+          // plus qA2 rows 2-3.  Page by page, to keep few results live.
+          auto logit2 = [&](const v8i& kb, uint2 szk) {
+            const floatx4 a = mfma128<kFmtFp6, kFmtFp6>(qA0, kb, zero4, qsc_hi);
+            const floatx4 bb = mfma128<kFmtFp6, kFmtFp6>(qA1, kb, zero4, qsc_hi);
+            const floatx4 cc = mfma128<kFmtFp6, kFmtFp6>(qA2, kb, zero4, qsc_lo);
+            const float D = ((a[0] + a[1]) + (a[2] + a[3])) + (cc[0] + cc[1]);
+            const float E = ((bb[0] + bb[1]) + (bb[2] + bb[3])) + (cc[2] + cc[3]);
+            return fmaf(f16_lo_to_f32(szk.x), D, f16_hi_to_f32(szk.x) * sq0) +
+                   fmaf(f16_lo_to_f32(szk.y), E, f16_hi_to_f32(szk.y) * sq1);
+          };
+          l0 = logit2(k0, c.szk0);
+          l1 = logit2(k1, c.szk1);
         }
         const int pg = pblk + 2 * s;
         const int pos = pg * kBlock + t;
@@ -700,18 +702,17 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
       st.zs1 *= alpha;
       st.m = mnew;
     }
-    float w0[8], w1[8];
+    float p[8];
+    uint32_t sz0[8], sz1[8];
     float lsum = 0.f, z0 = 0.f, z1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = exp2_hw(lg[j] - st.m);
-      lsum += p;
-      z0 = fmaf(p, f16_hi_to_f32(szv[j].x), z0);
-      w0[j] = p * f16_lo_to_f32(szv[j].x);
-      if constexpr (G == 2) {
-        z1 = fmaf(p, f16_hi_to_f32(szv[j].y), z1);
-        w1[j] = p * f16_lo_to_f32(szv[j].y);
-      }
+      p[j] = exp2_hw(lg[j] - st.m);
+      lsum += p[j];
+      sz0[j] = szv[j].x;
+      sz1[j] = szv[j].y;
+      z0 = fmaf(p[j], f16_hi_to_f32(sz0[j]), z0);
+      if constexpr (G == 2) z1 = fmaf(p[j], f16_hi_to_f32(sz1[j]), z1);
     }
     st.l += lsum;
     st.zs0 += z0;
@@ -719,10 +720,10 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     // the slot of the block's last slice (read above; no DMA targets it yet)
     uint8_t* ptile = myring + ((4 * bi + 3 < nsl ? 4 * bi + 3 : nsl - 1) % kRing) * kSlot;
     if constexpr (G == 1) {
-      block_pv<0, 8>(st, w0, ptile, pexp[wave], vw, lane);
+      block_pv<0, 8>(st, p, sz0, ptile, pexp[wave], vw, lane);
     } else {
-      block_pv<0, 4>(st, w0, ptile, pexp[wave], vw, lane);
-      block_pv<4, 8>(st, w1, ptile, pexp[wave], vw, lane);
+      block_pv<0, 4>(st, p, sz0, ptile, pexp[wave], vw, lane);
+      block_pv<4, 8>(st, p, sz1, ptile, pexp[wave], vw, lane);
     }
   }
 
@@ -775,13 +776,18 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // ---- merge: log-sum-exp merge of the ns partials of the nh query heads of
 // one head tile, then o = o_r * R_V[h]^T.  grid (Hkv * QG, B), block 256.
 // Thread (j = tid/2, half) loads its R_V row half before reading any partial,
-// so the two memory latencies overlap.
+// so the two memory latencies overlap.  The merge takes two passes: wave u
+// finds head u's maximum lse and the splits' weights; then every thread sums
+// its two channels over the splits with independent loads.
+constexpr int kMergeLds = 1024;  // splits whose weights the merge keeps in LDS
+
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
                                                     const int* __restrict__ ctx_len, int max_ctx,
                                                     int Hq, int Hkv, int QG, int spw, int S,
                                                     const float* __restrict__ rot_v,
                                                     float* __restrict__ out) {
   __shared__ float orow[kHT * kHeadDim];
+  __shared__ float wts[kHT][kMergeLds];
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
@@ -807,33 +813,61 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     return;
   }
 
+  // pass 1, wave u: the splits' weights exp2(lse_s - M) / sum into LDS
+  // (splits beyond kMergeLds are folded in pass 2 with an online rescale)
+  const int nsl = min(ns, kMergeLds);
+  const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) * S *
+                              kPartStride;
+  float M = -INFINITY;
+  for (int s = c; s < nsl; s += 64) M = fmaxf(M, p[s * kPartStride]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor(M, m));
+  float W = 0.f;
+  for (int s = c; s < nsl; s += 64) {
+    const float a = exp2_hw(p[s * kPartStride] - M);
+    wts[u][s] = a;
+    W += a;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) W += shfl_xor(W, m);
+  __syncthreads();
   if (u < nh) {
-    // one pass, online rescale; eight splits' loads in flight at a time
-    const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * S * kPartStride;
-    float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      float l[8], x0[8], x1[8];
+    // pass 2: eight splits at a time, the next eight's loads issued before
+    // this eight's are used (software pipelined)
+    float a0 = 0.f, a1 = 0.f;
+    float x0[8], x1[8];
+    auto load8 = [&](int s0) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int s = min(s0 + k, ns - 1);
-        l[k] = (s0 + k < ns) ? p[s * kPartStride] : -INFINITY;
+        const int s = min(s0 + k, nsl - 1);
         x0[k] = p[s * kPartStride + 4 + c];
         x1[k] = p[s * kPartStride + 4 + c + 64];
       }
-      float Mn = M;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, l[k]);
-      const float sc = exp2_hw(M - Mn);  // M = -inf at the start: 0
-      W *= sc;
-      a0 *= sc;
-      a1 *= sc;
+    };
+    load8(0);
+    for (int s0 = 0; s0 < nsl; s0 += 8) {
+      float y0[8], y1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a = exp2_hw(l[k] - Mn);
-        W += a;
-        a0 = fmaf(a, x0[k], a0);
-        a1 = fmaf(a, x1[k], a1);
+        y0[k] = x0[k];
+        y1[k] = x1[k];
       }
+      if (s0 + 8 < nsl) load8(s0 + 8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a = (s0 + k < nsl) ? wts[u][min(s0 + k, nsl - 1)] : 0.f;
+        a0 = fmaf(a, y0[k], a0);
+        a1 = fmaf(a, y1[k], a1);
+      }
+    }
+    // splits past the LDS table (very long contexts): online rescale
+    for (int s = nsl; s < ns; ++s) {
+      const float l = p[s * kPartStride];
+      const float Mn = fmaxf(M, l);
+      const float sc = exp2_hw(M - Mn), a = exp2_hw(l - Mn);
+      W = W * sc + a;
+      a0 = fmaf(a, p[s * kPartStride + 4 + c], a0 * sc);
+      a1 = fmaf(a, p[s * kPartStride + 4 + c + 64], a1 * sc);
       M = Mn;
     }
     const float inv = 1.0f / W;
@@ -864,12 +898,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Pages per split: about 1024 workgroups (four per CU), in whole 32-page
-// steps so that each wave gets whole 8-page blocks.
+// steps so that each wave gets whole 8-page blocks, and at least 128 pages
+// (four blocks per wave), below which per-workgroup start-up and the merge of
+// many partials cost more than the extra workgroups bring (measured at 128K
+// context, batch 1).
 int choose_split_pages(int B, int Hkv, int QG, int max_ctx) {
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
   const int64_t total = static_cast<int64_t>(B) * Hkv * QG * max_pages;
   int64_t spw = (total / 1024 + 16) / 32 * 32;
-  if (spw < 32) spw = 32;
+  if (spw < 128) spw = 128;
   if (spw > 512) spw = 512;
   return static_cast<int>(spw);
 }
