@@ -533,10 +533,19 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
   __shared__ float cm[4][kHT], cl[4][kHT];
 
-  const int h = blockIdx.y / QG;
-  const int qg = blockIdx.y % QG;
-  const int b = blockIdx.z;
-  const int wgs = blockIdx.x;
+  // Workgroups go to the eight XCDs round-robin in launch order, and each XCD
+  // has its own L2.  Renumber them so that every XCD takes one contiguous run of
+  // (query group, split) pairs: the splits of a query group then share one L2
+  // copy of its query operand instead of fetching it once per XCD.
+  const int n_wg = gridDim.x * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = lin & 7;
+  const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
+  const int wgs = job % S;
+  const int hy = (job / S) % gridDim.y;
+  const int b = job / (S * gridDim.y);
+  const int h = hy / QG;
+  const int qg = hy % QG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ctx = min(max(ctx_len[b], 0), max_ctx);
