@@ -143,9 +143,10 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *   workspace      device  at least kvq_decode_workspace_bytes(...) bytes,
  *                          256-byte aligned; contents are scratch
  *   split_pages    host    pages per workgroup split: 0 = automatic, else a
- *                          positive multiple of 8.  A context of n pages is
- *                          cut into max(1, round(n / split_pages)) splits of
- *                          split_pages pages, the last taking the rest.
+ *                          positive multiple of 8, at most 512.  A context of
+ *                          n pages is cut into max(1, round(n / split_pages))
+ *                          splits of split_pages pages, the last taking the
+ *                          rest.
  * num_q_heads must be a multiple of num_kv_heads.
  */
 int kvq_decode_attn(const void *pages, int64_t num_blocks, int32_t num_kv_heads,

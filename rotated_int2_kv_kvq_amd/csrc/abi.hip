@@ -63,7 +63,7 @@ bool valid_decode_shape(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
                         int32_t max_ctx_len, int32_t split_pages) {
   if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_q_heads < num_kv_heads) return false;
   if (num_q_heads % num_kv_heads != 0 || max_ctx_len < 0) return false;
-  if (split_pages < 0 || split_pages % 8 != 0) return false;
+  if (split_pages < 0 || split_pages % 8 != 0 || split_pages > 512) return false;
   const int qg = (num_q_heads / num_kv_heads + 3) / 4;
   if (static_cast<int64_t>(num_kv_heads) * qg > 65535) return false;
   return true;

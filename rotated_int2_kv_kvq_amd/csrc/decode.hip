@@ -44,6 +44,7 @@ constexpr int kHT = 4;            // query heads per MFMA row tile (x 4 digit ro
 constexpr int kPartStride = 132;  // floats per partial: [0] = lse2, [4..131] = o
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp2(l - m) is 0, not NaN
+constexpr float kLazy = 8.0f;        // log2 headroom before the running maximum is raised
 // Per lane of the q.K A operands: [0, 6) and [6, 12) and (group 64) [12, 18)
 // three FP6 operands, [28] and [29] the E8M0 row scales of the high- and
 // low-digit operands.
@@ -55,6 +56,20 @@ constexpr int kScaleOne = 127;  // E8M0 2^0
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
+// A compile-time value passed to a generic lambda.
+template <typename T, T V>
+struct Const {
+  static constexpr T value = V;
+};
+// f(Const<int, I>{}) for I = I0 .. N-1, in order.
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(Const<int, I0>{});
+    static_for<I0 + 1, N>(f);
+  }
+}
+
 // 16x16x128 MFMA, D = A*B + C with per-lane E8M0 scales (A scale = this lane's
 // row; every lane of a row passes the same value).
 template <int FA, int FB>
@@ -64,17 +79,14 @@ __device__ __forceinline__ floatx4 mfma128(const v8i& a, const v8i& b, const flo
 
 // FP6 operand from two code words (16 codes each, code u at bits 2u): field j
 // of the 32 holds code (3*(j%16)) mod 16 of word j/16, as the value code/8.
+// An FP6 operand is six dwords; the MFMA never reads the last two of the
+// eight-register tuple, so they are left undefined (no moves to fill them).
+typedef int v4i __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v8i fp6_codes(uint32_t w0, uint32_t w1) {
-  v8i r;
-  r[0] = static_cast<int>(w0 & 0xC30C30C3u);
-  r[1] = static_cast<int>(w0 & 0x30C30C30u);
-  r[2] = static_cast<int>(w0 & 0x0C30C30Cu);
-  r[3] = static_cast<int>(w1 & 0xC30C30C3u);
-  r[4] = static_cast<int>(w1 & 0x30C30C30u);
-  r[5] = static_cast<int>(w1 & 0x0C30C30Cu);
-  r[6] = 0;
-  r[7] = 0;
-  return r;
+  const v4i a = {static_cast<int>(w0 & 0xC30C30C3u), static_cast<int>(w0 & 0x30C30C30u),
+                 static_cast<int>(w0 & 0x0C30C30Cu), static_cast<int>(w1 & 0xC30C30C3u)};
+  const v4i c = {static_cast<int>(w1 & 0x30C30C30u), static_cast<int>(w1 & 0x0C30C30Cu), 0, 0};
+  return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, -1, -1);
 }
 
 // 2^x on the hardware exp unit
@@ -264,10 +276,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
 // images exactly as laid out in the cache: codes [0, 1024) and (scale, zero)
 // pairs [1024, 1024 + 128G).  One slice is kDmaPerSlice DMA instructions.
 // Two slices in flight per wave (measured on the 36-layer stream: one is too
-// few, three no better); the P tile lives in a ring slot.
+// few, three no better).  Four slots, one per slice of an 8-page block, so
+// that every slot address is a compile-time offset; the P tile lives in the
+// slot of the block's last slice.
 constexpr int kDepth = 2;
-constexpr int kRing = kDepth + 1;
+constexpr int kRing = 4;
 constexpr int kDmaPerSlice = 4;
+// Pages one workgroup may take: splits of at most 512 pages, the last split
+// of a context taking up to half a split more.
+constexpr int kMaxSplitPages = 768;
 // P tile: 16 rows (4 heads x 4 digits) x 8 pages x 16 tokens of FP8 digit
 // bytes; the row stride is padded to 144 bytes so that the A-operand reads
 // (16 rows at one page) and the digit writes spread over all LDS banks.  It
@@ -289,22 +306,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
 }
 
-// Physical blocks of the two pages [pg0, pg0 + 1] of a slice, clamped into
-// the cache (a page past the range repeats pg0; its tokens are masked out).
-// Loaded one slice before their DMAs are issued so that the scalar loads are
-// never waited for on the critical path.
-struct SliceIds {
-  int b0, b1;
-};
-__device__ __forceinline__ SliceIds load_ids(const int* __restrict__ row, int pg0, int p_end,
-                                             int max_block) {
-  const int b0 = row[pg0];
-  const int b1 = (pg0 + 1 < p_end) ? row[pg0 + 1] : b0;
-  return {static_cast<int>(min(static_cast<uint32_t>(b0), static_cast<uint32_t>(max_block))),
-          static_cast<int>(min(static_cast<uint32_t>(b1), static_cast<uint32_t>(max_block)))};
-}
-
-// DMA a slice's two pages into a ring slot.  Each page is a buffer resource
+// DMA one page into a ring slot (wide form): the page is a buffer resource
 // built in scalar registers (base = the page, 1 record per byte up to the page
 // size); the per-lane offsets are fixed, so issuing takes no vector ALU work.
 constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
@@ -320,14 +322,17 @@ __device__ __forceinline__ void dma_page(const uint8_t* page, uint8_t* slot, uin
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSzOff), 4, off4, 0, 0, 0);
 }
 
+// The same DMA through one buffer resource over the whole cache (when it
+// spans less than 4 GiB): the page is the scalar offset, so issuing a page
+// takes two scalar ALU operations for its offset and no descriptor set-up.
 template <int G>
-__device__ __forceinline__ void issue_slice(uint8_t* slot, const uint8_t* __restrict__ pages,
-                                            int Hkv, int h, SliceIds ids, uint32_t off16,
-                                            uint32_t off4, bool sz_lane) {
-  constexpr int PB = page_bytes_for_groups(G);
-  dma_page<G>(pages + (static_cast<int64_t>(ids.b0) * Hkv + h) * PB, slot, off16, off4, sz_lane);
-  dma_page<G>(pages + (static_cast<int64_t>(ids.b1) * Hkv + h) * PB, slot + PB, off16, off4,
-              sz_lane);
+__device__ __forceinline__ void dma_page_at(__amdgpu_buffer_rsrc_t r, uint32_t page_off,
+                                            uint8_t* slot, uint32_t off16, uint32_t off4,
+                                            bool sz_lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)slot, 16, off16, page_off, 0, 0);
+  if (sz_lane)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSzOff), 4, off4, page_off, 0,
+                                             0);
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -344,21 +349,22 @@ struct Slice {
   uint2 szk0, szk1, szv0, szv1;
 };
 
-template <int G>
+template <int G, int kOff>
 __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
   constexpr int PB = page_bytes_for_groups(G);
   if constexpr (G == 2) {
     u32x2 s0, s1, s2, s3;
     asm volatile(
-        "ds_read_b64 %0, %6\n"
-        "ds_read_b64 %1, %6 offset:%8\n"
-        "ds_read_b64 %2, %7\n"
-        "ds_read_b64 %3, %7 offset:%8\n"
-        "ds_read_b64 %4, %7 offset:%9\n"
-        "ds_read_b64 %5, %7 offset:%10\n"
+        "ds_read_b64 %0, %6 offset:%8\n"
+        "ds_read_b64 %1, %6 offset:%9\n"
+        "ds_read_b64 %2, %7 offset:%8\n"
+        "ds_read_b64 %3, %7 offset:%9\n"
+        "ds_read_b64 %4, %7 offset:%10\n"
+        "ds_read_b64 %5, %7 offset:%11\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-        : "v"(ak), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
+        : "v"(ak), "v"(as), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
+          "i"(kOff + PB + 64 * G)
         : "memory");
     c.szk0 = make_uint2(s0.x, s0.y);
     c.szk1 = make_uint2(s1.x, s1.y);
@@ -367,15 +373,16 @@ __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
   } else {
     uint32_t s0, s1, s2, s3;
     asm volatile(
-        "ds_read_b64 %0, %6\n"
-        "ds_read_b64 %1, %6 offset:%8\n"
-        "ds_read_b32 %2, %7\n"
-        "ds_read_b32 %3, %7 offset:%8\n"
-        "ds_read_b32 %4, %7 offset:%9\n"
-        "ds_read_b32 %5, %7 offset:%10\n"
+        "ds_read_b64 %0, %6 offset:%8\n"
+        "ds_read_b64 %1, %6 offset:%9\n"
+        "ds_read_b32 %2, %7 offset:%8\n"
+        "ds_read_b32 %3, %7 offset:%9\n"
+        "ds_read_b32 %4, %7 offset:%10\n"
+        "ds_read_b32 %5, %7 offset:%11\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-        : "v"(ak), "v"(as), "i"(PB), "i"(64 * G), "i"(PB + 64 * G)
+        : "v"(ak), "v"(as), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
+          "i"(kOff + PB + 64 * G)
         : "memory");
     c.szk0 = make_uint2(s0, s0);
     c.szk1 = make_uint2(s1, s1);
@@ -384,18 +391,36 @@ __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
   }
 }
 
+// Eight block ids (one 8-page block of the workgroup's id table) into scalar
+// registers; `ai` is the same LDS address in every lane.
+__device__ __forceinline__ void read_ids8(uint32_t ai, int (&id)[8]) {
+  u32x4 x, y;
+  asm volatile(
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %2 offset:16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x), "=&v"(y)
+      : "v"(ai)
+      : "memory");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    id[k] = __builtin_amdgcn_readfirstlane(static_cast<int>(x[k]));
+    id[4 + k] = __builtin_amdgcn_readfirstlane(static_cast<int>(y[k]));
+  }
+}
+
 // Value code words of channel 16*tau + n (tau = 0..7) of both pages of a slot:
 // word position 8n + tau, i.e. 32 contiguous bytes per page.
-__device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av, int PB) {
-  const uint32_t av1 = av + PB;
+template <int PB, int kOff>
+__device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av) {
   asm volatile(
-      "ds_read_b128 %0, %4\n"
-      "ds_read_b128 %1, %4 offset:16\n"
-      "ds_read_b128 %2, %5\n"
-      "ds_read_b128 %3, %5 offset:16\n"
+      "ds_read_b128 %0, %4 offset:%5\n"
+      "ds_read_b128 %1, %4 offset:%6\n"
+      "ds_read_b128 %2, %4 offset:%7\n"
+      "ds_read_b128 %3, %4 offset:%8\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(vw[0]), "=&v"(vw[1]), "=&v"(vw[2]), "=&v"(vw[3])
-      : "v"(av), "v"(av1)
+      : "v"(av), "i"(kOff), "i"(kOff + 16), "i"(kOff + PB), "i"(kOff + PB + 16)
       : "memory");
 }
 
@@ -422,17 +447,18 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // Write four digit bytes to rows 4*hl + 0..3 of the P tile at this lane's
-// (page, token) column.
+// (page kJ, token) column.
+template <int kJ>
 __device__ __forceinline__ void put_digits(uint32_t wbase, uint32_t d0, uint32_t d1, uint32_t d2,
                                            uint32_t d3) {
   asm volatile(
-      "ds_write_b8 %0, %1\n"
-      "ds_write_b8 %0, %2 offset:%5\n"
-      "ds_write_b8 %0, %3 offset:%6\n"
-      "ds_write_b8 %0, %4 offset:%7"
+      "ds_write_b8 %0, %1 offset:%5\n"
+      "ds_write_b8 %0, %2 offset:%6\n"
+      "ds_write_b8 %0, %3 offset:%7\n"
+      "ds_write_b8 %0, %4 offset:%8"
       :
-      : "v"(wbase), "v"(d0), "v"(d1), "v"(d2), "v"(d3), "i"(kPRow), "i"(2 * kPRow),
-        "i"(3 * kPRow)
+      : "v"(wbase), "v"(d0), "v"(d1), "v"(d2), "v"(d3), "i"(16 * kJ), "i"(16 * kJ + kPRow),
+        "i"(16 * kJ + 2 * kPRow), "i"(16 * kJ + 3 * kPRow)
       : "memory");
 }
 
@@ -468,17 +494,21 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
   uint32_t W[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) W[j] = static_cast<uint32_t>(fmaf(w[j], sc, 0.5f));
-  const uint32_t wbase = lds_addr(ptile) + 4 * hl * kPRow + t;
-  const uint32_t hdr = lds_addr(reinterpret_cast<const uint8_t*>(pexp));
+  // kept opaque: computed here, not held across the scan loop
+  uint32_t wbase = lds_addr(ptile) + 4 * hl * kPRow + t;
+  uint32_t hdr = lds_addr(reinterpret_cast<const uint8_t*>(pexp));
+  asm volatile("" : "+v"(wbase), "+v"(hdr));
   if (t == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(hdr + 4 * hl), "v"(e) : "memory");
   const int r = lane & 15, g = lane >> 4;
-  const uint32_t ra = lds_addr(ptile) + r * kPRow + 16 * g;
+  uint32_t ra = lds_addr(ptile) + r * kPRow + 16 * g;
+  asm volatile("" : "+v"(ra));
   u32x4 h0, h1, l0, l1;
   int er;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    put_digits(wbase + 16 * j, (W[j] >> 20) & 15u, (W[j] >> 16) & 15u, (W[j] >> 12) & 15u,
-               (W[j] >> 8) & 15u);
+  static_for<0, 8>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    put_digits<j>(wbase, (W[j] >> 20) & 15u, (W[j] >> 16) & 15u, (W[j] >> 12) & 15u,
+                  (W[j] >> 8) & 15u);
+  });
   asm volatile(
       "ds_read_b128 %0, %3\n"
       "ds_read_b128 %1, %3 offset:64\n"
@@ -487,8 +517,10 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
       : "=&v"(h0), "=&v"(h1), "=&v"(er)
       : "v"(ra), "v"(hdr + 4 * (r >> 2))
       : "memory");
-#pragma unroll
-  for (int j = 0; j < 8; ++j) put_digits(wbase + 16 * j, (W[j] >> 4) & 15u, W[j] & 15u, 0u, 0u);
+  static_for<0, 8>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    put_digits<j>(wbase, (W[j] >> 4) & 15u, W[j] & 15u, 0u, 0u);
+  });
   asm volatile(
       "ds_read_b128 %0, %2\n"
       "ds_read_b128 %1, %2 offset:64\n"
@@ -519,8 +551,9 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
 // cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
 // 128 VGPRs (four waves per SIMD); group 64, with a third q.K operand and a
 // second value group, gets up to 168 (three waves per SIMD) rather than spill
-// inside the loop (a spill reload waits for every outstanding DMA).
-template <int G>
+// inside the loop (a spill reload waits for every outstanding DMA).  kWide
+// builds a buffer descriptor per page for caches of 4 GiB and more.
+template <int G, bool kWide>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
@@ -529,7 +562,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
   static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
+  static_assert(kRing == 4 && kDepth == 2, "slots are the slices of a block; two in flight");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
+  __shared__ __attribute__((aligned(16))) int wids[kMaxSplitPages];  // block ids of the pages
   __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
   __shared__ float cm[4][kHT], cl[4][kHT];
 
@@ -555,7 +590,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int p_begin = wgs * spw;
   if (p_begin >= n_pages) return;
   const int p_end = (wgs == ns_b - 1) ? n_pages : p_begin + spw;
-  const int np = p_end - p_begin;
+  const int np = p_end - p_begin;  // at most kMaxSplitPages - 1 (split_pages <= 512)
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
   // 8-page blocks of this range; this wave's are wave, wave + 4, ...  Only the
   // range's last block can be short; its slices past the range are skipped.
@@ -564,9 +599,47 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const bool owns_last = nbw > 0 && ((nblk - 1 - wave) & 3) == 0;
   const int ns_last = owns_last ? min(4, (np - 8 * (nblk - 1) + 1) >> 1) : 4;
   const int nsl = nbw > 0 ? 4 * (nbw - 1) + ns_last : 0;
-  auto slice_page = [&](int i) { return p_begin + 8 * (wave + 4 * (i >> 2)) + 2 * (i & 3); };
 
-  // query operand first: waiting for it must not drain the ring's DMAs
+  // Block ids, clamped into the cache (block ids past INT32_MAX cannot be
+  // addressed by the table anyway).  The wave's first block comes in scalar
+  // loads, so its first DMAs wait for nothing else; the range's whole id table
+  // (padded with block 0 to whole 8-page blocks; padding pages are masked out)
+  // goes to LDS through vector loads issued alongside.
+  const int max_block = static_cast<int>(min(num_blocks, static_cast<int64_t>(0x7fffffff)) - 1);
+  auto clamp_id = [&](int id) {
+    return static_cast<int>(min(static_cast<uint32_t>(id), static_cast<uint32_t>(max_block)));
+  };
+  int idc[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // ids of the current block's pages
+  int idn[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // of the next block's
+  // (indices clamped into the range, not branched on, so that all loads
+  // issue back to back; entries past the range are never used unmasked)
+  if (8 * wave + 8 <= np) {  // a whole block: one 8-dword scalar load
+    typedef int int8v __attribute__((ext_vector_type(8)));
+    const int8v v = *reinterpret_cast<const int8v*>(row + p_begin + 8 * wave);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) idc[k] = clamp_id(v[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) idc[k] = clamp_id(row[min(p_begin + 8 * wave + k, p_end - 1)]);
+  }
+  const int np8 = (np + 7) & ~7;
+  static_assert(kMaxSplitPages == 3 * 256, "three table entries per thread");
+  int idv[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    idv[k] = row[min(p_begin + static_cast<int>(threadIdx.x) + 256 * k, p_end - 1)];
+  auto fill_table = [&]() {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int lp = threadIdx.x + 256 * k;
+      if (lp < np8) wids[lp] = lp < np ? clamp_id(idv[k]) : 0;
+    }
+  };
+
+  // The query operand is loaded next and the ring's first slices are issued
+  // right after it; the operand is then waited for on each path separately, so
+  // the wait counts only the loads ahead of the slices (they complete in order
+  // and the slices stay in flight) and the loop never waits on it again.
   const size_t hgi = (static_cast<size_t>(b) * Hkv + h) * QG + qg;
   const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
   const uint4 q0 = qap[0], q1 = qap[1], q2 = qap[2];
@@ -576,33 +649,70 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int t = lane & 15;
   const int hl = lane >> 4;
   const float4 fq = qf[hgi * kHT + hl];
-  asm volatile("" ::"v"(__builtin_bit_cast(u32x4, q0)), "v"(__builtin_bit_cast(u32x4, q1)),
-               "v"(__builtin_bit_cast(u32x4, q2)), "v"(__builtin_bit_cast(u32x4, q3)),
-               "v"(__builtin_bit_cast(u32x4, q4)), "v"(__builtin_bit_cast(u32x4, qsv)),
-               "v"(fq.y), "v"(fq.z));
-  auto op6 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
-    return v8i{static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
-               static_cast<int>(e), static_cast<int>(f), 0, 0};
-  };
-  const v8i qA0 = op6(q0.x, q0.y, q0.z, q0.w, q1.x, q1.y);
-  const v8i qA1 = op6(q1.z, q1.w, q2.x, q2.y, q2.z, q2.w);
-  const v8i qA2 = op6(q3.x, q3.y, q3.z, q3.w, q4.x, q4.y);
-  const int qsc_hi = static_cast<int>(qsv.x);
-  const int qsc_lo = static_cast<int>(qsv.y);
-  const float sq0 = G == 1 ? fq.y + fq.z : fq.y;
-  const float sq1 = fq.z;
 
-  // block ids past INT32_MAX cannot be addressed by the table anyway
-  const int max_block = static_cast<int>(min(num_blocks, static_cast<int64_t>(0x7fffffff)) - 1);
   uint8_t* myring = &ring[wave][0][0];
   // DMA lane offsets: 16 code bytes per lane; one (scale, zero) word per lane
   const uint32_t off16 = 16u * lane, off4 = kSzOff + 4u * lane;
   const bool sz_lane = G == 2 || lane < 32;
-  for (int i = 0; i < kDepth && i < nsl; ++i)
-    issue_slice<G>(myring + i * kSlot, pages, Hkv, h,
-                   load_ids(row, slice_page(i), p_end, max_block), off16, off4, sz_lane);
-  SliceIds next_ids = {0, 0};  // of slice kDepth, and then of each slice kDepth ahead
-  if (kDepth < nsl) next_ids = load_ids(row, slice_page(kDepth), p_end, max_block);
+  // one descriptor over the whole cache (narrow form): page = scalar offset
+  const uint32_t pstride = static_cast<uint32_t>(Hkv) * PB, hoff = static_cast<uint32_t>(h) * PB;
+  const uint32_t cache_bytes =
+      kWide ? 0u : static_cast<uint32_t>(static_cast<uint64_t>(num_blocks) * pstride);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(pages), 0, static_cast<int>(cache_bytes), kBufferWord3);
+  auto issue = [&](uint8_t* slot, int b0, int b1) {
+    if constexpr (kWide) {
+      dma_page<G>(pages + (static_cast<int64_t>(b0) * Hkv + h) * PB, slot, off16, off4, sz_lane);
+      dma_page<G>(pages + (static_cast<int64_t>(b1) * Hkv + h) * PB, slot + PB, off16, off4,
+                  sz_lane);
+    } else {
+      dma_page_at<G>(rsrc, static_cast<uint32_t>(b0) * pstride + hoff, slot, off16, off4, sz_lane);
+      dma_page_at<G>(rsrc, static_cast<uint32_t>(b1) * pstride + hoff, slot + PB, off16, off4,
+                     sz_lane);
+    }
+  };
+  // LDS address of the ids of this wave's block m (the same in every lane)
+  const uint32_t ids_base = lds_addr(reinterpret_cast<const uint8_t*>(&wids[0]));
+  auto ids_addr = [&](int m) { return ids_base + 32u * static_cast<uint32_t>(wave + 4 * m); };
+
+  // The operand passes through an empty asm on each path: the compiler waits
+  // for it there, and afterwards sees it as defined by the asm, not by a
+  // pending load.  Distinct texts keep the three from being merged.
+  u32x4 qv0 = __builtin_bit_cast(u32x4, q0), qv1 = __builtin_bit_cast(u32x4, q1);
+  u32x4 qv2 = __builtin_bit_cast(u32x4, q2), qv3 = __builtin_bit_cast(u32x4, q3);
+  u32x4 qv4 = __builtin_bit_cast(u32x4, q4), qvs = __builtin_bit_cast(u32x4, qsv);
+  float fqy = fq.y, fqz = fq.z;
+#define KVQ_HOLD_Q(tag)                                                                        \
+  asm volatile("; q operand " tag                                                              \
+               : "+v"(qv0), "+v"(qv1), "+v"(qv2), "+v"(qv3), "+v"(qv4), "+v"(qvs), "+v"(fqy),  \
+                 "+v"(fqz))
+  if (nsl >= 2) {
+    issue(myring, idc[0], idc[1]);
+    issue(myring + kSlot, idc[2], idc[3]);
+    fill_table();
+    KVQ_HOLD_Q("after two slices");
+  } else if (nsl == 1) {
+    issue(myring, idc[0], idc[1]);
+    fill_table();
+    KVQ_HOLD_Q("after one slice");
+  } else {
+    fill_table();
+    KVQ_HOLD_Q("alone");
+  }
+#undef KVQ_HOLD_Q
+  __syncthreads();  // the id table is complete
+
+  auto op6 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
+    return v8i{static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
+               static_cast<int>(e), static_cast<int>(f), 0, 0};
+  };
+  const v8i qA0 = op6(qv0.x, qv0.y, qv0.z, qv0.w, qv1.x, qv1.y);
+  const v8i qA1 = op6(qv1.z, qv1.w, qv2.x, qv2.y, qv2.z, qv2.w);
+  const v8i qA2 = op6(qv3.x, qv3.y, qv3.z, qv3.w, qv4.x, qv4.y);
+  const int qsc_hi = static_cast<int>(qvs.x);
+  const int qsc_lo = static_cast<int>(qvs.y);
+  const float sq0 = G == 1 ? fqy + fqz : fqy;
+  const float sq1 = fqz;
 
   ScanState st;
   st.m = kNegBig;
@@ -613,41 +723,44 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   for (int j = 0; j < 8; ++j) st.acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
   u32x4 vw[4] = {};
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // this lane's LDS read addresses in slot 0 (other slots: immediate offsets)
+  const uint32_t ring0 = lds_addr(myring);
+  const uint32_t ak = ring0 + kKCodeOff + 32 * t + 8 * hl;
+  const uint32_t as = ring0 + kSzOff + 4 * G * t;
+  const uint32_t av = ring0 + kVCodeOff + 32 * t;
 
-  for (int bi = 0; bi < nbw; ++bi) {
+  // One 8-page block.  kFast: a block whose four slices all exist, each with
+  // its successor two slices ahead to issue, and whose pages are all full (it
+  // is neither the range's last block nor holds the context's last page):
+  // no per-slice conditions.
+  auto run_block = [&](auto fast, int bi) {
+    constexpr bool kFast = decltype(fast)::value;
     const int pblk = p_begin + 8 * (wave + 4 * bi);
     float lg[8];
     uint2 szv[8];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    auto slice = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
       const int i = 4 * bi + s;
-      if (i < nsl) {
-        if (i + kDepth < nsl) {
-          issue_slice<G>(myring + ((i + kDepth) % kRing) * kSlot, pages, Hkv, h, next_ids, off16,
-                         off4, sz_lane);
-          if (i + kDepth + 1 < nsl)
-            next_ids = load_ids(row, slice_page(i + kDepth + 1), p_end, max_block);
+      if (kFast || i < nsl) {
+        // slice i + 2: slices 2, 3 of this block, then 0, 1 of the next
+        if (kFast || i + kDepth < nsl) {
+          if (s < 2)
+            issue(myring + (s + 2) * kSlot, idc[2 * s + 4], idc[2 * s + 5]);
+          else
+            issue(myring + (s - 2) * kSlot, idn[2 * s - 4], idn[2 * s - 3]);
         }
         // slice i has landed once at most the DMAs of the slices behind it are pending
-        const int behind = min(kDepth, nsl - 1 - i);
-        if (kDepth >= 3 && behind == 3)
-          wait_vmem<3 * kDmaPerSlice>();
-        else if (kDepth >= 2 && behind == 2)
-          wait_vmem<2 * kDmaPerSlice>();
-        else if (behind == 1)
+        if (kFast || i + kDepth < nsl)
+          wait_vmem<kDepth * kDmaPerSlice>();
+        else if (i + 1 < nsl)
           wait_vmem<kDmaPerSlice>();
         else
           wait_vmem<0>();
-        // the slot base is wave-uniform; the lane offsets are kept opaque so
-        // that the compiler adds them here instead of holding every
-        // (slot, offset) sum in registers across the loop
-        const uint32_t sbase = lds_addr(myring + (i % kRing) * kSlot);
-        uint32_t ok = kKCodeOff + 32 * t + 8 * hl, os = kSzOff + 4 * G * t;
-        uint32_t ov = kVCodeOff + 32 * t;
-        asm volatile("" : "+v"(ok), "+v"(os), "+v"(ov));
         Slice c;
-        read_slice<G>(c, sbase + ok, sbase + os);
-        if (hl == s) read_vwords(vw, sbase + ov, PB);
+        read_slice<G, s * kSlot>(c, ak, as);
+        if (hl == s) read_vwords<PB, s * kSlot>(vw, av);
+        // the next block's ids, two slices before its first DMA
+        if (s == 0 && (kFast || bi + 1 < nbw)) read_ids8(ids_addr(bi + 1), idn);
 
         // q.K: D[4*head + digit][token t]; the digit rows add up in-lane
         const v8i k0 = fp6_codes(c.kc0.x, c.kc0.y);
@@ -679,30 +792,55 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
           l0 = logit2(k0, c.szk0);
           l1 = logit2(k1, c.szk1);
         }
-        const int pg = pblk + 2 * s;
-        const int pos = pg * kBlock + t;
-        const bool v0 = pos < ctx;
-        const bool v1 = pg + 1 < p_end && pos + kBlock < ctx;
-        lg[2 * s] = v0 ? l0 : -INFINITY;
-        lg[2 * s + 1] = v1 ? l1 : -INFINITY;
-        // slots past the context hold arbitrary bytes (possibly NaN as fp16):
-        // their value scale and zero are replaced, not multiplied by p = 0
-        szv[2 * s] = v0 ? c.szv0 : make_uint2(0u, 0u);
-        szv[2 * s + 1] = v1 ? c.szv1 : make_uint2(0u, 0u);
+        // the logits are complete before the next slice's reads: otherwise the
+        // compiler sinks the q.K products to the softmax, holding every
+        // slice's code operands at once
+        asm volatile("" : "+v"(l0), "+v"(l1));
+        if constexpr (kFast) {
+          lg[2 * s] = l0;
+          lg[2 * s + 1] = l1;
+          szv[2 * s] = c.szv0;
+          szv[2 * s + 1] = c.szv1;
+        } else {
+          const int pg = pblk + 2 * s;
+          const int pos = pg * kBlock + t;
+          const bool v0 = pos < ctx;
+          const bool v1 = pg + 1 < p_end && pos + kBlock < ctx;
+          lg[2 * s] = v0 ? l0 : -INFINITY;
+          lg[2 * s + 1] = v1 ? l1 : -INFINITY;
+          // slots past the context hold arbitrary bytes (possibly NaN as fp16):
+          // their value scale and zero are replaced, not multiplied by p = 0
+          szv[2 * s] = v0 ? c.szv0 : make_uint2(0u, 0u);
+          szv[2 * s + 1] = v1 ? c.szv1 : make_uint2(0u, 0u);
+        }
       } else {
         lg[2 * s] = -INFINITY;
         lg[2 * s + 1] = -INFINITY;
         szv[2 * s] = make_uint2(0u, 0u);
         szv[2 * s + 1] = make_uint2(0u, 0u);
       }
-    }
+    };
+    // the scheduler keeps each slice's work between its reads and the next
+    // slice's (interleaving slices only raises register pressure)
+    slice(Const<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    slice(Const<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    slice(Const<int, 2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    slice(Const<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- online softmax over the block (base 2), lazy rescale
+    // ---- online softmax over the block (base 2).  The running maximum is
+    // raised only when the block's exceeds it by more than 2^kLazy: weights up
+    // to 2^kLazy are exact in the fixed-point P digits and harmless in fp32,
+    // and the accumulators are rescaled far less often.
     float mb = lg[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mb = fmaxf(mb, lg[j]);
-    const float mnew = fmaxf(st.m, row16_max(mb));
-    if (__any(mnew > st.m)) {
+    mb = row16_max(mb);
+    if (__any(mb > st.m + kLazy)) {
+      const float mnew = fmaxf(st.m, mb);
       const float alpha = exp2_hw(st.m - mnew);
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
@@ -726,15 +864,21 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     st.l += lsum;
     st.zs0 += z0;
     st.zs1 += z1;
-    // the slot of the block's last slice (read above; no DMA targets it yet)
-    uint8_t* ptile = myring + ((4 * bi + 3 < nsl ? 4 * bi + 3 : nsl - 1) % kRing) * kSlot;
+    // slot 3: read above; the DMAs in flight target slots 0 and 1
+    uint8_t* ptile = myring + 3 * kSlot;
     if constexpr (G == 1) {
       block_pv<0, 8>(st, p, sz0, ptile, pexp[wave], vw, lane);
     } else {
       block_pv<0, 4>(st, p, sz0, ptile, pexp[wave], vw, lane);
       block_pv<4, 8>(st, p, sz1, ptile, pexp[wave], vw, lane);
     }
-  }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) idc[k] = idn[k];
+  };
+  const int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
+  int bi = 0;
+  for (; bi < nfast; ++bi) run_block(Const<bool, true>{}, bi);
+  for (; bi < nbw; ++bi) run_block(Const<bool, false>{}, bi);
 
   // ---- per-wave finish: reduce row sums, form unnormalised outputs
   const float l = row16_sum(st.l);
@@ -965,14 +1109,17 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
   }
   if (p.S > 0 && (stages & 2)) {
     const dim3 g2(p.S, Hkv * p.QG, B);
+    // one buffer descriptor spans the cache when its byte size fits 32 bits
+    const bool wide = static_cast<uint64_t>(num_blocks) * Hkv * page_bytes_for_groups(G) >
+                      0xFFFFFFFFull;
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
+                         max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S);
+    };
     if (G == 2)
-      hipLaunchKernelGGL(split_kernel<2>, g2, dim3(256), 0, stream, pages, num_blocks, Hkv,
-                         block_table, max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part,
-                         p.S);
+      wide ? go(split_kernel<2, true>) : go(split_kernel<2, false>);
     else
-      hipLaunchKernelGGL(split_kernel<1>, g2, dim3(256), 0, stream, pages, num_blocks, Hkv,
-                         block_table, max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part,
-                         p.S);
+      wide ? go(split_kernel<1, true>) : go(split_kernel<1, false>);
   }
   if (stages & 4)
     hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(256), 0, stream, part, ctx_len,
