@@ -583,63 +583,33 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int qg = hy % QG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ctx = min(max(ctx_len[b], 0), max_ctx);
-  const int n_pages = (ctx + kBlock - 1) / kBlock;
-  const int ns_b = num_splits(n_pages, spw);
-  if (wgs >= ns_b) return;
   const int p_begin = wgs * spw;
-  if (p_begin >= n_pages) return;
-  const int p_end = (wgs == ns_b - 1) ? n_pages : p_begin + spw;
-  const int np = p_end - p_begin;  // at most kMaxSplitPages - 1 (split_pages <= 512)
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
-  // 8-page blocks of this range; this wave's are wave, wave + 4, ...  Only the
-  // range's last block can be short; its slices past the range are skipped.
-  const int nblk = (np + 7) >> 3;
-  const int nbw = wave < nblk ? (nblk - wave + 3) >> 2 : 0;
-  const bool owns_last = nbw > 0 && ((nblk - 1 - wave) & 3) == 0;
-  const int ns_last = owns_last ? min(4, (np - 8 * (nblk - 1) + 1) >> 1) : 4;
-  const int nsl = nbw > 0 ? 4 * (nbw - 1) + ns_last : 0;
 
   // Block ids, clamped into the cache (block ids past INT32_MAX cannot be
-  // addressed by the table anyway).  The wave's first block comes in scalar
-  // loads, so its first DMAs wait for nothing else; the range's whole id table
-  // (padded with block 0 to whole 8-page blocks; padding pages are masked out)
-  // goes to LDS through vector loads issued alongside.
+  // addressed by the table anyway).  They are loaded before the context
+  // length is known, with indices clamped into the table row rather than
+  // branched on, so that every load issues at once (entries past the range
+  // are never used unmasked): lanes 0-7 take the wave's first block, whose
+  // DMAs then wait for nothing else, and every thread up to three entries of
+  // the range's id table, which goes to LDS.
+  const int ctx_in = ctx_len[b];
   const int max_block = static_cast<int>(min(num_blocks, static_cast<int64_t>(0x7fffffff)) - 1);
   auto clamp_id = [&](int id) {
     return static_cast<int>(min(static_cast<uint32_t>(id), static_cast<uint32_t>(max_block)));
   };
-  int idc[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // ids of the current block's pages
-  int idn[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // of the next block's
-  // (indices clamped into the range, not branched on, so that all loads
-  // issue back to back; entries past the range are never used unmasked)
-  if (8 * wave + 8 <= np) {  // a whole block: one 8-dword scalar load
-    typedef int int8v __attribute__((ext_vector_type(8)));
-    const int8v v = *reinterpret_cast<const int8v*>(row + p_begin + 8 * wave);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) idc[k] = clamp_id(v[k]);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) idc[k] = clamp_id(row[min(p_begin + 8 * wave + k, p_end - 1)]);
-  }
-  const int np8 = (np + 7) & ~7;
+  const int id_lane = row[min(p_begin + 8 * wave + (lane & 7), max_blocks - 1)];
   static_assert(kMaxSplitPages == 3 * 256, "three table entries per thread");
   int idv[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k)
-    idv[k] = row[min(p_begin + static_cast<int>(threadIdx.x) + 256 * k, p_end - 1)];
-  auto fill_table = [&]() {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int lp = threadIdx.x + 256 * k;
-      if (lp < np8) wids[lp] = lp < np ? clamp_id(idv[k]) : 0;
-    }
-  };
+    idv[k] = row[min(p_begin + static_cast<int>(threadIdx.x) + 256 * k, max_blocks - 1)];
 
-  // The query operand is loaded next and the ring's first slices are issued
-  // right after it; the operand is then waited for on each path separately, so
-  // the wait counts only the loads ahead of the slices (they complete in order
-  // and the slices stay in flight) and the loop never waits on it again.
+  // The query operand is loaded next, and the ring's first slices are issued
+  // once the context length is known; the operand is then waited for on each
+  // path separately, so the wait counts only the loads ahead of the slices
+  // (they complete in order and the slices stay in flight) and the loop never
+  // waits on it again.
   const size_t hgi = (static_cast<size_t>(b) * Hkv + h) * QG + qg;
   const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
   const uint4 q0 = qap[0], q1 = qap[1], q2 = qap[2];
@@ -649,6 +619,35 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int t = lane & 15;
   const int hl = lane >> 4;
   const float4 fq = qf[hgi * kHT + hl];
+
+  const int ctx = min(max(ctx_in, 0), max_ctx);
+  const int n_pages = (ctx + kBlock - 1) / kBlock;
+  const int ns_b = num_splits(n_pages, spw);
+  if (wgs >= ns_b) return;
+  if (p_begin >= n_pages) return;
+  const int p_end = (wgs == ns_b - 1) ? n_pages : p_begin + spw;
+  const int np = p_end - p_begin;  // at most kMaxSplitPages - 1 (split_pages <= 512)
+  // 8-page blocks of this range; this wave's are wave, wave + 4, ...  Only the
+  // range's last block can be short; its slices past the range are skipped.
+  const int nblk = (np + 7) >> 3;
+  const int nbw = wave < nblk ? (nblk - wave + 3) >> 2 : 0;
+  const bool owns_last = nbw > 0 && ((nblk - 1 - wave) & 3) == 0;
+  const int ns_last = owns_last ? min(4, (np - 8 * (nblk - 1) + 1) >> 1) : 4;
+  const int nsl = nbw > 0 ? 4 * (nbw - 1) + ns_last : 0;
+  // the table, padded with block 0 to whole 8-page blocks (padding pages are
+  // masked out)
+  const int np8 = (np + 7) & ~7;
+  int idc[8];                             // ids of the current block's pages
+  int idn[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // of the next block's
+#pragma unroll
+  for (int k = 0; k < 8; ++k) idc[k] = clamp_id(__builtin_amdgcn_readlane(id_lane, k));
+  auto fill_table = [&]() {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int lp = threadIdx.x + 256 * k;
+      if (lp < np8) wids[lp] = lp < np ? clamp_id(idv[k]) : 0;
+    }
+  };
 
   uint8_t* myring = &ring[wave][0][0];
   // DMA lane offsets: 16 code bytes per lane; one (scale, zero) word per lane
