@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the rotated INT2 KV-cache hot path on one MI355X.
 
-One step runs the whole hot path once per layer: kvq_append encodes one new
-bf16 key/value token per sequence (centre, rotate, clip, INT2 group RTN,
-pack into the paged cache) and kvq_decode_attn runs single-token attention
+One step runs the whole hot path once per layer through kvq_append_decode:
+it encodes one new bf16 key/value token per sequence (centre, rotate, clip,
+INT2 group RTN, pack into the paged cache) and runs single-token attention
 over the updated INT2 cache (rotated query, split-K online softmax,
-log-sum-exp merge, inverse value rotation).
+log-sum-exp merge, inverse value rotation).  --separate-calls runs the same
+step as kvq_append followed by kvq_decode_attn.
 
 Default workload: 36 layers x batch 16 of Qwen3-8B-shaped attention (32
 query / 8 KV heads, head_dim 128), 16K tokens of prior context per sequence,
@@ -39,6 +40,8 @@ def parse():
                     help="bound on the oracle's CPU time for the cpu_baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="kvq_append + kvq_decode_attn per layer instead of kvq_append_decode")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the measurement, run a plain fp32 copy kernel (y = -x) over this "
                          "many MiB three times: the reference for HBM byte counters")
@@ -142,10 +145,17 @@ def main():
 
     def run_step(step):
         for layer in range(L):
-            kvq.append(pages[layer], table, spos[step], kn[step][layer], vn[step][layer],
-                       mus[layer], rks[layer], rvs[layer], w.group, w.clip_k, w.clip_v)
-            kvq.decode(pages[layer], table, ctxs[step], maxc[step], qs[step][layer], rks[layer],
-                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=ws)
+            if args.separate_calls:
+                kvq.append(pages[layer], table, spos[step], kn[step][layer], vn[step][layer],
+                           mus[layer], rks[layer], rvs[layer], w.group, w.clip_k, w.clip_v)
+                kvq.decode(pages[layer], table, ctxs[step], maxc[step], qs[step][layer],
+                           rks[layer], rvs[layer], w.group, sm_scale, out=outs[layer],
+                           workspace=ws)
+            else:
+                kvq.append_decode(pages[layer], table, spos[step], ctxs[step], maxc[step],
+                                  kn[step][layer], vn[step][layer], mus[layer], qs[step][layer],
+                                  rks[layer], rvs[layer], w.group, w.clip_k, w.clip_v, sm_scale,
+                                  out=outs[layer], workspace=ws)
 
     graphs = []
     if not args.no_graph:
@@ -267,6 +277,8 @@ def main():
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "clip": w.clip_k,
             "cache": f"INT2 + fp16 scale/zero per {w.group} ({per_tok_head} B per token-head)",
             "launch": "eager" if args.no_graph else "hipGraph per step", "parallelism": "none",
+            "step_call": ("kvq_append + kvq_decode_attn" if args.separate_calls
+                          else "kvq_append_decode"),
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(B * args.steps / (gpu_ms * 1e-3), 1),

@@ -179,6 +179,35 @@ int kvq_decode_attn_staged(const void *pages, int64_t num_blocks, int32_t num_kv
                            float sm_scale, float *out, void *workspace, size_t workspace_bytes,
                            int32_t split_pages, int32_t stages, void *stream);
 
+/*
+ * kvq_append_decode -- one decode step of one layer: append one new token per
+ * sequence, then attend over the cache including it.
+ *
+ * The same computation as kvq_append with num_new = 1 followed by
+ * kvq_decode_attn on the same stream (the two steps of the OptR review page,
+ * "What carries the argument": encode the new key and value, then attention
+ * over the quantised cache and the inverse value rotation), with the append
+ * and the decode's query rotation sharing one launch.  Arguments are those
+ * of the two calls:
+ *   start_pos      device  int32 [batch]: position of the new token
+ *   k, v           device  [batch][1][num_kv_heads][head_dim] of kv_dtype
+ *   ctx_len        device  int32 [batch]: tokens attended, normally
+ *                          start_pos[b] + 1
+ *   q              device  [batch][num_q_heads][head_dim] of q_dtype
+ *   out, workspace, split_pages, sm_scale, max_ctx_len: as kvq_decode_attn
+ * Validation is that of both calls; the workspace size is
+ * kvq_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+ * max_ctx_len, split_pages).  batch == 0 is a no-op.
+ */
+int kvq_append_decode(void *pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t group, const int32_t *block_table, int32_t max_blocks_per_seq,
+                      const int32_t *start_pos, const int32_t *ctx_len, int32_t max_ctx_len,
+                      int32_t batch, const void *k, const void *v, int32_t kv_dtype,
+                      const float *mu, float clip_k, float clip_v, int32_t num_q_heads,
+                      const void *q, int32_t q_dtype, const float *rot_k, const float *rot_v,
+                      float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                      int32_t split_pages, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

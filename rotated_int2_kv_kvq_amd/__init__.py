@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     STAGE_SPLITS,
     KvqError,
     append,
+    append_decode,
     decode,
     decode_workspace_bytes,
     lib,

@@ -36,6 +36,9 @@ SIGNATURES = {
     "kvq_decode_attn_staged": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32,
                                 c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_sz,
                                 c_i32, c_i32, c_vp], c_i32),
+    "kvq_append_decode": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32,
+                           c_i32, c_vp, c_vp, c_i32, c_vp, c_f32, c_f32, c_i32, c_vp, c_i32,
+                           c_vp, c_vp, c_f32, c_vp, c_vp, c_sz, c_i32, c_vp], c_i32),
 }
 STAGE_PREPARE, STAGE_SPLITS, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 7
 
@@ -136,4 +139,36 @@ def decode(pages: torch.Tensor, block_table: torch.Tensor, ctx_len: torch.Tensor
     else:
         _check(lib().kvq_decode_attn_staged(*args, stages, _stream(stream)),
                "kvq_decode_attn_staged")
+    return out
+
+
+def append_decode(pages: torch.Tensor, block_table: torch.Tensor, start_pos: torch.Tensor,
+                  ctx_len: torch.Tensor, max_ctx_len: int, k: torch.Tensor, v: torch.Tensor,
+                  mu: torch.Tensor, q: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor,
+                  group: int, clip_k: float, clip_v: float, sm_scale: float | None = None,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  split_pages: int = 0, stream=None) -> torch.Tensor:
+    """kvq_append_decode: k, v [B][1][Hkv][128] appended at start_pos, then
+    q [B][Hq][128] attends over ctx_len tokens -> out float32 [B][Hq][128]."""
+    num_blocks, hkv, _ = pages.shape
+    B, Hq, d = q.shape
+    if k.dtype not in _DTYPES or v.dtype != k.dtype:
+        raise ValueError("k and v must both be float32 or bfloat16")
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    if k.shape[1] != 1:
+        raise ValueError("append_decode appends exactly one token per sequence")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, hkv, max_ctx_len, d, split_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().kvq_append_decode(
+        _ptr(pages), num_blocks, hkv, d, group, _ptr(block_table), block_table.shape[1],
+        _ptr(start_pos), _ptr(ctx_len), max_ctx_len, B, _ptr(k), _ptr(v), _DTYPES[k.dtype],
+        _ptr(mu), clip_k, clip_v, Hq, _ptr(q), _DTYPES[q.dtype], _ptr(rot_k), _ptr(rot_v),
+        sm_scale, _ptr(out), _ptr(workspace), workspace.numel(), split_pages, _stream(stream)),
+        "kvq_append_decode")
     return out

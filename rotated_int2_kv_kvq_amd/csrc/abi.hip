@@ -32,11 +32,14 @@ KVQ_API size_t kvq_page_bytes(int32_t head_dim, int32_t group) {
   return static_cast<size_t>(kvq::page_bytes_for_groups(head_dim / group));
 }
 
-KVQ_API int kvq_append(void* pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t group, const int32_t* block_table, int32_t max_blocks_per_seq,
-                       const int32_t* start_pos, int32_t batch, int32_t num_new, const void* k,
-                       const void* v, int32_t kv_dtype, const float* mu, const float* rot_k,
-                       const float* rot_v, float clip_k, float clip_v, void* stream) {
+namespace {
+// Host-side checks of kvq_append's arguments (num_new tokens); KVQ_OK when the
+// call may proceed (batch or num_new zero included).
+int check_append(const void* pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t group, const int32_t* block_table, int32_t max_blocks_per_seq,
+                 const int32_t* start_pos, int32_t batch, int32_t num_new, const void* k,
+                 const void* v, int32_t kv_dtype, const float* mu, const float* rot_k,
+                 const float* rot_v, float clip_k, float clip_v) {
   if (!valid_geometry(head_dim, group)) return KVQ_ERR_INVALID_ARG;
   if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
   if (batch < 0 || num_new < 0 || num_kv_heads < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
@@ -51,6 +54,19 @@ KVQ_API int kvq_append(void* pages, int64_t num_blocks, int32_t num_kv_heads, in
   if (!aligned(pages, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(mu, 16) ||
       !aligned(rot_k, 16) || !aligned(rot_v, 16))
     return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+}  // namespace
+
+KVQ_API int kvq_append(void* pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t group, const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* start_pos, int32_t batch, int32_t num_new, const void* k,
+                       const void* v, int32_t kv_dtype, const float* mu, const float* rot_k,
+                       const float* rot_v, float clip_k, float clip_v, void* stream) {
+  const int st = check_append(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                              max_blocks_per_seq, start_pos, batch, num_new, k, v, kv_dtype, mu,
+                              rot_k, rot_v, clip_k, clip_v);
+  if (st != KVQ_OK || batch == 0 || num_new == 0) return st;
   const int rc = kvq::launch_append(static_cast<uint8_t*>(pages), num_blocks, num_kv_heads,
                                     head_dim / group, block_table, max_blocks_per_seq, start_pos,
                                     batch, num_new, k, v, kv_dtype == KVQ_BF16, mu, rot_k, rot_v,
@@ -78,15 +94,15 @@ KVQ_API size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
   return kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages).total;
 }
 
-KVQ_API int kvq_decode_attn_staged(const void* pages, int64_t num_blocks, int32_t num_kv_heads,
-                                   int32_t head_dim, int32_t group, const int32_t* block_table,
-                                   int32_t max_blocks_per_seq, const int32_t* ctx_len,
-                                   int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
-                                   const void* q, int32_t q_dtype, const float* rot_k,
-                                   const float* rot_v, float sm_scale, float* out,
-                                   void* workspace, size_t workspace_bytes, int32_t split_pages,
-                                   int32_t stages, void* stream) {
-  if (stages < 1 || stages > KVQ_STAGE_ALL) return KVQ_ERR_INVALID_ARG;
+namespace {
+// Host-side checks of the decode arguments; on KVQ_OK with batch > 0, *plan
+// is the workspace carve-up.
+int check_decode(const void* pages, int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t group, const int32_t* block_table, int32_t max_blocks_per_seq,
+                 const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                 const void* q, int32_t q_dtype, const float* rot_k, const float* rot_v,
+                 float sm_scale, const float* out, const void* workspace, size_t workspace_bytes,
+                 int32_t split_pages, kvq::DecodePlan* plan) {
   if (!valid_geometry(head_dim, group)) return KVQ_ERR_INVALID_ARG;
   if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
   if (!valid_decode_shape(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages))
@@ -102,10 +118,28 @@ KVQ_API int kvq_decode_attn_staged(const void* pages, int64_t num_blocks, int32_
     return KVQ_ERR_INVALID_ARG;
   if (!aligned(pages, 16) || !aligned(rot_k, 16) || !aligned(rot_v, 16))
     return KVQ_ERR_INVALID_ARG;
-  const kvq::DecodePlan plan =
-      kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
-  if (!workspace || workspace_bytes < plan.total || !aligned(workspace, 256))
+  *plan = kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
+  if (!workspace || workspace_bytes < plan->total || !aligned(workspace, 256))
     return KVQ_ERR_WORKSPACE;
+  return KVQ_OK;
+}
+}  // namespace
+
+KVQ_API int kvq_decode_attn_staged(const void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t group, const int32_t* block_table,
+                                   int32_t max_blocks_per_seq, const int32_t* ctx_len,
+                                   int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                                   const void* q, int32_t q_dtype, const float* rot_k,
+                                   const float* rot_v, float sm_scale, float* out,
+                                   void* workspace, size_t workspace_bytes, int32_t split_pages,
+                                   int32_t stages, void* stream) {
+  if (stages < 1 || stages > KVQ_STAGE_ALL) return KVQ_ERR_INVALID_ARG;
+  kvq::DecodePlan plan{};
+  const int st = check_decode(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                              max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q,
+                              q_dtype, rot_k, rot_v, sm_scale, out, workspace, workspace_bytes,
+                              split_pages, &plan);
+  if (st != KVQ_OK || batch == 0) return st;
   const int rc = kvq::launch_decode(
       static_cast<const uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
       max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k,
@@ -124,4 +158,30 @@ KVQ_API int kvq_decode_attn(const void* pages, int64_t num_blocks, int32_t num_k
                                 max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q,
                                 q_dtype, rot_k, rot_v, sm_scale, out, workspace, workspace_bytes,
                                 split_pages, KVQ_STAGE_ALL, stream);
+}
+
+KVQ_API int kvq_append_decode(void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t group, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* start_pos,
+                              const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch,
+                              const void* k, const void* v, int32_t kv_dtype, const float* mu,
+                              float clip_k, float clip_v, int32_t num_q_heads, const void* q,
+                              int32_t q_dtype, const float* rot_k, const float* rot_v,
+                              float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, int32_t split_pages, void* stream) {
+  int st = check_append(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                        max_blocks_per_seq, start_pos, batch, 1, k, v, kv_dtype, mu, rot_k, rot_v,
+                        clip_k, clip_v);
+  if (st != KVQ_OK) return st;
+  kvq::DecodePlan plan{};
+  st = check_decode(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                    max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype,
+                    rot_k, rot_v, sm_scale, out, workspace, workspace_bytes, split_pages, &plan);
+  if (st != KVQ_OK || batch == 0) return st;
+  const int rc = kvq::launch_append_decode(
+      static_cast<uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
+      max_blocks_per_seq, start_pos, k, v, kv_dtype == KVQ_BF16, mu, clip_k, clip_v, ctx_len,
+      max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k, rot_v, sm_scale, out,
+      workspace, plan, static_cast<hipStream_t>(stream));
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
 }

@@ -34,6 +34,7 @@
 //      through a last-workgroup counter needs device-scope release/acquire,
 //      i.e. an L2 writeback and invalidate per workgroup on this multi-XCD
 //      part, which costs far more than the launch.)
+#include "append_one.h"
 #include "kvq_common.h"
 #include "kvq_launch.h"
 
@@ -112,78 +113,27 @@ __host__ __device__ inline int num_splits(int n_pages, int spw) {
 // |x| is fixed-point with 32 fraction bits under 2^e: eight 4-bit digits,
 // digit d (0 = most significant) worth b * 2^(e - 4 - 4d), as the FP6 value
 // b/8 under the row scale 2^(e + 2 - 4d): the extra 8 cancels the code
-// operand's code/8, so the MFMA rows sum to x . code.  In an A operand, lane L has row
-// r = L%16 and lane group g = L/16; FP6 field j (k = 32g + j) is channel
-// 32g + 16(j/16) + (3(j%16) mod 16), the channel order fp6_codes gives the
-// key code words.
+// operand's code/8, so the MFMA rows sum to x . code.  In an A operand, lane
+// L has row r = L%16 and lane group g = L/16; FP6 field j (k = 32g + j) is
+// channel 32g + 16(j/16) + (3(j%16) mod 16), the channel order fp6_codes
+// gives the key code words.
 //   group 128: operand 0 rows (head r/4, digit r%4), operand 1 rows
 //              (head r/4, digit 4 + r%4);
 //   group 64:  operand 0 and 1 rows (head r/4, digit r%4) over the channels
 //              of group 0 and 1 (zero in the other lanes), operand 2 rows
 //              (head r/4, group (r/2)%2, digit 4 + r%2) over that group's
 //              channels: 24 bits.
-template <bool kBf16, int G>
-__global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ q,
-                                                       const float* __restrict__ rot_k, int Hq,
-                                                       int Hkv, int QG, float qscale,
-                                                       uint32_t* __restrict__ qa,
-                                                       float4* __restrict__ qf) {
-  __shared__ float qin[kHT][kHeadDim];
-  __shared__ float red[4][kHT][kHeadDim];  // split-K partial products
-  __shared__ uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
-  __shared__ int qe[kHT];
-  const int h = blockIdx.x / QG;
-  const int qg = blockIdx.x % QG;
-  const int b = blockIdx.y;
-  const int Hg = Hq / Hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int nh = min(kHT, Hg - qg * kHT);
 
-  // the tile's query rows (zero for rows past the KV head's query heads)
-  {
-    const int hh = tid >> 6, c = (tid & 63) * 2;
-    float v0 = 0.f, v1 = 0.f;
-    if (hh < nh) {
-      const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + hh) * kHeadDim + c;
-      if constexpr (kBf16) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + qrow);
-        v0 = bf16_to_f32(static_cast<uint16_t>(u & 0xffffu));
-        v1 = bf16_to_f32(static_cast<uint16_t>(u >> 16));
-      } else {
-        const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(q) + qrow);
-        v0 = f.x;
-        v1 = f.y;
-      }
-    }
-    qin[hh][c] = v0;
-    qin[hh][c + 1] = v1;
-  }
-  // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
-  // before the products, one pass over R_K for the four heads
-  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
-  float ra[32], rb[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    ra[i] = R[i * kHeadDim + lane];
-    rb[i] = R[i * kHeadDim + lane + 64];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < kHT; ++hh) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float qi = qin[hh][32 * wv + i];
-      a0 = fmaf(qi, ra[i], a0);
-      a1 = fmaf(qi, rb[i], a1);
-    }
-    red[wv][hh][lane] = a0;
-    red[wv][hh][lane + 64] = a1;
-  }
-  __syncthreads();
-
+// Wave hl of the first 256 threads: the digits of query head hl of the tile
+// into dig, its exponent into qe and its per-group sums into qf.
+template <int G>
+__device__ __forceinline__ void prologue_digits(int h, int qg, int b, int Hkv, int QG,
+                                                float qscale,
+                                                const float (&red)[4][kHT][kHeadDim],
+                                                uint8_t (&dig)[kHT][kHeadDim][8],
+                                                int (&qe)[kHT], float4* __restrict__ qf) {
+  const int lane = threadIdx.x & 63;
+  const int wv = (threadIdx.x >> 6) & 3;
   // wave hl: x = qscale * q_r of head hl, channels lane and lane + 64
   const int hl = wv;
   float r0 = ((red[0][hl][lane] + red[1][hl][lane]) + (red[2][hl][lane] + red[3][hl][lane]));
@@ -219,8 +169,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
     // per-group sums of x for the zero-point term (channels < 64, >= 64)
     qf[((static_cast<size_t>(b) * Hkv + h) * QG + qg) * kHT + hl] = make_float4(0.f, s0, s1, 0.f);
   }
-  __syncthreads();
+}
 
+// The A operands, one thread per (operand, lane).
+template <int G>
+__device__ __forceinline__ void prologue_pack(int h, int qg, int b, int Hkv, int QG,
+                                              const uint8_t (&dig)[kHT][kHeadDim][8],
+                                              const int (&qe)[kHT], uint32_t* __restrict__ qa) {
+  const int lane = threadIdx.x & 63;
+  const int wv = (threadIdx.x >> 6) & 3;
   // thread (operand, lane L): FP6 field j of lane L (row r = L%16, lane group
   // g = L/16) holds the digit of channel 32g + 16(j/16) + (3(j%16) mod 16)
   constexpr int kOps = G == 1 ? 2 : 3;
@@ -268,6 +225,107 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
           static_cast<uint32_t>(min(max(kScaleOne + qe[head] + 2 - 4 * dlo, 1), 254));
     }
   }
+}
+
+// The body is a device function of (query tile hx = h*QG + qg, sequence b):
+// threads 0-255 do the work; further threads of a larger workgroup only pass
+// the barriers (the fused decode step runs it in 1024-thread workgroups).
+template <bool kBf16, int G>
+__device__ __forceinline__ void prologue_body(int hx, int b, const void* __restrict__ q,
+                                              const float* __restrict__ rot_k, int Hq, int Hkv,
+                                              int QG, float qscale, uint32_t* __restrict__ qa,
+                                              float4* __restrict__ qf) {
+  __shared__ float qin[kHT][kHeadDim];
+  __shared__ float red[4][kHT][kHeadDim];  // split-K partial products
+  __shared__ uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
+  __shared__ int qe[kHT];
+  const int h = hx / QG;
+  const int qg = hx % QG;
+  const int Hg = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const bool act = tid < 256;
+  const int lane = tid & 63;
+  const int wv = (tid >> 6) & 3;
+  const int nh = min(kHT, Hg - qg * kHT);
+
+  // the tile's query rows (zero for rows past the KV head's query heads)
+  if (act) {
+    const int hh = tid >> 6, c = (tid & 63) * 2;
+    float v0 = 0.f, v1 = 0.f;
+    if (hh < nh) {
+      const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + hh) * kHeadDim + c;
+      if constexpr (kBf16) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + qrow);
+        v0 = bf16_to_f32(static_cast<uint16_t>(u & 0xffffu));
+        v1 = bf16_to_f32(static_cast<uint16_t>(u >> 16));
+      } else {
+        const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(q) + qrow);
+        v0 = f.x;
+        v1 = f.y;
+      }
+    }
+    qin[hh][c] = v0;
+    qin[hh][c + 1] = v1;
+  }
+  // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
+  // before the products, one pass over R_K for the four heads
+  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
+  float ra[32], rb[32];
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      ra[i] = R[i * kHeadDim + lane];
+      rb[i] = R[i * kHeadDim + lane + 64];
+    }
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int hh = 0; hh < kHT; ++hh) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float qi = qin[hh][32 * wv + i];
+        a0 = fmaf(qi, ra[i], a0);
+        a1 = fmaf(qi, rb[i], a1);
+      }
+      red[wv][hh][lane] = a0;
+      red[wv][hh][lane + 64] = a1;
+    }
+  }
+  __syncthreads();
+  if (act) prologue_digits<G>(h, qg, b, Hkv, QG, qscale, red, dig, qe, qf);
+  __syncthreads();
+  if (act) prologue_pack<G>(h, qg, b, Hkv, QG, dig, qe, qa);
+}
+
+template <bool kBf16, int G>
+__global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ q,
+                                                       const float* __restrict__ rot_k, int Hq,
+                                                       int Hkv, int QG, float qscale,
+                                                       uint32_t* __restrict__ qa,
+                                                       float4* __restrict__ qf) {
+  prologue_body<kBf16, G>(blockIdx.x, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa, qf);
+}
+
+// --------------------------------------------------------------------------- decode step
+// The single-token append and the query rotation in one launch (both read
+// R_K of the KV head; neither depends on the other).  grid (Hkv * (1 + QG),
+// B), block 1024: x < Hkv appends the new token of KV head x, the others
+// prepare query tile x - Hkv.
+template <bool kKvBf16, bool kQBf16, int G>
+__global__ __launch_bounds__(1024) void step_prep_kernel(
+    uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, const int* __restrict__ block_table,
+    int max_blocks, const int* __restrict__ start_pos, const void* __restrict__ k,
+    const void* __restrict__ v, const float* __restrict__ mu, const float* __restrict__ rot_k,
+    const float* __restrict__ rot_v, float clip_k, float clip_v, const void* __restrict__ q,
+    int Hq, int QG, float qscale, uint32_t* __restrict__ qa, float4* __restrict__ qf) {
+  if (static_cast<int>(blockIdx.x) < Hkv)
+    append_one_body<kKvBf16>(blockIdx.x, blockIdx.y, pages, num_blocks, Hkv, G, block_table,
+                             max_blocks, start_pos, k, v, mu, rot_k, rot_v, clip_k, clip_v);
+  else
+    prologue_body<kQBf16, G>(blockIdx.x - Hkv, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa,
+                             qf);
 }
 
 // --------------------------------------------------------------------------- scan
@@ -1124,6 +1182,39 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
     hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(256), 0, stream, part, ctx_len,
                        max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                         const int* block_table, int max_blocks, const int* start_pos,
+                         const void* k, const void* v, bool kv_bf16, const float* mu,
+                         float clip_k, float clip_v, const int* ctx_len, int max_ctx, int B,
+                         int Hq, const void* q, bool q_bf16, const float* rot_k,
+                         const float* rot_v, float sm_scale, float* out, void* workspace,
+                         const DecodePlan& p, hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
+  float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
+  const float qscale = sm_scale * kLog2e;
+  const dim3 grid(Hkv * (1 + p.QG), B);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(1024), 0, stream, pages, num_blocks, Hkv, block_table,
+                       max_blocks, start_pos, k, v, mu, rot_k, rot_v, clip_k, clip_v, q, Hq,
+                       p.QG, qscale, qa, qf);
+  };
+  if (G == 2) {
+    if (kv_bf16)
+      q_bf16 ? go(step_prep_kernel<true, true, 2>) : go(step_prep_kernel<true, false, 2>);
+    else
+      q_bf16 ? go(step_prep_kernel<false, true, 2>) : go(step_prep_kernel<false, false, 2>);
+  } else {
+    if (kv_bf16)
+      q_bf16 ? go(step_prep_kernel<true, true, 1>) : go(step_prep_kernel<true, false, 1>);
+    else
+      q_bf16 ? go(step_prep_kernel<false, true, 1>) : go(step_prep_kernel<false, false, 1>);
+  }
+  if (hipGetLastError() != hipSuccess) return -1;
+  return launch_decode(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len, max_ctx, B,
+                       Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace, p, 2 | 4, stream);
 }
 
 }  // namespace kvq

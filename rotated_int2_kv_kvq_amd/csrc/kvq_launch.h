@@ -28,4 +28,14 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                   float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
                   hipStream_t stream);
 
+// The single-token append of one decode step fused with the first decode
+// stage, then the scan and the merge.
+int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                         const int* block_table, int max_blocks, const int* start_pos,
+                         const void* k, const void* v, bool kv_bf16, const float* mu,
+                         float clip_k, float clip_v, const int* ctx_len, int max_ctx, int B,
+                         int Hq, const void* q, bool q_bf16, const float* rot_k,
+                         const float* rot_v, float sm_scale, float* out, void* workspace,
+                         const DecodePlan& p, hipStream_t stream);
+
 }  // namespace kvq

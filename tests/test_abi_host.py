@@ -27,8 +27,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
-        "kvq_append", "kvq_decode_attn", "kvq_decode_attn_staged", "kvq_decode_workspace_bytes",
-        "kvq_page_bytes", "kvq_status_string"])
+        "kvq_append", "kvq_append_decode", "kvq_decode_attn", "kvq_decode_attn_staged",
+        "kvq_decode_workspace_bytes", "kvq_page_bytes", "kvq_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,6 +54,8 @@ def test_workspace_bytes(lib):
     assert 0 < a < b
     assert kvq.decode_workspace_bytes(4, 30, 8, 8192) == 0          # Hq % Hkv
     assert kvq.decode_workspace_bytes(4, 32, 8, 8192, split_pages=12) == 0
+    assert kvq.decode_workspace_bytes(4, 32, 8, 8192, split_pages=512) > 0
+    assert kvq.decode_workspace_bytes(4, 32, 8, 8192, split_pages=520) == 0  # above 512
     assert kvq.decode_workspace_bytes(4, 32, 8, 8192, head_dim=64) == 0
     assert kvq.decode_workspace_bytes(4, 32, 8, 0) > 0
     # workspace grows with the number of splits
@@ -116,3 +118,34 @@ def test_decode_rejects_invalid_arguments(lib):
     bad = list(base)
     bad[10] = 30
     assert lib.kvq_decode_attn_staged(*bad, 7, None) == -1
+
+
+def _append_decode(lib, **kw):
+    args = dict(pages=1 << 20, nb=4, hkv=8, d=128, g=128, table=1 << 21, maxb=4, start=1 << 22,
+                ctx=1 << 22, maxctx=64, B=1, k=1 << 23, v=1 << 24, kdt=1, mu=1 << 25, ck=0.9,
+                cv=0.9, hq=32, q=1 << 26, qdt=1, rk=1 << 27, rv=1 << 28, scale=0.088, out=1 << 29,
+                ws=1 << 30, wsb=1 << 30, sp=0)
+    args.update(kw)
+    a = args
+    return lib.kvq_append_decode(a["pages"], a["nb"], a["hkv"], a["d"], a["g"], a["table"],
+                                 a["maxb"], a["start"], a["ctx"], a["maxctx"], a["B"], a["k"],
+                                 a["v"], a["kdt"], a["mu"], a["ck"], a["cv"], a["hq"], a["q"],
+                                 a["qdt"], a["rk"], a["rv"], a["scale"], a["out"], a["ws"],
+                                 a["wsb"], a["sp"], None)
+
+
+def test_append_decode_rejects_invalid_arguments(lib):
+    # the append's checks
+    assert _append_decode(lib, ck=0.0) == -1
+    assert _append_decode(lib, kdt=5) == -1
+    assert _append_decode(lib, k=None) == -1
+    assert _append_decode(lib, mu=(1 << 25) + 4) == -1         # misaligned
+    # the decode's checks
+    assert _append_decode(lib, hq=30) == -1
+    assert _append_decode(lib, maxctx=65) == -1
+    assert _append_decode(lib, qdt=3) == -1
+    assert _append_decode(lib, sp=520) == -1
+    assert _append_decode(lib, out=None) == -1
+    assert _append_decode(lib, d=64, g=64) == -2
+    assert _append_decode(lib, wsb=16) == -3
+    assert _append_decode(lib, B=0) == 0

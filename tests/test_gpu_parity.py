@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle as O
-from workload import WORKLOADS, scaled
+from workload import WORKLOADS, kv_for_sequence, scaled
 
 from cases import (append_range, decode, fill_context, host_pages, new_case, oracle_decode,
                    oracle_encode, query)
@@ -22,9 +22,11 @@ from parity import ATTN_TOL, EXEMPT_FRACTION, attention_error, check_codes, chec
 
 pytestmark = pytest.mark.gpu
 
-# Derived bound: q is split into fp16 hi + lo parts (2^-22 relative), products
-# with exact 2-bit codes accumulate in fp32, and p = exp2 is fp32; the worst
-# logit error is ~1e-5 absolute for logits O(100), so outputs agree to ~1e-5.
+# Derived bound: q_r enters the q.K products as 32-bit fixed point (digit
+# products with exact 2-bit codes sum exactly in the MFMA), so a logit carries
+# ~2^-24 relative error from the fp32 scale/zero terms; the softmax weights
+# p * s_V enter P.V as 24-bit fixed point under a per-block power of two,
+# rounded to nearest.  With logits O(100) this gives ~1e-5 on the outputs.
 TIGHT = 5e-5
 
 
@@ -240,6 +242,52 @@ def test_stream_append_then_decode():
         assert err <= TIGHT
     near, n, _ = _append_parity(case, 1, int(case.ctx[1]), w.steps)
     assert near <= max(EXEMPT_FRACTION * n, 1)
+
+
+STEP_CASES = {
+    "cfg4_b3_layer5": SMALL["cfg4_b3_layer5"],
+    "cfg2_b5_ragged_g64": scaled(W2, batch=5, ctx_min=1, ctx_max=300, steps=3),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_append_decode_step(name):
+    """kvq_append_decode equals kvq_append + kvq_decode_attn bit for bit (cache
+    and output) and matches the oracle on the cache it wrote."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = STEP_CASES[name]
+    say(f"[step] {name}")
+    layer = min(1, w.layers - 1)
+    a = new_case(w, layer=layer, keep_initial=False)
+    b = new_case(w, layer=layer, keep_initial=False)
+    fill_context(a)
+    fill_context(b)
+    ctx = a.ctx.copy()
+    dev = a.device
+    for step in range(w.steps):
+        kv = [kv_for_sequence(w, a.st, a.layer, s, int(ctx[s]), 1, dev) for s in range(w.batch)]
+        k = torch.stack([x[0] for x in kv]).contiguous()
+        v = torch.stack([x[1] for x in kv]).contiguous()
+        sp = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        kvq.append(a.pages, a.table, sp, k, v, a.mu, a.rot_k, a.rot_v, w.group, w.clip_k,
+                   w.clip_v)
+        ctx = ctx + 1
+        q = query(a, step)
+        out_a = decode(a, q, ctx=ctx)
+        ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        out_b = kvq.append_decode(b.pages, b.table, sp, ctx_t, int(ctx.max()), k, v, b.mu, q,
+                                  b.rot_k, b.rot_v, w.group, w.clip_k, w.clip_v, b.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(a.pages, b.pages), step
+        assert torch.equal(out_a, out_b), step
+    for s in range(w.batch):
+        b.written[s] = int(ctx[s])
+    pairs = [(s, hq) for s in range(w.batch) for hq in (0, 9, 31)]
+    ref = oracle_decode(b, q, pairs, ctx=ctx)
+    out = out_b.cpu().numpy()
+    err = max(attention_error(out[s, hq], ref[(s, hq)]) for (s, hq) in pairs)
+    say(f"  last step max rel err {err:.3e}")
+    assert err <= TIGHT
 
 
 FULL = {
