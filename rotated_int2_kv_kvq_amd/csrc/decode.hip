@@ -1010,10 +1010,27 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   float4 rr[16];
 #pragma unroll
   for (int i4 = 0; i4 < 16; ++i4) rr[i4] = R[i4];
-  const int ctx = min(max(ctx_len[b], 0), max_ctx);
-  const int ns = num_splits((ctx + kBlock - 1) / kBlock, spw);
+  const int ctx_in = ctx_len[b];
   const int u = threadIdx.x >> 6;
   const int c = threadIdx.x & 63;
+  const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) * S *
+                              kPartStride;
+  // Loaded before the context length (and so the split count) is known:
+  // split c's lse and the first eight splits' outputs, indices clamped to the
+  // S allocated splits; entries of splits past the count are never used.
+  const float lse_c = p[min(c, S - 1) * kPartStride];
+  float x0[8], x1[8];
+  auto load8 = [&](int s0, int lim) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = min(s0 + k, lim - 1);
+      x0[k] = p[s * kPartStride + 4 + c];
+      x1[k] = p[s * kPartStride + 4 + c + 64];
+    }
+  };
+  load8(0, S);
+  const int ctx = min(max(ctx_in, 0), max_ctx);
+  const int ns = num_splits((ctx + kBlock - 1) / kBlock, spw);
   if (ns == 0) {  // empty context: zero output
     if (u < nh) {
       float* o = out + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * kHeadDim;
@@ -1026,15 +1043,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   // pass 1, wave u: the splits' weights exp2(lse_s - M) / sum into LDS
   // (splits beyond kMergeLds are folded in pass 2 with an online rescale)
   const int nsl = min(ns, kMergeLds);
-  const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) * S *
-                              kPartStride;
-  float M = -INFINITY;
-  for (int s = c; s < nsl; s += 64) M = fmaxf(M, p[s * kPartStride]);
+  float M = c < nsl ? lse_c : -INFINITY;
+  for (int s = c + 64; s < nsl; s += 64) M = fmaxf(M, p[s * kPartStride]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor(M, m));
   float W = 0.f;
   for (int s = c; s < nsl; s += 64) {
-    const float a = exp2_hw(p[s * kPartStride] - M);
+    const float a = exp2_hw((s == c ? lse_c : p[s * kPartStride]) - M);
     wts[u][s] = a;
     W += a;
   }
@@ -1043,18 +1058,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   __syncthreads();
   if (u < nh) {
     // pass 2: eight splits at a time, the next eight's loads issued before
-    // this eight's are used (software pipelined)
+    // this eight's are used (software pipelined); a split past the count
+    // contributes nothing (its stale values are never multiplied)
     float a0 = 0.f, a1 = 0.f;
-    float x0[8], x1[8];
-    auto load8 = [&](int s0) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s = min(s0 + k, nsl - 1);
-        x0[k] = p[s * kPartStride + 4 + c];
-        x1[k] = p[s * kPartStride + 4 + c + 64];
-      }
-    };
-    load8(0);
     for (int s0 = 0; s0 < nsl; s0 += 8) {
       float y0[8], y1[8];
 #pragma unroll
@@ -1062,12 +1068,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
         y0[k] = x0[k];
         y1[k] = x1[k];
       }
-      if (s0 + 8 < nsl) load8(s0 + 8);
+      if (s0 + 8 < nsl) load8(s0 + 8, nsl);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a = (s0 + k < nsl) ? wts[u][min(s0 + k, nsl - 1)] : 0.f;
-        a0 = fmaf(a, y0[k], a0);
-        a1 = fmaf(a, y1[k], a1);
+        if (s0 + k < nsl) {
+          const float a = wts[u][s0 + k];
+          a0 = fmaf(a, y0[k], a0);
+          a1 = fmaf(a, y1[k], a1);
+        }
       }
     }
     // splits past the LDS table (very long contexts): online rescale
