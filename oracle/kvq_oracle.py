@@ -55,7 +55,8 @@ __all__ = [
     "HEAD_DIM", "BLOCK", "F16_MAX", "fp16_sat", "page_bytes", "bits_per_element",
     "rotate", "encode_groups", "quantize_on_grid", "encode_tokens", "k_code_site", "v_code_site",
     "sz_site", "write_tokens", "read_tokens", "dequant", "attend", "decode",
-    "append", "plain_attention",
+    "append", "plain_attention", "SINK", "RECENT", "WINDOW", "window_slot", "window_parts",
+    "bf16_round", "window_write", "append_windowed", "decode_windowed",
 ]
 
 
@@ -299,4 +300,119 @@ def decode(cache, block_table, ctx_len, q, rot_k, rot_v, sm_scale: float, num_kv
                 q_r = q[b, hq] @ Rk
                 o_r = attend(q_r, k_hat, v_hat, sm_scale)
                 out[b, hq] = o_r @ Rv.T
+    return out
+
+
+# --------------------------------------------------------------------------- BF16 windows
+# [OptR] "Assumptions & free parameters": the deployed cache keeps 64 sink
+# tokens and the 256 most recent tokens in BF16 beside the INT2 body.  The
+# pages give only the two sizes; the readings taken here:
+#   - a context of n tokens splits into sinks [0, min(64, n)), the recent
+#     window [max(64, n - 256), n) and the INT2 body [64, n - 256) between;
+#   - window tokens are kept as given (uncentred, unrotated), rounded to BF16;
+#     their logits subtract the key mean too, q . (k - mu), so that every
+#     logit of the context carries the same -q . mu shift as the centred body
+#     keys (softmax-invariant, "What carries the argument", mechanism 2);
+#   - a token leaving the recent window is encoded into the INT2 body from its
+#     BF16 window copy;
+#   - window store: slot of position p is p for p < 64, else
+#     64 + (p - 64) mod 256 (a ring).
+SINK = 64
+RECENT = 256
+WINDOW = SINK + RECENT
+
+
+def window_slot(pos):
+    """Window-store slot of a token position (sinks first, then the ring)."""
+    pos = np.asarray(pos)
+    return np.where(pos < SINK, pos, SINK + (pos - SINK) % RECENT)
+
+
+def window_parts(n: int):
+    """(sink, body, recent) position ranges of a context of n tokens."""
+    n = int(n)
+    sink = range(0, min(SINK, n))
+    recent = range(max(SINK, n - RECENT), n)
+    body = range(SINK, max(SINK, n - RECENT))
+    return sink, body, recent
+
+
+def bf16_round(x):
+    """Nearest bfloat16 value (round half to even) as float64."""
+    f = np.asarray(x, np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return (r.astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def window_write(win_k, win_v, start_pos, k, v):
+    """Store tokens k, v [B][T][Hkv][d] at positions start_pos[b] + tau into the
+    window store win_k, win_v [B][Hkv][WINDOW][d] (float64 holding BF16
+    values), later positions winning a shared ring slot."""
+    k = np.asarray(k, np.float64)
+    B, T = k.shape[:2]
+    for b in range(B):
+        for tau in range(T):
+            slot = int(window_slot(int(start_pos[b]) + tau))
+            win_k[b, :, slot] = bf16_round(k[b, tau])
+            win_v[b, :, slot] = bf16_round(np.asarray(v, np.float64)[b, tau])
+
+
+def append_windowed(cache, block_table, win_k, win_v, start_pos, k, v, mu, rot_k, rot_v,
+                    group, clip_k, clip_v):
+    """One token per sequence (k, v [B][1][Hkv][d]) at position p = start_pos[b]:
+    when p >= WINDOW the token it displaces from the ring, position p - RECENT,
+    is encoded into the INT2 body from its window copy; then the new token
+    takes the slot."""
+    B = np.asarray(k).shape[0]
+    for b in range(B):
+        p = int(start_pos[b])
+        slot = int(window_slot(p))
+        if p >= WINDOW:
+            old_k = win_k[b:b + 1, :, slot][:, None]
+            old_v = win_v[b:b + 1, :, slot][:, None]
+            append(cache, block_table[b:b + 1], [p - RECENT], old_k, old_v, mu, rot_k, rot_v,
+                   group, clip_k, clip_v)
+        window_write(win_k[b:b + 1], win_v[b:b + 1], [p], np.asarray(k)[b:b + 1],
+                     np.asarray(v)[b:b + 1])
+
+
+def decode_windowed(cache, block_table, ctx_len, q, rot_k, rot_v, mu, win_k, win_v,
+                    sm_scale: float, num_kv_heads: int, group: int, pairs=None):
+    """Decode attention over sinks + INT2 body + recent window: one softmax over
+    the whole context.  Body tokens as in decode(); window token t scores
+    sm_scale * q . (k_t - mu_h) and contributes its value as stored.
+    Returns o [B][Hq][d] float64 (NaN for pairs not requested)."""
+    q = np.asarray(q, np.float64)
+    mu = np.asarray(mu, np.float64)
+    B, Hq, d = q.shape
+    Hg = Hq // num_kv_heads
+    out = np.full((B, Hq, d), np.nan)
+    want = set(pairs) if pairs is not None else None
+    for b in range(B):
+        sink, body, recent = window_parts(int(ctx_len[b]))
+        wpos = np.array(list(sink) + list(recent), dtype=np.int64)
+        bpos = np.array(list(body), dtype=np.int64)
+        for h in range(num_kv_heads):
+            heads = [hq for hq in range(h * Hg, (h + 1) * Hg) if want is None or (b, hq) in want]
+            if not heads:
+                continue
+            slots = window_slot(wpos)
+            kw = np.asarray(win_k[b, h], np.float64)[slots] - mu[h]
+            vw = np.asarray(win_v[b, h], np.float64)[slots]
+            tok = read_tokens(cache, block_table, b, bpos, h, num_kv_heads, group)
+            k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
+            v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
+            Rk = np.asarray(rot_k[h], np.float64)
+            Rv = np.asarray(rot_v[h], np.float64)
+            for hq in heads:
+                if len(wpos) + len(bpos) == 0:
+                    out[b, hq] = 0.0
+                    continue
+                logits = np.float64(sm_scale) * np.concatenate(
+                    [kw @ q[b, hq], k_hat @ (q[b, hq] @ Rk)])
+                p = np.exp(logits - logits.max())
+                p /= p.sum()
+                nw = len(wpos)
+                out[b, hq] = p[:nw] @ vw + (p[nw:] @ v_hat) @ Rv.T
     return out

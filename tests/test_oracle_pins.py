@@ -360,3 +360,128 @@ def test_decode_scores_with_rotated_query_and_maps_gqa_heads():
     # empty context -> zeros
     o0 = O.decode(cache, table, [0], q, Rk, Rv, scale, Hkv, group)
     assert np.array_equal(o0, np.zeros_like(o0))
+
+
+# ----------------------------------------------------------------- BF16 windows
+# [OptR] "Assumptions & free parameters": 64 sink and 256 recent tokens kept in
+# BF16 beside the INT2 body.  The slot mapping, the part boundaries and the
+# key-mean convention for window keys are readings stated in the oracle.
+def test_window_slots_and_parts_hand_examples():
+    assert O.SINK == 64 and O.RECENT == 256 and O.WINDOW == 320
+    pos = [0, 1, 63, 64, 65, 319, 320, 321, 575, 576, 1000]
+    slot = [0, 1, 63, 64, 65, 319, 64, 65, 319, 64, 64 + (1000 - 64) % 256]
+    assert list(O.window_slot(pos)) == slot
+    for n, parts in [(0, (0, 0, 0)), (10, (10, 0, 0)), (64, (64, 0, 0)), (65, (64, 0, 1)),
+                     (320, (64, 0, 256)), (321, (64, 1, 256)), (400, (64, 80, 256))]:
+        s, b, r = O.window_parts(n)
+        assert (len(s), len(b), len(r)) == parts, n
+        assert sorted(list(s) + list(b) + list(r)) == list(range(n))
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(4096) * 10.0 ** rng.integers(-8, 8, 4096),
+                        [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 65504.0, 3.0e38]])
+    ref = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_round(x), ref)
+    assert O.bf16_round(1 + 2 ** -8) == 1.0 and O.bf16_round(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+
+
+def _windowed_layer(rng, n_blocks=40, Hkv=1, group=128):
+    cache = np.zeros((n_blocks, Hkv, O.page_bytes(128, group)), np.uint8)
+    table = rng.permutation(n_blocks).astype(np.int32)[None]
+    return cache, table
+
+
+def test_windowed_single_token_returns_its_value():
+    rng = np.random.default_rng(22)
+    cache, table = _windowed_layer(rng)
+    win_k = np.zeros((1, 1, O.WINDOW, 128))
+    win_v = np.zeros_like(win_k)
+    k = rng.standard_normal((1, 1, 1, 128))
+    v = rng.standard_normal((1, 1, 1, 128))
+    O.window_write(win_k, win_v, [0], k, v)
+    q = rng.standard_normal((1, 2, 128))
+    R = np.eye(128)[None]
+    o = O.decode_windowed(cache, table, [1], q, R, R, rng.standard_normal((1, 128)), win_k, win_v,
+                          0.1, 1, 128)
+    assert np.array_equal(o[0, 0], O.bf16_round(v[0, 0, 0]))
+    assert np.array_equal(o[0, 1], O.bf16_round(v[0, 0, 0]))
+
+
+def test_windowed_equal_keys_give_the_mean_of_all_values():
+    """Every key equals the key mean: window logits q . (k - mu) are 0, and the
+    body keys encode to zero codes with scale 0 and zero 0, so every logit is 0
+    and the output is the plain mean of the window values (as stored) and the
+    dequantised, inverse-rotated body values."""
+    rng = np.random.default_rng(23)
+    n, group = 400, 128
+    Rk = _signed_perm(rng, 128)[0][None]
+    Rv = np.linalg.qr(rng.standard_normal((128, 128)))[0][None]
+    mu = rng.integers(-40, 40, size=(1, 128)) / 8.0
+    cache, table = _windowed_layer(rng)
+    win_k = np.zeros((1, 1, O.WINDOW, 128))
+    win_v = np.zeros_like(win_k)
+    vals = rng.standard_normal((n, 128))
+    for p in range(n):
+        O.append_windowed(cache, table, win_k, win_v, [p], mu[None, None], vals[p][None, None, None],
+                          mu, Rk, Rv, group, 0.9, 0.9)
+    q = rng.standard_normal((1, 2, 128))
+    o = O.decode_windowed(cache, table, [n], q, Rk, Rv, mu, win_k, win_v, 0.2, 1, group)
+    body = np.arange(O.SINK, n - O.RECENT)
+    tok = O.read_tokens(cache, table, 0, body, 0, 1, group)
+    assert not tok["k_codes"].any() and not tok["k_s"].any() and not tok["k_z"].any()
+    v_body = O.dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group) @ Rv[0].T
+    win = np.concatenate([np.arange(O.SINK), np.arange(n - O.RECENT, n)])
+    expect = np.concatenate([O.bf16_round(vals[win]), v_body]).mean(0)
+    assert np.allclose(o[0, 0], expect, rtol=1e-12, atol=1e-12)
+    assert np.allclose(o[0, 1], expect, rtol=1e-12, atol=1e-12)
+
+
+def test_windowed_key_mean_shift_is_softmax_invariant_without_a_body():
+    rng = np.random.default_rng(24)
+    n = 300
+    cache, table = _windowed_layer(rng)
+    win_k = np.zeros((1, 1, O.WINDOW, 128))
+    win_v = np.zeros_like(win_k)
+    O.window_write(win_k, win_v, [0], rng.standard_normal((1, n, 1, 128)),
+                   rng.standard_normal((1, n, 1, 128)))
+    q = rng.standard_normal((1, 1, 128))
+    R = np.eye(128)[None]
+    mu = rng.standard_normal((1, 128))
+    o1 = O.decode_windowed(cache, table, [n], q, R, R, mu, win_k, win_v, 0.3, 1, 128)
+    o2 = O.decode_windowed(cache, table, [n], q, R, R, mu + 5.0, win_k, win_v, 0.3, 1, 128)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12)
+
+
+def test_windowed_stream_keeps_windows_and_encodes_evicted_tokens_like_bulk():
+    """Tokens appended one at a time: the window store holds the BF16 sinks and
+    the last 256 tokens in their ring slots, and the body holds exactly what a
+    bulk append of the BF16-rounded body tokens writes."""
+    rng = np.random.default_rng(25)
+    n, group, Hkv = 420, 64, 2
+    Rk = np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(Hkv)])
+    Rv = np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(Hkv)])
+    mu = rng.standard_normal((Hkv, 128))
+    k = rng.standard_normal((n, Hkv, 128)) * 3
+    v = rng.standard_normal((n, Hkv, 128))
+    cache, table = _windowed_layer(rng, Hkv=Hkv, group=group)
+    win_k = np.zeros((1, Hkv, O.WINDOW, 128))
+    win_v = np.zeros_like(win_k)
+    for p in range(n):
+        O.append_windowed(cache, table, win_k, win_v, [p], k[p][None, None], v[p][None, None], mu,
+                          Rk, Rv, group, 0.9, 0.8)
+    for p in list(range(O.SINK)) + list(range(n - O.RECENT, n)):
+        s = int(O.window_slot(p))
+        assert np.array_equal(win_k[0, :, s], O.bf16_round(k[p]))
+        assert np.array_equal(win_v[0, :, s], O.bf16_round(v[p]))
+    body = np.arange(O.SINK, n - O.RECENT)
+    bulk, _ = _windowed_layer(np.random.default_rng(0), Hkv=Hkv, group=group)
+    O.append(bulk, table, [O.SINK], O.bf16_round(k[body])[None], O.bf16_round(v[body])[None], mu,
+             Rk, Rv, group, 0.9, 0.8)
+    for h in range(Hkv):
+        a = O.read_tokens(cache, table, 0, body, h, Hkv, group)
+        b = O.read_tokens(bulk, table, 0, body, h, Hkv, group)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), key
