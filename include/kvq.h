@@ -208,6 +208,70 @@ int kvq_append_decode(void *pages, int64_t num_blocks, int32_t num_kv_heads, int
                       float sm_scale, float *out, void *workspace, size_t workspace_bytes,
                       int32_t split_pages, void *stream);
 
+/*
+ * BF16 windows -- the deployed cache of the OptR review page ("Assumptions &
+ * free parameters": 64 sink tokens and the 256 most recent tokens kept in
+ * BF16 beside the INT2 body).  With windows, a context of n tokens is
+ *     sinks  [0, min(64, n))            bfloat16, window store
+ *     body   [64, n - 256)  (n > 320)   INT2 pages, as kvq_append writes them
+ *     recent [max(64, n - 256), n)      bfloat16, window store
+ * and attention is one softmax over all n tokens: window keys score
+ * sm_scale * q . (k - mu[h]) (the unrotated query; the same key-mean shift as
+ * the centred body keys), window values enter as stored, and the body is
+ * attended as in kvq_decode_attn.
+ *
+ * Window store of one layer: bfloat16 [batch][num_kv_heads][2: K, V][320]
+ * [head_dim], caller-owned device memory of kvq_window_bytes() bytes; position
+ * p lives in slot p for p < 64, else in ring slot 64 + (p - 64) mod 256.
+ * Tokens are stored as given (k not centred, neither rotated), rounded to
+ * bfloat16 (round to nearest even).
+ */
+size_t kvq_window_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * kvq_window_write -- store tokens start_pos[b] .. start_pos[b] + num_new - 1
+ * (k, v [batch][num_new][num_kv_heads][head_dim] of kv_dtype) in their window
+ * slots; within one call a ring slot keeps the latest of its tokens.  Used to
+ * fill the windows of a prompt (whose body goes through kvq_append).
+ * batch == 0 or num_new == 0 is a no-op.
+ */
+int kvq_window_write(void *window, int32_t num_kv_heads, int32_t head_dim, int32_t batch,
+                     const int32_t *start_pos, int32_t num_new, const void *k, const void *v,
+                     int32_t kv_dtype, void *stream);
+
+/*
+ * kvq_decode_attn_window -- kvq_decode_attn over sinks + INT2 body + recent
+ * window (see above).  window and mu (float32 [num_kv_heads][head_dim], the
+ * key mean the body was encoded with) are device pointers; the other
+ * arguments, the workspace size and the errors are those of kvq_decode_attn.
+ */
+int kvq_decode_attn_window(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t group, const int32_t *block_table,
+                           int32_t max_blocks_per_seq, const void *window, const float *mu,
+                           const int32_t *ctx_len, int32_t max_ctx_len, int32_t batch,
+                           int32_t num_q_heads, const void *q, int32_t q_dtype,
+                           const float *rot_k, const float *rot_v, float sm_scale, float *out,
+                           void *workspace, size_t workspace_bytes, int32_t split_pages,
+                           void *stream);
+
+/*
+ * kvq_append_decode_window -- one decode step with windows: the new token of
+ * sequence b (position p = start_pos[b], with ctx_len[b] = p + 1) enters the
+ * recent window; when p >= 320 the token it displaces, position p - 256, is
+ * first encoded from its window copy into the INT2 body (as kvq_append would
+ * encode it).  Then kvq_decode_attn_window over ctx_len[b] tokens.  Arguments
+ * as kvq_append_decode plus the window store (read and written).
+ */
+int kvq_append_decode_window(void *pages, int64_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t group, const int32_t *block_table,
+                             int32_t max_blocks_per_seq, void *window, const int32_t *start_pos,
+                             const int32_t *ctx_len, int32_t max_ctx_len, int32_t batch,
+                             const void *k, const void *v, int32_t kv_dtype, const float *mu,
+                             float clip_k, float clip_v, int32_t num_q_heads, const void *q,
+                             int32_t q_dtype, const float *rot_k, const float *rot_v,
+                             float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                             int32_t split_pages, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,9 +12,16 @@ from ._lib import (  # noqa: F401
     KvqError,
     append,
     append_decode,
+    append_decode_window,
     decode,
+    decode_window,
     decode_workspace_bytes,
     lib,
     page_bytes,
     status_string,
+    new_window,
+    window_bytes,
+    window_write,
+    WINDOW_SINK,
+    WINDOW_RECENT,
 )

@@ -39,8 +39,18 @@ SIGNATURES = {
     "kvq_append_decode": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32,
                            c_i32, c_vp, c_vp, c_i32, c_vp, c_f32, c_f32, c_i32, c_vp, c_i32,
                            c_vp, c_vp, c_f32, c_vp, c_vp, c_sz, c_i32, c_vp], c_i32),
+    "kvq_window_bytes": ([c_i32, c_i32, c_i32], c_sz),
+    "kvq_window_write": ([c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp], c_i32),
+    "kvq_decode_attn_window": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp,
+                                c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp,
+                                c_sz, c_i32, c_vp], c_i32),
+    "kvq_append_decode_window": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp,
+                                  c_vp, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_f32, c_f32,
+                                  c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_sz, c_i32,
+                                  c_vp], c_i32),
 }
 STAGE_PREPARE, STAGE_SPLITS, STAGE_MERGE, STAGE_ALL = 1, 2, 4, 7
+WINDOW_SINK, WINDOW_RECENT = 64, 256
 
 
 class KvqError(RuntimeError):
@@ -171,4 +181,81 @@ def append_decode(pages: torch.Tensor, block_table: torch.Tensor, start_pos: tor
         _ptr(mu), clip_k, clip_v, Hq, _ptr(q), _DTYPES[q.dtype], _ptr(rot_k), _ptr(rot_v),
         sm_scale, _ptr(out), _ptr(workspace), workspace.numel(), split_pages, _stream(stream)),
         "kvq_append_decode")
+    return out
+
+
+# ----------------------------------------------------------------- BF16 windows
+def window_bytes(batch: int, num_kv_heads: int, head_dim: int = 128) -> int:
+    return int(lib().kvq_window_bytes(batch, num_kv_heads, head_dim))
+
+
+def new_window(batch: int, num_kv_heads: int, device="cuda") -> torch.Tensor:
+    """A window store: bfloat16 [B][Hkv][2][320][128] (contents unspecified)."""
+    return torch.empty(batch, num_kv_heads, 2, WINDOW_SINK + WINDOW_RECENT, 128,
+                       dtype=torch.bfloat16, device=device)
+
+
+def window_write(window: torch.Tensor, start_pos: torch.Tensor, k: torch.Tensor,
+                 v: torch.Tensor, stream=None) -> None:
+    """kvq_window_write: k, v [B][T][Hkv][128] at positions start_pos[b] + tau."""
+    B, T, hkv, d = k.shape
+    if k.dtype not in _DTYPES or v.dtype != k.dtype:
+        raise ValueError("k and v must both be float32 or bfloat16")
+    _check(lib().kvq_window_write(_ptr(window), hkv, d, B, _ptr(start_pos), T, _ptr(k), _ptr(v),
+                                  _DTYPES[k.dtype], _stream(stream)), "kvq_window_write")
+
+
+def decode_window(pages: torch.Tensor, block_table: torch.Tensor, window: torch.Tensor,
+                  mu: torch.Tensor, ctx_len: torch.Tensor, max_ctx_len: int, q: torch.Tensor,
+                  rot_k: torch.Tensor, rot_v: torch.Tensor, group: int,
+                  sm_scale: float | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, split_pages: int = 0,
+                  stream=None) -> torch.Tensor:
+    """kvq_decode_attn_window: attention over BF16 sinks + INT2 body + BF16 recent."""
+    num_blocks, hkv, _ = pages.shape
+    B, Hq, d = q.shape
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, hkv, max_ctx_len, d, split_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().kvq_decode_attn_window(
+        _ptr(pages), num_blocks, hkv, d, group, _ptr(block_table), block_table.shape[1],
+        _ptr(window), _ptr(mu), _ptr(ctx_len), max_ctx_len, B, Hq, _ptr(q), _DTYPES[q.dtype],
+        _ptr(rot_k), _ptr(rot_v), sm_scale, _ptr(out), _ptr(workspace), workspace.numel(),
+        split_pages, _stream(stream)), "kvq_decode_attn_window")
+    return out
+
+
+def append_decode_window(pages: torch.Tensor, block_table: torch.Tensor, window: torch.Tensor,
+                         start_pos: torch.Tensor, ctx_len: torch.Tensor, max_ctx_len: int,
+                         k: torch.Tensor, v: torch.Tensor, mu: torch.Tensor, q: torch.Tensor,
+                         rot_k: torch.Tensor, rot_v: torch.Tensor, group: int, clip_k: float,
+                         clip_v: float, sm_scale: float | None = None,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         split_pages: int = 0, stream=None) -> torch.Tensor:
+    """kvq_append_decode_window: one decode step with BF16 windows."""
+    num_blocks, hkv, _ = pages.shape
+    B, Hq, d = q.shape
+    if k.dtype not in _DTYPES or v.dtype != k.dtype or q.dtype not in _DTYPES:
+        raise ValueError("k, v and q must be float32 or bfloat16")
+    if k.shape[1] != 1:
+        raise ValueError("append_decode_window appends exactly one token per sequence")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, hkv, max_ctx_len, d, split_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().kvq_append_decode_window(
+        _ptr(pages), num_blocks, hkv, d, group, _ptr(block_table), block_table.shape[1],
+        _ptr(window), _ptr(start_pos), _ptr(ctx_len), max_ctx_len, B, _ptr(k), _ptr(v),
+        _DTYPES[k.dtype], _ptr(mu), clip_k, clip_v, Hq, _ptr(q), _DTYPES[q.dtype], _ptr(rot_k),
+        _ptr(rot_v), sm_scale, _ptr(out), _ptr(workspace), workspace.numel(), split_pages,
+        _stream(stream)), "kvq_append_decode_window")
     return out

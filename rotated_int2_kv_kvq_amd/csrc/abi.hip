@@ -185,3 +185,77 @@ KVQ_API int kvq_append_decode(void* pages, int64_t num_blocks, int32_t num_kv_he
       workspace, plan, static_cast<hipStream_t>(stream));
   return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
 }
+
+// ----------------------------------------------------------------- BF16 windows
+KVQ_API size_t kvq_window_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim) {
+  if (head_dim != kvq::kHeadDim || batch < 0 || num_kv_heads < 1) return 0;
+  return static_cast<size_t>(batch) * num_kv_heads * 2 * kvq::kWindow * kvq::kHeadDim * 2;
+}
+
+KVQ_API int kvq_window_write(void* window, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t batch, const int32_t* start_pos, int32_t num_new,
+                             const void* k, const void* v, int32_t kv_dtype, void* stream) {
+  if (head_dim != kvq::kHeadDim) return head_dim > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
+  if (batch < 0 || batch > 65535 || num_new < 0 || num_kv_heads < 1 || num_kv_heads > 65535)
+    return KVQ_ERR_INVALID_ARG;
+  if (kv_dtype != KVQ_F32 && kv_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if (batch == 0 || num_new == 0) return KVQ_OK;
+  if (!window || !start_pos || !k || !v) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(window, 16) || !aligned(k, 16) || !aligned(v, 16)) return KVQ_ERR_INVALID_ARG;
+  const int rc = kvq::launch_window_write(static_cast<uint16_t*>(window), num_kv_heads, batch,
+                                          start_pos, num_new, k, v, kv_dtype == KVQ_BF16,
+                                          static_cast<hipStream_t>(stream));
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+KVQ_API int kvq_decode_attn_window(const void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t group, const int32_t* block_table,
+                                   int32_t max_blocks_per_seq, const void* window,
+                                   const float* mu, const int32_t* ctx_len, int32_t max_ctx_len,
+                                   int32_t batch, int32_t num_q_heads, const void* q,
+                                   int32_t q_dtype, const float* rot_k, const float* rot_v,
+                                   float sm_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, int32_t split_pages, void* stream) {
+  kvq::DecodePlan plan{};
+  const int st = check_decode(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                              max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q,
+                              q_dtype, rot_k, rot_v, sm_scale, out, workspace, workspace_bytes,
+                              split_pages, &plan);
+  if (st != KVQ_OK || batch == 0) return st;
+  if (!window || !mu || !aligned(window, 16) || !aligned(mu, 16)) return KVQ_ERR_INVALID_ARG;
+  const int rc = kvq::launch_decode(
+      static_cast<const uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
+      max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k,
+      rot_v, sm_scale, out, workspace, plan, KVQ_STAGE_ALL, static_cast<hipStream_t>(stream),
+      static_cast<const uint16_t*>(window), mu);
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+KVQ_API int kvq_append_decode_window(void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t group, const int32_t* block_table,
+                                     int32_t max_blocks_per_seq, void* window,
+                                     const int32_t* start_pos, const int32_t* ctx_len,
+                                     int32_t max_ctx_len, int32_t batch, const void* k,
+                                     const void* v, int32_t kv_dtype, const float* mu,
+                                     float clip_k, float clip_v, int32_t num_q_heads,
+                                     const void* q, int32_t q_dtype, const float* rot_k,
+                                     const float* rot_v, float sm_scale, float* out,
+                                     void* workspace, size_t workspace_bytes, int32_t split_pages,
+                                     void* stream) {
+  int st = check_append(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                        max_blocks_per_seq, start_pos, batch, 1, k, v, kv_dtype, mu, rot_k, rot_v,
+                        clip_k, clip_v);
+  if (st != KVQ_OK) return st;
+  kvq::DecodePlan plan{};
+  st = check_decode(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                    max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype,
+                    rot_k, rot_v, sm_scale, out, workspace, workspace_bytes, split_pages, &plan);
+  if (st != KVQ_OK || batch == 0) return st;
+  if (!window || !aligned(window, 16)) return KVQ_ERR_INVALID_ARG;
+  const int rc = kvq::launch_append_decode(
+      static_cast<uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
+      max_blocks_per_seq, start_pos, k, v, kv_dtype == KVQ_BF16, mu, clip_k, clip_v, ctx_len,
+      max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k, rot_v, sm_scale, out,
+      workspace, plan, static_cast<hipStream_t>(stream), static_cast<uint16_t*>(window));
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}

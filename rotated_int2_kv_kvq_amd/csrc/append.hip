@@ -243,8 +243,48 @@ __global__ __launch_bounds__(1024) void append_one_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ mu,
     const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
     float clip_v) {
-  append_one_body<kBf16>(blockIdx.x, blockIdx.y, pages, num_blocks, Hkv, G, block_table,
-                         max_blocks, start_pos, k, v, mu, rot_k, rot_v, clip_k, clip_v);
+  const int h = blockIdx.x, b = blockIdx.y;
+  append_one_body<kBf16>(h, b, pages, num_blocks, Hkv, G, block_table, max_blocks, start_pos, 0,
+                         token_row<kBf16>(k, b, h, Hkv), token_row<kBf16>(v, b, h, Hkv), mu,
+                         rot_k, rot_v, clip_k, clip_v);
+}
+
+// ---------------------------------------------------------------------------
+// BF16 window store writes ([OptR] "Assumptions & free parameters": sink and
+// recent tokens kept in BF16).  grid (T, Hkv, B), 256 threads: thread
+// m*128 + c copies element c of the key (m = 0) or value (m = 1) row of token
+// tau, rounded to bfloat16, into the slot of its position.  A ring slot that a
+// later token of the same call also takes keeps the later one (the earlier
+// write is skipped, so the result does not depend on write order).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void window_write_kernel(uint16_t* __restrict__ win, int Hkv,
+                                                           const int* __restrict__ start_pos,
+                                                           int T, const void* __restrict__ k,
+                                                           const void* __restrict__ v) {
+  const int tau = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int p0 = start_pos[b];
+  const int p = p0 + tau;
+  if (p0 < 0) return;
+  if (p >= kSink && p + kRecent < p0 + T) return;
+  const int m = threadIdx.x >> 7, c = threadIdx.x & 127;
+  const size_t off = ((static_cast<size_t>(b) * T + tau) * Hkv + h) * kHeadDim + c;
+  const void* src = m ? v : k;
+  const uint16_t x = kBf16 ? static_cast<const uint16_t*>(src)[off]
+                           : f32_to_bf16(static_cast<const float*>(src)[off]);
+  win[((static_cast<size_t>(b) * Hkv + h) * 2 + m) * kWindow * kHeadDim +
+      static_cast<size_t>(window_slot(p)) * kHeadDim + c] = x;
+}
+
+int launch_window_write(uint16_t* win, int Hkv, int B, const int* start_pos, int T, const void* k,
+                        const void* v, bool bf16, hipStream_t stream) {
+  const dim3 grid(T, Hkv, B);
+  if (bf16)
+    hipLaunchKernelGGL(window_write_kernel<true>, grid, dim3(256), 0, stream, win, Hkv, start_pos,
+                       T, k, v);
+  else
+    hipLaunchKernelGGL(window_write_kernel<false>, grid, dim3(256), 0, stream, win, Hkv,
+                       start_pos, T, k, v);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_append(uint8_t* pages, int64_t num_blocks, int Hkv, int G, const int* block_table,

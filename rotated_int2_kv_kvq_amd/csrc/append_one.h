@@ -24,14 +24,16 @@ namespace kvq {
 //
 // The body is a device function of (KV head h, sequence b) so that a decode
 // step can run it in the same launch as the query rotation.  It needs all
-// 1024 threads of the workgroup.
+// 1024 threads of the workgroup.  k_row, v_row are the token's 128 key and
+// value elements (kBf16: bfloat16, else float32); it goes to position
+// start_pos[b] + pos_delta.
 template <bool kBf16>
 __device__ __forceinline__ void append_one_body(
     int h, int b, uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
-    const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ mu,
-    const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
-    float clip_v) {
+    int pos_delta, const void* __restrict__ k_row, const void* __restrict__ v_row,
+    const float* __restrict__ mu, const float* __restrict__ rot_k,
+    const float* __restrict__ rot_v, float clip_k, float clip_v) {
   __shared__ float a_s[2][kHeadDim];
   __shared__ float part[2][4][kHeadDim];
   __shared__ float red[4][2];
@@ -47,12 +49,12 @@ __device__ __forceinline__ void append_one_body(
 #pragma unroll
     for (int i = 0; i < 32; ++i) rcol[i] = R[i * kHeadDim];
     if (kq == 0) {
-      const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim + jc;
       float x;
       if constexpr (kBf16)
-        x = bf16_to_f32((pm ? static_cast<const uint16_t*>(v) : static_cast<const uint16_t*>(k))[off]);
+        x = bf16_to_f32((pm ? static_cast<const uint16_t*>(v_row)
+                            : static_cast<const uint16_t*>(k_row))[jc]);
       else
-        x = (pm ? static_cast<const float*>(v) : static_cast<const float*>(k))[off];
+        x = (pm ? static_cast<const float*>(v_row) : static_cast<const float*>(k_row))[jc];
       if (pm == 0) x -= mu[h * kHeadDim + jc];
       a_s[pm][jc] = x;
     }
@@ -70,7 +72,7 @@ __device__ __forceinline__ void append_one_body(
   }
   // destination page (a position outside the table, or a block id outside
   // the cache, writes nothing)
-  const int pos = start_pos[b];
+  const int pos = start_pos[b] + pos_delta;
   int blk = -1;
   if (pos >= 0 && pos / kBlock < max_blocks) blk = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
   const bool valid = blk >= 0 && blk < num_blocks;
@@ -132,6 +134,16 @@ __device__ __forceinline__ void append_one_body(
                         (static_cast<uint32_t>(f16_bits(z16)) << 16);
     *reinterpret_cast<uint32_t*>(page + kSzOff + mat * 64 * G + (t * G + j / gl) * 4) = sz;
   }
+}
+
+// Row pointer of sequence b, KV head h in a [B][1][Hkv][128] token tensor.
+template <bool kBf16>
+__device__ __forceinline__ const void* token_row(const void* x, int b, int h, int Hkv) {
+  const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim;
+  if constexpr (kBf16)
+    return static_cast<const uint16_t*>(x) + off;
+  else
+    return static_cast<const float*>(x) + off;
 }
 
 }  // namespace kvq

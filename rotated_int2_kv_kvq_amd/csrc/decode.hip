@@ -227,14 +227,134 @@ __device__ __forceinline__ void prologue_pack(int h, int qg, int b, int Hkv, int
   }
 }
 
+// ---- BF16 windows ([OptR] "Assumptions & free parameters": 64 sink and 256
+// recent tokens kept in BF16 beside the INT2 body).  One wave per query head
+// scores the window tokens of its sequence against the unrotated query,
+// subtracting q . mu as the centred body keys do (the same shift for every
+// logit of the context), and writes one partial (lse2, o) in the unrotated
+// basis; the merge folds it in after the inverse value rotation.
+struct WindowArgs {
+  const uint16_t* win = nullptr;    // window store of the layer
+  const float* mu = nullptr;        // key mean [Hkv][128]
+  const int* ctx_len = nullptr;
+  int max_ctx = 0;
+  const int* start_pos = nullptr;   // decode step: position of the new token
+  const void* knew = nullptr;       // decode step: the new token [B][1][Hkv][128]
+  const void* vnew = nullptr;
+  float* wpart = nullptr;           // window partials [B][Hq][kPartStride]
+};
+
+// Element c of a 128-element row, as the window keeps it (bfloat16 value).
+template <bool kBf16>
+__device__ __forceinline__ float window_elem(const void* row, int c) {
+  if constexpr (kBf16)
+    return bf16_to_f32(static_cast<const uint16_t*>(row)[c]);
+  else
+    return bf16_to_f32(f32_to_bf16(static_cast<const float*>(row)[c]));
+}
+
+// Wave of query head hq (row qrow of the tile in LDS, raw q) of KV head h,
+// sequence b; lg is this wave's LDS scratch of kWindow floats.
+template <bool kNewBf16>
+__device__ __forceinline__ void window_attend(const WindowArgs& wa, int b, int h, int hq, int Hq,
+                                              int Hkv, float qscale, const float* qrow,
+                                              float* lg) {
+  const int lane = threadIdx.x & 63;
+  const int n = min(max(wa.ctx_len[b], 0), wa.max_ctx);
+  const int newp = wa.start_pos ? wa.start_pos[b] : -1;
+  const uint16_t* wk = wa.win + (static_cast<size_t>(b) * Hkv + h) * 2 * kWindow * kHeadDim;
+  const uint16_t* wv = wk + kWindow * kHeadDim;
+  const void* kn = nullptr;
+  const void* vn = nullptr;
+  if (newp >= 0) {
+    const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim;
+    kn = kNewBf16 ? static_cast<const void*>(static_cast<const uint16_t*>(wa.knew) + off)
+                  : static_cast<const void*>(static_cast<const float*>(wa.knew) + off);
+    vn = kNewBf16 ? static_cast<const void*>(static_cast<const uint16_t*>(wa.vnew) + off)
+                  : static_cast<const void*>(static_cast<const float*>(wa.vnew) + off);
+  }
+  const float* muh = wa.mu + static_cast<size_t>(h) * kHeadDim;
+  float qm = qrow[lane] * muh[lane] + qrow[lane + 64] * muh[lane + 64];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) qm += shfl_xor(qm, m);
+  const int nsk = min(kSink, n);
+  const int rlo = max(kSink, n - kRecent);
+  const int nw = nsk + max(0, n - rlo);
+  // logits; the new token (its slot may be rewritten by this launch) comes
+  // from the step's input
+  float mloc = -INFINITY;
+  for (int i = lane; i < nw; i += 64) {
+    const int pos = i < nsk ? i : rlo + (i - nsk);
+    float dot = 0.f;
+    if (pos == newp) {
+      for (int c = 0; c < kHeadDim; ++c) dot = fmaf(qrow[c], window_elem<kNewBf16>(kn, c), dot);
+    } else {
+      const uint4* kr = reinterpret_cast<const uint4*>(wk + window_slot(pos) * kHeadDim);
+#pragma unroll 4
+      for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+        const uint4 u = kr[c8];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot = fmaf(qrow[8 * c8 + 2 * e], __uint_as_float(w[e] << 16), dot);
+          dot = fmaf(qrow[8 * c8 + 2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), dot);
+        }
+      }
+    }
+    const float l = qscale * (dot - qm);
+    lg[i] = l;
+    mloc = fmaxf(mloc, l);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) mloc = fmaxf(mloc, shfl_xor(mloc, m));
+  float lsum = 0.f;
+  for (int i = lane; i < nw; i += 64) {
+    const float pi = exp2_hw(lg[i] - mloc);
+    lg[i] = pi;
+    lsum += pi;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) lsum += shfl_xor(lsum, m);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // o: lane owns channels 2*lane, 2*lane + 1
+  float o0 = 0.f, o1 = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    const int pos = i < nsk ? i : rlo + (i - nsk);
+    const float pi = lg[i];
+    float v0, v1;
+    if (pos == newp) {
+      v0 = window_elem<kNewBf16>(vn, 2 * lane);
+      v1 = window_elem<kNewBf16>(vn, 2 * lane + 1);
+    } else {
+      const uint32_t w =
+          reinterpret_cast<const uint32_t*>(wv + window_slot(pos) * kHeadDim)[lane];
+      v0 = __uint_as_float(w << 16);
+      v1 = __uint_as_float(w & 0xffff0000u);
+    }
+    o0 = fmaf(pi, v0, o0);
+    o1 = fmaf(pi, v1, o1);
+  }
+  float* dst = wa.wpart + (static_cast<size_t>(b) * Hq + hq) * kPartStride;
+  const float inv = nw > 0 ? 1.0f / lsum : 0.f;
+  dst[4 + 2 * lane] = o0 * inv;
+  dst[5 + 2 * lane] = o1 * inv;
+  if (lane == 0) dst[0] = nw > 0 ? mloc + __log2f(lsum) : kNegBig;
+}
+
 // The body is a device function of (query tile hx = h*QG + qg, sequence b):
 // threads 0-255 do the work; further threads of a larger workgroup only pass
 // the barriers (the fused decode step runs it in 1024-thread workgroups).
-template <bool kBf16, int G>
+//
+// kWin: also the window partials of the tile's heads (kNewBf16: dtype of the
+// decode step's new token).
+template <bool kBf16, int G, bool kWin = false, bool kNewBf16 = false>
 __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restrict__ q,
                                               const float* __restrict__ rot_k, int Hq, int Hkv,
                                               int QG, float qscale, uint32_t* __restrict__ qa,
-                                              float4* __restrict__ qf) {
+                                              float4* __restrict__ qf,
+                                              const WindowArgs& wa = WindowArgs{}) {
   __shared__ float qin[kHT][kHeadDim];
   __shared__ float red[4][kHT][kHeadDim];  // split-K partial products
   __shared__ uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
@@ -297,15 +417,34 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
   if (act) prologue_digits<G>(h, qg, b, Hkv, QG, qscale, red, dig, qe, qf);
   __syncthreads();
   if (act) prologue_pack<G>(h, qg, b, Hkv, QG, dig, qe, qa);
+  if constexpr (kWin) {
+    __shared__ float wlg[kHT][kWindow];
+    if (act && wv < nh)
+      window_attend<kNewBf16>(wa, b, h, h * Hg + qg * kHT + wv, Hq, Hkv, qscale, qin[wv],
+                              wlg[wv]);
+  }
 }
 
-template <bool kBf16, int G>
+template <bool kBf16, int G, bool kWin>
 __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ q,
                                                        const float* __restrict__ rot_k, int Hq,
                                                        int Hkv, int QG, float qscale,
                                                        uint32_t* __restrict__ qa,
-                                                       float4* __restrict__ qf) {
-  prologue_body<kBf16, G>(blockIdx.x, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa, qf);
+                                                       float4* __restrict__ qf,
+                                                       const uint16_t* __restrict__ win,
+                                                       const float* __restrict__ mu,
+                                                       const int* __restrict__ ctx_len,
+                                                       int max_ctx, float* __restrict__ wpart) {
+  WindowArgs wa;
+  if constexpr (kWin) {
+    wa.win = win;
+    wa.mu = mu;
+    wa.ctx_len = ctx_len;
+    wa.max_ctx = max_ctx;
+    wa.wpart = wpart;
+  }
+  prologue_body<kBf16, G, kWin>(blockIdx.x, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa, qf,
+                                wa);
 }
 
 // --------------------------------------------------------------------------- decode step
@@ -313,19 +452,64 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
 // R_K of the KV head; neither depends on the other).  grid (Hkv * (1 + QG),
 // B), block 1024: x < Hkv appends the new token of KV head x, the others
 // prepare query tile x - Hkv.
-template <bool kKvBf16, bool kQBf16, int G>
+//
+// kWin (BF16 windows): the append role first encodes the token that the new
+// one displaces from the recent window (position p - 256, from its window
+// copy) into the INT2 body, then writes the new token into the window; the
+// prologue role also computes the window partials (taking the new token from
+// the input, not from its slot, which this launch rewrites).
+template <bool kKvBf16, bool kQBf16, int G, bool kWin>
 __global__ __launch_bounds__(1024) void step_prep_kernel(
     uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, const int* __restrict__ block_table,
     int max_blocks, const int* __restrict__ start_pos, const void* __restrict__ k,
     const void* __restrict__ v, const float* __restrict__ mu, const float* __restrict__ rot_k,
     const float* __restrict__ rot_v, float clip_k, float clip_v, const void* __restrict__ q,
-    int Hq, int QG, float qscale, uint32_t* __restrict__ qa, float4* __restrict__ qf) {
-  if (static_cast<int>(blockIdx.x) < Hkv)
-    append_one_body<kKvBf16>(blockIdx.x, blockIdx.y, pages, num_blocks, Hkv, G, block_table,
-                             max_blocks, start_pos, k, v, mu, rot_k, rot_v, clip_k, clip_v);
-  else
-    prologue_body<kQBf16, G>(blockIdx.x - Hkv, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa,
-                             qf);
+    int Hq, int QG, float qscale, uint32_t* __restrict__ qa, float4* __restrict__ qf,
+    uint16_t* __restrict__ win, const int* __restrict__ ctx_len, int max_ctx,
+    float* __restrict__ wpart) {
+  const int b = blockIdx.y;
+  if (static_cast<int>(blockIdx.x) < Hkv) {
+    const int h = blockIdx.x;
+    if constexpr (!kWin) {
+      append_one_body<kKvBf16>(h, b, pages, num_blocks, Hkv, G, block_table, max_blocks,
+                               start_pos, 0, token_row<kKvBf16>(k, b, h, Hkv),
+                               token_row<kKvBf16>(v, b, h, Hkv), mu, rot_k, rot_v, clip_k,
+                               clip_v);
+    } else {
+      const int p = start_pos[b];
+      if (p < 0) return;
+      uint16_t* wk = win + (static_cast<size_t>(b) * Hkv + h) * 2 * kWindow * kHeadDim;
+      uint16_t* wv = wk + kWindow * kHeadDim;
+      const int slot = window_slot(p);
+      if (p >= kWindow)  // position p - 256 leaves the recent window for the body
+        append_one_body<true>(h, b, pages, num_blocks, Hkv, G, block_table, max_blocks,
+                              start_pos, -kRecent, wk + slot * kHeadDim, wv + slot * kHeadDim,
+                              mu, rot_k, rot_v, clip_k, clip_v);
+      __syncthreads();  // the displaced token has been read
+      const int tid = threadIdx.x;
+      if (tid < 2 * kHeadDim) {
+        const int m = tid >> 7, c = tid & 127;
+        const void* src = token_row<kKvBf16>(m ? v : k, b, h, Hkv);
+        const uint16_t x = kKvBf16 ? static_cast<const uint16_t*>(src)[c]
+                                   : f32_to_bf16(static_cast<const float*>(src)[c]);
+        (m ? wv : wk)[slot * kHeadDim + c] = x;
+      }
+    }
+  } else {
+    WindowArgs wa;
+    if constexpr (kWin) {
+      wa.win = win;
+      wa.mu = mu;
+      wa.ctx_len = ctx_len;
+      wa.max_ctx = max_ctx;
+      wa.start_pos = start_pos;
+      wa.knew = k;
+      wa.vnew = v;
+      wa.wpart = wpart;
+    }
+    prologue_body<kQBf16, G, kWin, kKvBf16>(blockIdx.x - Hkv, b, q, rot_k, Hq, Hkv, QG, qscale,
+                                            qa, qf, wa);
+  }
 }
 
 // --------------------------------------------------------------------------- scan
@@ -616,7 +800,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
              int max_ctx, int Hq, int QG, int spw, const uint32_t* __restrict__ qa,
-             const float4* __restrict__ qf, float* __restrict__ part, int S) {
+             const float4* __restrict__ qf, float* __restrict__ part, int S, int win) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
   static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
@@ -641,7 +825,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int qg = hy % QG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p_begin = wgs * spw;
+  // with BF16 windows the body starts after the sinks (a whole number of pages)
+  const int lo_pages = win ? kSink / kBlock : 0;
+  const int p_begin = lo_pages + wgs * spw;
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
 
   // Block ids, clamped into the cache (block ids past INT32_MAX cannot be
@@ -679,8 +865,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const float4 fq = qf[hgi * kHT + hl];
 
   const int ctx = min(max(ctx_in, 0), max_ctx);
-  const int n_pages = (ctx + kBlock - 1) / kBlock;
-  const int ns_b = num_splits(n_pages, spw);
+  const int hi_tok = win ? body_end(ctx) : ctx;  // tokens scanned: [lo_pages * 16, hi_tok)
+  const int n_pages = (hi_tok + kBlock - 1) / kBlock;
+  const int ns_b = num_splits(n_pages - lo_pages, spw);
   if (wgs >= ns_b) return;
   if (p_begin >= n_pages) return;
   const int p_end = (wgs == ns_b - 1) ? n_pages : p_begin + spw;
@@ -861,8 +1048,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         } else {
           const int pg = pblk + 2 * s;
           const int pos = pg * kBlock + t;
-          const bool v0 = pos < ctx;
-          const bool v1 = pg + 1 < p_end && pos + kBlock < ctx;
+          const bool v0 = pos < hi_tok;
+          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok;
           lg[2 * s] = v0 ? l0 : -INFINITY;
           lg[2 * s + 1] = v1 ? l1 : -INFINITY;
           // slots past the context hold arbitrary bytes (possibly NaN as fp16):
@@ -995,8 +1182,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
                                                     const int* __restrict__ ctx_len, int max_ctx,
                                                     int Hq, int Hkv, int QG, int spw, int S,
                                                     const float* __restrict__ rot_v,
-                                                    float* __restrict__ out) {
+                                                    float* __restrict__ out,
+                                                    const float* __restrict__ wpart) {
   __shared__ float orow[kHT * kHeadDim];
+  __shared__ float wwin[kHT];  // the window partial's share of each head's output
   __shared__ float wts[kHT][kMergeLds];
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
@@ -1030,12 +1219,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   };
   load8(0, S);
   const int ctx = min(max(ctx_in, 0), max_ctx);
-  const int ns = num_splits((ctx + kBlock - 1) / kBlock, spw);
-  if (ns == 0) {  // empty context: zero output
+  // with BF16 windows (wpart != null) the splits cover the body only
+  const int lo_pages = wpart ? kSink / kBlock : 0;
+  const int hi_tok = wpart ? body_end(ctx) : ctx;
+  const int ns = num_splits((hi_tok + kBlock - 1) / kBlock - lo_pages, spw);
+  const float* wp =
+      wpart ? wpart + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) *
+                          kPartStride
+            : nullptr;
+  if (ns == 0) {  // no body: the window's output, or zero for an empty context
     if (u < nh) {
       float* o = out + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * kHeadDim;
-      o[c] = 0.f;
-      o[c + 64] = 0.f;
+      o[c] = wp ? wp[4 + c] : 0.f;
+      o[c + 64] = wp ? wp[4 + c + 64] : 0.f;
     }
     return;
   }
@@ -1047,6 +1243,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   for (int s = c + 64; s < nsl; s += 64) M = fmaxf(M, p[s * kPartStride]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor(M, m));
+  const float lse_w = wp ? wp[0] : kNegBig;
+  M = fmaxf(M, lse_w);
   float W = 0.f;
   for (int s = c; s < nsl; s += 64) {
     const float a = exp2_hw((s == c ? lse_c : p[s * kPartStride]) - M);
@@ -1055,6 +1253,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) W += shfl_xor(W, m);
+  float a_w = exp2_hw(lse_w - M);  // 0 without windows
+  W += a_w;
   __syncthreads();
   if (u < nh) {
     // pass 2: eight splits at a time, the next eight's loads issued before
@@ -1084,6 +1284,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
       const float Mn = fmaxf(M, l);
       const float sc = exp2_hw(M - Mn), a = exp2_hw(l - Mn);
       W = W * sc + a;
+      a_w *= sc;
       a0 = fmaf(a, p[s * kPartStride + 4 + c], a0 * sc);
       a1 = fmaf(a, p[s * kPartStride + 4 + c + 64], a1 * sc);
       M = Mn;
@@ -1091,6 +1292,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const float inv = 1.0f / W;
     orow[u * kHeadDim + c] = a0 * inv;
     orow[u * kHeadDim + c + 64] = a1 * inv;
+    if (c == 0) wwin[u] = a_w * inv;
   }
   __syncthreads();
   float o[kHT] = {0.f, 0.f, 0.f, 0.f};
@@ -1106,9 +1308,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   }
 #pragma unroll
   for (int uu = 0; uu < kHT; ++uu) {
-    const float tot = o[uu] + __shfl_xor(o[uu], 1, 64);
-    if (half == 0 && uu < nh)
-      out[(static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + uu) * kHeadDim + j] = tot;
+    float tot = o[uu] + __shfl_xor(o[uu], 1, 64);
+    const size_t row = static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + uu;
+    if (wpart && half == 0 && uu < nh) tot += wwin[uu] * wpart[row * kPartStride + 4 + j];
+    if (half == 0 && uu < nh) out[row * kHeadDim + j] = tot;
   }
 }
 
@@ -1140,7 +1343,9 @@ DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages) {
   p.qa_off = 0;
   p.qf_off = align256(hg * 64 * kQaDwords * 4);
   p.part_off = p.qf_off + align256(hg * kHT * 16);
-  p.total = p.part_off + align256(static_cast<size_t>(B) * Hq * (p.S ? p.S : 1) * kPartStride * 4);
+  p.wpart_off =
+      p.part_off + align256(static_cast<size_t>(B) * Hq * (p.S ? p.S : 1) * kPartStride * 4);
+  p.total = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
   return p;
 }
 
@@ -1148,28 +1353,29 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                   const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
                   int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
                   float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
-                  hipStream_t stream) {
+                  hipStream_t stream, const uint16_t* win, const float* mu) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
   float* part = reinterpret_cast<float*>(ws + p.part_off);
+  float* wpart = win ? reinterpret_cast<float*>(ws + p.wpart_off) : nullptr;
   const float qscale = sm_scale * kLog2e;
-  if (p.S > 0 && (stages & 1)) {
+  if ((p.S > 0 || win) && (stages & 1)) {
     const dim3 g1(Hkv * p.QG, B);
-    if (q_bf16) {
-      if (G == 2)
-        hipLaunchKernelGGL((prologue_kernel<true, 2>), g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv,
-                           p.QG, qscale, qa, qf);
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv, p.QG, qscale, qa, qf,
+                         win, mu, ctx_len, max_ctx, wpart);
+    };
+    if (win) {
+      if (q_bf16)
+        G == 2 ? go(prologue_kernel<true, 2, true>) : go(prologue_kernel<true, 1, true>);
       else
-        hipLaunchKernelGGL((prologue_kernel<true, 1>), g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv,
-                           p.QG, qscale, qa, qf);
+        G == 2 ? go(prologue_kernel<false, 2, true>) : go(prologue_kernel<false, 1, true>);
     } else {
-      if (G == 2)
-        hipLaunchKernelGGL((prologue_kernel<false, 2>), g1, dim3(256), 0, stream, q, rot_k, Hq,
-                           Hkv, p.QG, qscale, qa, qf);
+      if (q_bf16)
+        G == 2 ? go(prologue_kernel<true, 2, false>) : go(prologue_kernel<true, 1, false>);
       else
-        hipLaunchKernelGGL((prologue_kernel<false, 1>), g1, dim3(256), 0, stream, q, rot_k, Hq,
-                           Hkv, p.QG, qscale, qa, qf);
+        G == 2 ? go(prologue_kernel<false, 2, false>) : go(prologue_kernel<false, 1, false>);
     }
   }
   if (p.S > 0 && (stages & 2)) {
@@ -1179,7 +1385,8 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                       0xFFFFFFFFull;
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
-                         max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S);
+                         max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S,
+                         win ? 1 : 0);
     };
     if (G == 2)
       wide ? go(split_kernel<2, true>) : go(split_kernel<2, false>);
@@ -1188,7 +1395,8 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
   }
   if (stages & 4)
     hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(256), 0, stream, part, ctx_len,
-                       max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out);
+                       max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
+                       static_cast<const float*>(wpart));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -1198,31 +1406,35 @@ int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          float clip_k, float clip_v, const int* ctx_len, int max_ctx, int B,
                          int Hq, const void* q, bool q_bf16, const float* rot_k,
                          const float* rot_v, float sm_scale, float* out, void* workspace,
-                         const DecodePlan& p, hipStream_t stream) {
+                         const DecodePlan& p, hipStream_t stream, uint16_t* win) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
+  float* wpart = reinterpret_cast<float*>(ws + p.wpart_off);
   const float qscale = sm_scale * kLog2e;
   const dim3 grid(Hkv * (1 + p.QG), B);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(1024), 0, stream, pages, num_blocks, Hkv, block_table,
                        max_blocks, start_pos, k, v, mu, rot_k, rot_v, clip_k, clip_v, q, Hq,
-                       p.QG, qscale, qa, qf);
+                       p.QG, qscale, qa, qf, win, ctx_len, max_ctx, wpart);
   };
-  if (G == 2) {
-    if (kv_bf16)
-      q_bf16 ? go(step_prep_kernel<true, true, 2>) : go(step_prep_kernel<true, false, 2>);
-    else
-      q_bf16 ? go(step_prep_kernel<false, true, 2>) : go(step_prep_kernel<false, false, 2>);
-  } else {
-    if (kv_bf16)
-      q_bf16 ? go(step_prep_kernel<true, true, 1>) : go(step_prep_kernel<true, false, 1>);
-    else
-      q_bf16 ? go(step_prep_kernel<false, true, 1>) : go(step_prep_kernel<false, false, 1>);
-  }
+  // (kv dtype, q dtype, group, windows) -> one instantiation
+  auto pick = [&](auto kvb, auto qb, auto g) {
+    constexpr bool KV = decltype(kvb)::value, QB = decltype(qb)::value;
+    constexpr int GG = decltype(g)::value;
+    win ? go(step_prep_kernel<KV, QB, GG, true>) : go(step_prep_kernel<KV, QB, GG, false>);
+  };
+  auto pick_g = [&](auto kvb, auto qb) {
+    G == 2 ? pick(kvb, qb, Const<int, 2>{}) : pick(kvb, qb, Const<int, 1>{});
+  };
+  auto pick_q = [&](auto kvb) {
+    q_bf16 ? pick_g(kvb, Const<bool, true>{}) : pick_g(kvb, Const<bool, false>{});
+  };
+  kv_bf16 ? pick_q(Const<bool, true>{}) : pick_q(Const<bool, false>{});
   if (hipGetLastError() != hipSuccess) return -1;
   return launch_decode(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len, max_ctx, B,
-                       Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace, p, 2 | 4, stream);
+                       Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace, p, 2 | 4, stream,
+                       win, mu);
 }
 
 }  // namespace kvq

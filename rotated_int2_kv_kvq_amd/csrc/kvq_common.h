@@ -15,6 +15,19 @@ constexpr float kF16Max = 65504.0f;
 
 __host__ __device__ constexpr int page_bytes_for_groups(int G) { return 1024 + 128 * G; }
 
+// BF16 windows: the first kSink tokens of a sequence and its last kRecent
+// tokens, kept as given (rounded to bfloat16) beside the INT2 body.  Window
+// store of one layer: bfloat16 [batch][Hkv][2: K, V][kWindow][head_dim]; the
+// slot of position p is p for a sink, else a ring slot.
+constexpr int kSink = 64;
+constexpr int kRecent = 256;
+constexpr int kWindow = kSink + kRecent;
+__host__ __device__ constexpr int window_slot(int p) {
+  return p < kSink ? p : kSink + (p - kSink) % kRecent;
+}
+// First sink-free token of the body and the body's end for a context of n.
+__host__ __device__ constexpr int body_end(int n) { return n - kRecent > kSink ? n - kRecent : kSink; }
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -34,6 +47,12 @@ __device__ __forceinline__ float f16_lo_to_f32(uint32_t w) {
 }
 __device__ __forceinline__ float f16_hi_to_f32(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// bfloat16 of x, round to nearest even (finite x).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 template <typename T>

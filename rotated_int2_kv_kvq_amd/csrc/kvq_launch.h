@@ -17,7 +17,7 @@ struct DecodePlan {
   int QG;    // query-head tiles of 4 per KV head
   int spw;   // pages per workgroup split
   int S;     // splits for the longest context
-  size_t qa_off, qf_off, part_off, total;
+  size_t qa_off, qf_off, part_off, wpart_off, total;
 };
 
 DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages);
@@ -26,7 +26,7 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                   const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
                   int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
                   float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
-                  hipStream_t stream);
+                  hipStream_t stream, const uint16_t* win = nullptr, const float* mu = nullptr);
 
 // The single-token append of one decode step fused with the first decode
 // stage, then the scan and the merge.
@@ -36,6 +36,10 @@ int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          float clip_k, float clip_v, const int* ctx_len, int max_ctx, int B,
                          int Hq, const void* q, bool q_bf16, const float* rot_k,
                          const float* rot_v, float sm_scale, float* out, void* workspace,
-                         const DecodePlan& p, hipStream_t stream);
+                         const DecodePlan& p, hipStream_t stream, uint16_t* win = nullptr);
+
+// Copy tokens (rounded to bfloat16) into the BF16 window store.
+int launch_window_write(uint16_t* win, int Hkv, int B, const int* start_pos, int T, const void* k,
+                        const void* v, bool bf16, hipStream_t stream);
 
 }  // namespace kvq

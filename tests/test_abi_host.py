@@ -27,8 +27,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
-        "kvq_append", "kvq_append_decode", "kvq_decode_attn", "kvq_decode_attn_staged",
-        "kvq_decode_workspace_bytes", "kvq_page_bytes", "kvq_status_string"])
+        "kvq_append", "kvq_append_decode", "kvq_append_decode_window", "kvq_decode_attn",
+        "kvq_decode_attn_staged", "kvq_decode_attn_window", "kvq_decode_workspace_bytes",
+        "kvq_page_bytes", "kvq_status_string", "kvq_window_bytes", "kvq_window_write"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -149,3 +150,41 @@ def test_append_decode_rejects_invalid_arguments(lib):
     assert _append_decode(lib, d=64, g=64) == -2
     assert _append_decode(lib, wsb=16) == -3
     assert _append_decode(lib, B=0) == 0
+
+
+def test_window_entry_points_reject_invalid_arguments(lib):
+    import rotated_int2_kv_kvq_amd as kvq
+    assert kvq.window_bytes(16, 8) == 16 * 8 * 2 * 320 * 128 * 2
+    assert kvq.window_bytes(1, 8, head_dim=64) == 0
+    w = lib.kvq_window_write
+    assert w(None, 8, 128, 1, 1 << 21, 4, 1 << 22, 1 << 23, 1, None) == -1
+    assert w(1 << 20, 8, 128, 1, 1 << 21, 4, 1 << 22, 1 << 23, 7, None) == -1   # dtype
+    assert w(1 << 20, 8, 64, 1, 1 << 21, 4, 1 << 22, 1 << 23, 1, None) == -2
+    assert w(1 << 20, 8, 128, 0, 1 << 21, 4, 1 << 22, 1 << 23, 1, None) == 0    # no-op
+    assert w(1 << 20, 8, 128, 1, 1 << 21, 0, 1 << 22, 1 << 23, 1, None) == 0    # no-op
+    d = [1 << 20, 4, 8, 128, 128, 1 << 21, 4, 1 << 22, 1 << 23, 1 << 24, 64, 1, 32, 1 << 25, 1,
+         1 << 26, 1 << 27, 0.088, 1 << 28, 1 << 29, 1 << 30, 0, None]
+    bad = list(d)
+    bad[7] = None                                             # window
+    assert lib.kvq_decode_attn_window(*bad) == -1
+    bad = list(d)
+    bad[8] = None                                             # mu
+    assert lib.kvq_decode_attn_window(*bad) == -1
+    bad = list(d)
+    bad[12] = 30                                              # Hq % Hkv
+    assert lib.kvq_decode_attn_window(*bad) == -1
+    bad = list(d)
+    bad[11] = 0                                               # batch 0: no-op
+    assert lib.kvq_decode_attn_window(*bad) == 0
+    a = [1 << 20, 4, 8, 128, 128, 1 << 21, 4, 1 << 22, 1 << 23, 1 << 23, 64, 1, 1 << 24, 1 << 25, 1,
+         1 << 26, 0.9, 0.9, 32, 1 << 27, 1, 1 << 28, 1 << 29, 0.088, 1 << 30, 1 << 31, 1 << 30, 0,
+         None]
+    bad = list(a)
+    bad[7] = None                                             # window
+    assert lib.kvq_append_decode_window(*bad) == -1
+    bad = list(a)
+    bad[16] = 0.0                                             # clip
+    assert lib.kvq_append_decode_window(*bad) == -1
+    bad = list(a)
+    bad[26] = 16                                              # workspace too small
+    assert lib.kvq_append_decode_window(*bad) == -3

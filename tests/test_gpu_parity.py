@@ -290,6 +290,124 @@ def test_append_decode_step(name):
     assert err <= TIGHT
 
 
+WIN_CASES = {
+    # (workload, context lengths before the stream): empty-ish, sinks only,
+    # no body yet, a body that starts during the stream, long
+    "bf16_g128": (scaled(W4, batch=5, ctx_min=600, ctx_max=600, layers=2, steps=6),
+                  [5, 63, 300, 317, 600]),
+    "f32_g64_h8x2": (scaled(W0, batch=3, ctx_min=700, ctx_max=700, group=64, steps=5),
+                     [0, 318, 700]),
+}
+
+
+def _window_ref(case, win, q, ctx, pairs):
+    """Float64 windowed decode of the GPU's own cache and window store."""
+    w = case.w
+    out = {}
+    for b in sorted({p[0] for p in pairs}):
+        n = int(ctx[b])
+        cache, table = host_pages(case, b, max(n, 1))
+        wk = win[b:b + 1, :, 0].float().cpu().double().numpy()
+        wv = win[b:b + 1, :, 1].float().cpu().double().numpy()
+        heads = [hq for (bb, hq) in pairs if bb == b]
+        o = O.decode_windowed(cache, table, [n], q[b:b + 1].float().cpu().double().numpy(),
+                              case.st.rot_k[case.layer], case.st.rot_v[case.layer],
+                              case.mu.cpu().double().numpy(), wk, wv, case.sm_scale,
+                              w.num_kv_heads, w.group, pairs=[(0, hq) for hq in heads])
+        for hq in heads:
+            out[(b, hq)] = o[0, hq]
+    return out
+
+
+@pytest.mark.parametrize("name", list(WIN_CASES))
+def test_windows_prefill_decode_and_stream(name):
+    """BF16 sink/recent windows: the window store holds the BF16 tokens, decode
+    over sinks + INT2 body + recent matches the oracle, and a stream of decode
+    steps (the body growing by the tokens leaving the recent window) matches
+    the oracle at every step, with the displaced tokens' INT2 encoding under
+    the append parity rules."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w, ctx_list = WIN_CASES[name]
+    say(f"[window] {name}")
+    case = new_case(w, keep_initial=False)
+    dev = case.device
+    B, Hkv = w.batch, w.num_kv_heads
+    ctx = np.array(ctx_list, np.int64)
+    win = kvq.new_window(B, Hkv, dev)
+    win.zero_()
+    for b in range(B):
+        n = int(ctx[b])
+        if n == 0:
+            continue
+        k, v = kv_for_sequence(w, case.st, case.layer, b, 0, n, dev)
+        sp = torch.zeros(1, dtype=torch.int32, device=dev)
+        kvq.window_write(win[b:b + 1], sp, k[None].contiguous(), v[None].contiguous())
+        if n > O.WINDOW:
+            sp_body = torch.full((1,), O.SINK, dtype=torch.int32, device=dev)
+            kvq.append(case.pages, case.table[b:b + 1].contiguous(), sp_body,
+                       k[None, O.SINK:n - O.RECENT].contiguous(),
+                       v[None, O.SINK:n - O.RECENT].contiguous(), case.mu, case.rot_k,
+                       case.rot_v, w.group, w.clip_k, w.clip_v)
+        # the window holds the BF16 tokens of the sinks and the recent window
+        keep = [p for p in range(n) if p < O.SINK or p >= n - O.RECENT]
+        slots = torch.as_tensor(O.window_slot(np.array(keep)), device=dev)
+        kk = torch.as_tensor(keep, device=dev)
+        assert torch.equal(win[b, :, 0, slots].transpose(0, 1), k[kk].to(torch.bfloat16))
+        assert torch.equal(win[b, :, 1, slots].transpose(0, 1), v[kk].to(torch.bfloat16))
+    pairs = [(b, hq) for b in range(B) for hq in (0, w.num_q_heads // 2, w.num_q_heads - 1)]
+    q = query(case, 0)
+    ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    out = kvq.decode_window(case.pages, case.table, win, case.mu, ctx_t, int(ctx.max()), q,
+                            case.rot_k, case.rot_v, w.group, case.sm_scale).cpu().numpy()
+    ref = _window_ref(case, win, q, ctx, pairs)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  prefill decode max rel err {err:.3e}")
+    assert err <= TIGHT
+    ctx0 = ctx.copy()
+    for step in range(w.steps):
+        kv = [kv_for_sequence(w, case.st, case.layer, b, int(ctx[b]), 1, dev) for b in range(B)]
+        k = torch.stack([x[0] for x in kv]).contiguous()
+        v = torch.stack([x[1] for x in kv]).contiguous()
+        sp = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        ctx = ctx + 1
+        ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        q = query(case, step + 1)
+        out = kvq.append_decode_window(case.pages, case.table, win, sp, ctx_t, int(ctx.max()), k,
+                                       v, case.mu, q, case.rot_k, case.rot_v, w.group, w.clip_k,
+                                       w.clip_v, case.sm_scale).cpu().numpy()
+        ref = _window_ref(case, win, q, ctx, pairs)
+        err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+        say(f"  step {step} max rel err {err:.3e}")
+        assert err <= TIGHT
+    # tokens displaced into the body during the stream
+    near = n_el = 0
+    for b in range(B):
+        lo = max(O.SINK, int(ctx0[b]) - O.RECENT)
+        hi = int(ctx[b]) - O.RECENT
+        if hi <= lo:
+            continue
+        kk, vv = kv_for_sequence(w, case.st, case.layer, b, lo, hi - lo, dev)
+        enc = O.encode_tokens(O.bf16_round(kk.float().cpu().numpy()),
+                              O.bf16_round(vv.float().cpu().numpy()),
+                              case.mu.cpu().double().numpy(), case.st.rot_k[case.layer],
+                              case.st.rot_v[case.layer], w.group, w.clip_k, w.clip_v)
+        cache, table = host_pages(case, b, hi)
+        for h in range(Hkv):
+            got = O.read_tokens(cache, table, 0, np.arange(lo, hi), h, Hkv, w.group)
+            for kind, xkey in (("k", "x"), ("v", "y")):
+                bad_sz, _ = check_scale_zero(got[kind + "_s"], got[kind + "_z"],
+                                             enc[kind + "_s"][:, h], enc[kind + "_z"][:, h],
+                                             enc[kind + "_s_raw"][:, h],
+                                             enc[kind + "_z_raw"][:, h])
+                assert bad_sz == 0
+                bad, nr, n = check_codes(got[kind + "_codes"], enc[xkey][:, h],
+                                         got[kind + "_s"], got[kind + "_z"], w.group)
+                assert bad == 0
+                near += nr
+                n_el += n
+    assert n_el > 0 and near <= max(EXEMPT_FRACTION * n_el, 1)
+
+
 FULL = {
     "cfg1_full": (W1, [(0, 0), (3, 31), (2, 17)]),
     "cfg2_full": (W2, [(0, 0), (17, 9), (63, 31), (40, 4)]),
