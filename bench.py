@@ -40,6 +40,8 @@ def parse():
                     help="bound on the oracle's CPU time for the cpu_baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--no-windows", action="store_true",
+                    help="skip the second pass with BF16 sink/recent windows")
     ap.add_argument("--separate-calls", action="store_true",
                     help="kvq_append + kvq_decode_attn per layer instead of kvq_append_decode")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -96,7 +98,7 @@ def main():
     ctx0 = st.ctx_lens.astype(np.int64)
 
     # ---------------------------------------------------------------- build the cache
-    pages, mus, rks, rvs = [], [], [], []
+    pages, mus, rks, rvs, wins = [], [], [], [], []
     t_bulk = 0.0
     n_bulk = 0
     for layer in range(L):
@@ -121,6 +123,20 @@ def main():
             torch.cuda.synchronize()
             t_bulk += time.perf_counter() - t0
             n_bulk += len(seqs) * n
+            if not args.no_windows:
+                # BF16 windows of the prompt: its sinks and its last 256 tokens
+                if len(wins) == layer:
+                    wins.append(kvq.new_window(B, Hkv, dev))
+                for i, b in enumerate(seqs):
+                    wb = wins[layer][b:b + 1]
+                    ns = min(n, kvq.WINDOW_SINK)
+                    r0 = max(ns, n - kvq.WINDOW_RECENT)
+                    for a0, a1 in ((0, ns), (r0, n)):
+                        if a1 > a0:
+                            kvq.window_write(wb, torch.full((1,), a0, dtype=torch.int32,
+                                                            device=dev),
+                                             k[i:i + 1, a0:a1].contiguous(),
+                                             v[i:i + 1, a0:a1].contiguous())
             del k, v
         print(f"[bench] layer {layer} cache built", file=sys.stderr, flush=True)
 
@@ -241,6 +257,58 @@ def main():
     split_bytes = int((ctx0 + last + 1).sum()) * Hkv * per_tok_head
     achieved = split_bytes / (split_avg_ms * 1e-3) / 1e9
 
+    # ---------------------------------------------------------------- BF16 windows pass
+    # The same steps again through kvq_append_decode_window: each step's token
+    # enters the recent window and the token it displaces (position p - 256)
+    # is encoded into the INT2 body (the same bytes the first pass wrote there).
+    win_line = None
+    if not args.no_windows:
+        def run_wstep(step):
+            for layer in range(L):
+                kvq.append_decode_window(pages[layer], table, wins[layer], spos[step], ctxs[step],
+                                         maxc[step], kn[step][layer], vn[step][layer], mus[layer],
+                                         qs[step][layer], rks[layer], rvs[layer], w.group,
+                                         w.clip_k, w.clip_v, sm_scale, out=outs[layer],
+                                         workspace=ws)
+        wgraphs = []
+        if not args.no_graph:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            for step in range(total_steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    run_wstep(step)
+                wgraphs.append(g)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+        for step in range(args.warmup):
+            wgraphs[step].replay() if wgraphs else run_wstep(step)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for step in range(args.warmup, total_steps):
+            wgraphs[step].replay() if wgraphs else run_wstep(step)
+        e1.record()
+        torch.cuda.synchronize()
+        w_ms = e0.elapsed_time(e1)
+        assert all(torch.isfinite(o).all().item() for o in outs)
+        body_b = win_b = 0
+        for s_ in range(args.warmup, total_steps):
+            for n in (ctx0 + s_ + 1):
+                nw = min(int(n), kvq.WINDOW_SINK) + min(max(int(n) - kvq.WINDOW_SINK, 0),
+                                                        kvq.WINDOW_RECENT)
+                body_b += max(int(n) - nw, 0) * Hkv * per_tok_head * L
+                win_b += nw * Hkv * 2 * d * 2 * L
+        win_line = {
+            "step_call": "kvq_append_decode_window",
+            "sink": kvq.WINDOW_SINK, "recent": kvq.WINDOW_RECENT,
+            "ms_per_step": round(w_ms / args.steps, 4),
+            "value": round((body_b + win_b) / (w_ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s (INT2 body + BF16 window bytes read)",
+            "decode_tokens_per_s": round(B * args.steps / (w_ms * 1e-3), 1),
+        }
+        del wgraphs
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -298,6 +366,7 @@ def main():
             "algorithmic_bytes": split_bytes,
         },
         "cpu_baseline": cpu,
+        "windows": win_line,
     }
     print(json.dumps(line), flush=True)
 

@@ -228,134 +228,155 @@ __device__ __forceinline__ void prologue_pack(int h, int qg, int b, int Hkv, int
 }
 
 // ---- BF16 windows ([OptR] "Assumptions & free parameters": 64 sink and 256
-// recent tokens kept in BF16 beside the INT2 body).  One wave per query head
-// scores the window tokens of its sequence against the unrotated query,
-// subtracting q . mu as the centred body keys do (the same shift for every
-// logit of the context), and writes one partial (lse2, o) in the unrotated
-// basis; the merge folds it in after the inverse value rotation.
-struct WindowArgs {
-  const uint16_t* win = nullptr;    // window store of the layer
-  const float* mu = nullptr;        // key mean [Hkv][128]
-  const int* ctx_len = nullptr;
-  int max_ctx = 0;
-  const int* start_pos = nullptr;   // decode step: position of the new token
-  const void* knew = nullptr;       // decode step: the new token [B][1][Hkv][128]
-  const void* vnew = nullptr;
-  float* wpart = nullptr;           // window partials [B][Hq][kPartStride]
-};
-
-// Element c of a 128-element row, as the window keeps it (bfloat16 value).
-template <bool kBf16>
-__device__ __forceinline__ float window_elem(const void* row, int c) {
-  if constexpr (kBf16)
-    return bf16_to_f32(static_cast<const uint16_t*>(row)[c]);
-  else
-    return bf16_to_f32(f32_to_bf16(static_cast<const float*>(row)[c]));
-}
-
-// Wave of query head hq (row qrow of the tile in LDS, raw q) of KV head h,
-// sequence b; lg is this wave's LDS scratch of kWindow floats.
-template <bool kNewBf16>
-__device__ __forceinline__ void window_attend(const WindowArgs& wa, int b, int h, int hq, int Hq,
-                                              int Hkv, float qscale, const float* qrow,
-                                              float* lg) {
-  const int lane = threadIdx.x & 63;
-  const int n = min(max(wa.ctx_len[b], 0), wa.max_ctx);
-  const int newp = wa.start_pos ? wa.start_pos[b] : -1;
-  const uint16_t* wk = wa.win + (static_cast<size_t>(b) * Hkv + h) * 2 * kWindow * kHeadDim;
-  const uint16_t* wv = wk + kWindow * kHeadDim;
-  const void* kn = nullptr;
-  const void* vn = nullptr;
-  if (newp >= 0) {
-    const size_t off = (static_cast<size_t>(b) * Hkv + h) * kHeadDim;
-    kn = kNewBf16 ? static_cast<const void*>(static_cast<const uint16_t*>(wa.knew) + off)
-                  : static_cast<const void*>(static_cast<const float*>(wa.knew) + off);
-    vn = kNewBf16 ? static_cast<const void*>(static_cast<const uint16_t*>(wa.vnew) + off)
-                  : static_cast<const void*>(static_cast<const float*>(wa.vnew) + off);
-  }
-  const float* muh = wa.mu + static_cast<size_t>(h) * kHeadDim;
-  float qm = qrow[lane] * muh[lane] + qrow[lane + 64] * muh[lane + 64];
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) qm += shfl_xor(qm, m);
+// recent tokens kept in BF16 beside the INT2 body).  Workgroups of the scan
+// launch, dispatched ahead of its split workgroups, score the window tokens
+// of one (sequence, query tile) against the unrotated query, subtracting
+// q . mu as the centred body keys do (the same shift for every logit of the
+// context), and write one partial (lse2, o) per query head in the unrotated
+// basis; the merge folds it in after the inverse value rotation.  The window
+// store already holds every token of the context when the scan runs.
+//
+// By 256 threads (all call it).  Logits: one thread per window token, its
+// key row read once for the four heads.  Softmax: one wave per head.  P.V:
+// four groups of 64 threads take every fourth token (a group's loads in
+// flight together), a lane two channels of all four heads; the groups' sums
+// meet in LDS.  lds: kWinLds floats of scratch; qin: the tile's raw query
+// rows (zero past nh).
+constexpr int kWinLds = kHT * kWindow + 4 * kHT * kHeadDim + 3 * kHT;
+__device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
+                                             const float* __restrict__ mu, int n, int b, int h,
+                                             int qg, int nh, int Hq, int Hkv, float qscale,
+                                             const float (*qin)[kHeadDim], float* lds,
+                                             float* __restrict__ wpart) {
+  float(*lg)[kWindow] = reinterpret_cast<float(*)[kWindow]>(lds);  // logits, then weights
+  float(*acc)[kHT][kHeadDim] = reinterpret_cast<float(*)[kHT][kHeadDim]>(lds + kHT * kWindow);
+  float(*hs)[kHT] = reinterpret_cast<float(*)[kHT]>(lds + kHT * kWindow + 4 * kHT * kHeadDim);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint16_t* wk = win + (static_cast<size_t>(b) * Hkv + h) * 2 * kWindow * kHeadDim;
+  const uint16_t* wvs = wk + kWindow * kHeadDim;
   const int nsk = min(kSink, n);
   const int rlo = max(kSink, n - kRecent);
   const int nw = nsk + max(0, n - rlo);
-  // logits; the new token (its slot may be rewritten by this launch) comes
-  // from the step's input
-  float mloc = -INFINITY;
-  for (int i = lane; i < nw; i += 64) {
-    const int pos = i < nsk ? i : rlo + (i - nsk);
-    float dot = 0.f;
-    if (pos == newp) {
-      for (int c = 0; c < kHeadDim; ++c) dot = fmaf(qrow[c], window_elem<kNewBf16>(kn, c), dot);
-    } else {
-      const uint4* kr = reinterpret_cast<const uint4*>(wk + window_slot(pos) * kHeadDim);
-#pragma unroll 4
-      for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
-        const uint4 u = kr[c8];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  auto slot_of = [&](int i) { return window_slot(i < nsk ? i : rlo + (i - nsk)); };
+
+  {  // q . mu per head (wave wv)
+    const float* muh = mu + static_cast<size_t>(h) * kHeadDim;
+    float qm = qin[wv][lane] * muh[lane] + qin[wv][lane + 64] * muh[lane + 64];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dot = fmaf(qrow[8 * c8 + 2 * e], __uint_as_float(w[e] << 16), dot);
-          dot = fmaf(qrow[8 * c8 + 2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), dot);
+    for (int m = 1; m < 64; m <<= 1) qm += shfl_xor(qm, m);
+    if (lane == 0) hs[0][wv] = qm;
+  }
+  __syncthreads();
+  for (int i = tid; i < nw; i += 256) {
+    // the query values are re-read from LDS for every token rather than held
+    // in registers across the loop (512 of them)
+    asm volatile("" ::: "memory");
+    const uint4* kr = reinterpret_cast<const uint4*>(wk + slot_of(i) * kHeadDim);
+    uint4 kw[16];
+#pragma unroll
+    for (int c8 = 0; c8 < 16; ++c8) kw[c8] = kr[c8];
+    float dot[kHT] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c8 = 0; c8 < 16; ++c8) {
+      const uint32_t w4[4] = {kw[c8].x, kw[c8].y, kw[c8].z, kw[c8].w};
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = __uint_as_float(w4[e] << 16);
+        kf[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int u = 0; u < kHT; ++u) {
+        const float4 qa4 = *reinterpret_cast<const float4*>(&qin[u][8 * c8]);
+        const float4 qb4 = *reinterpret_cast<const float4*>(&qin[u][8 * c8 + 4]);
+        dot[u] = fmaf(qa4.x, kf[0], dot[u]);
+        dot[u] = fmaf(qa4.y, kf[1], dot[u]);
+        dot[u] = fmaf(qa4.z, kf[2], dot[u]);
+        dot[u] = fmaf(qa4.w, kf[3], dot[u]);
+        dot[u] = fmaf(qb4.x, kf[4], dot[u]);
+        dot[u] = fmaf(qb4.y, kf[5], dot[u]);
+        dot[u] = fmaf(qb4.z, kf[6], dot[u]);
+        dot[u] = fmaf(qb4.w, kf[7], dot[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kHT; ++u) lg[u][i] = qscale * (dot[u] - hs[0][u]);
+  }
+  __syncthreads();
+  {  // softmax of head wv
+    float m = -INFINITY;
+    for (int i = lane; i < nw; i += 64) m = fmaxf(m, lg[wv][i]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, shfl_xor(m, k));
+    float l = 0.f;
+    for (int i = lane; i < nw; i += 64) {
+      const float pi = exp2_hw(lg[wv][i] - m);
+      lg[wv][i] = pi;
+      l += pi;
+    }
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) l += shfl_xor(l, k);
+    if (lane == 0) {
+      hs[1][wv] = m;
+      hs[2][wv] = l;
+    }
+  }
+  __syncthreads();
+  {  // P.V: group wv takes tokens wv, wv + 4, ... (80 at most), 20 loads at a time
+    constexpr int kChunk = 20;
+    float a[kHT][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+    for (int i0 = wv; i0 < nw; i0 += 4 * kChunk) {
+      uint32_t w2[kChunk];
+#pragma unroll
+      for (int r = 0; r < kChunk; ++r) {
+        const int i = min(i0 + 4 * r, nw - 1);
+        w2[r] = reinterpret_cast<const uint32_t*>(wvs + slot_of(i) * kHeadDim)[lane];
+      }
+#pragma unroll
+      for (int r = 0; r < kChunk; ++r) {
+        const int i = i0 + 4 * r;
+        if (i < nw) {
+          const float v0 = __uint_as_float(w2[r] << 16);
+          const float v1 = __uint_as_float(w2[r] & 0xffff0000u);
+#pragma unroll
+          for (int u = 0; u < kHT; ++u) {
+            a[u][0] = fmaf(lg[u][i], v0, a[u][0]);
+            a[u][1] = fmaf(lg[u][i], v1, a[u][1]);
+          }
         }
       }
     }
-    const float l = qscale * (dot - qm);
-    lg[i] = l;
-    mloc = fmaxf(mloc, l);
-  }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) mloc = fmaxf(mloc, shfl_xor(mloc, m));
-  float lsum = 0.f;
-  for (int i = lane; i < nw; i += 64) {
-    const float pi = exp2_hw(lg[i] - mloc);
-    lg[i] = pi;
-    lsum += pi;
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) lsum += shfl_xor(lsum, m);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // o: lane owns channels 2*lane, 2*lane + 1
-  float o0 = 0.f, o1 = 0.f;
-  for (int i = 0; i < nw; ++i) {
-    const int pos = i < nsk ? i : rlo + (i - nsk);
-    const float pi = lg[i];
-    float v0, v1;
-    if (pos == newp) {
-      v0 = window_elem<kNewBf16>(vn, 2 * lane);
-      v1 = window_elem<kNewBf16>(vn, 2 * lane + 1);
-    } else {
-      const uint32_t w =
-          reinterpret_cast<const uint32_t*>(wv + window_slot(pos) * kHeadDim)[lane];
-      v0 = __uint_as_float(w << 16);
-      v1 = __uint_as_float(w & 0xffff0000u);
+    for (int u = 0; u < kHT; ++u) {
+      acc[wv][u][2 * lane] = a[u][0];
+      acc[wv][u][2 * lane + 1] = a[u][1];
     }
-    o0 = fmaf(pi, v0, o0);
-    o1 = fmaf(pi, v1, o1);
   }
-  float* dst = wa.wpart + (static_cast<size_t>(b) * Hq + hq) * kPartStride;
-  const float inv = nw > 0 ? 1.0f / lsum : 0.f;
-  dst[4 + 2 * lane] = o0 * inv;
-  dst[5 + 2 * lane] = o1 * inv;
-  if (lane == 0) dst[0] = nw > 0 ? mloc + __log2f(lsum) : kNegBig;
+  __syncthreads();
+  if (wv < nh) {  // head wv: the four groups' sums, normalised
+    const int hq = h * (Hq / Hkv) + qg * kHT + wv;
+    float* dst = wpart + (static_cast<size_t>(b) * Hq + hq) * kPartStride;
+    const float inv = nw > 0 ? 1.0f / hs[2][wv] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = lane + 64 * e;
+      dst[4 + c] = ((acc[0][wv][c] + acc[1][wv][c]) + (acc[2][wv][c] + acc[3][wv][c])) * inv;
+    }
+    if (lane == 0) dst[0] = nw > 0 ? hs[1][wv] + __log2f(hs[2][wv]) : kNegBig;
+  }
 }
 
 // The body is a device function of (query tile hx = h*QG + qg, sequence b):
 // threads 0-255 do the work; further threads of a larger workgroup only pass
 // the barriers (the fused decode step runs it in 1024-thread workgroups).
-//
-// kWin: also the window partials of the tile's heads (kNewBf16: dtype of the
-// decode step's new token).
-template <bool kBf16, int G, bool kWin = false, bool kNewBf16 = false>
+template <bool kBf16, int G>
 __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restrict__ q,
                                               const float* __restrict__ rot_k, int Hq, int Hkv,
                                               int QG, float qscale, uint32_t* __restrict__ qa,
-                                              float4* __restrict__ qf,
-                                              const WindowArgs& wa = WindowArgs{}) {
-  __shared__ float qin[kHT][kHeadDim];
+                                              float4* __restrict__ qf) {
+  __shared__ __attribute__((aligned(16))) float qin[kHT][kHeadDim];
   __shared__ float red[4][kHT][kHeadDim];  // split-K partial products
   __shared__ uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
   __shared__ int qe[kHT];
@@ -417,34 +438,15 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
   if (act) prologue_digits<G>(h, qg, b, Hkv, QG, qscale, red, dig, qe, qf);
   __syncthreads();
   if (act) prologue_pack<G>(h, qg, b, Hkv, QG, dig, qe, qa);
-  if constexpr (kWin) {
-    __shared__ float wlg[kHT][kWindow];
-    if (act && wv < nh)
-      window_attend<kNewBf16>(wa, b, h, h * Hg + qg * kHT + wv, Hq, Hkv, qscale, qin[wv],
-                              wlg[wv]);
-  }
 }
 
-template <bool kBf16, int G, bool kWin>
+template <bool kBf16, int G>
 __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ q,
                                                        const float* __restrict__ rot_k, int Hq,
                                                        int Hkv, int QG, float qscale,
                                                        uint32_t* __restrict__ qa,
-                                                       float4* __restrict__ qf,
-                                                       const uint16_t* __restrict__ win,
-                                                       const float* __restrict__ mu,
-                                                       const int* __restrict__ ctx_len,
-                                                       int max_ctx, float* __restrict__ wpart) {
-  WindowArgs wa;
-  if constexpr (kWin) {
-    wa.win = win;
-    wa.mu = mu;
-    wa.ctx_len = ctx_len;
-    wa.max_ctx = max_ctx;
-    wa.wpart = wpart;
-  }
-  prologue_body<kBf16, G, kWin>(blockIdx.x, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa, qf,
-                                wa);
+                                                       float4* __restrict__ qf) {
+  prologue_body<kBf16, G>(blockIdx.x, blockIdx.y, q, rot_k, Hq, Hkv, QG, qscale, qa, qf);
 }
 
 // --------------------------------------------------------------------------- decode step
@@ -455,9 +457,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ 
 //
 // kWin (BF16 windows): the append role first encodes the token that the new
 // one displaces from the recent window (position p - 256, from its window
-// copy) into the INT2 body, then writes the new token into the window; the
-// prologue role also computes the window partials (taking the new token from
-// the input, not from its slot, which this launch rewrites).
+// copy) into the INT2 body, then writes the new token into the window.
 template <bool kKvBf16, bool kQBf16, int G, bool kWin>
 __global__ __launch_bounds__(1024) void step_prep_kernel(
     uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, const int* __restrict__ block_table,
@@ -465,8 +465,7 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(
     const void* __restrict__ v, const float* __restrict__ mu, const float* __restrict__ rot_k,
     const float* __restrict__ rot_v, float clip_k, float clip_v, const void* __restrict__ q,
     int Hq, int QG, float qscale, uint32_t* __restrict__ qa, float4* __restrict__ qf,
-    uint16_t* __restrict__ win, const int* __restrict__ ctx_len, int max_ctx,
-    float* __restrict__ wpart) {
+    uint16_t* __restrict__ win) {
   const int b = blockIdx.y;
   if (static_cast<int>(blockIdx.x) < Hkv) {
     const int h = blockIdx.x;
@@ -496,19 +495,7 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(
       }
     }
   } else {
-    WindowArgs wa;
-    if constexpr (kWin) {
-      wa.win = win;
-      wa.mu = mu;
-      wa.ctx_len = ctx_len;
-      wa.max_ctx = max_ctx;
-      wa.start_pos = start_pos;
-      wa.knew = k;
-      wa.vnew = v;
-      wa.wpart = wpart;
-    }
-    prologue_body<kQBf16, G, kWin, kKvBf16>(blockIdx.x - Hkv, b, q, rot_k, Hq, Hkv, QG, qscale,
-                                            qa, qf, wa);
+    prologue_body<kQBf16, G>(blockIdx.x - Hkv, b, q, rot_k, Hq, Hkv, QG, qscale, qa, qf);
   }
 }
 
@@ -789,7 +776,12 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
   }
 }
 
-// grid (S, Hkv * QG, B), block 256: workgroup x covers pages [x*spw, (x+1)*spw),
+// 1-D grid of n_win + S * Hkv * QG * B workgroups of 256 threads.  With BF16
+// windows (wstore != null) the first n_win = Hkv * QG * B workgroups each
+// score the window of one (query tile, sequence) and write its partial to
+// wpart (q: the raw queries, bf16 when q_bf16); they are dispatched first and
+// run beside the splits.  The rest are the splits: split x of a query tile
+// covers body pages [x*spw, (x+1)*spw) (after the sink pages with windows),
 // cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
 // 128 VGPRs (four waves per SIMD); group 64, with a third q.K operand and a
 // second value group, gets up to 168 (three waves per SIMD) rather than spill
@@ -800,7 +792,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
              int max_ctx, int Hq, int QG, int spw, const uint32_t* __restrict__ qa,
-             const float4* __restrict__ qf, float* __restrict__ part, int S, int win) {
+             const float4* __restrict__ qf, float* __restrict__ part, int S,
+             const uint16_t* __restrict__ wstore, int n_win, const void* __restrict__ q,
+             int q_bf16, const float* __restrict__ mu, float qscale, float* __restrict__ wpart) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
   static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
@@ -809,23 +803,54 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   __shared__ __attribute__((aligned(16))) int wids[kMaxSplitPages];  // block ids of the pages
   __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
   __shared__ float cm[4][kHT], cl[4][kHT];
+  const int Y = Hkv * QG;
+
+  if (static_cast<int>(blockIdx.x) < n_win) {  // a window workgroup
+    static_assert(sizeof(ring) >= (kHT * kHeadDim + kWinLds) * sizeof(float),
+                  "window scratch lives in the ring");
+    float(*qin)[kHeadDim] = reinterpret_cast<float(*)[kHeadDim]>(&ring[0][0][0]);
+    const int hy = blockIdx.x % Y, b = blockIdx.x / Y;
+    const int h = hy / QG, qg = hy % QG;
+    const int Hg = Hq / Hkv;
+    const int nh = min(kHT, Hg - qg * kHT);
+    const int u = threadIdx.x >> 6, c = threadIdx.x & 63;
+    const size_t qrow =
+        (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) * kHeadDim;
+    float x0, x1;
+    if (q_bf16) {
+      const uint16_t* qp = static_cast<const uint16_t*>(q) + qrow;
+      x0 = bf16_to_f32(qp[c]);
+      x1 = bf16_to_f32(qp[c + 64]);
+    } else {
+      const float* qp = static_cast<const float*>(q) + qrow;
+      x0 = qp[c];
+      x1 = qp[c + 64];
+    }
+    qin[u][c] = u < nh ? x0 : 0.f;
+    qin[u][c + 64] = u < nh ? x1 : 0.f;
+    const int n = min(max(ctx_len[b], 0), max_ctx);
+    __syncthreads();
+    window_block(wstore, mu, n, b, h, qg, nh, Hq, Hkv, qscale, qin, &qin[kHT][0], wpart);
+    return;
+  }
 
   // Workgroups go to the eight XCDs round-robin in launch order, and each XCD
-  // has its own L2.  Renumber them so that every XCD takes one contiguous run of
-  // (query group, split) pairs: the splits of a query group then share one L2
-  // copy of its query operand instead of fetching it once per XCD.
-  const int n_wg = gridDim.x * gridDim.y * gridDim.z;
-  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  // has its own L2.  Renumber the splits so that every XCD takes one contiguous
+  // run of (query group, split) pairs: the splits of a query group then share
+  // one L2 copy of its query operand instead of fetching it once per XCD.
+  const int n_wg = static_cast<int>(gridDim.x) - n_win;
+  const int lin = static_cast<int>(blockIdx.x) - n_win;
   const int xcd = lin & 7;
   const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
   const int wgs = job % S;
-  const int hy = (job / S) % gridDim.y;
-  const int b = job / (S * gridDim.y);
+  const int hy = (job / S) % Y;
+  const int b = job / (S * Y);
   const int h = hy / QG;
   const int qg = hy % QG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // with BF16 windows the body starts after the sinks (a whole number of pages)
+  const bool win = wstore != nullptr;
   const int lo_pages = win ? kSink / kBlock : 0;
   const int p_begin = lo_pages + wgs * spw;
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
@@ -1360,33 +1385,27 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
   float* part = reinterpret_cast<float*>(ws + p.part_off);
   float* wpart = win ? reinterpret_cast<float*>(ws + p.wpart_off) : nullptr;
   const float qscale = sm_scale * kLog2e;
-  if ((p.S > 0 || win) && (stages & 1)) {
+  if (p.S > 0 && (stages & 1)) {
     const dim3 g1(Hkv * p.QG, B);
     auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv, p.QG, qscale, qa, qf,
-                         win, mu, ctx_len, max_ctx, wpart);
+      hipLaunchKernelGGL(kernel, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv, p.QG, qscale, qa,
+                         qf);
     };
-    if (win) {
-      if (q_bf16)
-        G == 2 ? go(prologue_kernel<true, 2, true>) : go(prologue_kernel<true, 1, true>);
-      else
-        G == 2 ? go(prologue_kernel<false, 2, true>) : go(prologue_kernel<false, 1, true>);
-    } else {
-      if (q_bf16)
-        G == 2 ? go(prologue_kernel<true, 2, false>) : go(prologue_kernel<true, 1, false>);
-      else
-        G == 2 ? go(prologue_kernel<false, 2, false>) : go(prologue_kernel<false, 1, false>);
-    }
+    if (q_bf16)
+      G == 2 ? go(prologue_kernel<true, 2>) : go(prologue_kernel<true, 1>);
+    else
+      G == 2 ? go(prologue_kernel<false, 2>) : go(prologue_kernel<false, 1>);
   }
-  if (p.S > 0 && (stages & 2)) {
-    const dim3 g2(p.S, Hkv * p.QG, B);
+  const int n_win = win ? B * Hkv * p.QG : 0;
+  if ((p.S > 0 || win) && (stages & 2)) {
+    const dim3 g2(n_win + p.S * Hkv * p.QG * B);
     // one buffer descriptor spans the cache when its byte size fits 32 bits
     const bool wide = static_cast<uint64_t>(num_blocks) * Hkv * page_bytes_for_groups(G) >
                       0xFFFFFFFFull;
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
-                         max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S,
-                         win ? 1 : 0);
+                         max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S, win,
+                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart);
     };
     if (G == 2)
       wide ? go(split_kernel<2, true>) : go(split_kernel<2, false>);
@@ -1410,13 +1429,12 @@ int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
-  float* wpart = reinterpret_cast<float*>(ws + p.wpart_off);
   const float qscale = sm_scale * kLog2e;
   const dim3 grid(Hkv * (1 + p.QG), B);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(1024), 0, stream, pages, num_blocks, Hkv, block_table,
                        max_blocks, start_pos, k, v, mu, rot_k, rot_v, clip_k, clip_v, q, Hq,
-                       p.QG, qscale, qa, qf, win, ctx_len, max_ctx, wpart);
+                       p.QG, qscale, qa, qf, win);
   };
   // (kv dtype, q dtype, group, windows) -> one instantiation
   auto pick = [&](auto kvb, auto qb, auto g) {
