@@ -356,7 +356,7 @@ def main():
         "split_kernel_avg_us": round(split_avg_ms * 1e3, 2),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "split_kernel (decode split-K scan)",
+            "kernel": "split_kernel<1, false, false> (decode split-K scan)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

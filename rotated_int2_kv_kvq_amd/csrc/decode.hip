@@ -777,7 +777,7 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
 }
 
 // 1-D grid of n_win + S * Hkv * QG * B workgroups of 256 threads.  With BF16
-// windows (wstore != null) the first n_win = Hkv * QG * B workgroups each
+// windows (kWin; n_win = 0 otherwise) the first n_win = Hkv * QG * B workgroups each
 // score the window of one (query tile, sequence) and write its partial to
 // wpart (q: the raw queries, bf16 when q_bf16); they are dispatched first and
 // run beside the splits.  The rest are the splits: split x of a query tile
@@ -787,7 +787,7 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
 // second value group, gets up to 168 (three waves per SIMD) rather than spill
 // inside the loop (a spill reload waits for every outstanding DMA).  kWide
 // builds a buffer descriptor per page for caches of 4 GiB and more.
-template <int G, bool kWide>
+template <int G, bool kWide, bool kWin>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
@@ -805,7 +805,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   __shared__ float cm[4][kHT], cl[4][kHT];
   const int Y = Hkv * QG;
 
-  if (static_cast<int>(blockIdx.x) < n_win) {  // a window workgroup
+  if (kWin && static_cast<int>(blockIdx.x) < n_win) {  // a window workgroup
     static_assert(sizeof(ring) >= (kHT * kHeadDim + kWinLds) * sizeof(float),
                   "window scratch lives in the ring");
     float(*qin)[kHeadDim] = reinterpret_cast<float(*)[kHeadDim]>(&ring[0][0][0]);
@@ -850,7 +850,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // with BF16 windows the body starts after the sinks (a whole number of pages)
-  const bool win = wstore != nullptr;
+  constexpr bool win = kWin;
   const int lo_pages = win ? kSink / kBlock : 0;
   const int p_begin = lo_pages + wgs * spw;
   const int* row = block_table + static_cast<size_t>(b) * max_blocks;
@@ -1407,10 +1407,15 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S, win,
                          n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart);
     };
-    if (G == 2)
-      wide ? go(split_kernel<2, true>) : go(split_kernel<2, false>);
-    else
-      wide ? go(split_kernel<1, true>) : go(split_kernel<1, false>);
+    auto pick = [&](auto g, auto wd) {
+      constexpr int GG = decltype(g)::value;
+      constexpr bool WD = decltype(wd)::value;
+      win ? go(split_kernel<GG, WD, true>) : go(split_kernel<GG, WD, false>);
+    };
+    auto pick_w = [&](auto g) {
+      wide ? pick(g, Const<bool, true>{}) : pick(g, Const<bool, false>{});
+    };
+    G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
   if (stages & 4)
     hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(256), 0, stream, part, ctx_len,

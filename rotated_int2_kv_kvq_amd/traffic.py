@@ -25,7 +25,8 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/decode.hip", "csrc/kvq_common.h", "csrc/kvq_launch.h")
-SCAN_KERNEL = "split_kernel"
+# the scan without windows, group 128, one buffer descriptor over the cache
+SCAN_KERNEL = "split_kernel<1, false, false>"
 COPY_KERNEL = "neg_kernel"
 
 
