@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_36l_b16_ctx16k_stream")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for the cpu_baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
@@ -44,6 +44,10 @@ def parse():
                     help="skip the second pass with BF16 sink/recent windows")
     ap.add_argument("--separate-calls", action="store_true",
                     help="kvq_append + kvq_decode_attn per layer instead of kvq_append_decode")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the cold long-context decode leg (128K batch 1; ragged 1K-32K batch 64)")
+    ap.add_argument("--long-reps", type=int, default=24,
+                    help="decode calls timed per long-context workload (at least one per cache copy)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the measurement, run a plain fp32 copy kernel (y = -x) over this "
                          "many MiB three times: the reference for HBM byte counters")
@@ -309,10 +313,21 @@ def main():
         }
         del wgraphs
 
+    layer0_pages = pages[0].cpu()
+
+    # ---------------------------------------------------------------- long contexts, cold
+    long_line = None
+    if not args.no_long:
+        del pages, wins, new_kv, kn, vn
+        pages = None
+        torch.cuda.empty_cache()
+        long_line = {name: long_context_leg(name, args.long_reps)
+                     for name in LONG_WORKLOADS}
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, st, pages[0], table, ctxs[last], qs[last][0], per_tok_head,
+        cpu = cpu_baseline(w, st, layer0_pages, table, ctxs[last], qs[last][0], per_tok_head,
                            args.cpu_seconds, sm_scale)
 
     if args.calibrate_copy_mib > 0:
@@ -367,6 +382,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "windows": win_line,
+        "long_context": long_line,
     }
     print(json.dumps(line), flush=True)
 
@@ -386,32 +402,142 @@ def cpu_baseline(w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s, sm
 def _cpu_baseline(O, w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s, sm_scale):
     import numpy as np
     ctx = ctx_t.cpu().numpy()
+    tab = table.cpu()
     q = q_l0.float().cpu().double().numpy()
     Hkv, Hg = w.num_kv_heads, w.num_q_heads // w.num_kv_heads
     done_bytes = 0
     pairs = 0
     t0 = time.perf_counter()
-    for b in range(w.batch):
-        n = int(ctx[b])
-        n_pages = (n + 15) // 16
-        cache = pages_l0.index_select(0, table[b, :n_pages].long()).cpu().numpy()
-        ident = np.arange(n_pages, dtype=np.int32)[None, :]
-        for h in range(Hkv):
-            heads = [(0, hq) for hq in range(h * Hg, (h + 1) * Hg)]
-            O.decode(cache, ident, [n], q[b:b + 1], st.rot_k[0], st.rot_v[0], sm_scale, Hkv,
-                     w.group, pairs=heads)
-            done_bytes += n * per_tok_head
-            pairs += 1
+    # passes over the (sequence, KV head) pairs until the time budget is spent
+    while time.perf_counter() - t0 < budget_s:
+        for b in range(w.batch):
+            n = int(ctx[b])
+            n_pages = (n + 15) // 16
+            cache = pages_l0.index_select(0, tab[b, :n_pages].long()).numpy()
+            ident = np.arange(n_pages, dtype=np.int32)[None, :]
+            for h in range(Hkv):
+                heads = [(0, hq) for hq in range(h * Hg, (h + 1) * Hg)]
+                O.decode(cache, ident, [n], q[b:b + 1], st.rot_k[0], st.rot_v[0], sm_scale, Hkv,
+                         w.group, pairs=heads)
+                done_bytes += n * per_tok_head
+                pairs += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
             if time.perf_counter() - t0 > budget_s:
                 break
-        if time.perf_counter() - t0 > budget_s:
-            break
     el = time.perf_counter() - t0
     return {"value": round(done_bytes / el / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"float64 numpy oracle decode of layer 0, {pairs} (sequence, KV head) pairs "
                       f"x {Hg} query heads at {int(ctx.max())} tokens, BLAS limited to 1 thread, "
                       f"{el:.1f} s"}
+
+
+# Long-context decode workloads, timed cold with the automatic split plan:
+# the calls cycle through copies of the cache that together exceed the 256 MB
+# Infinity Cache several times, so that each call reads its cache from HBM
+# (a flushing write between calls would leave dirty lines whose write-back
+# competes with the reads).
+LONG_WORKLOADS = ("qwen3_8b_b1_ctx128k_sinks", "qwen3_8b_b64_ctx1k_32k_g64")
+COLD_BYTES = 1200 << 20
+
+
+def build_decode_cache(name: str, dev: str = "cuda"):
+    """The INT2 cache of one layer of a workload, built by the bulk append."""
+    import numpy as np
+    import torch
+
+    import rotated_int2_kv_kvq_amd as kvq
+    from workload import WORKLOADS, key_mean, kv_for_sequence, make_static, query_for
+
+    w = WORKLOADS[name]
+    st = make_static(w)
+    pages = torch.empty(st.num_blocks, w.num_kv_heads, kvq.page_bytes(w.head_dim, w.group),
+                        dtype=torch.uint8, device=dev)
+    table = torch.from_numpy(st.block_table).to(dev)
+    mu = key_mean(w, st, 0, device=dev).contiguous()
+    rk = torch.from_numpy(st.rot_k[0]).to(dev).contiguous()
+    rv = torch.from_numpy(st.rot_v[0]).to(dev).contiguous()
+    chunk = 4096
+    for b, n in enumerate(st.ctx_lens):
+        for s0 in range(0, int(n), chunk):
+            c = min(chunk, int(n) - s0)
+            k, v = kv_for_sequence(w, st, 0, b, s0, c, dev)
+            kvq.append(pages, table[b:b + 1].contiguous(),
+                       torch.full((1,), s0, dtype=torch.int32, device=dev),
+                       k[None].contiguous(), v[None].contiguous(), mu, rk, rv, w.group,
+                       w.clip_k, w.clip_v)
+    q = query_for(w, 0, 0, dev).contiguous()
+    ctx = torch.from_numpy(st.ctx_lens.astype(np.int32)).to(dev)
+    return w, st, pages, table, ctx, q, rk, rv
+
+
+def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
+    """Cold decode of one layer of a long-context workload: the whole call
+    (query rotation, scan, merge) and the scan alone.  Calls run back to back
+    over copies of the cache, queued behind a GPU sleep, between one pair of
+    events; the figure is the mean per call."""
+    import numpy as np
+    import torch
+
+    import rotated_int2_kv_kvq_amd as kvq
+
+    w, st, pages, table, ctx, q, rk, rv = cache or build_decode_cache(name)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    max_ctx = int(st.ctx_lens.max())
+    sm = 1.0 / math.sqrt(d)
+    nbytes = int(st.ctx_lens.astype(np.int64).sum()) * Hkv * cache_bytes_per_token_head(w.group)
+    ncopy = max(2, -(-COLD_BYTES // (pages.numel())))
+    copies = [pages] + [pages.clone() for _ in range(ncopy - 1)]
+    wsb = kvq.decode_workspace_bytes(B, Hq, Hkv, max_ctx, d, split_pages)
+    wss = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    calls = max(reps, ncopy)
+
+    def call(i, stages):
+        kvq.decode(copies[i % ncopy], table, ctx, max_ctx, q, rk, rv, w.group, sm, out=out,
+                   workspace=wss[i % ncopy], split_pages=split_pages, stages=stages)
+
+    full_ms, scan_ms = [], []
+    for rep in range(3):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            call(i, kvq.STAGE_ALL)
+        e1.record()
+        for i in range(ncopy):
+            call(i, kvq.STAGE_PREPARE)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record()
+        for i in range(calls):
+            call(i, kvq.STAGE_SPLITS)
+        e3.record()
+        torch.cuda.synchronize()
+        if rep:
+            full_ms.append(e0.elapsed_time(e1) / calls)
+            scan_ms.append(e2.elapsed_time(e3) / calls)
+    call(0, kvq.STAGE_ALL)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    full_us = float(np.mean(full_ms)) * 1e3
+    scan_us = float(np.mean(scan_ms)) * 1e3
+    del copies, wss, out
+    return {
+        "batch": B, "ctx": [int(st.ctx_lens.min()), max_ctx], "group": w.group,
+        "cache_bytes": nbytes, "cold": f"{ncopy} cache copies cycled",
+        "decode_us": round(full_us, 2),
+        "decode_gbs": round(nbytes / (full_us * 1e-6) / 1e9, 1),
+        "decode_frac": round(nbytes / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "scan_us": round(scan_us, 2),
+        "scan_gbs": round(nbytes / (scan_us * 1e-6) / 1e9, 1),
+        "scan_frac": round(nbytes / (scan_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(B / (full_us * 1e-6), 1),
+        "split_pages": split_pages or "auto",
+    }
 
 
 if __name__ == "__main__":

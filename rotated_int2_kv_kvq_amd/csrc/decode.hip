@@ -675,6 +675,25 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Reductions over the whole wave, the same value in every lane: the rows by
+// DPP, then the four row results read as scalars.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Write four digit bytes to rows 4*hl + 0..3 of the P tile at this lane's
 // (page kJ, token) column.
 template <int kJ>
@@ -1013,7 +1032,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
       if (kFast || i < nsl) {
         // slice i + 2: slices 2, 3 of this block, then 0, 1 of the next
         if (kFast || i + kDepth < nsl) {
-          if (s < 2)
+          if constexpr (s < 2)
             issue(myring + (s + 2) * kSlot, idc[2 * s + 4], idc[2 * s + 5]);
           else
             issue(myring + (s - 2) * kSlot, idn[2 * s - 4], idn[2 * s - 3]);
@@ -1196,162 +1215,157 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 }
 
 // ---- merge: log-sum-exp merge of the ns partials of the nh query heads of
-// one head tile, then o = o_r * R_V[h]^T.  grid (Hkv * QG, B), block 256.
-// Thread (j = tid/2, half) loads its R_V row half before reading any partial,
-// so the two memory latencies overlap.  The merge takes two passes: wave u
-// finds head u's maximum lse and the splits' weights; then every thread sums
-// its two channels over the splits with independent loads.
-constexpr int kMergeLds = 1024;  // splits whose weights the merge keeps in LDS
+// one head tile, then o = o_r * R_V[h]^T.  grid (Hkv * QG, B), block 1024.
+// Latency-bound, so every load is issued before the first one is used:
+//   - thread (j = tid/8, part = tid%8) loads its sixteen entries of row j of
+//     R_V for the rotation;
+//   - thread (head u = tid/256, half = (tid/128)%2, channel c = tid%128) loads
+//     channel c of splits half, half + 2, ... (kMergeSplits of them per round,
+//     with their lse values: one address per wave), and lane l of each wave
+//     the lse of split l.
+// Each wave of head u then reduces the head's maximum lse and weight sum over
+// the splits itself, so one barrier (the per-half channel sums into LDS)
+// separates the merge from the rotation.
+constexpr int kMergeSplits = 16;  // splits per thread and round (two halves: 32 per round)
 
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
-                                                    const int* __restrict__ ctx_len, int max_ctx,
-                                                    int Hq, int Hkv, int QG, int spw, int S,
-                                                    const float* __restrict__ rot_v,
-                                                    float* __restrict__ out,
-                                                    const float* __restrict__ wpart) {
-  __shared__ float orow[kHT * kHeadDim];
-  __shared__ float wwin[kHT];  // the window partial's share of each head's output
-  __shared__ float wts[kHT][kMergeLds];
+__global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ part,
+                                                     const int* __restrict__ ctx_len, int max_ctx,
+                                                     int Hq, int Hkv, int QG, int spw, int S,
+                                                     const float* __restrict__ rot_v,
+                                                     float* __restrict__ out,
+                                                     const float* __restrict__ wpart) {
+  __shared__ __attribute__((aligned(16))) float osum[2][kHT][kHeadDim];
+  __shared__ float hinv[kHT];  // 1 / (weight sum) per head
+  __shared__ float hwin[kHT];  // the window partial's share of each head's output
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
   const int Hg = Hq / Hkv;
   const int nh = min(kHT, Hg - qg * kHT);
-  const int j = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
+  const int tid = threadIdx.x;
+  const int j = tid >> 3, part8 = tid & 7;
+  // input channels 4 part + 32 i4 + (0..3): eight lanes read 128 contiguous bytes
   const float4* R = reinterpret_cast<const float4*>(
-      rot_v + static_cast<size_t>(h) * kHeadDim * kHeadDim + j * kHeadDim + 64 * half);
-  float4 rr[16];
+      rot_v + (static_cast<size_t>(h) * kHeadDim + j) * kHeadDim + 4 * part8);
+  float4 rr[4];
 #pragma unroll
-  for (int i4 = 0; i4 < 16; ++i4) rr[i4] = R[i4];
+  for (int i4 = 0; i4 < 4; ++i4) rr[i4] = R[8 * i4];
+  const int u = tid >> 8, half = (tid >> 7) & 1, c = tid & 127, lane = tid & 63;
+  const size_t row0 = static_cast<size_t>(b) * Hq + h * Hg + qg * kHT;
+  const float* p = part + (row0 + min(u, nh - 1)) * S * kPartStride;
   const int ctx_in = ctx_len[b];
-  const int u = threadIdx.x >> 6;
-  const int c = threadIdx.x & 63;
-  const float* p = part + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) * S *
-                              kPartStride;
-  // Loaded before the context length (and so the split count) is known:
-  // split c's lse and the first eight splits' outputs, indices clamped to the
-  // S allocated splits; entries of splits past the count are never used.
-  const float lse_c = p[min(c, S - 1) * kPartStride];
-  float x0[8], x1[8];
-  auto load8 = [&](int s0, int lim) {
+  // Loaded before the context length (and so the split count) is known, for
+  // the S allocated splits; entries of splits past the count are never used.
+  const float lse_l = p[min(lane, S - 1) * kPartStride];
+  float xv[kMergeSplits], lv[kMergeSplits];
+  auto load_round = [&](int r, float(&x)[kMergeSplits], float(&l)[kMergeSplits]) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = min(s0 + k, lim - 1);
-      x0[k] = p[s * kPartStride + 4 + c];
-      x1[k] = p[s * kPartStride + 4 + c + 64];
+    for (int k = 0; k < kMergeSplits; ++k) {
+      const int s = 2 * (kMergeSplits * r + k) + half;  // the same in the whole wave
+      if (s < S) {
+        x[k] = p[s * kPartStride + 4 + c];
+        l[k] = p[s * kPartStride];
+      }
     }
   };
-  load8(0, S);
+  load_round(0, xv, lv);
+  // the window partial's lse, and the window output this thread adds
+  const float lse_w = wpart ? wpart[(row0 + min(u, nh - 1)) * kPartStride] : kNegBig;
+  const float wv = wpart ? wpart[(row0 + min(part8 & 3, nh - 1)) * kPartStride + 4 + j] : 0.f;
   const int ctx = min(max(ctx_in, 0), max_ctx);
   // with BF16 windows (wpart != null) the splits cover the body only
   const int lo_pages = wpart ? kSink / kBlock : 0;
   const int hi_tok = wpart ? body_end(ctx) : ctx;
   const int ns = num_splits((hi_tok + kBlock - 1) / kBlock - lo_pages, spw);
-  const float* wp =
-      wpart ? wpart + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + min(u, nh - 1)) *
-                          kPartStride
-            : nullptr;
   if (ns == 0) {  // no body: the window's output, or zero for an empty context
-    if (u < nh) {
-      float* o = out + (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + u) * kHeadDim;
-      o[c] = wp ? wp[4 + c] : 0.f;
-      o[c + 64] = wp ? wp[4 + c + 64] : 0.f;
+    if (half == 0 && u < nh) {
+      const size_t row = row0 + u;
+      out[row * kHeadDim + c] = wpart ? wpart[row * kPartStride + 4 + c] : 0.f;
     }
     return;
   }
 
-  // pass 1, wave u: the splits' weights exp2(lse_s - M) / sum into LDS
-  // (splits beyond kMergeLds are folded in pass 2 with an online rescale)
-  const int nsl = min(ns, kMergeLds);
-  float M = c < nsl ? lse_c : -INFINITY;
-  for (int s = c + 64; s < nsl; s += 64) M = fmaxf(M, p[s * kPartStride]);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor(M, m));
-  const float lse_w = wp ? wp[0] : kNegBig;
+  // head u's maximum lse and weight sum over the ns splits (every wave of the
+  // head computes them), with the window partial's
+  float M = lane < ns ? lse_l : -INFINITY;
+  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
+  M = wave_max(M);
   M = fmaxf(M, lse_w);
-  float W = 0.f;
-  for (int s = c; s < nsl; s += 64) {
-    const float a = exp2_hw((s == c ? lse_c : p[s * kPartStride]) - M);
-    wts[u][s] = a;
-    W += a;
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) W += shfl_xor(W, m);
-  float a_w = exp2_hw(lse_w - M);  // 0 without windows
+  float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
+  for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
+  W = wave_sum(W);
+  const float a_w = exp2_hw(lse_w - M);  // 0 without windows
   W += a_w;
-  __syncthreads();
-  if (u < nh) {
-    // pass 2: eight splits at a time, the next eight's loads issued before
-    // this eight's are used (software pipelined); a split past the count
-    // contributes nothing (its stale values are never multiplied)
-    float a0 = 0.f, a1 = 0.f;
-    for (int s0 = 0; s0 < nsl; s0 += 8) {
-      float y0[8], y1[8];
+
+  // channel c over this half's splits, a round at a time (one round covers
+  // 32 splits); a split past the count contributes nothing (its stale values
+  // are never multiplied)
+  float acc = 0.f;
+  const int nr = (ns + 2 * kMergeSplits - 1) / (2 * kMergeSplits);
+  for (int r = 0; r < nr; ++r) {
+    if (r > 0) load_round(r, xv, lv);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        y0[k] = x0[k];
-        y1[k] = x1[k];
-      }
-      if (s0 + 8 < nsl) load8(s0 + 8, nsl);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (s0 + k < nsl) {
-          const float a = wts[u][s0 + k];
-          a0 = fmaf(a, y0[k], a0);
-          a1 = fmaf(a, y1[k], a1);
-        }
-      }
+    for (int k = 0; k < kMergeSplits; ++k) {
+      const int s = 2 * (kMergeSplits * r + k) + half;
+      if (s < ns) acc = fmaf(exp2_hw(lv[k] - M), xv[k], acc);
     }
-    // splits past the LDS table (very long contexts): online rescale
-    for (int s = nsl; s < ns; ++s) {
-      const float l = p[s * kPartStride];
-      const float Mn = fmaxf(M, l);
-      const float sc = exp2_hw(M - Mn), a = exp2_hw(l - Mn);
-      W = W * sc + a;
-      a_w *= sc;
-      a0 = fmaf(a, p[s * kPartStride + 4 + c], a0 * sc);
-      a1 = fmaf(a, p[s * kPartStride + 4 + c + 64], a1 * sc);
-      M = Mn;
-    }
+  }
+  osum[half][u][c] = acc;
+  if ((tid & 255) == 0) {
     const float inv = 1.0f / W;
-    orow[u * kHeadDim + c] = a0 * inv;
-    orow[u * kHeadDim + c + 64] = a1 * inv;
-    if (c == 0) wwin[u] = a_w * inv;
+    hinv[u] = inv;
+    hwin[u] = a_w * inv;
   }
   __syncthreads();
+
+  // o * R_V^T: thread (j, part) over input channels 4 part + 32 i4 + (0..3)
+  // for the four heads, then a sum over the eight parts (eight adjacent lanes)
   float o[kHT] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i4 = 0; i4 < 16; ++i4) {
+  for (int i4 = 0; i4 < 4; ++i4) {
     const float4 r = rr[i4];
-    const int i = 64 * half + 4 * i4;
+    const int i = 4 * part8 + 32 * i4;
 #pragma unroll
     for (int uu = 0; uu < kHT; ++uu) {
-      const float* orr = orow + uu * kHeadDim + i;
-      o[uu] = fmaf(orr[0], r.x, fmaf(orr[1], r.y, fmaf(orr[2], r.z, fmaf(orr[3], r.w, o[uu]))));
+      const float4 x0 = *reinterpret_cast<const float4*>(&osum[0][uu][i]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&osum[1][uu][i]);
+      o[uu] = fmaf(x0.x + x1.x, r.x,
+                   fmaf(x0.y + x1.y, r.y, fmaf(x0.z + x1.z, r.z, fmaf(x0.w + x1.w, r.w, o[uu]))));
     }
+  }
+  // quad_perm [1,0,3,2], [2,3,0,1], then row_half_mirror (lane i and 7 - i
+  // of each eight hold the two quads' sums)
+#pragma unroll
+  for (int uu = 0; uu < kHT; ++uu) {
+    o[uu] += dpp<0xb1>(o[uu]);
+    o[uu] += dpp<0x4e>(o[uu]);
+    o[uu] += dpp<0x141>(o[uu]);
   }
 #pragma unroll
   for (int uu = 0; uu < kHT; ++uu) {
-    float tot = o[uu] + __shfl_xor(o[uu], 1, 64);
-    const size_t row = static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + uu;
-    if (wpart && half == 0 && uu < nh) tot += wwin[uu] * wpart[row * kPartStride + 4 + j];
-    if (half == 0 && uu < nh) out[row * kHeadDim + j] = tot;
+    if (part8 == uu && uu < nh) {
+      const size_t row = row0 + uu;
+      out[row * kHeadDim + j] = fmaf(hwin[uu], wv, o[uu] * hinv[uu]);
+    }
   }
 }
 
 // --------------------------------------------------------------------------- host side
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Pages per split: about 1024 workgroups (four per CU), in whole 32-page
-// steps so that each wave gets whole 8-page blocks, and at least 128 pages
-// (four blocks per wave), below which per-workgroup start-up and the merge of
-// many partials cost more than the extra workgroups bring (measured at 128K
-// context, batch 1).
+// Pages per split, from the longest context (the lengths themselves stay on
+// the device): at least 128 pages (four 8-page blocks per wave), below which
+// per-workgroup start-up and the merge of many partials cost more than the
+// extra workgroups bring; above that, about 8192 workgroups for the longest
+// context in every sequence, in whole 32-page steps, so that a ragged batch
+// (whose actual work may be half of that) still leaves the dispatcher many
+// short workgroups to balance; at most 512 pages.  Measured cold on MI355X:
+// 128K context batch 1 and 16K batch 16 are fastest at 128 pages; a batch of
+// 64 with contexts of 1K-32K at 128 (230 us) against 512 (258 us).
 int choose_split_pages(int B, int Hkv, int QG, int max_ctx) {
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
   const int64_t total = static_cast<int64_t>(B) * Hkv * QG * max_pages;
-  int64_t spw = (total / 1024 + 16) / 32 * 32;
+  int64_t spw = (total / 8192 + 16) / 32 * 32;
   if (spw < 128) spw = 128;
   if (spw > 512) spw = 512;
   return static_cast<int>(spw);
@@ -1418,7 +1432,7 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
     G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
   if (stages & 4)
-    hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(256), 0, stream, part, ctx_len,
+    hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
                        max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
                        static_cast<const float*>(wpart));
   return hipGetLastError() == hipSuccess ? 0 : -1;
