@@ -6,17 +6,21 @@
 // rotation; rotation, clipping, grouping, rounding) and "Core claim" (one
 // orthogonal rotation per KV head and layer).
 //
-// Work decomposition.  One workgroup (4 waves) owns one (sequence, KV head)
-// and a run of consecutive pages touched by this call; it stages R_K and R_V
-// in LDS (transposed, columns permuted so that each lane ends up holding 8
-// consecutive rotated channels), then waves 0-1 encode keys and waves 2-3
-// values, alternating pages.  A wave encodes one 16-token page at a time:
+// Work decomposition.  One workgroup (8 waves, two per SIMD) owns one
+// (sequence, KV head) and a run of consecutive pages touched by this call; it
+// stages R_K and R_V in LDS once (transposed, columns permuted so that each
+// lane ends up holding 8 consecutive rotated channels; 135 KB, so one
+// workgroup per CU), then waves 0-3 encode keys and waves 4-7 values, each
+// taking every fourth page, with the next page's token rows loaded while the
+// current page is rotated.  A wave encodes one 16-token page at a time:
 // the 16 x 128 x 128 rotation is 256 fp32 MFMAs (16x16x4), whose output
 // gives lane l tokens 4*(l/16)..+3 and channels 8*(l%16)..+7; group min/max
 // is a 16-lane (or 8-lane) butterfly; codes are packed in registers and
 // written to the page.  Because a page is owned by one wave for the whole
 // call, partially filled V-code words are updated read-modify-write without
 // races.
+#include <algorithm>
+
 #include "append_one.h"
 #include "kvq_common.h"
 #include "kvq_launch.h"
@@ -25,14 +29,32 @@ namespace kvq {
 
 constexpr int kRStride = 132;  // LDS row stride (floats) of a staged rotation
 
+// One lane's 32 input channels of a token row as loaded (bf16: four 16-byte
+// loads; fp32: eight), kept raw while in flight.
 template <bool kBf16>
-__device__ __forceinline__ void load_row32(const void* src, size_t elem_off, float (&a)[32]) {
+struct RawRow {
+  uint4 u[kBf16 ? 4 : 8];
+};
+
+template <bool kBf16>
+__device__ __forceinline__ void load_raw32(const void* src, size_t elem_off, RawRow<kBf16>& r) {
   if constexpr (kBf16) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + elem_off);
 #pragma unroll
+    for (int q = 0; q < 4; ++q) r.u[q] = p[q];
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(src) + elem_off);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) r.u[q] = p[q];
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void raw_to_f32(const RawRow<kBf16>& r, float (&a)[32]) {
+  if constexpr (kBf16) {
+#pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint4 u = p[q];
-      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      const uint32_t w[4] = {r.u[q].x, r.u[q].y, r.u[q].z, r.u[q].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         a[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
@@ -40,20 +62,18 @@ __device__ __forceinline__ void load_row32(const void* src, size_t elem_off, flo
       }
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + elem_off);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      float4 f = p[q];
-      a[4 * q] = f.x;
-      a[4 * q + 1] = f.y;
-      a[4 * q + 2] = f.z;
-      a[4 * q + 3] = f.w;
+      a[4 * q] = __uint_as_float(r.u[q].x);
+      a[4 * q + 1] = __uint_as_float(r.u[q].y);
+      a[4 * q + 2] = __uint_as_float(r.u[q].z);
+      a[4 * q + 3] = __uint_as_float(r.u[q].w);
     }
   }
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(256) void append_kernel(
+__global__ __launch_bounds__(512) void append_kernel(
     uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
     int T, const void* __restrict__ k, const void* __restrict__ v,
@@ -79,7 +99,7 @@ __global__ __launch_bounds__(256) void append_kernel(
   // MFMA output column (tile nt, lane n) is rotated channel 8*n + nt.
   for (int mat = 0; mat < 2; ++mat) {
     const float* R = (mat ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim;
-    for (int idx = tid; idx < kHeadDim * kHeadDim / 4; idx += 256) {
+    for (int idx = tid; idx < kHeadDim * kHeadDim / 4; idx += 512) {
       const int krow = idx >> 5;
       const int c4 = (idx & 31) * 4;
       const float4 r = *reinterpret_cast<const float4*>(R + krow * kHeadDim + c4);
@@ -93,7 +113,8 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
   __syncthreads();
 
-  const int mat = wave >> 1;  // 0 = keys, 1 = values
+  const int mat = wave >> 2;  // 0 = keys, 1 = values
+  const int w4 = wave & 3;    // pages wg_first + w4, + 4, ...
   const float clip = mat ? clip_v : clip_k;
   const void* src = mat ? v : k;
   const int PB = page_bytes_for_groups(G);
@@ -102,35 +123,51 @@ __global__ __launch_bounds__(256) void append_kernel(
   const int t = lane & 15;   // A row: token slot in the page
   const int r4 = lane >> 4;  // D rows: tokens 4*r4..4*r4+3
 
-  for (int pg = wg_first + (wave & 1); pg <= wg_last; pg += 2) {
+  // the key mean of this lane's 32 input channels (keys only)
+  float mr[32];
+#pragma unroll
+  for (int s = 0; s < 32; ++s) mr[s] = 0.f;
+  if (mat == 0) {
+    const float4* m4 = reinterpret_cast<const float4*>(mu + h * kHeadDim + 32 * kg);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 m = m4[q];
+      mr[4 * q] = m.x;
+      mr[4 * q + 1] = m.y;
+      mr[4 * q + 2] = m.z;
+      mr[4 * q + 3] = m.w;
+    }
+  }
+  // Token row t of page pg (input channels 32kg..32kg+31) if that token is
+  // one this call writes; false (nothing loaded) otherwise.
+  auto fetch = [&](int pg, RawRow<kBf16>& r) {
+    const int pos = pg * kBlock + t;
+    const bool row_new = pg <= wg_last && pos >= s0 && pos < s0 + T;
+    if (row_new)
+      load_raw32<kBf16>(src,
+                        (static_cast<size_t>(b) * T + (pos - s0)) * Hkv * kHeadDim +
+                            static_cast<size_t>(h) * kHeadDim + 32 * kg,
+                        r);
+    return row_new;
+  };
+  RawRow<kBf16> raw;
+  bool cur_new = fetch(wg_first + w4, raw);
+
+  for (int pg = wg_first + w4; pg <= wg_last; pg += 4) {
     if (pg >= max_blocks) break;
+    // A operand: this lane's token row (centred keys); zero for old tokens
+    float a[32];
+    raw_to_f32<kBf16>(raw, a);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) a[s] = cur_new ? a[s] - mr[s] : 0.f;
+    // the next page's rows are in flight during this page's products
+    RawRow<kBf16> nraw;
+    const bool nxt_new = fetch(pg + 4, nraw);
     const int blk = block_table[static_cast<size_t>(b) * max_blocks + pg];
+    raw = nraw;
+    cur_new = nxt_new;
     if (blk < 0 || blk >= num_blocks) continue;
     uint8_t* page = pages + (static_cast<int64_t>(blk) * Hkv + h) * PB;
-
-    // A operand: this lane's token row, input channels 32kg..32kg+31 (centred keys).
-    float a[32];
-    const int pos = pg * kBlock + t;
-    const bool row_new = pos >= s0 && pos < s0 + T;
-    if (row_new) {
-      const size_t off = (static_cast<size_t>(b) * T + (pos - s0)) * Hkv * kHeadDim +
-                         static_cast<size_t>(h) * kHeadDim + 32 * kg;
-      load_row32<kBf16>(src, off, a);
-      if (mat == 0) {
-        const float4* m4 = reinterpret_cast<const float4*>(mu + h * kHeadDim + 32 * kg);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 m = m4[q];
-          a[4 * q] -= m.x;
-          a[4 * q + 1] -= m.y;
-          a[4 * q + 2] -= m.z;
-          a[4 * q + 3] -= m.w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 32; ++s) a[s] = 0.f;
-    }
 
     floatx4 acc[8];
 #pragma unroll
@@ -303,15 +340,19 @@ int launch_append(uint8_t* pages, int64_t num_blocks, int Hkv, int G, const int*
                          clip_k, clip_v);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  // Pages per workgroup: each stages 128 KB of rotations, so large appends
+  // take up to 64 pages (16 per wave), keeping about 2048 workgroups (eight
+  // per CU over the launch) when there are fewer pages; at least 8.
   const int max_pages = (T + kBlock - 1) / kBlock + 1;
-  const int ppw = max_pages <= 2 ? 2 : 16;
+  const int64_t total = static_cast<int64_t>(B) * Hkv * max_pages;
+  const int ppw = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(8, (total / 2048 + 3) / 4 * 4)));
   const dim3 grid((max_pages + ppw - 1) / ppw, Hkv, B);
   if (bf16)
-    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(256), 0, stream, pages, num_blocks, Hkv, G,
+    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(512), 0, stream, pages, num_blocks, Hkv, G,
                        block_table, max_blocks, start_pos, T, k, v, mu, rot_k, rot_v, clip_k,
                        clip_v, ppw);
   else
-    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(256), 0, stream, pages, num_blocks, Hkv,
+    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(512), 0, stream, pages, num_blocks, Hkv,
                        G, block_table, max_blocks, start_pos, T, k, v, mu, rot_k, rot_v, clip_k,
                        clip_v, ppw);
   return hipGetLastError() == hipSuccess ? 0 : -1;
