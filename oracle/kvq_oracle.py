@@ -56,7 +56,8 @@ __all__ = [
     "rotate", "encode_groups", "quantize_on_grid", "encode_tokens", "k_code_site", "v_code_site",
     "sz_site", "write_tokens", "read_tokens", "dequant", "attend", "decode",
     "append", "plain_attention", "SINK", "RECENT", "WINDOW", "window_slot", "window_parts",
-    "bf16_round", "window_write", "append_windowed", "decode_windowed",
+    "bf16_round", "window_write", "append_windowed", "decode_windowed", "dequantized_kv",
+    "eq8_decomposition",
 ]
 
 
@@ -301,6 +302,53 @@ def decode(cache, block_table, ctx_len, q, rot_k, rot_v, sm_scale: float, num_kv
                 o_r = attend(q_r, k_hat, v_hat, sm_scale)
                 out[b, hq] = o_r @ Rv.T
     return out
+
+
+# --------------------------------------------------------------------------- Eq. 8
+# [OptR] abstract, "What carries the argument" and "Core claim": the error of
+# the attention output after the output projection W_O splits exactly into a
+# key-induced term (the quantised keys move the attention distribution, the
+# change weighted by the exact values) and a value-induced term (the value
+# errors weighted by the quantised-key distribution):
+#     y  = (sum_s p_s v_s) W_O^T,   y~ = (sum_s p~_s v~_s) W_O^T
+#     y~ - y = (sum_s (p~_s - p_s) v_s) W_O^T + (sum_s p~_s (v~_s - v_s)) W_O^T
+# with p = softmax(sm_scale q . k_s), p~ = softmax(sm_scale q . k~_s).
+def dequantized_kv(cache, block_table, b, n, h, num_kv_heads, group, mu, rot_k, rot_v):
+    """Keys and values of KV head h, positions [0, n) of sequence b, as the
+    INT2 cache represents them in the original basis: k~ = k_hat R_K^T + mu,
+    v~ = v_hat R_V^T (the inverse of the append's centring and rotations)."""
+    tok = read_tokens(cache, block_table, b, np.arange(n), h, num_kv_heads, group)
+    k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
+    v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
+    Rk = np.asarray(rot_k[h], np.float64)
+    Rv = np.asarray(rot_v[h], np.float64)
+    return k_hat @ Rk.T + np.asarray(mu[h], np.float64), v_hat @ Rv.T
+
+
+def _softmax_weights(q, keys, sm_scale):
+    logits = np.float64(sm_scale) * (np.asarray(keys, np.float64) @ np.asarray(q, np.float64))
+    p = np.exp(logits - logits.max())
+    return p / p.sum()
+
+
+def eq8_decomposition(q, k, v, k_tilde, v_tilde, w_o, sm_scale: float):
+    """Post-W_O error of one query's attention over N tokens and its two terms.
+
+    q [d]; k, v [N][d] exact keys and values; k_tilde, v_tilde [N][d] their
+    quantised versions in the same basis; w_o [D][d] (y = o W_O^T).
+    Returns y, y_tilde, key_term, value_term (each [D]) and e_out = |y~ - y|^2.
+    """
+    p = _softmax_weights(q, k, sm_scale)
+    p_t = _softmax_weights(q, k_tilde, sm_scale)
+    v = np.asarray(v, np.float64)
+    v_t = np.asarray(v_tilde, np.float64)
+    w_o = np.asarray(w_o, np.float64)
+    y = (p @ v) @ w_o.T
+    y_t = (p_t @ v_t) @ w_o.T
+    key_term = ((p_t - p) @ v) @ w_o.T
+    value_term = (p_t @ (v_t - v)) @ w_o.T
+    return {"y": y, "y_tilde": y_t, "key_term": key_term, "value_term": value_term,
+            "e_out": float(np.sum((y_t - y) ** 2))}
 
 
 # --------------------------------------------------------------------------- BF16 windows

@@ -408,6 +408,55 @@ def test_windows_prefill_decode_and_stream(name):
     assert n_el > 0 and near <= max(EXEMPT_FRACTION * n_el, 1)
 
 
+def test_corrected_rotations_and_eq8_decomposition():
+    """Rotations drawn as R0 exp(A - A^T) (the pages' corrected-rotation
+    parameterisation, "What carries the argument"): append parity (P1-P3) and
+    decode parity (P4); then the Eq. 8 decomposition of the post-W_O error on
+    the GPU's output.  The oracle splits y~ - y, for the cache the GPU wrote,
+    into the key- and value-induced terms (exact to round-off); the GPU's own
+    y~ must match the oracle's y~ within the attention tolerance."""
+    w = scaled(W1, batch=2, ctx_min=600, ctx_max=600, rotation="hadamard_expm")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    out = decode(case, q).cpu().numpy()
+    pairs = [(0, 0), (0, 21), (1, 13), (1, 31)]
+    ref = oracle_decode(case, q, pairs)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  corrected rotations: max rel err {err:.3e}")
+    assert err <= TIGHT
+    near = n = 0
+    for b in range(w.batch):
+        a, c, _ = _append_parity(case, b, 0, 600)
+        near += a
+        n += c
+    assert near <= max(EXEMPT_FRACTION * n, 1)
+
+    rng = np.random.default_rng(31)
+    D = 256  # width of the synthetic output projection of one head
+    w_o = rng.standard_normal((D, w.head_dim)) / math.sqrt(w.head_dim)
+    qh = q.float().cpu().double().numpy()
+    mu = case.mu.cpu().double().numpy()
+    Hg = w.num_q_heads // w.num_kv_heads
+    for (b, hq) in pairs:
+        h = hq // Hg
+        cache, table = host_pages(case, b, 600)
+        kt, vt = O.dequantized_kv(cache, table, 0, 600, h, w.num_kv_heads, w.group, mu,
+                                  case.st.rot_k[0], case.st.rot_v[0])
+        k, v = kv_for_sequence(w, case.st, 0, b, 0, 600, case.device)
+        k = k[:, h].cpu().double().numpy()
+        v = v[:, h].cpu().double().numpy()
+        r = O.eq8_decomposition(qh[b, hq], k, v, kt, vt, w_o, case.sm_scale)
+        y_gpu = out[b, hq].astype(np.float64) @ w_o.T
+        dy = r["y_tilde"] - r["y"]
+        assert np.abs(r["key_term"] + r["value_term"] - dy).max() <= 1e-12 * np.abs(dy).max()
+        rel = np.abs(y_gpu - r["y_tilde"]).max() / np.abs(r["y_tilde"]).max()
+        assert rel <= TIGHT
+        kn, vn = np.sum(r["key_term"] ** 2), np.sum(r["value_term"] ** 2)
+        say(f"  eq8 (b={b}, hq={hq}): E_out {r['e_out']:.3e}, |key term|^2 {kn:.3e}, "
+            f"|value term|^2 {vn:.3e}, GPU y~ rel err {rel:.2e}")
+
+
 FULL = {
     "cfg1_full": (W1, [(0, 0), (3, 31), (2, 17)]),
     "cfg2_full": (W2, [(0, 0), (17, 9), (63, 31), (40, 4)]),

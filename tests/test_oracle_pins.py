@@ -20,7 +20,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from workload import haar_orthogonal, hadamard
+from workload import EXPM_SCALE, WORKLOADS, corrected_rotation, haar_orthogonal, hadamard, \
+    make_static, scaled
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -485,3 +486,112 @@ def test_windowed_stream_keeps_windows_and_encodes_evicted_tokens_like_bulk():
         b = O.read_tokens(bulk, table, 0, body, h, Hkv, group)
         for key in a:
             assert np.array_equal(a[key], b[key]), key
+
+
+# ----------------------------------------------------------------- corrected rotations R0 exp(A - A^T)
+def test_corrected_rotation_of_a_single_plane_is_a_givens_rotation():
+    """A = theta e_i e_j^T: exp(A - A^T) turns the (i, j) plane by theta
+    (closed form cos/sin) and leaves every other axis fixed; A = 0 gives R0."""
+    d = 16
+    for (i, j, theta) in [(0, 1, 0.3), (5, 2, -1.1), (3, 15, 2.5)]:
+        a = np.zeros((d, d))
+        a[i, j] = theta
+        r = corrected_rotation(np.eye(d), a)
+        want = np.eye(d)
+        want[i, i] = want[j, j] = math.cos(theta)
+        want[i, j] = math.sin(theta)
+        want[j, i] = -math.sin(theta)
+        assert np.allclose(r, want, rtol=0, atol=1e-14)
+    r0 = hadamard(d) / 4.0
+    assert np.array_equal(corrected_rotation(r0, np.zeros((d, d))), r0)
+
+
+def test_corrected_rotations_are_orthogonal_with_unit_determinant():
+    rng = np.random.default_rng(21)
+    r0 = hadamard(128) / math.sqrt(128)
+    for scale in (EXPM_SCALE, 0.3):
+        a = scale * rng.standard_normal((128, 128))
+        e = corrected_rotation(np.eye(128), a)
+        assert np.abs(e.T @ e - np.eye(128)).max() < 1e-12
+        assert abs(np.linalg.det(e) - 1.0) < 1e-9          # exp(trace S) = 1
+        r = corrected_rotation(r0, a)
+        assert np.abs(r.T @ r - np.eye(128)).max() < 1e-12
+    # the workload's corrected rotations, stored float32, stay orthogonal and
+    # near their Hadamard base
+    w = scaled(WORKLOADS["qwen3_8b_b4_ctx8k"], rotation="hadamard_expm", batch=1, ctx_min=16,
+               ctx_max=16)
+    st = make_static(w)
+    for rk in (st.rot_k[0, 0], st.rot_v[0, 0]):
+        rk = rk.astype(np.float64)
+        assert np.abs(rk.T @ rk - np.eye(128)).max() < 1e-5
+        dist = np.abs(rk - r0).max()
+        assert 1e-4 < dist < 0.1
+
+
+# ----------------------------------------------------------------- Eq. 8 error decomposition
+def test_eq8_hand_example():
+    """d = 1, two tokens: p = (1/2, 1/2) from equal keys; the quantised keys
+    give logits (ln 3, 0), so p~ = (3/4, 1/4); v = (1, 3), v~ = (1, 2),
+    W_O = [2].  y = 4, y~ = 2.5; key term ((1/4) 1 - (1/4) 3) 2 = -1; value
+    term (3/4 * 0 + 1/4 * (-1)) 2 = -1/2; the two add to y~ - y = -3/2."""
+    r = O.eq8_decomposition(np.array([1.0]), np.array([[0.0], [0.0]]), np.array([[1.0], [3.0]]),
+                            np.array([[math.log(3.0)], [0.0]]), np.array([[1.0], [2.0]]),
+                            np.array([[2.0]]), 1.0)
+    assert math.isclose(r["y"][0], 4.0, rel_tol=1e-15)
+    assert math.isclose(r["y_tilde"][0], 2.5, rel_tol=1e-15)
+    assert math.isclose(r["key_term"][0], -1.0, rel_tol=1e-14)
+    assert math.isclose(r["value_term"][0], -0.5, rel_tol=1e-14)
+    assert math.isclose(r["e_out"], 2.25, rel_tol=1e-14)
+
+
+def test_eq8_terms_add_up_and_vanish_in_the_special_cases():
+    rng = np.random.default_rng(22)
+    n, d, D = 40, 128, 96
+    q = rng.standard_normal(d)
+    k = 3 * rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    kt = k + 0.2 * rng.standard_normal((n, d))
+    vt = v + 0.2 * rng.standard_normal((n, d))
+    w_o = rng.standard_normal((D, d)) / math.sqrt(d)
+    sm = 1 / math.sqrt(d)
+    r = O.eq8_decomposition(q, k, v, kt, vt, w_o, sm)
+    dy = r["y_tilde"] - r["y"]
+    assert np.abs(r["key_term"] + r["value_term"] - dy).max() <= 1e-13 * np.abs(dy).max()
+    assert r["e_out"] > 0
+    # exact keys: the key-induced term is zero; exact values: the value-induced one
+    r = O.eq8_decomposition(q, k, v, k, vt, w_o, sm)
+    assert not r["key_term"].any()
+    assert np.allclose(r["value_term"], r["y_tilde"] - r["y"], rtol=0, atol=1e-13)
+    r = O.eq8_decomposition(q, k, v, kt, v, w_o, sm)
+    assert not r["value_term"].any()
+    # one token: p = p~ = 1, so only the value error remains
+    r = O.eq8_decomposition(q, k[:1], v[:1], kt[:1], vt[:1], w_o, sm)
+    assert not r["key_term"].any()
+    assert np.allclose(r["y_tilde"] - r["y"], (vt[0] - v[0]) @ w_o.T, rtol=0, atol=1e-13)
+    # adding one vector to every quantised key (the key mean) changes nothing
+    r2 = O.eq8_decomposition(q, k, v, kt + 5.0 * rng.standard_normal(d), vt, w_o, sm)
+    r1 = O.eq8_decomposition(q, k, v, kt, vt, w_o, sm)
+    assert np.allclose(r2["key_term"], r1["key_term"], rtol=1e-9, atol=1e-12)
+
+
+def test_dequantized_kv_inverts_centring_and_rotations_exactly_on_grid():
+    """Keys k = x P^T + mu and values v = y P'^T with x, y on dyadic grids and
+    P, P' signed permutations: the cache represents them exactly, so the
+    original-basis keys and values read back are k and v themselves."""
+    rng = np.random.default_rng(23)
+    for group in (64, 128):
+        R_k, _, _ = _signed_perm(rng, 128)
+        R_v, _, _ = _signed_perm(rng, 128)
+        mu = rng.integers(-64, 64, size=128) / 8.0
+        n = 5
+        x = np.stack([np.concatenate([_grid_group(rng, group, 0.25, -0.5)[1]
+                                      for _ in range(128 // group)]) for _ in range(n)])
+        y = np.stack([np.concatenate([_grid_group(rng, group, 0.5, -1.0)[1]
+                                      for _ in range(128 // group)]) for _ in range(n)])
+        k = x @ R_k.T + mu
+        v = y @ R_v.T
+        cache, table = _one_layer(rng, 1, group, R_k, R_v)
+        O.append(cache, table, [0], k[None, :, None], v[None, :, None], mu[None], R_k[None],
+                 R_v[None], group, 1.0, 1.0)
+        kt, vt = O.dequantized_kv(cache, table, 0, n, 0, 1, group, mu[None], R_k[None], R_v[None])
+        assert np.array_equal(kt, k) and np.array_equal(vt, v)

@@ -6,9 +6,11 @@ quantisation or attention); both the float64 oracle and the HIP path consume
 what it produces.
 """
 from .gen import (  # noqa: F401
+    EXPM_SCALE,
     WORKLOADS,
     Workload,
     block_table_for,
+    corrected_rotation,
     ctx_lens_for,
     haar_orthogonal,
     hadamard,

@@ -4,9 +4,12 @@ Recipe (inputs only; nothing here centres, rotates, quantises or attends):
 
 * Rotations: a Haar-random orthogonal matrix (QR of a Gaussian, columns
   sign-fixed by the diagonal of R) or, for the Qwen3-8B-shaped workloads, the
-  normalised Sylvester Hadamard matrix times a Haar matrix.  Drawn in float64,
-  stored as float32.  Key and value rotations are drawn separately per
-  (layer, KV head).
+  normalised Sylvester Hadamard matrix times a Haar matrix; or, in the pages'
+  parameterisation of a corrected rotation, R0 exp(A - A^T) with R0 the
+  normalised Hadamard matrix and A a seeded Gaussian matrix (entries
+  N(0, 0.01^2); the calibration that would fit A is out of scope).  Drawn in
+  float64, stored as float32.  Key and value rotations are drawn separately
+  per (layer, KV head).
 * Keys and values: N(0, 1) per element; the same 4 seeded channels per
   (layer, KV head) are multiplied by 20 in both K and V; keys then get a
   per-channel offset drawn once from N(0, sigma) (sigma 3, or 5 for the
@@ -112,11 +115,29 @@ def haar_orthogonal(rng: np.random.Generator, d: int) -> np.ndarray:
     return q * np.sign(np.diag(r))[None, :]
 
 
+# Standard deviation of the entries of the generator A of a corrected rotation.
+EXPM_SCALE = 0.01
+
+
+def corrected_rotation(r0: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """R0 exp(A - A^T): a base rotation times the exponential of a
+    skew-symmetric generator ("Output-Aware Rotation for INT2 KV-Cache
+    Quantization", "What carries the argument", mechanism 1; "Assumptions &
+    free parameters": the exponential of a skew-symmetric matrix is
+    orthogonal).  Float64, scipy's matrix exponential."""
+    from scipy.linalg import expm
+    a = np.asarray(a, np.float64)
+    return np.asarray(r0, np.float64) @ expm(a - a.T)
+
+
 def _rotation(rng: np.random.Generator, d: int, kind: str) -> np.ndarray:
     if kind == "haar":
         return haar_orthogonal(rng, d)
     if kind == "hadamard_haar":
         return (hadamard(d) / math.sqrt(d)) @ haar_orthogonal(rng, d)
+    if kind == "hadamard_expm":
+        return corrected_rotation(hadamard(d) / math.sqrt(d),
+                                  EXPM_SCALE * rng.standard_normal((d, d)))
     if kind == "identity":
         return np.eye(d)
     raise ValueError(kind)
