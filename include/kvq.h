@@ -99,7 +99,12 @@ size_t kvq_page_bytes(int32_t head_dim, int32_t group);
  *                          start_pos[b] + num_new - 1 (block pos/16, slot pos%16)
  *   k, v           device  [batch][num_new][num_kv_heads][head_dim] of kv_dtype
  *   mu             device  float32 [num_kv_heads][head_dim] key mean
- *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]
+ *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]; rot_v
+ *                          may be NULL: the value rotation is folded into the
+ *                          caller's W_V and W_O (the OptR review page, "If this
+ *                          is right": value-side rotations are folded into the
+ *                          projection weights), so v arrives already rotated and
+ *                          is encoded as given (y = v)
  *   clip_k, clip_v host    clipping ratios in (0, 1]
  * Only the written tokens' codes, scales and zeros change; other tokens in the
  * same pages keep their contents.  Two sequences must not share a physical
@@ -137,7 +142,10 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *   ctx_len        device  int32 [batch], each in [0, max_ctx_len]
  *   max_ctx_len    host    upper bound of ctx_len; <= 16 * max_blocks_per_seq
  *   q              device  [batch][num_q_heads][head_dim] of q_dtype
- *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]
+ *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]; rot_v
+ *                          may be NULL (value rotation folded into W_V and W_O):
+ *                          out is then sum_t p_t v_hat_t, left in the rotated
+ *                          value basis for the caller's folded W_O
  *   sm_scale       host    softmax scale (1/sqrt(head_dim) for standard attention)
  *   out            device  float32 [batch][num_q_heads][head_dim] (written)
  *   workspace      device  at least kvq_decode_workspace_bytes(...) bytes,

@@ -57,7 +57,7 @@ __all__ = [
     "sz_site", "write_tokens", "read_tokens", "dequant", "attend", "decode",
     "append", "plain_attention", "SINK", "RECENT", "WINDOW", "window_slot", "window_parts",
     "bf16_round", "window_write", "append_windowed", "decode_windowed", "dequantized_kv",
-    "eq8_decomposition",
+    "eq8_decomposition", "value_rotation",
 ]
 
 
@@ -137,15 +137,26 @@ def quantize_on_grid(x, s16, z16, group: int):
     return codes.reshape(x.shape)
 
 
+def value_rotation(rot_v, h, d: int = HEAD_DIM):
+    """R_V of KV head h as float64; rot_v None is the folded form ([OptR]
+    "If this is right": the value rotations are folded into W_V and W_O), where
+    the values arrive already rotated and the output stays in that basis, i.e.
+    the identity here."""
+    if rot_v is None:
+        return np.eye(d)
+    return np.asarray(rot_v[h], np.float64)
+
+
 def encode_tokens(k, v, mu, rot_k, rot_v, group: int, clip_k: float, clip_v: float):
     """Centre, rotate and quantise new tokens.
 
-    k, v: [..., Hkv, d]; mu: [Hkv, d]; rot_k, rot_v: [Hkv, d, d].
+    k, v: [..., Hkv, d]; mu: [Hkv, d]; rot_k, rot_v: [Hkv, d, d] (rot_v None:
+    values folded, encoded as given).
     Key centring subtracts mu before rotation ([OptR] "What carries the
     argument", mechanism 2); values are not centred.
     """
     x = rotate(np.asarray(k, np.float64) - np.asarray(mu, np.float64), rot_k)
-    y = rotate(v, rot_v)
+    y = np.asarray(v, np.float64) if rot_v is None else rotate(v, rot_v)
     ks, kz, kc, ks_raw, kz_raw = encode_groups(x, group, clip_k)
     vs, vz, vc, vs_raw, vz_raw = encode_groups(y, group, clip_v)
     return dict(x=x, y=y, k_s=ks, k_z=kz, k_codes=kc, v_s=vs, v_z=vz, v_codes=vc,
@@ -296,7 +307,7 @@ def decode(cache, block_table, ctx_len, q, rot_k, rot_v, sm_scale: float, num_kv
             k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
             v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
             Rk = np.asarray(rot_k[h], np.float64)
-            Rv = np.asarray(rot_v[h], np.float64)
+            Rv = value_rotation(rot_v, h, d)
             for hq in heads:
                 q_r = q[b, hq] @ Rk
                 o_r = attend(q_r, k_hat, v_hat, sm_scale)
@@ -321,7 +332,7 @@ def dequantized_kv(cache, block_table, b, n, h, num_kv_heads, group, mu, rot_k, 
     k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
     v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
     Rk = np.asarray(rot_k[h], np.float64)
-    Rv = np.asarray(rot_v[h], np.float64)
+    Rv = value_rotation(rot_v, h)
     return k_hat @ Rk.T + np.asarray(mu[h], np.float64), v_hat @ Rv.T
 
 
@@ -452,7 +463,7 @@ def decode_windowed(cache, block_table, ctx_len, q, rot_k, rot_v, mu, win_k, win
             k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
             v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
             Rk = np.asarray(rot_k[h], np.float64)
-            Rv = np.asarray(rot_v[h], np.float64)
+            Rv = value_rotation(rot_v, h)
             for hq in heads:
                 if len(wpos) + len(bpos) == 0:
                     out[b, hq] = 0.0

@@ -5,6 +5,9 @@ in include/kvq.h; this module turns torch tensors into device pointers and
 shapes into integers, and raises on a non-zero status.  torch is imported
 first so that libkvq binds to the HIP runtime torch already loaded (both are
 libamdhip64.so.7): device pointers and streams are then shared.
+
+rot_v=None selects the folded form: the value rotation lives in the caller's
+W_V and W_O, values are encoded as given and outputs stay in that basis.
 """
 from __future__ import annotations
 
@@ -105,7 +108,7 @@ def _check(status: int, where: str) -> None:
 
 def append(pages: torch.Tensor, block_table: torch.Tensor, start_pos: torch.Tensor,
            k: torch.Tensor, v: torch.Tensor, mu: torch.Tensor, rot_k: torch.Tensor,
-           rot_v: torch.Tensor, group: int, clip_k: float, clip_v: float, stream=None) -> None:
+           rot_v: torch.Tensor | None, group: int, clip_k: float, clip_v: float, stream=None) -> None:
     """kvq_append: pages uint8 [num_blocks][Hkv][page_bytes]; k, v [B][T][Hkv][128]."""
     num_blocks, hkv, _ = pages.shape
     B, T = k.shape[0], k.shape[1]
@@ -124,7 +127,7 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_
 
 
 def decode(pages: torch.Tensor, block_table: torch.Tensor, ctx_len: torch.Tensor,
-           max_ctx_len: int, q: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor,
+           max_ctx_len: int, q: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor | None,
            group: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, split_pages: int = 0,
            stages: int = STAGE_ALL, stream=None) -> torch.Tensor:
@@ -154,7 +157,7 @@ def decode(pages: torch.Tensor, block_table: torch.Tensor, ctx_len: torch.Tensor
 
 def append_decode(pages: torch.Tensor, block_table: torch.Tensor, start_pos: torch.Tensor,
                   ctx_len: torch.Tensor, max_ctx_len: int, k: torch.Tensor, v: torch.Tensor,
-                  mu: torch.Tensor, q: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor,
+                  mu: torch.Tensor, q: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor | None,
                   group: int, clip_k: float, clip_v: float, sm_scale: float | None = None,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                   split_pages: int = 0, stream=None) -> torch.Tensor:
@@ -207,7 +210,7 @@ def window_write(window: torch.Tensor, start_pos: torch.Tensor, k: torch.Tensor,
 
 def decode_window(pages: torch.Tensor, block_table: torch.Tensor, window: torch.Tensor,
                   mu: torch.Tensor, ctx_len: torch.Tensor, max_ctx_len: int, q: torch.Tensor,
-                  rot_k: torch.Tensor, rot_v: torch.Tensor, group: int,
+                  rot_k: torch.Tensor, rot_v: torch.Tensor | None, group: int,
                   sm_scale: float | None = None, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, split_pages: int = 0,
                   stream=None) -> torch.Tensor:
@@ -234,7 +237,7 @@ def decode_window(pages: torch.Tensor, block_table: torch.Tensor, window: torch.
 def append_decode_window(pages: torch.Tensor, block_table: torch.Tensor, window: torch.Tensor,
                          start_pos: torch.Tensor, ctx_len: torch.Tensor, max_ctx_len: int,
                          k: torch.Tensor, v: torch.Tensor, mu: torch.Tensor, q: torch.Tensor,
-                         rot_k: torch.Tensor, rot_v: torch.Tensor, group: int, clip_k: float,
+                         rot_k: torch.Tensor, rot_v: torch.Tensor | None, group: int, clip_k: float,
                          clip_v: float, sm_scale: float | None = None,
                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                          split_pages: int = 0, stream=None) -> torch.Tensor:

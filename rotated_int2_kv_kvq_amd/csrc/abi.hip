@@ -49,10 +49,11 @@ int check_append(const void* pages, int64_t num_blocks, int32_t num_kv_heads, in
   if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
     return KVQ_ERR_INVALID_ARG;
   if (batch == 0 || num_new == 0) return KVQ_OK;
-  if (!pages || !block_table || !start_pos || !k || !v || !mu || !rot_k || !rot_v)
+  // rot_v may be null: the value rotation is folded into the caller's weights
+  if (!pages || !block_table || !start_pos || !k || !v || !mu || !rot_k)
     return KVQ_ERR_INVALID_ARG;
   if (!aligned(pages, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(mu, 16) ||
-      !aligned(rot_k, 16) || !aligned(rot_v, 16))
+      !aligned(rot_k, 16) || (rot_v && !aligned(rot_v, 16)))
     return KVQ_ERR_INVALID_ARG;
   return KVQ_OK;
 }
@@ -114,9 +115,10 @@ int check_decode(const void* pages, int64_t num_blocks, int32_t num_kv_heads, in
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KVQ_ERR_INVALID_ARG;
   if (batch == 0) return KVQ_OK;
-  if (!pages || !block_table || !ctx_len || !q || !rot_k || !rot_v || !out)
+  // rot_v may be null: the output stays in the rotated value basis
+  if (!pages || !block_table || !ctx_len || !q || !rot_k || !out)
     return KVQ_ERR_INVALID_ARG;
-  if (!aligned(pages, 16) || !aligned(rot_k, 16) || !aligned(rot_v, 16))
+  if (!aligned(pages, 16) || !aligned(rot_k, 16) || (rot_v && !aligned(rot_v, 16)))
     return KVQ_ERR_INVALID_ARG;
   *plan = kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
   if (!workspace || workspace_bytes < plan->total || !aligned(workspace, 256))

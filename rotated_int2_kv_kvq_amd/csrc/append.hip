@@ -95,9 +95,12 @@ __global__ __launch_bounds__(512) void append_kernel(
   if (wg_first > last_page) return;
   const int wg_last = min(last_page, wg_first + pages_per_wg - 1);
 
+  // rot_v null: the value rotation is folded into the caller's weights and
+  // values are encoded as given (no products for them).
+  const bool v_ident = rot_v == nullptr;
   // Stage R_K and R_V: LDS row r = 16*(c%8) + c/8 holds column c of R, so the
   // MFMA output column (tile nt, lane n) is rotated channel 8*n + nt.
-  for (int mat = 0; mat < 2; ++mat) {
+  for (int mat = 0; mat < (v_ident ? 1 : 2); ++mat) {
     const float* R = (mat ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim;
     for (int idx = tid; idx < kHeadDim * kHeadDim / 4; idx += 512) {
       const int krow = idx >> 5;
@@ -140,9 +143,10 @@ __global__ __launch_bounds__(512) void append_kernel(
   }
   // Token row t of page pg (input channels 32kg..32kg+31) if that token is
   // one this call writes; false (nothing loaded) otherwise.
+  const bool direct = mat == 1 && v_ident;  // values read in the output layout below
   auto fetch = [&](int pg, RawRow<kBf16>& r) {
     const int pos = pg * kBlock + t;
-    const bool row_new = pg <= wg_last && pos >= s0 && pos < s0 + T;
+    const bool row_new = !direct && pg <= wg_last && pos >= s0 && pos < s0 + T;
     if (row_new)
       load_raw32<kBf16>(src,
                         (static_cast<size_t>(b) * T + (pos - s0)) * Hkv * kHeadDim +
@@ -172,17 +176,46 @@ __global__ __launch_bounds__(512) void append_kernel(
     floatx4 acc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const float* Bm = Bt[mat];
+    if (direct) {
+      // lane holds tokens 4*r4 + i, channels 8n..8n+7 of the value as given
 #pragma unroll
-    for (int sb = 0; sb < 8; ++sb) {
+      for (int i = 0; i < 4; ++i) {
+        const int tpos = pg * kBlock + 4 * r4 + i;
+        if (tpos >= s0 && tpos < s0 + T) {
+          const size_t off = (static_cast<size_t>(b) * T + (tpos - s0)) * Hkv * kHeadDim +
+                             static_cast<size_t>(h) * kHeadDim + 8 * n;
+          float x8[8];
+          if constexpr (kBf16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const float4 bv =
-            *reinterpret_cast<const float4*>(Bm + (nt * 16 + n) * kRStride + 32 * kg + 4 * sb);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 0], bv.x, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 1], bv.y, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 2], bv.z, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 3], bv.w, acc[nt], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              x8[2 * e] = __uint_as_float(w[e] << 16);
+              x8[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+          } else {
+            const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
+            const float4 f0 = f[0], f1 = f[1];
+            x8[0] = f0.x; x8[1] = f0.y; x8[2] = f0.z; x8[3] = f0.w;
+            x8[4] = f1.x; x8[5] = f1.y; x8[6] = f1.z; x8[7] = f1.w;
+          }
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) acc[nt][i] = x8[nt];
+        }
+      }
+    } else {
+      const float* Bm = Bt[mat];
+#pragma unroll
+      for (int sb = 0; sb < 8; ++sb) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const float4 bv =
+              *reinterpret_cast<const float4*>(Bm + (nt * 16 + n) * kRStride + 32 * kg + 4 * sb);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 0], bv.x, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 1], bv.y, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 2], bv.z, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * sb + 3], bv.w, acc[nt], 0, 0, 0);
+        }
       }
     }
 

@@ -41,13 +41,18 @@ __device__ __forceinline__ void append_one_body(
 
   // split-K partial products: thread -> (mat, quarter kq, column jc).  The
   // rotation loads go out first: nothing they need depends on another load.
+  // rot_v null (value rotation folded into the caller's weights): the value
+  // is encoded as given.
   {
     const int pm = tid >> 9, kq = (tid >> 7) & 3, jc = tid & 127;
-    const float* R = (pm ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim +
-                     32 * kq * kHeadDim + jc;
+    const bool ident = pm == 1 && rot_v == nullptr;
     float rcol[32];
+    if (!ident) {
+      const float* R = (pm ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim +
+                       32 * kq * kHeadDim + jc;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) rcol[i] = R[i * kHeadDim];
+      for (int i = 0; i < 32; ++i) rcol[i] = R[i * kHeadDim];
+    }
     if (kq == 0) {
       float x;
       if constexpr (kBf16)
@@ -59,16 +64,20 @@ __device__ __forceinline__ void append_one_body(
       a_s[pm][jc] = x;
     }
     __syncthreads();
-    const float* a = a_s[pm] + 32 * kq;
-    float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+    if (ident) {
+      part[pm][kq][jc] = kq == 0 ? a_s[pm][jc] : 0.f;
+    } else {
+      const float* a = a_s[pm] + 32 * kq;
+      float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; i += 4) {
-      x0 = fmaf(a[i], rcol[i], x0);
-      x1 = fmaf(a[i + 1], rcol[i + 1], x1);
-      x2 = fmaf(a[i + 2], rcol[i + 2], x2);
-      x3 = fmaf(a[i + 3], rcol[i + 3], x3);
+      for (int i = 0; i < 32; i += 4) {
+        x0 = fmaf(a[i], rcol[i], x0);
+        x1 = fmaf(a[i + 1], rcol[i + 1], x1);
+        x2 = fmaf(a[i + 2], rcol[i + 2], x2);
+        x3 = fmaf(a[i + 3], rcol[i + 3], x3);
+      }
+      part[pm][kq][jc] = (x0 + x1) + (x2 + x3);
     }
-    part[pm][kq][jc] = (x0 + x1) + (x2 + x3);
   }
   // destination page (a position outside the table, or a block id outside
   // the cache, writes nothing)

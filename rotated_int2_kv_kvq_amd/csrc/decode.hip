@@ -1245,11 +1245,16 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   const int tid = threadIdx.x;
   const int j = tid >> 3, part8 = tid & 7;
   // input channels 4 part + 32 i4 + (0..3): eight lanes read 128 contiguous bytes
-  const float4* R = reinterpret_cast<const float4*>(
-      rot_v + (static_cast<size_t>(h) * kHeadDim + j) * kHeadDim + 4 * part8);
-  float4 rr[4];
+  // rot_v null: the value rotation is folded into the caller's weights and
+  // the output stays in the rotated basis
+  const bool rotate_out = rot_v != nullptr;
+  float4 rr[4] = {};
+  if (rotate_out) {
+    const float4* R = reinterpret_cast<const float4*>(
+        rot_v + (static_cast<size_t>(h) * kHeadDim + j) * kHeadDim + 4 * part8);
 #pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) rr[i4] = R[8 * i4];
+    for (int i4 = 0; i4 < 4; ++i4) rr[i4] = R[8 * i4];
+  }
   const int u = tid >> 8, half = (tid >> 7) & 1, c = tid & 127, lane = tid & 63;
   const size_t row0 = static_cast<size_t>(b) * Hq + h * Hg + qg * kHT;
   const float* p = part + (row0 + min(u, nh - 1)) * S * kPartStride;
@@ -1318,6 +1323,15 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   }
   __syncthreads();
 
+  if (!rotate_out) {
+    // thread (j, part) with part = head < nh writes channel j of that head
+    if (part8 < nh) {
+      const size_t row = row0 + part8;
+      out[row * kHeadDim + j] =
+          fmaf(hwin[part8], wv, (osum[0][part8][j] + osum[1][part8][j]) * hinv[part8]);
+    }
+    return;
+  }
   // o * R_V^T: thread (j, part) over input channels 4 part + 32 i4 + (0..3)
   // for the four heads, then a sum over the eight parts (eight adjacent lanes)
   float o[kHT] = {0.f, 0.f, 0.f, 0.f};

@@ -9,7 +9,12 @@ P1  fp16 scale/zero: equal bit for bit, except groups whose float64 value
 P2  codes: equal to the oracle's codes of the float64 rotated value on the
     GPU's own stored grid, except elements whose float64 value lies within
     1e-6 * max(|b|, s16) of a code boundary b = z16 + (j + 1/2) s16; the
-    exempt count must be <= 1e-5 of all elements.
+    exempt count must be <= 1e-5 of all elements.  Values encoded as given
+    (the value rotation folded into the caller's weights) keep the 8
+    significant bits of bfloat16, so many of them sit exactly on a boundary
+    of the fp16 grid, where both codes are correct: there the exempt count is
+    a property of the input and is only reported, and the exempt elements
+    whose code differs must be <= 1e-5 of all elements instead.
 P3  bytes: the cache is read back through the oracle's layout functions; bytes
     of slots that were not written keep their previous contents.
 P4  attention: the oracle decodes the GPU's own cache in float64; the max over
@@ -49,8 +54,9 @@ def check_scale_zero(gpu_s, gpu_z, ref_s, ref_z, raw_s, raw_z):
     return int(bad.sum()), int(boundary.sum())
 
 
-def check_codes(gpu_codes, x, gpu_s, gpu_z, group):
-    """P2.  Returns (mismatches outside exemptions, exempt elements, elements)."""
+def check_codes(gpu_codes, x, gpu_s, gpu_z, group, with_exempt_mismatches=False):
+    """P2.  Returns (mismatches outside exemptions, exempt elements, elements)
+    and, with with_exempt_mismatches, the exempt elements whose code differs."""
     ref = O.quantize_on_grid(x, gpu_s, gpu_z, group)
     d = x.shape[-1]
     G = d // group
@@ -63,7 +69,10 @@ def check_codes(gpu_codes, x, gpu_s, gpu_z, group):
         near |= (np.abs(xg - bnd) <= REL * np.maximum(np.abs(bnd), s)) & (s > 0)
     near = near.reshape(x.shape)
     mismatch = np.asarray(gpu_codes) != ref
-    return int((mismatch & ~near).sum()), int(near.sum()), int(mismatch.size)
+    res = (int((mismatch & ~near).sum()), int(near.sum()), int(mismatch.size))
+    if with_exempt_mismatches:
+        return res + (int((mismatch & near).sum()),)
+    return res
 
 
 def attention_error(o_gpu, o_ref):

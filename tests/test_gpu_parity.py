@@ -55,7 +55,14 @@ SMALL = {
     "cfg2_b6_ragged_g64": scaled(W2, batch=6, ctx_min=1, ctx_max=700),
     "cfg3_ctx3000_sinks": scaled(W3, ctx_min=3000, ctx_max=3000),
     "cfg4_b3_layer5": scaled(W4, batch=3, ctx_min=333, ctx_max=333, layers=6, steps=4),
+    # value rotation folded into W_V / W_O (rot_v passed as None)
+    "cfg1_b3_ctx700_folded": scaled(W1, batch=3, ctx_min=700, ctx_max=700),
+    "cfg0_g64_folded": scaled(W0, group=64),
 }
+
+
+def _folded(name: str) -> bool:
+    return name.endswith("_folded")
 
 
 def _append_parity(case, b, start, count):
@@ -71,10 +78,13 @@ def _append_parity(case, b, start, count):
                                            enc[kind + "_z"][:, h], enc[kind + "_s_raw"][:, h],
                                            enc[kind + "_z_raw"][:, h])
             assert bad_sz == 0, f"{kind} scale/zero mismatch outside boundary groups (h={h})"
-            bad, near, n = check_codes(got[kind + "_codes"], enc[xkey][:, h], got[kind + "_s"],
-                                       got[kind + "_z"], w.group)
+            bad, near, n, near_bad = check_codes(got[kind + "_codes"], enc[xkey][:, h],
+                                                 got[kind + "_s"], got[kind + "_z"], w.group,
+                                                 with_exempt_mismatches=True)
             assert bad == 0, f"{kind} code mismatches outside exemptions: {bad} (h={h})"
-            tot_near += near
+            # values encoded as given (folded): exact ties are an input property;
+            # the exempt elements that differ are counted instead (P2)
+            tot_near += near_bad if (case.folded and kind == "v") else near
             tot_n += n
             tot_bnd += bnd
     return tot_near, tot_n, tot_bnd
@@ -113,6 +123,7 @@ def test_append_parity_small(name):
     w = SMALL[name]
     say(f"[append] {name}")
     case = new_case(w)
+    case.folded = _folded(name)
     fill_context(case, pieces=[5, 11, 1, 16, 37, 200, 64, 1000])
     torch.cuda.synchronize()
     near = n = bnd = 0
@@ -133,6 +144,7 @@ def test_decode_parity_small(name):
     w = SMALL[name]
     say(f"[decode] {name}")
     case = new_case(w, keep_initial=False)
+    case.folded = _folded(name)
     fill_context(case)
     q = query(case)
     out = decode(case, q).cpu().numpy()
@@ -247,6 +259,7 @@ def test_stream_append_then_decode():
 STEP_CASES = {
     "cfg4_b3_layer5": SMALL["cfg4_b3_layer5"],
     "cfg2_b5_ragged_g64": scaled(W2, batch=5, ctx_min=1, ctx_max=300, steps=3),
+    "cfg4_b3_layer5_folded": SMALL["cfg4_b3_layer5"],
 }
 
 
@@ -260,6 +273,7 @@ def test_append_decode_step(name):
     layer = min(1, w.layers - 1)
     a = new_case(w, layer=layer, keep_initial=False)
     b = new_case(w, layer=layer, keep_initial=False)
+    a.folded = b.folded = _folded(name)
     fill_context(a)
     fill_context(b)
     ctx = a.ctx.copy()
@@ -269,14 +283,14 @@ def test_append_decode_step(name):
         k = torch.stack([x[0] for x in kv]).contiguous()
         v = torch.stack([x[1] for x in kv]).contiguous()
         sp = torch.from_numpy(ctx.astype(np.int32)).to(dev)
-        kvq.append(a.pages, a.table, sp, k, v, a.mu, a.rot_k, a.rot_v, w.group, w.clip_k,
+        kvq.append(a.pages, a.table, sp, k, v, a.mu, a.rot_k, a.rv, w.group, w.clip_k,
                    w.clip_v)
         ctx = ctx + 1
         q = query(a, step)
         out_a = decode(a, q, ctx=ctx)
         ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
         out_b = kvq.append_decode(b.pages, b.table, sp, ctx_t, int(ctx.max()), k, v, b.mu, q,
-                                  b.rot_k, b.rot_v, w.group, w.clip_k, w.clip_v, b.sm_scale)
+                                  b.rot_k, b.rv, w.group, w.clip_k, w.clip_v, b.sm_scale)
         torch.cuda.synchronize()
         assert torch.equal(a.pages, b.pages), step
         assert torch.equal(out_a, out_b), step
@@ -297,6 +311,8 @@ WIN_CASES = {
                   [5, 63, 300, 317, 600]),
     "f32_g64_h8x2": (scaled(W0, batch=3, ctx_min=700, ctx_max=700, group=64, steps=5),
                      [0, 318, 700]),
+    "bf16_g128_folded": (scaled(W4, batch=3, ctx_min=600, ctx_max=600, layers=2, steps=4),
+                         [40, 317, 600]),
 }
 
 
@@ -311,7 +327,7 @@ def _window_ref(case, win, q, ctx, pairs):
         wv = win[b:b + 1, :, 1].float().cpu().double().numpy()
         heads = [hq for (bb, hq) in pairs if bb == b]
         o = O.decode_windowed(cache, table, [n], q[b:b + 1].float().cpu().double().numpy(),
-                              case.st.rot_k[case.layer], case.st.rot_v[case.layer],
+                              case.st.rot_k[case.layer], case.rv_host,
                               case.mu.cpu().double().numpy(), wk, wv, case.sm_scale,
                               w.num_kv_heads, w.group, pairs=[(0, hq) for hq in heads])
         for hq in heads:
@@ -330,6 +346,7 @@ def test_windows_prefill_decode_and_stream(name):
     w, ctx_list = WIN_CASES[name]
     say(f"[window] {name}")
     case = new_case(w, keep_initial=False)
+    case.folded = _folded(name)
     dev = case.device
     B, Hkv = w.batch, w.num_kv_heads
     ctx = np.array(ctx_list, np.int64)
@@ -347,7 +364,7 @@ def test_windows_prefill_decode_and_stream(name):
             kvq.append(case.pages, case.table[b:b + 1].contiguous(), sp_body,
                        k[None, O.SINK:n - O.RECENT].contiguous(),
                        v[None, O.SINK:n - O.RECENT].contiguous(), case.mu, case.rot_k,
-                       case.rot_v, w.group, w.clip_k, w.clip_v)
+                       case.rv, w.group, w.clip_k, w.clip_v)
         # the window holds the BF16 tokens of the sinks and the recent window
         keep = [p for p in range(n) if p < O.SINK or p >= n - O.RECENT]
         slots = torch.as_tensor(O.window_slot(np.array(keep)), device=dev)
@@ -358,7 +375,7 @@ def test_windows_prefill_decode_and_stream(name):
     q = query(case, 0)
     ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
     out = kvq.decode_window(case.pages, case.table, win, case.mu, ctx_t, int(ctx.max()), q,
-                            case.rot_k, case.rot_v, w.group, case.sm_scale).cpu().numpy()
+                            case.rot_k, case.rv, w.group, case.sm_scale).cpu().numpy()
     ref = _window_ref(case, win, q, ctx, pairs)
     err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
     say(f"  prefill decode max rel err {err:.3e}")
@@ -373,7 +390,7 @@ def test_windows_prefill_decode_and_stream(name):
         ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
         q = query(case, step + 1)
         out = kvq.append_decode_window(case.pages, case.table, win, sp, ctx_t, int(ctx.max()), k,
-                                       v, case.mu, q, case.rot_k, case.rot_v, w.group, w.clip_k,
+                                       v, case.mu, q, case.rot_k, case.rv, w.group, w.clip_k,
                                        w.clip_v, case.sm_scale).cpu().numpy()
         ref = _window_ref(case, win, q, ctx, pairs)
         err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
@@ -390,7 +407,7 @@ def test_windows_prefill_decode_and_stream(name):
         enc = O.encode_tokens(O.bf16_round(kk.float().cpu().numpy()),
                               O.bf16_round(vv.float().cpu().numpy()),
                               case.mu.cpu().double().numpy(), case.st.rot_k[case.layer],
-                              case.st.rot_v[case.layer], w.group, w.clip_k, w.clip_v)
+                              case.rv_host, w.group, w.clip_k, w.clip_v)
         cache, table = host_pages(case, b, hi)
         for h in range(Hkv):
             got = O.read_tokens(cache, table, 0, np.arange(lo, hi), h, Hkv, w.group)
@@ -400,10 +417,12 @@ def test_windows_prefill_decode_and_stream(name):
                                              enc[kind + "_s_raw"][:, h],
                                              enc[kind + "_z_raw"][:, h])
                 assert bad_sz == 0
-                bad, nr, n = check_codes(got[kind + "_codes"], enc[xkey][:, h],
-                                         got[kind + "_s"], got[kind + "_z"], w.group)
+                bad, nr, n, nr_bad = check_codes(got[kind + "_codes"], enc[xkey][:, h],
+                                                 got[kind + "_s"], got[kind + "_z"], w.group,
+                                                 with_exempt_mismatches=True)
                 assert bad == 0
-                near += nr
+                # the BF16 window copies are encoded as given when folded (P2)
+                near += nr_bad if (case.folded and kind == "v") else nr
                 n_el += n
     assert n_el > 0 and near <= max(EXEMPT_FRACTION * n_el, 1)
 

@@ -595,3 +595,39 @@ def test_dequantized_kv_inverts_centring_and_rotations_exactly_on_grid():
                  R_v[None], group, 1.0, 1.0)
         kt, vt = O.dequantized_kv(cache, table, 0, n, 0, 1, group, mu[None], R_k[None], R_v[None])
         assert np.array_equal(kt, k) and np.array_equal(vt, v)
+
+
+# ----------------------------------------------------------------- value rotation folded into W_V / W_O
+def test_folded_value_rotation_writes_the_same_cache_and_output_through_the_weights():
+    """Folded form (rot_v None): the caller's values are h (W_V R_V) and its
+    output projection W_O R_V.  With R_V a signed permutation the folded
+    append of v R_V writes exactly the bytes the unfolded append of v does;
+    the folded decode is the unfolded one before the inverse rotation, and
+    after the folded output projection both give the same y."""
+    rng = np.random.default_rng(24)
+    d, Hkv, Hq, group, n = 128, 2, 4, 64, 40
+    R_k = np.stack([haar_orthogonal(rng, d) for _ in range(Hkv)])
+    R_v = np.stack([_signed_perm(rng, d)[0] for _ in range(Hkv)])
+    mu = rng.standard_normal((Hkv, d))
+    h_in = rng.standard_normal((1, n, Hkv, 96))
+    w_v = rng.standard_normal((Hkv, 96, d)) / math.sqrt(96)
+    k = 2 * rng.standard_normal((1, n, Hkv, d)) + mu
+    v = np.einsum("btki,kid->btkd", h_in, w_v)                 # h W_V
+    v_fold = np.einsum("btki,kid->btkd", h_in, w_v @ R_v)      # h (W_V R_V)
+    assert np.array_equal(v_fold, np.einsum("btkd,kde->btke", v, R_v))
+    table = np.array([[2, 0, 1]], np.int32)
+    c_unf = np.zeros((3, Hkv, O.page_bytes(d, group)), np.uint8)
+    c_fold = np.zeros_like(c_unf)
+    O.append(c_unf, table, [0], k, v, mu, R_k, R_v, group, 0.9, 0.9)
+    O.append(c_fold, table, [0], k, v_fold, mu, R_k, None, group, 0.9, 0.9)
+    assert np.array_equal(c_unf, c_fold)
+    q = rng.standard_normal((1, Hq, d))
+    o_unf = O.decode(c_unf, table, [n], q, R_k, R_v, 0.1, Hkv, group)
+    o_fold = O.decode(c_fold, table, [n], q, R_k, None, 0.1, Hkv, group)
+    w_o = rng.standard_normal((64, d))
+    for hq in range(Hq):
+        kv = hq // (Hq // Hkv)
+        assert np.array_equal(o_fold[0, hq] @ R_v[kv].T, o_unf[0, hq])
+        y = o_unf[0, hq] @ w_o.T
+        y_fold = o_fold[0, hq] @ (w_o @ R_v[kv]).T
+        assert np.allclose(y_fold, y, rtol=1e-12, atol=1e-12)
