@@ -39,6 +39,27 @@ __device__ __forceinline__ void append_one_body(
   __shared__ float red[4][2];
   const int tid = threadIdx.x;
 
+  // Destination page first (a position outside the table, or a block id
+  // outside the cache, writes nothing): its chain of loads (start position,
+  // block id, the value byte this thread updates) overlaps the rotation's.
+  const int pos = start_pos[b] + pos_delta;
+  int blk = -1;
+  if (pos >= 0 && pos / kBlock < max_blocks)
+    blk = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
+  const bool valid = blk >= 0 && blk < num_blocks;
+  const int PB = page_bytes_for_groups(G);
+  uint8_t* page = pages + (static_cast<int64_t>(valid ? blk : 0) * Hkv + h) * PB;
+  const int t = (pos >= 0 ? pos : 0) % kBlock;
+  const bool own = tid < 256 && valid;  // threads 0-255 own one rotated channel each
+  const int mat = (tid >> 7) & 1;
+  const int j = tid & 127;
+  const int wave = (tid >> 6) & 3;
+  // the value byte this thread will update (only this thread writes it):
+  // word 8*(j % 16) + j / 16, code position 3t mod 16
+  const int u = (3 * t) & 15;
+  uint8_t* vdst = page + kVCodeOff + 4 * (8 * (j & 15) + (j >> 4)) + (u >> 2);
+  const uint32_t vold = (own && mat) ? *vdst : 0u;
+
   // split-K partial products: thread -> (mat, quarter kq, column jc).  The
   // rotation loads go out first: nothing they need depends on another load.
   // rot_v null (value rotation folded into the caller's weights): the value
@@ -79,26 +100,8 @@ __device__ __forceinline__ void append_one_body(
       part[pm][kq][jc] = (x0 + x1) + (x2 + x3);
     }
   }
-  // destination page (a position outside the table, or a block id outside
-  // the cache, writes nothing)
-  const int pos = start_pos[b] + pos_delta;
-  int blk = -1;
-  if (pos >= 0 && pos / kBlock < max_blocks) blk = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
-  const bool valid = blk >= 0 && blk < num_blocks;
-  const int PB = page_bytes_for_groups(G);
-  uint8_t* page = pages + (static_cast<int64_t>(valid ? blk : 0) * Hkv + h) * PB;
-  const int t = (pos >= 0 ? pos : 0) % kBlock;
   __syncthreads();
 
-  const bool own = tid < 256 && valid;  // threads 0-255 own one rotated channel each
-  const int mat = (tid >> 7) & 1;
-  const int j = tid & 127;
-  const int wave = (tid >> 6) & 3;
-  // the value byte this thread will update (read early; only this thread writes
-  // it): word 8*(j % 16) + j / 16, code position 3t mod 16
-  const int u = (3 * t) & 15;
-  uint8_t* vdst = page + kVCodeOff + 4 * (8 * (j & 15) + (j >> 4)) + (u >> 2);
-  const uint32_t vold = (own && mat) ? *vdst : 0u;
   const float x = (part[mat][0][j] + part[mat][1][j]) + (part[mat][2][j] + part[mat][3][j]);
 
   float mn = x, mx = x;

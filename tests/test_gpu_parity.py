@@ -196,6 +196,43 @@ def test_gqa_ratios(hg):
     assert err <= TIGHT
 
 
+def test_cache_beyond_4gib():
+    """A cache buffer larger than 4 GiB (the scan then builds a buffer
+    descriptor per page instead of one over the whole cache) with every
+    sequence's blocks placed past the 4 GiB offset: append and decode parity."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = scaled(W1, batch=2, ctx_min=500, ctx_max=523)
+    say("[wide] cache > 4 GiB")
+    case = new_case(w, keep_initial=False)
+    hkv = w.num_kv_heads
+    pb = kvq.page_bytes(w.head_dim, w.group)
+    nb = (4 << 30) // (hkv * pb) + 4096
+    assert nb * hkv * pb > (4 << 30) and case.st.num_blocks <= 2048
+    big = torch.zeros((nb, hkv, pb), dtype=torch.uint8, device=case.device)
+    try:
+        case.pages = big
+        case.table = (case.table + (nb - 2048)).contiguous()
+        assert int(case.table.min()) * hkv * pb > (4 << 30)
+        fill_context(case, pieces=[200, 77])
+        q = query(case)
+        out = decode(case, q).cpu().numpy()
+        pairs = [(b, hq) for b in range(w.batch) for hq in (0, 17, 31)]
+        ref = oracle_decode(case, q, pairs)
+        err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+        say(f"  max rel err {err:.3e}")
+        assert err <= TIGHT
+        near = n = 0
+        for b in range(w.batch):
+            a, c, _ = _append_parity(case, b, 0, int(case.ctx[b]))
+            near += a
+            n += c
+        assert near <= max(EXEMPT_FRACTION * n, 1)
+    finally:
+        case.pages = None
+        del big
+        torch.cuda.empty_cache()
+
+
 def test_degenerate_groups_and_no_ops():
     """Constant rotated groups store scale 0 and codes 0; empty calls are no-ops."""
     import rotated_int2_kv_kvq_amd as kvq
