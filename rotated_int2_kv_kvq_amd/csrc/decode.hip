@@ -620,6 +620,63 @@ __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
   }
 }
 
+// read_slice and read_ids8 under one wait (slice 0 of a block whose
+// successor exists).
+template <int G, int kOff>
+__device__ __forceinline__ void read_slice_ids(Slice& c, uint32_t ak, uint32_t as, uint32_t ai,
+                                               int (&id)[8]) {
+  constexpr int PB = page_bytes_for_groups(G);
+  u32x4 x, y;
+  if constexpr (G == 2) {
+    u32x2 s0, s1, s2, s3;
+    asm volatile(
+        "ds_read_b64 %0, %8 offset:%11\n"
+        "ds_read_b64 %1, %8 offset:%12\n"
+        "ds_read_b64 %2, %9 offset:%11\n"
+        "ds_read_b64 %3, %9 offset:%12\n"
+        "ds_read_b64 %4, %9 offset:%13\n"
+        "ds_read_b64 %5, %9 offset:%14\n"
+        "ds_read_b128 %6, %10\n"
+        "ds_read_b128 %7, %10 offset:16\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3), "=&v"(x),
+          "=&v"(y)
+        : "v"(ak), "v"(as), "v"(ai), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
+          "i"(kOff + PB + 64 * G)
+        : "memory");
+    c.szk0 = make_uint2(s0.x, s0.y);
+    c.szk1 = make_uint2(s1.x, s1.y);
+    c.szv0 = make_uint2(s2.x, s2.y);
+    c.szv1 = make_uint2(s3.x, s3.y);
+  } else {
+    uint32_t s0, s1, s2, s3;
+    asm volatile(
+        "ds_read_b64 %0, %8 offset:%11\n"
+        "ds_read_b64 %1, %8 offset:%12\n"
+        "ds_read_b32 %2, %9 offset:%11\n"
+        "ds_read_b32 %3, %9 offset:%12\n"
+        "ds_read_b32 %4, %9 offset:%13\n"
+        "ds_read_b32 %5, %9 offset:%14\n"
+        "ds_read_b128 %6, %10\n"
+        "ds_read_b128 %7, %10 offset:16\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3), "=&v"(x),
+          "=&v"(y)
+        : "v"(ak), "v"(as), "v"(ai), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
+          "i"(kOff + PB + 64 * G)
+        : "memory");
+    c.szk0 = make_uint2(s0, s0);
+    c.szk1 = make_uint2(s1, s1);
+    c.szv0 = make_uint2(s2, s2);
+    c.szv1 = make_uint2(s3, s3);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    id[k] = __builtin_amdgcn_readfirstlane(static_cast<int>(x[k]));
+    id[4 + k] = __builtin_amdgcn_readfirstlane(static_cast<int>(y[k]));
+  }
+}
+
 // Eight block ids (one 8-page block of the workgroup's id table) into scalar
 // registers; `ai` is the same LDS address in every lane.
 __device__ __forceinline__ void read_ids8(uint32_t ai, int (&id)[8]) {
@@ -660,13 +717,21 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true));
 }
+// The maximum with a DPP source operand: one v_max_f32 per step (fmaxf would
+// add a NaN-quieting max before each; these values are never NaN).  The nop
+// gives the two wait states a DPP read of a just-written VGPR needs.
+#define KVQ_MAX_DPP(v, ctrl)                                                            \
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1" \
+      : "=v"(v)                                                                         \
+      : "v"(v))
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0xb1>(v));
-  v = fmaxf(v, dpp<0x4e>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
+  KVQ_MAX_DPP(v, "quad_perm:[1,0,3,2]");
+  KVQ_MAX_DPP(v, "quad_perm:[2,3,0,1]");
+  KVQ_MAX_DPP(v, "row_half_mirror");
+  KVQ_MAX_DPP(v, "row_mirror");
   return v;
 }
+#undef KVQ_MAX_DPP
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0xb1>(v);
   v += dpp<0x4e>(v);
@@ -1045,10 +1110,13 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         else
           wait_vmem<0>();
         Slice c;
-        read_slice<G, s * kSlot>(c, ak, as);
+        // the next block's ids (two slices before its first DMA) with slice 0
+        if constexpr (kFast && s == 0)
+          read_slice_ids<G, s * kSlot>(c, ak, as, ids_addr(bi + 1), idn);
+        else
+          read_slice<G, s * kSlot>(c, ak, as);
         if (hl == s) read_vwords<PB, s * kSlot>(vw, av);
-        // the next block's ids, two slices before its first DMA
-        if (s == 0 && (kFast || bi + 1 < nbw)) read_ids8(ids_addr(bi + 1), idn);
+        if (!kFast && s == 0 && bi + 1 < nbw) read_ids8(ids_addr(bi + 1), idn);
 
         // q.K: D[4*head + digit][token t]; the digit rows add up in-lane
         const v8i k0 = fp6_codes(c.kc0.x, c.kc0.y);
