@@ -501,16 +501,23 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(
 
 // --------------------------------------------------------------------------- scan
 // ---- LDS ring: each wave keeps kDepth 2-page slices in flight, loaded with
-// global->LDS DMA (no VGPRs held while in flight).  A slot holds the two page
-// images exactly as laid out in the cache: codes [0, 1024) and (scale, zero)
-// pairs [1024, 1024 + 128G).  One slice is kDmaPerSlice DMA instructions.
-// Two slices in flight per wave (measured on the 36-layer stream: one is too
-// few, three no better).  Four slots, one per slice of an 8-page block, so
-// that every slot address is a compile-time offset; the P tile lives in the
-// slot of the block's last slice.
+// global->LDS DMA (no VGPRs held while in flight).  A slot holds a slice's two
+// pages as [codes of page 0 (1024 B)][codes of page 1][(scale, zero) pairs of
+// page 0 (128G B)][pairs of page 1], each part as laid out in the cache, so
+// that for group 128 one 64-lane DMA fetches both pages' pairs: a slice is
+// dma_per_slice<G>() DMA instructions, with no lane-dependent branch for the
+// compiler to duplicate (the waits count them exactly).  Two slices in flight
+// per wave.  Four slots, one per slice of an 8-page block, so that every slot
+// address is a compile-time offset; the P tile lives in the slot of the
+// block's last slice.
 constexpr int kDepth = 2;
 constexpr int kRing = 4;
-constexpr int kDmaPerSlice = 4;
+constexpr int kSlotCodes1 = 1024;  // codes of a slot's second page
+constexpr int kSlotPairs = 2048;   // (scale, zero) pairs of its first page
+template <int G>
+__host__ __device__ constexpr int dma_per_slice() {
+  return G == 1 ? 3 : 4;
+}
 // Pages one workgroup may take: splits of at most 512 pages, the last split
 // of a context taking up to half a split more.
 constexpr int kMaxSplitPages = 768;
@@ -535,33 +542,52 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
 }
 
-// DMA one page into a ring slot (wide form): the page is a buffer resource
+// One slice into a ring slot (wide form): each page is a buffer resource
 // built in scalar registers (base = the page, 1 record per byte up to the page
-// size); the per-lane offsets are fixed, so issuing takes no vector ALU work.
+// size); the per-lane offsets are fixed.  Group 128 fetches each page's 32
+// pair words with lanes 0-31 (the DMA writes lane L's word at slot base + 4L).
 constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 
 template <int G>
-__device__ __forceinline__ void dma_page(const uint8_t* page, uint8_t* slot, uint32_t off16,
-                                         uint32_t off4, bool sz_lane) {
+__device__ __forceinline__ void dma_slice(const uint8_t* page0, const uint8_t* page1,
+                                          uint8_t* slot, uint32_t off16, uint32_t off4,
+                                          bool lo_lane) {
   constexpr int PB = page_bytes_for_groups(G);
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page), 0, PB, kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)slot, 16, off16, 0, 0, 0);
-  if (sz_lane)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSzOff), 4, off4, 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t r0 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page0), 0, PB, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t r1 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page1), 0, PB, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, (lds_void_t*)slot, 16, off16, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_void_t*)(slot + kSlotCodes1), 16, off16, 0, 0,
+                                           0);
+  if (G == 2 || lo_lane) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, (lds_void_t*)(slot + kSlotPairs), 4, off4, 0, 0,
+                                             0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_void_t*)(slot + kSlotPairs + 128 * G), 4,
+                                             off4, 0, 0, 0);
+  }
 }
 
-// The same DMA through one buffer resource over the whole cache (when it
-// spans less than 4 GiB): the page is the scalar offset, so issuing a page
-// takes two scalar ALU operations for its offset and no descriptor set-up.
+// The same through one buffer resource over the whole cache (when it spans
+// less than 4 GiB): a page is the scalar offset o0 or o1.  Group 128: lanes
+// 0-31 fetch page 0's pair words and lanes 32-63 page 1's in one DMA
+// (off4 = this lane's word offset inside a page).
 template <int G>
-__device__ __forceinline__ void dma_page_at(__amdgpu_buffer_rsrc_t r, uint32_t page_off,
-                                            uint8_t* slot, uint32_t off16, uint32_t off4,
-                                            bool sz_lane) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)slot, 16, off16, page_off, 0, 0);
-  if (sz_lane)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSzOff), 4, off4, page_off, 0,
+__device__ __forceinline__ void dma_slice_at(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t o1,
+                                             uint8_t* slot, uint32_t off16, uint32_t off4,
+                                             bool lo_lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)slot, 16, off16, o0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSlotCodes1), 16, off16, o1, 0,
+                                           0);
+  if constexpr (G == 2) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSlotPairs), 4, off4, o0, 0,
                                              0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSlotPairs + 256), 4, off4,
+                                             o1, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + kSlotPairs), 4,
+                                             off4 + (lo_lane ? o0 : o1), 0, 0, 0);
+  }
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -580,20 +606,19 @@ struct Slice {
 
 template <int G, int kOff>
 __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
-  constexpr int PB = page_bytes_for_groups(G);
   if constexpr (G == 2) {
     u32x2 s0, s1, s2, s3;
     asm volatile(
         "ds_read_b64 %0, %6 offset:%8\n"
         "ds_read_b64 %1, %6 offset:%9\n"
         "ds_read_b64 %2, %7 offset:%8\n"
-        "ds_read_b64 %3, %7 offset:%9\n"
-        "ds_read_b64 %4, %7 offset:%10\n"
-        "ds_read_b64 %5, %7 offset:%11\n"
+        "ds_read_b64 %3, %7 offset:%10\n"
+        "ds_read_b64 %4, %7 offset:%11\n"
+        "ds_read_b64 %5, %7 offset:%12\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-        : "v"(ak), "v"(as), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
-          "i"(kOff + PB + 64 * G)
+        : "v"(ak), "v"(as), "i"(kOff), "i"(kOff + kSlotCodes1), "i"(kOff + 128 * G),
+          "i"(kOff + 64 * G), "i"(kOff + 192 * G)
         : "memory");
     c.szk0 = make_uint2(s0.x, s0.y);
     c.szk1 = make_uint2(s1.x, s1.y);
@@ -605,13 +630,13 @@ __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
         "ds_read_b64 %0, %6 offset:%8\n"
         "ds_read_b64 %1, %6 offset:%9\n"
         "ds_read_b32 %2, %7 offset:%8\n"
-        "ds_read_b32 %3, %7 offset:%9\n"
-        "ds_read_b32 %4, %7 offset:%10\n"
-        "ds_read_b32 %5, %7 offset:%11\n"
+        "ds_read_b32 %3, %7 offset:%10\n"
+        "ds_read_b32 %4, %7 offset:%11\n"
+        "ds_read_b32 %5, %7 offset:%12\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-        : "v"(ak), "v"(as), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
-          "i"(kOff + PB + 64 * G)
+        : "v"(ak), "v"(as), "i"(kOff), "i"(kOff + kSlotCodes1), "i"(kOff + 128 * G),
+          "i"(kOff + 64 * G), "i"(kOff + 192 * G)
         : "memory");
     c.szk0 = make_uint2(s0, s0);
     c.szk1 = make_uint2(s1, s1);
@@ -625,7 +650,6 @@ __device__ __forceinline__ void read_slice(Slice& c, uint32_t ak, uint32_t as) {
 template <int G, int kOff>
 __device__ __forceinline__ void read_slice_ids(Slice& c, uint32_t ak, uint32_t as, uint32_t ai,
                                                int (&id)[8]) {
-  constexpr int PB = page_bytes_for_groups(G);
   u32x4 x, y;
   if constexpr (G == 2) {
     u32x2 s0, s1, s2, s3;
@@ -633,16 +657,16 @@ __device__ __forceinline__ void read_slice_ids(Slice& c, uint32_t ak, uint32_t a
         "ds_read_b64 %0, %8 offset:%11\n"
         "ds_read_b64 %1, %8 offset:%12\n"
         "ds_read_b64 %2, %9 offset:%11\n"
-        "ds_read_b64 %3, %9 offset:%12\n"
-        "ds_read_b64 %4, %9 offset:%13\n"
-        "ds_read_b64 %5, %9 offset:%14\n"
+        "ds_read_b64 %3, %9 offset:%13\n"
+        "ds_read_b64 %4, %9 offset:%14\n"
+        "ds_read_b64 %5, %9 offset:%15\n"
         "ds_read_b128 %6, %10\n"
         "ds_read_b128 %7, %10 offset:16\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3), "=&v"(x),
           "=&v"(y)
-        : "v"(ak), "v"(as), "v"(ai), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
-          "i"(kOff + PB + 64 * G)
+        : "v"(ak), "v"(as), "v"(ai), "i"(kOff), "i"(kOff + kSlotCodes1), "i"(kOff + 128 * G),
+          "i"(kOff + 64 * G), "i"(kOff + 192 * G)
         : "memory");
     c.szk0 = make_uint2(s0.x, s0.y);
     c.szk1 = make_uint2(s1.x, s1.y);
@@ -654,16 +678,16 @@ __device__ __forceinline__ void read_slice_ids(Slice& c, uint32_t ak, uint32_t a
         "ds_read_b64 %0, %8 offset:%11\n"
         "ds_read_b64 %1, %8 offset:%12\n"
         "ds_read_b32 %2, %9 offset:%11\n"
-        "ds_read_b32 %3, %9 offset:%12\n"
-        "ds_read_b32 %4, %9 offset:%13\n"
-        "ds_read_b32 %5, %9 offset:%14\n"
+        "ds_read_b32 %3, %9 offset:%13\n"
+        "ds_read_b32 %4, %9 offset:%14\n"
+        "ds_read_b32 %5, %9 offset:%15\n"
         "ds_read_b128 %6, %10\n"
         "ds_read_b128 %7, %10 offset:16\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(c.kc0), "=&v"(c.kc1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3), "=&v"(x),
           "=&v"(y)
-        : "v"(ak), "v"(as), "v"(ai), "i"(kOff), "i"(kOff + PB), "i"(kOff + 64 * G),
-          "i"(kOff + PB + 64 * G)
+        : "v"(ak), "v"(as), "v"(ai), "i"(kOff), "i"(kOff + kSlotCodes1), "i"(kOff + 128 * G),
+          "i"(kOff + 64 * G), "i"(kOff + 192 * G)
         : "memory");
     c.szk0 = make_uint2(s0, s0);
     c.szk1 = make_uint2(s1, s1);
@@ -697,7 +721,7 @@ __device__ __forceinline__ void read_ids8(uint32_t ai, int (&id)[8]) {
 
 // Value code words of channel 16*tau + n (tau = 0..7) of both pages of a slot:
 // word position 8n + tau, i.e. 32 contiguous bytes per page.
-template <int PB, int kOff>
+template <int kOff>
 __device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av) {
   asm volatile(
       "ds_read_b128 %0, %4 offset:%5\n"
@@ -706,7 +730,7 @@ __device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av) {
       "ds_read_b128 %3, %4 offset:%8\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(vw[0]), "=&v"(vw[1]), "=&v"(vw[2]), "=&v"(vw[3])
-      : "v"(av), "i"(kOff), "i"(kOff + 16), "i"(kOff + PB), "i"(kOff + PB + 16)
+      : "v"(av), "i"(kOff), "i"(kOff + 16), "i"(kOff + kSlotCodes1), "i"(kOff + kSlotCodes1 + 16)
       : "memory");
 }
 
@@ -1005,8 +1029,10 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 
   uint8_t* myring = &ring[wave][0][0];
   // DMA lane offsets: 16 code bytes per lane; one (scale, zero) word per lane
-  const uint32_t off16 = 16u * lane, off4 = kSzOff + 4u * lane;
-  const bool sz_lane = G == 2 || lane < 32;
+  // (group 128: lanes 0-31 and 32-63 take the same words of the two pages)
+  const uint32_t off16 = 16u * lane;
+  const uint32_t off4 = kSzOff + 4u * static_cast<uint32_t>(G == 2 ? lane : (lane & 31));
+  const bool lo_lane = lane < 32;
   // one descriptor over the whole cache (narrow form): page = scalar offset
   const uint32_t pstride = static_cast<uint32_t>(Hkv) * PB, hoff = static_cast<uint32_t>(h) * PB;
   const uint32_t cache_bytes =
@@ -1014,15 +1040,12 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(pages), 0, static_cast<int>(cache_bytes), kBufferWord3);
   auto issue = [&](uint8_t* slot, int b0, int b1) {
-    if constexpr (kWide) {
-      dma_page<G>(pages + (static_cast<int64_t>(b0) * Hkv + h) * PB, slot, off16, off4, sz_lane);
-      dma_page<G>(pages + (static_cast<int64_t>(b1) * Hkv + h) * PB, slot + PB, off16, off4,
-                  sz_lane);
-    } else {
-      dma_page_at<G>(rsrc, static_cast<uint32_t>(b0) * pstride + hoff, slot, off16, off4, sz_lane);
-      dma_page_at<G>(rsrc, static_cast<uint32_t>(b1) * pstride + hoff, slot + PB, off16, off4,
-                     sz_lane);
-    }
+    if constexpr (kWide)
+      dma_slice<G>(pages + (static_cast<int64_t>(b0) * Hkv + h) * PB,
+                   pages + (static_cast<int64_t>(b1) * Hkv + h) * PB, slot, off16, off4, lo_lane);
+    else
+      dma_slice_at<G>(rsrc, static_cast<uint32_t>(b0) * pstride + hoff,
+                      static_cast<uint32_t>(b1) * pstride + hoff, slot, off16, off4, lo_lane);
   };
   // LDS address of the ids of this wave's block m (the same in every lane)
   const uint32_t ids_base = lds_addr(reinterpret_cast<const uint8_t*>(&wids[0]));
@@ -1079,7 +1102,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   // this lane's LDS read addresses in slot 0 (other slots: immediate offsets)
   const uint32_t ring0 = lds_addr(myring);
   const uint32_t ak = ring0 + kKCodeOff + 32 * t + 8 * hl;
-  const uint32_t as = ring0 + kSzOff + 4 * G * t;
+  const uint32_t as = ring0 + kSlotPairs + 4 * G * t;
   const uint32_t av = ring0 + kVCodeOff + 32 * t;
 
   // One 8-page block.  kFast: a block whose four slices all exist, each with
@@ -1104,9 +1127,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         }
         // slice i has landed once at most the DMAs of the slices behind it are pending
         if (kFast || i + kDepth < nsl)
-          wait_vmem<kDepth * kDmaPerSlice>();
+          wait_vmem<kDepth * dma_per_slice<G>()>();
         else if (i + 1 < nsl)
-          wait_vmem<kDmaPerSlice>();
+          wait_vmem<dma_per_slice<G>()>();
         else
           wait_vmem<0>();
         Slice c;
@@ -1115,7 +1138,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
           read_slice_ids<G, s * kSlot>(c, ak, as, ids_addr(bi + 1), idn);
         else
           read_slice<G, s * kSlot>(c, ak, as);
-        if (hl == s) read_vwords<PB, s * kSlot>(vw, av);
+        if (hl == s) read_vwords<s * kSlot>(vw, av);
         if (!kFast && s == 0 && bi + 1 < nbw) read_ids8(ids_addr(bi + 1), idn);
 
         // q.K: D[4*head + digit][token t]; the digit rows add up in-lane
