@@ -244,7 +244,20 @@ __global__ __launch_bounds__(512) void append_kernel(
       const float sf = static_cast<float>(s16);
       const float zf = static_cast<float>(z16);
       uint32_t bits = 0;
-      if (sf != 0.f) {
+      if (sf != 0.f && !direct) {
+        // rotated values: one division per group; the product differs from
+        // the quotient by about an ulp, which moves a code only within the
+        // rounding-boundary tolerance the codes are held to
+        const float inv = 1.0f / sf;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          float qv = rintf((acc[nt][i] - zf) * inv);
+          qv = fminf(fmaxf(qv, 0.f), 3.f);
+          bits |= static_cast<uint32_t>(qv) << (2 * nt);
+        }
+      } else if (sf != 0.f) {
+        // values as given (bfloat16 ones often lie exactly on a rounding
+        // boundary): the correctly rounded quotient breaks ties to even
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
           float qv = rintf((acc[nt][i] - zf) / sf);
