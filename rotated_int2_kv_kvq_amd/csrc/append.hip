@@ -72,6 +72,31 @@ __device__ __forceinline__ void raw_to_f32(const RawRow<kBf16>& r, float (&a)[32
   }
 }
 
+// Minimum and maximum over the 16 lanes of a DPP row (kHalfRow: over each
+// 8-lane half row), the same in every lane: quad_perm [1,0,3,2],
+// [2,3,0,1], row_half_mirror, row_mirror, one min and one max per step (the
+// values are finite, so no NaN quieting is needed).  The nop gives the two
+// wait states a DPP read of a just-written VGPR needs.
+#define KVQ_MINMAX_DPP(ctrl)                                                                \
+  asm("s_nop 1\n\t"                                                                         \
+      "v_min_f32_dpp %0, %2, %2 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"         \
+      "v_max_f32_dpp %1, %3, %3 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1"            \
+      : "=&v"(a), "=&v"(b)                                                                  \
+      : "v"(mn), "v"(mx));                                                                  \
+  mn = a;                                                                                   \
+  mx = b
+template <bool kHalfRow>
+__device__ __forceinline__ void row_minmax(float& mn, float& mx) {
+  float a, b;
+  KVQ_MINMAX_DPP("quad_perm:[1,0,3,2]");
+  KVQ_MINMAX_DPP("quad_perm:[2,3,0,1]");
+  KVQ_MINMAX_DPP("row_half_mirror");
+  if constexpr (!kHalfRow) {
+    KVQ_MINMAX_DPP("row_mirror");
+  }
+}
+#undef KVQ_MINMAX_DPP
+
 template <bool kBf16>
 __global__ __launch_bounds__(512) void append_kernel(
     uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
@@ -230,13 +255,11 @@ __global__ __launch_bounds__(512) void append_kernel(
         mn = fminf(mn, acc[nt][i]);
         mx = fmaxf(mx, acc[nt][i]);
       }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        if (m < gl) {
-          mn = fminf(mn, shfl_xor(mn, m));
-          mx = fmaxf(mx, shfl_xor(mx, m));
-        }
-      }
+      // over the group's lanes: a DPP row (group 128) or half row (group 64)
+      if (G == 2)
+        row_minmax<true>(mn, mx);
+      else
+        row_minmax<false>(mn, mx);
       const float lo = clip * mn;
       const float hi = clip * mx;
       const _Float16 s16 = f16_sat((hi - lo) / 3.0f);
