@@ -104,12 +104,7 @@ __device__ __forceinline__ void append_one_body(
 
   const float x = (part[mat][0][j] + part[mat][1][j]) + (part[mat][2][j] + part[mat][3][j]);
 
-  float mn = x, mx = x;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    mn = fminf(mn, shfl_xor(mn, m));
-    mx = fmaxf(mx, shfl_xor(mx, m));
-  }
+  float mn = wave_min(x), mx = wave_max(x);
   if (G == 1) {  // group of 128 channels spans this thread's two waves
     if (own && (tid & 63) == 0) {
       red[wave][0] = mn;

@@ -141,14 +141,8 @@ __device__ __forceinline__ void prologue_digits(int h, int qg, int b, int Hkv, i
               (red[2][hl][lane + 64] + red[3][hl][lane + 64]));
   r0 *= qscale;  // logits in log2 units
   r1 *= qscale;
-  float amax = fmaxf(fabsf(r0), fabsf(r1));
-  float s0 = r0, s1 = r1;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    amax = fmaxf(amax, shfl_xor(amax, m));
-    s0 += shfl_xor(s0, m);
-    s1 += shfl_xor(s1, m);
-  }
+  const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
+  const float s0 = wave_sum(r0), s1 = wave_sum(r1);
   // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest; digit d
   // (0 = most significant) as the FP6 field sign | nibble
   const int e = min(max(exp_above(amax), -100), 100);
@@ -264,8 +258,7 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
   {  // q . mu per head (wave wv)
     const float* muh = mu + static_cast<size_t>(h) * kHeadDim;
     float qm = qin[wv][lane] * muh[lane] + qin[wv][lane + 64] * muh[lane + 64];
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) qm += shfl_xor(qm, m);
+    qm = wave_sum(qm);
     if (lane == 0) hs[0][wv] = qm;
   }
   __syncthreads();
@@ -308,16 +301,14 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
   {  // softmax of head wv
     float m = -INFINITY;
     for (int i = lane; i < nw; i += 64) m = fmaxf(m, lg[wv][i]);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, shfl_xor(m, k));
+    m = wave_max(m);
     float l = 0.f;
     for (int i = lane; i < nw; i += 64) {
       const float pi = exp2_hw(lg[wv][i] - m);
       lg[wv][i] = pi;
       l += pi;
     }
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) l += shfl_xor(l, k);
+    l = wave_sum(l);
     if (lane == 0) {
       hs[1][wv] = m;
       hs[2][wv] = l;
@@ -732,55 +723,6 @@ __device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av) {
       : "=&v"(vw[0]), "=&v"(vw[1]), "=&v"(vw[2]), "=&v"(vw[3])
       : "v"(av), "i"(kOff), "i"(kOff + 16), "i"(kOff + kSlotCodes1), "i"(kOff + kSlotCodes1 + 16)
       : "memory");
-}
-
-// Reductions over the 16 lanes of a DPP row (all lanes of one query head):
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true));
-}
-// The maximum with a DPP source operand: one v_max_f32 per step (fmaxf would
-// add a NaN-quieting max before each; these values are never NaN).  The nop
-// gives the two wait states a DPP read of a just-written VGPR needs.
-#define KVQ_MAX_DPP(v, ctrl)                                                            \
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1" \
-      : "=v"(v)                                                                         \
-      : "v"(v))
-__device__ __forceinline__ float row16_max(float v) {
-  KVQ_MAX_DPP(v, "quad_perm:[1,0,3,2]");
-  KVQ_MAX_DPP(v, "quad_perm:[2,3,0,1]");
-  KVQ_MAX_DPP(v, "row_half_mirror");
-  KVQ_MAX_DPP(v, "row_mirror");
-  return v;
-}
-#undef KVQ_MAX_DPP
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0xb1>(v);
-  v += dpp<0x4e>(v);
-  v += dpp<0x141>(v);
-  v += dpp<0x140>(v);
-  return v;
-}
-
-// Reductions over the whole wave, the same value in every lane: the rows by
-// DPP, then the four row results read as scalars.
-__device__ __forceinline__ float wave_max(float v) {
-  v = row16_max(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row16_sum(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
 }
 
 // Write four digit bytes to rows 4*hl + 0..3 of the P tile at this lane's

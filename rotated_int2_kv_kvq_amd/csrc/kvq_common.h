@@ -60,4 +60,71 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// Reductions over the 16 lanes of a DPP row:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true));
+}
+// The maximum with a DPP source operand: one v_max_f32 per step (fmaxf would
+// add a NaN-quieting max before each; these values are never NaN).  The nop
+// gives the two wait states a DPP read of a just-written VGPR needs.
+#define KVQ_MAX_DPP(v, ctrl)                                                            \
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1" \
+      : "=v"(v)                                                                         \
+      : "v"(v))
+__device__ __forceinline__ float row16_max(float v) {
+  KVQ_MAX_DPP(v, "quad_perm:[1,0,3,2]");
+  KVQ_MAX_DPP(v, "quad_perm:[2,3,0,1]");
+  KVQ_MAX_DPP(v, "row_half_mirror");
+  KVQ_MAX_DPP(v, "row_mirror");
+  return v;
+}
+#undef KVQ_MAX_DPP
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+
+// Reductions over the whole wave, the same value in every lane: the rows by
+// DPP, then the four row results read as scalars.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float row16_min(float v) {
+  asm("s_nop 1\n\tv_min_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\tv_min_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\tv_min_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\tv_min_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(v)
+      : "v"(v));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = row16_min(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fminf(fminf(r0, r1), fminf(r2, r3));
+}
+
 }  // namespace kvq
