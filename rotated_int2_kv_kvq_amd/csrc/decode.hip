@@ -380,6 +380,18 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
   const int wv = (tid >> 6) & 3;
   const int nh = min(kHT, Hg - qg * kHT);
 
+  // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
+  // first (before the query rows, whose store to LDS waits for them), one pass
+  // over R_K for the four heads
+  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
+  float ra[32], rb[32];
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      ra[i] = R[i * kHeadDim + lane];
+      rb[i] = R[i * kHeadDim + lane + 64];
+    }
+  }
   // the tile's query rows (zero for rows past the KV head's query heads)
   if (act) {
     const int hh = tid >> 6, c = (tid & 63) * 2;
@@ -398,17 +410,6 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
     }
     qin[hh][c] = v0;
     qin[hh][c + 1] = v1;
-  }
-  // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
-  // before the products, one pass over R_K for the four heads
-  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
-  float ra[32], rb[32];
-  if (act) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      ra[i] = R[i * kHeadDim + lane];
-      rb[i] = R[i * kHeadDim + lane + 64];
-    }
   }
   __syncthreads();
   if (act) {
@@ -1296,14 +1297,14 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   // the S allocated splits; entries of splits past the count are never used.
   const float lse_l = p[min(lane, S - 1) * kPartStride];
   float xv[kMergeSplits], lv[kMergeSplits];
+  // unconditional loads with the split index clamped (a guarded load becomes a
+  // branch whose result copy waits for it, serialising the round)
   auto load_round = [&](int r, float(&x)[kMergeSplits], float(&l)[kMergeSplits]) {
 #pragma unroll
     for (int k = 0; k < kMergeSplits; ++k) {
-      const int s = 2 * (kMergeSplits * r + k) + half;  // the same in the whole wave
-      if (s < S) {
-        x[k] = p[s * kPartStride + 4 + c];
-        l[k] = p[s * kPartStride];
-      }
+      const int s = min(2 * (kMergeSplits * r + k) + half, S - 1);
+      x[k] = p[s * kPartStride + 4 + c];
+      l[k] = p[s * kPartStride];
     }
   };
   load_round(0, xv, lv);
