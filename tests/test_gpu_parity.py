@@ -196,6 +196,38 @@ def test_gqa_ratios(hg):
     assert err <= TIGHT
 
 
+@pytest.mark.parametrize("name", ["cfg1_b4_ctx1000", "cfg2_b6_ragged_g64"])
+def test_staged_decode_matches_whole_call(name):
+    """kvq_decode_attn_staged: the three stages launched one at a time, or two
+    together, leave the same output as kvq_decode_attn, bit for bit."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = SMALL[name]
+    say(f"[staged] {name}")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    ctx_t = torch.from_numpy(case.ctx.astype(np.int32)).to(case.device)
+    max_ctx = int(case.ctx.max())
+    ws = torch.empty(kvq.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx),
+                     dtype=torch.uint8, device=case.device)
+
+    def run(stage_list):
+        out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"),
+                         device=case.device)
+        for st in stage_list:
+            kvq.decode(case.pages, case.table, ctx_t, max_ctx, q, case.rot_k, case.rot_v, w.group,
+                       case.sm_scale, out=out, workspace=ws, stages=st)
+        torch.cuda.synchronize()
+        return out
+
+    whole = run([kvq.STAGE_ALL])
+    assert torch.isfinite(whole).all()
+    for stage_list in ([kvq.STAGE_PREPARE, kvq.STAGE_SPLITS, kvq.STAGE_MERGE],
+                       [kvq.STAGE_PREPARE | kvq.STAGE_SPLITS, kvq.STAGE_MERGE],
+                       [kvq.STAGE_PREPARE, kvq.STAGE_SPLITS | kvq.STAGE_MERGE]):
+        assert torch.equal(run(stage_list), whole), stage_list
+
+
 def test_cache_beyond_4gib():
     """A cache buffer larger than 4 GiB (the scan then builds a buffer
     descriptor per page instead of one over the whole cache) with every
