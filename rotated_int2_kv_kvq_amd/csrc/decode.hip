@@ -889,12 +889,15 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   // has its own L2.  Renumber the splits so that every XCD takes one contiguous
   // run of (query group, split) pairs: the splits of a query group then share
   // one L2 copy of its query operand instead of fetching it once per XCD.
+  // Within the run the query groups of one split come first, so the KV heads
+  // of a sequence start on the same pages together and read neighbouring
+  // slices of each block (the ragged group-64 batch of 64: 224-232 -> 214 us).
   const int n_wg = static_cast<int>(gridDim.x) - n_win;
   const int lin = static_cast<int>(blockIdx.x) - n_win;
   const int xcd = lin & 7;
   const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
-  const int wgs = job % S;
-  const int hy = (job / S) % Y;
+  const int hy = job % Y;
+  const int wgs = (job / Y) % S;
   const int b = job / (S * Y);
   const int h = hy / QG;
   const int qg = hy % QG;
