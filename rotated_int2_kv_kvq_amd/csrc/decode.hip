@@ -1257,9 +1257,10 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 //   - thread (j = tid/8, part = tid%8) loads its sixteen entries of row j of
 //     R_V for the rotation;
 //   - thread (head u = tid/256, half = (tid/128)%2, channel c = tid%128) loads
-//     channel c of splits half, half + 2, ... (kMergeSplits of them per round,
-//     with their lse values: one address per wave), and lane l of each wave
-//     the lse of split l.
+//     channel c of splits half, half + 2, ... (kMergeSplits of them per round;
+//     the first two rounds at once), and lane l of each wave the lse of split
+//     l, which the wave's other lanes read from it (splits past 64 load their
+//     lse with the round).
 // Each wave of head u then reduces the head's maximum lse and weight sum over
 // the splits itself, so one barrier (the per-half channel sums into LDS)
 // separates the merge from the rotation.
@@ -1299,18 +1300,16 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   // Loaded before the context length (and so the split count) is known, for
   // the S allocated splits; entries of splits past the count are never used.
   const float lse_l = p[min(lane, S - 1) * kPartStride];
-  float xv[kMergeSplits], lv[kMergeSplits];
+  float xv[kMergeSplits], xw[kMergeSplits], lv[kMergeSplits];
   // unconditional loads with the split index clamped (a guarded load becomes a
   // branch whose result copy waits for it, serialising the round)
-  auto load_round = [&](int r, float(&x)[kMergeSplits], float(&l)[kMergeSplits]) {
+  auto load_x = [&](int r, float(&x)[kMergeSplits]) {
 #pragma unroll
-    for (int k = 0; k < kMergeSplits; ++k) {
-      const int s = min(2 * (kMergeSplits * r + k) + half, S - 1);
-      x[k] = p[s * kPartStride + 4 + c];
-      l[k] = p[s * kPartStride];
-    }
+    for (int k = 0; k < kMergeSplits; ++k)
+      x[k] = p[min(2 * (kMergeSplits * r + k) + half, S - 1) * kPartStride + 4 + c];
   };
-  load_round(0, xv, lv);
+  load_x(0, xv);
+  if (S > 2 * kMergeSplits) load_x(1, xw);  // S: the same in every thread
   // the window partial's lse, and the window output this thread adds
   const float lse_w = wpart ? wpart[(row0 + min(u, nh - 1)) * kPartStride] : kNegBig;
   const float wv = wpart ? wpart[(row0 + min(part8 & 3, nh - 1)) * kPartStride + 4 + j] : 0.f;
@@ -1341,14 +1340,34 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 
   // channel c over this half's splits, a round at a time (one round covers
   // 32 splits); a split past the count contributes nothing (its stale values
-  // are never multiplied)
+  // are never multiplied).  The lse of split s < 64 is lane s's lse_l.
   float acc = 0.f;
+  const int half_s = __builtin_amdgcn_readfirstlane(half);  // the same in the wave
+  auto lse_of = [&](int s) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_l), s));
+  };
   const int nr = (ns + 2 * kMergeSplits - 1) / (2 * kMergeSplits);
-  for (int r = 0; r < nr; ++r) {
-    if (r > 0) load_round(r, xv, lv);
+#pragma unroll
+  for (int k = 0; k < kMergeSplits; ++k) {
+    const int s = 2 * k + half_s;
+    if (s < ns) acc = fmaf(exp2_hw(lse_of(s) - M), xv[k], acc);
+  }
+  if (nr > 1) {
 #pragma unroll
     for (int k = 0; k < kMergeSplits; ++k) {
-      const int s = 2 * (kMergeSplits * r + k) + half;
+      const int s = 2 * (kMergeSplits + k) + half_s;
+      if (s < ns) acc = fmaf(exp2_hw(lse_of(s) - M), xw[k], acc);
+    }
+  }
+  for (int r = 2; r < nr; ++r) {
+    load_x(r, xv);
+#pragma unroll
+    for (int k = 0; k < kMergeSplits; ++k)
+      lv[k] = p[min(2 * (kMergeSplits * r + k) + half_s, S - 1) * kPartStride];
+#pragma unroll
+    for (int k = 0; k < kMergeSplits; ++k) {
+      const int s = 2 * (kMergeSplits * r + k) + half_s;
       if (s < ns) acc = fmaf(exp2_hw(lv[k] - M), xv[k], acc);
     }
   }
