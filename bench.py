@@ -546,7 +546,9 @@ def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
     """Cold decode of one layer of a long-context workload: the whole call
     (query rotation, scan, merge) and the scan alone.  Calls run back to back
     over copies of the cache, queued behind a GPU sleep, between one pair of
-    events; the figure is the mean per call."""
+    events; the figure is the mean per call.  Per-call medians come from an
+    event pair around each call: cold (copies cycled) and warm (one copy back
+    to back, partly served from the Infinity Cache)."""
     import numpy as np
     import torch
 
@@ -590,6 +592,21 @@ def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
         if rep:
             full_ms.append(e0.elapsed_time(e1) / calls)
             scan_ms.append(e2.elapsed_time(e3) / calls)
+
+    def per_call_us(copy_of):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * calls)]
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)
+        for i in range(calls):
+            ev[2 * i].record()
+            call(copy_of(i), kvq.STAGE_ALL)
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1])
+                                for i in range(1, calls)])) * 1e3
+
+    cold_med = per_call_us(lambda i: i)
+    warm_med = per_call_us(lambda i: 0)
     call(0, kvq.STAGE_ALL)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all().item()
@@ -600,6 +617,8 @@ def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
         "batch": B, "ctx": [int(st.ctx_lens.min()), max_ctx], "group": w.group,
         "cache_bytes": nbytes, "cold": f"{ncopy} cache copies cycled",
         "decode_us": round(full_us, 2),
+        "decode_us_median_cold": round(cold_med, 2),
+        "decode_us_median_warm": round(warm_med, 2),
         "decode_gbs": round(nbytes / (full_us * 1e-6) / 1e9, 1),
         "decode_frac": round(nbytes / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "scan_us": round(scan_us, 2),
