@@ -1,0 +1,40 @@
+"""Host-side pieces of bench.py that run without a GPU: the oracle's CPU
+baseline (one BLAS thread, then one per core) on a tiny cache."""
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+import bench
+import oracle as O
+
+
+def _tiny_cache(batch=2, n=40, hkv=2, hq=8, group=64, seed=5):
+    rng = np.random.default_rng(seed)
+    d = O.HEAD_DIM
+    n_pages = (n + 15) // 16
+    table = rng.permutation(batch * n_pages).astype(np.int32).reshape(batch, n_pages)
+    cache = np.zeros((batch * n_pages, hkv * O.page_bytes(d, group)), np.uint8)
+    rot = np.stack([np.linalg.qr(rng.standard_normal((d, d)))[0] for _ in range(hkv)])
+    k = rng.standard_normal((batch, n, hkv, d))
+    v = rng.standard_normal((batch, n, hkv, d))
+    mu = k.mean(axis=(0, 1))
+    O.append(cache, table, np.zeros(batch, np.int64), k, v, mu, rot, rot, group, 0.9, 0.9)
+    w = SimpleNamespace(batch=batch, num_kv_heads=hkv, num_q_heads=hq, group=group)
+    st = SimpleNamespace(rot_k=[rot], rot_v=[rot])
+    q = torch.from_numpy(rng.standard_normal((batch, hq, d)).astype(np.float32))
+    ctx = torch.full((batch,), n, dtype=torch.int32)
+    return w, st, torch.from_numpy(cache), torch.from_numpy(table), ctx, q
+
+
+def test_cpu_baseline_fields():
+    w, st, pages, table, ctx, q = _tiny_cache()
+    per = bench.cache_bytes_per_token_head(w.group)
+    res = bench.cpu_baseline(w, st, pages, table, ctx, q, per, 0.3, 1.0 / np.sqrt(O.HEAD_DIM))
+    assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["cores"] == 1
+    assert res["value"] > 0 and "1 thread," in res["sample"]
+    assert isinstance(res["cpu_model"], str) and res["cpu_model"]
+    import os
+    if (os.cpu_count() or 1) > 1:
+        allc = res["all_cores"]
+        assert allc["cores"] == min(os.cpu_count(), 16) and allc["value"] > 0
