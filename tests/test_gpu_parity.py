@@ -575,3 +575,26 @@ def test_full_size_sampled(name):
             n += c
     say(f"  sampled elements {n} exempt {near}")
     assert near <= max(EXEMPT_FRACTION * n, 1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("group", [128, 64])
+def test_largest_split(group):
+    """split_pages 512: a context of 767 pages is one split whose block-id
+    table (768 entries) is all but full; 750 pages leave a short last block."""
+    w = scaled(W1, batch=2, ctx_min=767 * 16, ctx_max=767 * 16, group=group)
+    say(f"[largest split] group {group}")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    ctx = np.array([767 * 16, 750 * 16 - 5], np.int32)
+    out = decode(case, q, ctx=ctx, split_pages=512).cpu().numpy()
+    assert np.isfinite(out).all()
+    pairs = [(b, hq) for b in range(2) for hq in (0, 7, 13, 31)]
+    ref = oracle_decode(case, q, pairs, ctx=ctx)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  sampled max rel err {err:.3e}")
+    assert err <= TIGHT
+    # the automatic plan splits the same contexts; the result agrees to round-off
+    auto = decode(case, q, ctx=ctx).cpu().numpy()
+    assert attention_error(auto, out) <= 1e-5
