@@ -598,3 +598,72 @@ def test_largest_split(group):
     # the automatic plan splits the same contexts; the result agrees to round-off
     auto = decode(case, q, ctx=ctx).cpu().numpy()
     assert attention_error(auto, out) <= 1e-5
+
+
+def test_graph_replay_matches_eager():
+    """Decode steps captured as HIP graphs (one per step, as the step loop of a
+    serving engine would) and replayed in order, with eager work and
+    synchronisations between replays, equal the eager calls bit for bit: the
+    cache after every step and every step's output.  A decode-only graph then
+    replays three times over the final cache, each replay equal to an eager
+    decode."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = SMALL["cfg4_b3_layer5"]
+    say("[graph] 4 captured steps, then a decode graph replayed 3 times")
+    a = new_case(w, layer=1, keep_initial=False)
+    b = new_case(w, layer=1, keep_initial=False)
+    fill_context(a)
+    fill_context(b)
+    dev = a.device
+    ctx = a.ctx.copy()
+    ins = []
+    for step in range(w.steps):
+        kv = [kv_for_sequence(w, a.st, a.layer, s, int(ctx[s]), 1, dev) for s in range(w.batch)]
+        k = torch.stack([x[0] for x in kv]).contiguous()
+        v = torch.stack([x[1] for x in kv]).contiguous()
+        sp = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        ctx = ctx + 1
+        ins.append((k, v, sp, torch.from_numpy(ctx.astype(np.int32)).to(dev), int(ctx.max()),
+                    query(a, step)))
+    max_ctx = int(ctx.max())
+    wsb = kvq.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    outs = [torch.empty(w.batch, w.num_q_heads, 128, device=dev) for _ in ins]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for step, (k, v, sp, ct, mc, q) in enumerate(ins):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            kvq.append_decode(b.pages, b.table, sp, ct, mc, k, v, b.mu, q, b.rot_k, b.rv,
+                              w.group, w.clip_k, w.clip_v, b.sm_scale, out=outs[step],
+                              workspace=ws)
+        graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for step, (k, v, sp, ct, mc, q) in enumerate(ins):
+        out_a = kvq.append_decode(a.pages, a.table, sp, ct, mc, k, v, a.mu, q, a.rot_k, a.rv,
+                                  w.group, w.clip_k, w.clip_v, a.sm_scale)
+        torch.cuda.synchronize()
+        graphs[step].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a.pages, b.pages), step
+        assert torch.equal(out_a, outs[step]), step
+
+    q = ins[-1][5]
+    ctx_t = ins[-1][3]
+    o = torch.empty(w.batch, w.num_q_heads, 128, device=dev)
+    g = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        kvq.decode(b.pages, b.table, ctx_t, max_ctx, q, b.rot_k, b.rv, w.group, b.sm_scale,
+                   out=o, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        ref = kvq.decode(a.pages, a.table, ctx_t, max_ctx, q, a.rot_k, a.rv, w.group,
+                         a.sm_scale)
+        torch.cuda.synchronize()
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), rep
