@@ -7,7 +7,10 @@ Every case below replaces one oracle function by a plausible wrong version:
   rotation, the softmax scale);
 - a wrong rounding mode, scale divisor or sign;
 - a wrong head mapping;
-- a wrong bit or word order.
+- a wrong bit or word order;
+- a wrong weighting in the Eq. 8 split;
+- a wrong window slot or window boundary;
+- bfloat16 truncation instead of rounding.
 
 It then runs the pins of test_oracle_pins and requires that one of them
 fails.  This shows the pins constrain each part of the oracle, not only its
@@ -23,7 +26,8 @@ import test_oracle_pins as pins
 
 ORIG = {name: getattr(K, name) for name in (
     "rotate", "encode_tokens", "encode_groups", "quantize_on_grid", "fp16_sat",
-    "value_rotation", "attend", "k_code_site", "v_code_site", "dequant", "decode")}
+    "value_rotation", "attend", "k_code_site", "v_code_site", "dequant", "decode",
+    "eq8_decomposition", "window_slot", "window_parts", "bf16_round")}
 
 
 def _rotate_transposed(x, R):
@@ -101,6 +105,33 @@ def _decode_gqa_interleaved(cache, block_table, ctx_len, q, rot_k, rot_v, sm_sca
                           num_kv_heads, group, pairs=pairs2)[:, pi]
 
 
+def _eq8_terms_with_exact_weights(q, k, v, k_tilde, v_tilde, w_o, sm_scale):
+    # the value term weighted by the exact-key distribution instead of p~
+    r = ORIG["eq8_decomposition"](q, k, v, k_tilde, v_tilde, w_o, sm_scale)
+    p = K._softmax_weights(q, k, sm_scale)
+    dv = np.asarray(v_tilde, np.float64) - np.asarray(v, np.float64)
+    r["value_term"] = (p @ dv) @ np.asarray(w_o, np.float64).T
+    return r
+
+
+def _window_slot_no_sinks(pos):
+    return np.asarray(pos) % (K.SINK + K.RECENT)
+
+
+def _window_parts_recent_short(n):
+    sink, body, recent = ORIG["window_parts"](n)
+    if len(recent) > 0:  # the last recent token counted in the body
+        body = range(body.start, max(body.stop, recent.start + 1))
+        recent = range(recent.start + 1, recent.stop)
+    return sink, body, recent
+
+
+def _bf16_truncated(x):
+    f = np.asarray(x, np.float32)
+    u = f.view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
 MUTATIONS = {
     "rotation_transposed": ("rotate", _rotate_transposed),
     "key_centring_dropped": ("encode_tokens", _encode_tokens_uncentred),
@@ -115,6 +146,10 @@ MUTATIONS = {
     "v_words_permuted": ("v_code_site", _v_code_site_other_words),
     "zero_point_sign": ("dequant", _dequant_zero_subtracted),
     "gqa_interleaved": ("decode", _decode_gqa_interleaved),
+    "eq8_value_term_weights": ("eq8_decomposition", _eq8_terms_with_exact_weights),
+    "window_slot_without_sinks": ("window_slot", _window_slot_no_sinks),
+    "window_recent_one_short": ("window_parts", _window_parts_recent_short),
+    "bf16_truncated": ("bf16_round", _bf16_truncated),
 }
 
 PINS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
