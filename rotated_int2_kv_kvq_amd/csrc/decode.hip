@@ -1420,6 +1420,107 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   }
 }
 
+// ---- merge of one query head per workgroup, for small grids without windows
+// (batch-1 long contexts, where one workgroup per KV head would leave most
+// CUs idle).  grid (Hq, B), block 256.  Lane l of every wave loads the lse of
+// split l (more in a loop), so every wave forms the head's maximum and weight
+// sum; wave w adds up splits w, w + 4, ... for channels lane and lane + 64,
+// all of its loads issued at once, and the four waves meet in LDS.  Then
+// thread (row j = tid / 2, half) takes 64 columns of R_V row j, loaded at the
+// start, and the two halves add by a DPP step.
+constexpr int kHeadMergeSplits = 16;  // splits per wave and round
+
+__global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict__ part,
+                                                         const int* __restrict__ ctx_len,
+                                                         int max_ctx, int Hq, int Hkv, int spw,
+                                                         int S, const float* __restrict__ rot_v,
+                                                         float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) float osum[4][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float ofin[kHeadDim];
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int h = hq / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = tid >> 1, half = tid & 1;
+  const bool rotate_out = rot_v != nullptr;
+  float4 rr[16] = {};
+  if (rotate_out) {
+    const float4* R = reinterpret_cast<const float4*>(
+        rot_v + (static_cast<size_t>(h) * kHeadDim + j) * kHeadDim + 64 * half);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) rr[m] = R[m];
+  }
+  const size_t row = static_cast<size_t>(b) * Hq + hq;
+  const float* p = part + row * S * kPartStride;
+  const int ctx_in = ctx_len[b];
+  const float lse_l = p[min(lane, S - 1) * kPartStride];
+  float x0[kHeadMergeSplits], x1[kHeadMergeSplits];
+  auto load_round = [&](int r) {
+#pragma unroll
+    for (int k = 0; k < kHeadMergeSplits; ++k) {
+      const float* e = p + min(4 * (kHeadMergeSplits * r + k) + w, S - 1) * kPartStride;
+      x0[k] = e[4 + lane];
+      x1[k] = e[4 + lane + 64];
+    }
+  };
+  load_round(0);
+  const int ctx = min(max(ctx_in, 0), max_ctx);
+  const int ns = num_splits((ctx + kBlock - 1) / kBlock, spw);
+  if (ns == 0) {
+    if (tid < kHeadDim) out[row * kHeadDim + tid] = 0.f;
+    return;
+  }
+  float M = lane < ns ? lse_l : -INFINITY;
+  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
+  M = wave_max(M);
+  float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
+  for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
+  W = wave_sum(W);
+  // this wave's splits; the lse of split s < 64 is lane s's lse_l
+  auto lse_of = [&](int s) {
+    return s < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                  __builtin_bit_cast(int, lse_l), s))
+                  : p[s * kPartStride];
+  };
+  float a0 = 0.f, a1 = 0.f;
+  const int nr = (ns + 4 * kHeadMergeSplits - 1) / (4 * kHeadMergeSplits);
+  for (int r = 0; r < nr; ++r) {
+    if (r > 0) load_round(r);
+#pragma unroll
+    for (int k = 0; k < kHeadMergeSplits; ++k) {
+      const int s = 4 * (kHeadMergeSplits * r + k) + w;
+      if (s < ns) {
+        const float wgt = exp2_hw(lse_of(s) - M);
+        a0 = fmaf(wgt, x0[k], a0);
+        a1 = fmaf(wgt, x1[k], a1);
+      }
+    }
+  }
+  osum[w][lane] = a0;
+  osum[w][lane + 64] = a1;
+  __syncthreads();
+  const float inv = 1.0f / W;
+  if (!rotate_out) {
+    if (tid < kHeadDim)
+      out[row * kHeadDim + tid] =
+          (((osum[0][tid] + osum[1][tid]) + osum[2][tid]) + osum[3][tid]) * inv;
+    return;
+  }
+  if (tid < kHeadDim)
+    ofin[tid] = (((osum[0][tid] + osum[1][tid]) + osum[2][tid]) + osum[3][tid]) * inv;
+  __syncthreads();
+  // out_j = sum_i o_i R_V[j][i]: columns 64 half + 4 m + (0..3)
+  float o = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float4 x = *reinterpret_cast<const float4*>(&ofin[64 * half + 4 * m]);
+    const float4 r = rr[m];
+    o = fmaf(x.x, r.x, fmaf(x.y, r.y, fmaf(x.z, r.z, fmaf(x.w, r.w, o))));
+  }
+  o += dpp<0xb1>(o);  // quad_perm [1,0,3,2]: the other half of row j
+  if (half == 0) out[row * kHeadDim + j] = o;
+}
+
 // --------------------------------------------------------------------------- host side
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -1501,7 +1602,12 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
     };
     G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
-  if (stages & 4)
+  // fewer than 64 query tiles without windows: a workgroup per query head
+  const bool per_head = !win && static_cast<int64_t>(B) * Hkv * p.QG < 64;
+  if ((stages & 4) && per_head)
+    hipLaunchKernelGGL(merge_head_kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len,
+                       max_ctx, Hq, Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
+  else if (stages & 4)
     hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
                        max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
                        static_cast<const float*>(wpart));
