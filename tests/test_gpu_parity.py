@@ -667,3 +667,33 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, ref), rep
+
+
+MANY_SPLITS = {
+    # 16 query tiles: one workgroup per query head merges 128 splits
+    "per_head_merge": (scaled(W1, batch=2, ctx_min=16384, ctx_max=16384), [16384, 11997]),
+    # 64 query tiles: the per-KV-head merge, 94 splits in three rounds
+    "per_tile_merge": (scaled(W1, batch=8, ctx_min=12000, ctx_max=12000),
+                       [12000, 11000, 9993, 8200, 5000, 1030, 16, 12000]),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_SPLITS))
+def test_many_splits(name):
+    """Split size 8 pages: more than 64 splits per sequence, so the merges run
+    several rounds and read lse values past the first 64 lanes."""
+    w, lens = MANY_SPLITS[name]
+    say(f"[many splits] {name}")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    ctx = np.array(lens, np.int32)
+    out = decode(case, q, ctx=ctx, split_pages=8).cpu().numpy()
+    assert np.isfinite(out).all()
+    pairs = [(b, hq) for b in range(w.batch) for hq in (0, 6, 17, 31)]
+    ref = oracle_decode(case, q, pairs, ctx=ctx)
+    err = max(attention_error(out[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  sampled max rel err {err:.3e}")
+    assert err <= TIGHT
+    auto = decode(case, q, ctx=ctx).cpu().numpy()
+    assert attention_error(auto, out) <= 1e-5
