@@ -697,3 +697,40 @@ def test_many_splits(name):
     assert err <= TIGHT
     auto = decode(case, q, ctx=ctx).cpu().numpy()
     assert attention_error(auto, out) <= 1e-5
+
+
+def test_full_size_decode_step_sampled():
+    """One layer of the 36-layer stream workload at full size (batch 16, 16K
+    prompt): two fused decode steps (kvq_append_decode, the call and split plan
+    the benchmark times), the last step's output on sampled heads against the
+    oracle over the GPU's cache, and the appended tokens' encoding."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = W4
+    say("[full] stream workload, one layer, two fused steps")
+    case = new_case(w, layer=0, keep_initial=False)
+    fill_context(case)
+    ctx = case.ctx.copy()
+    dev = case.device
+    for step in range(2):
+        kv = [kv_for_sequence(w, case.st, case.layer, s, int(ctx[s]), 1, dev)
+              for s in range(w.batch)]
+        k = torch.stack([x[0] for x in kv]).contiguous()
+        v = torch.stack([x[1] for x in kv]).contiguous()
+        sp = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        ctx = ctx + 1
+        ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        q = query(case, step)
+        out = kvq.append_decode(case.pages, case.table, sp, ctx_t, int(ctx.max()), k, v,
+                                case.mu, q, case.rot_k, case.rv, w.group, w.clip_k, w.clip_v,
+                                case.sm_scale)
+        torch.cuda.synchronize()
+    for s in range(w.batch):
+        case.written[s] = int(ctx[s])
+    pairs = [(0, 0), (5, 13), (11, 22), (15, 31)]
+    ref = oracle_decode(case, q, pairs, ctx=ctx)
+    o = out.cpu().numpy()
+    err = max(attention_error(o[b, hq], ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  sampled max rel err {err:.3e}")
+    assert err <= TIGHT
+    near, n, _ = _append_parity(case, 7, int(case.ctx[7]), 2)
+    assert near <= max(EXEMPT_FRACTION * n, 1)
