@@ -382,6 +382,8 @@ WIN_CASES = {
                      [0, 318, 700]),
     "bf16_g128_folded": (scaled(W4, batch=3, ctx_min=600, ctx_max=600, layers=2, steps=4),
                          [40, 317, 600]),
+    # one layer of the stream workload at full size: batch 16, 16K prompts
+    "bf16_g128_full": (scaled(W4, steps=2), [16384] * 16),
 }
 
 
