@@ -701,15 +701,18 @@ def test_many_splits(name):
     assert attention_error(auto, out) <= 1e-5
 
 
-def test_full_size_decode_step_sampled():
+@pytest.mark.parametrize("folded", [False, True])
+def test_full_size_decode_step_sampled(folded):
     """One layer of the 36-layer stream workload at full size (batch 16, 16K
     prompt): two fused decode steps (kvq_append_decode, the call and split plan
     the benchmark times), the last step's output on sampled heads against the
-    oracle over the GPU's cache, and the appended tokens' encoding."""
+    oracle over the GPU's cache, and the appended tokens' encoding; also in the
+    folded form (rot_v NULL), as the benchmark's folded pass runs it."""
     import rotated_int2_kv_kvq_amd as kvq
     w = W4
-    say("[full] stream workload, one layer, two fused steps")
+    say(f"[full] stream workload, one layer, two fused steps, folded={folded}")
     case = new_case(w, layer=0, keep_initial=False)
+    case.folded = folded
     fill_context(case)
     ctx = case.ctx.copy()
     dev = case.device
