@@ -188,3 +188,14 @@ def test_window_entry_points_reject_invalid_arguments(lib):
     bad = list(a)
     bad[26] = 16                                              # workspace too small
     assert lib.kvq_append_decode_window(*bad) == -3
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """With the library file absent the binding raises; there is no fallback."""
+    import rotated_int2_kv_kvq_amd._lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libkvq.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        L.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        L.page_bytes(128, 128)
