@@ -46,6 +46,9 @@ def parse():
                     help="kvq_append + kvq_decode_attn per layer instead of kvq_append_decode")
     ap.add_argument("--no-folded", action="store_true",
                     help="skip the pass with the value rotation folded into W_V/W_O (rot_v NULL)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill comparison (the prompts encoded with both rotations, "
+                         "with R_V folded, and unrotated)")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the cold long-context decode leg (128K batch 1; ragged 1K-32K batch 64)")
     ap.add_argument("--long-reps", type=int, default=24,
@@ -258,6 +261,9 @@ def main():
         split_ms.append(s0.elapsed_time(s1) / L)
         app_ms.append(a0.elapsed_time(a1) / L)
     del wss
+    # host copies of the first and last layers' caches as the main pass left
+    # them (later passes re-encode the prompt), for the CPU baseline
+    host_pages = {0: pages[0].cpu(), L - 1: pages[L - 1].cpu()}
     split_avg_ms = float(np.mean(split_ms))
     app_avg_ms = float(np.mean(app_ms))
     split_bytes = int((ctx0 + last + 1).sum()) * Hkv * per_tok_head
@@ -315,7 +321,6 @@ def main():
         }
         del wgraphs
 
-    layer0_pages = pages[0].cpu()
 
     # ---------------------------------------------------------------- folded value rotation
     # The pages' deployment form: R_V folded into W_V and W_O, so the library
@@ -384,6 +389,11 @@ def main():
         }
         del fgraphs
 
+    # ---------------------------------------------------------------- prefill overhead
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_leg(w, st, table, pages[0], mus[0], rks[0], rvs[0], dev)
+
     # ---------------------------------------------------------------- long contexts, cold
     long_line = None
     if not args.no_long:
@@ -396,8 +406,10 @@ def main():
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, st, layer0_pages, table, ctxs[last], qs[last][0], per_tok_head,
-                           args.cpu_seconds, sm_scale)
+        sample_steps = sorted({args.warmup, args.warmup + args.steps // 2, total_steps - 1})
+        samples = [(layer, step, host_pages[layer], ctxs[step].cpu(), qs[step][layer].cpu())
+                   for layer in sorted(host_pages) for step in sample_steps]
+        cpu = cpu_baseline(w, st, samples, table, per_tok_head, args.cpu_seconds, sm_scale)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -450,6 +462,9 @@ def main():
             "algorithmic_bytes": split_bytes,
         },
         "cpu_baseline": cpu,
+        "bits_per_element": bits_per_element(w.group),
+        "prefill": prefill,
+        "context": pages_context(w, ctx0, per_tok_head, prefill),
         "windows": win_line,
         "folded": fold_line,
         "long_context": long_line,
@@ -457,20 +472,22 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s, sm_scale):
-    """The float64 oracle's decode of layer 0 on the host, over as many
-    (sequence, KV head) pairs as fit in the time budget, in cache GB/s: with
-    one BLAS thread, then (under "all_cores") with one per host core, at most
-    16, for two thirds of the budget."""
+def cpu_baseline(w, st, samples, table, per_tok_head, budget_s, sm_scale):
+    """The float64 oracle's decode on the host, in cache GB/s, over a bounded
+    sample of the timed work: each (layer, step) of `samples` gets an equal
+    share of the time budget and decodes (sequence, KV head) pairs in order
+    until its share is spent.  First with one BLAS thread, then (under
+    "all_cores") with one per host core, at most 16, for two thirds of the
+    budget."""
     import oracle as O
     from threadpoolctl import threadpool_limits
-    args = (O, w, st, pages_l0, table, ctx_t, q_l0, per_tok_head)
     with threadpool_limits(1):
-        res = _cpu_baseline(*args, budget_s, sm_scale, 1)
+        res = _cpu_baseline(O, w, st, samples, table, per_tok_head, budget_s, sm_scale, 1)
     n = min(os.cpu_count() or 1, 16)
     if n > 1:
         with threadpool_limits(n):
-            res["all_cores"] = _cpu_baseline(*args, budget_s * 2 / 3, sm_scale, n)
+            res["all_cores"] = _cpu_baseline(O, w, st, samples, table, per_tok_head,
+                                             budget_s * 2 / 3, sm_scale, n)
     res["cpu_model"] = _cpu_model()
     return res
 
@@ -486,39 +503,133 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def _cpu_baseline(O, w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s, sm_scale,
-                  threads):
+def _cpu_baseline(O, w, st, samples, table, per_tok_head, budget_s, sm_scale, threads):
     import numpy as np
-    ctx = ctx_t.cpu().numpy()
     tab = table.cpu()
-    q = q_l0.float().cpu().double().numpy()
     Hkv, Hg = w.num_kv_heads, w.num_q_heads // w.num_kv_heads
     done_bytes = 0
     pairs = 0
+    share = budget_s / len(samples)
     t0 = time.perf_counter()
-    # passes over the (sequence, KV head) pairs until the time budget is spent
-    while time.perf_counter() - t0 < budget_s:
+    for (layer, step, pages_l, ctx_t, q_t) in samples:
+        ctx = ctx_t.numpy()
+        q = q_t.float().double().numpy()
+        ts = time.perf_counter()
         for b in range(w.batch):
             n = int(ctx[b])
             n_pages = (n + 15) // 16
-            cache = pages_l0.index_select(0, tab[b, :n_pages].long()).numpy()
+            cache = pages_l.index_select(0, tab[b, :n_pages].long()).numpy()
             ident = np.arange(n_pages, dtype=np.int32)[None, :]
             for h in range(Hkv):
                 heads = [(0, hq) for hq in range(h * Hg, (h + 1) * Hg)]
-                O.decode(cache, ident, [n], q[b:b + 1], st.rot_k[0], st.rot_v[0], sm_scale, Hkv,
-                         w.group, pairs=heads)
+                O.decode(cache, ident, [n], q[b:b + 1], st.rot_k[layer], st.rot_v[layer], sm_scale,
+                         Hkv, w.group, pairs=heads)
                 done_bytes += n * per_tok_head
                 pairs += 1
-                if time.perf_counter() - t0 > budget_s:
+                if time.perf_counter() - ts > share:
                     break
-            if time.perf_counter() - t0 > budget_s:
+            if time.perf_counter() - ts > share:
                 break
     el = time.perf_counter() - t0
+    where = ", ".join(f"layer {layer} step {step}" for (layer, step, *_rest) in samples)
     return {"value": round(done_bytes / el / 1e9, 6), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"float64 numpy oracle decode of layer 0, {pairs} (sequence, KV head) pairs "
-                      f"x {Hg} query heads at {int(ctx.max())} tokens, BLAS limited to "
-                      f"{threads} thread{'s' if threads > 1 else ''}, {el:.1f} s"}
+            "sample": f"float64 numpy oracle decode at ({where}), an equal share of "
+                      f"{budget_s:.0f} s each: {pairs} (sequence, KV head) pairs x {Hg} query "
+                      f"heads in order, BLAS limited to {threads} thread"
+                      f"{'s' if threads > 1 else ''}; {el:.1f} s in all"}
+
+
+def bits_per_element(group: int, head_dim: int = 128) -> float:
+    """Stored bits per cached K or V element: 2-bit codes plus one fp16
+    (scale, zero) pair per group: 2 + 32 / group."""
+    return 2.0 + 32.0 / group
+
+
+def pages_context(w, ctx0, per_tok_head, prefill):
+    """The pages' own figures beside this measurement (none is on MI355X and
+    none is a target), and this build's counterparts."""
+    import numpy as np
+    n = int(np.max(ctx0))
+    sink, recent = 64, 256
+    body = max(n - sink - recent, 0)
+    with_windows = (body * bits_per_element(w.group) + min(n, sink + recent) * 16) / max(n, 1)
+    return {
+        "pages": [
+            {"figure": "decode speed-up vs BF16 FlashDecoding-v2", "value": "up to 3.0x",
+             "method": "OScaR", "hardware": "not stated",
+             "source": "'The KV cache goes on a diet: INT2 quantization nears lossless', "
+                       "'Crush it to INT2'"},
+            {"figure": "memory reduction vs BF16", "value": "5.3x", "method": "OScaR",
+             "hardware": "not stated", "source": "same page and section"},
+            {"figure": "throughput increase vs BF16 FlashDecoding-v2", "value": "4.1x",
+             "method": "OScaR", "hardware": "not stated", "source": "same page and section"},
+            {"figure": "overhead on decode latency, throughput and prefill time",
+             "value": "<= ~2%", "method": "OptR", "hardware": "an NVIDIA GPU",
+             "source": "'Pith review of: Output-Aware Rotation for INT2 KV-Cache Quantization', "
+                       "'If this is right' and the efficiency figure"},
+            {"figure": "effective bits per cache element", "value": 2.32, "method": "OptR",
+             "source": "same review, 'The reading' and 'Core claim'"},
+        ],
+        "this_build": {
+            "bits_per_element": bits_per_element(w.group),
+            "memory_reduction_vs_bf16": round(16.0 / bits_per_element(w.group), 3),
+            "bits_per_element_with_bf16_windows": round(with_windows, 4),
+            "windows_context": n,
+            "prefill_overhead_pct": (prefill or {}).get("overhead_pct"),
+            "note": "bits with windows: the INT2 body plus 64 sink and 256 recent BF16 tokens "
+                    "over this context; the overhead compares the encoding kernels only "
+                    "(a real prefill adds attention and projections that dilute it)",
+        },
+    }
+
+
+def prefill_leg(w, st, table, pages0, mu, rk, rv, dev, reps: int = 3):
+    """The prompts of one layer (every sequence's prior context) encoded three
+    ways into a scratch cache: with R_K and R_V, with R_V folded into the
+    weights (rot_v NULL), and with neither rotation (rot_k and rot_v NULL: the
+    plain INT2 cache the rotations are measured against).  Mean of `reps`
+    timed calls each, after one warm-up, between HIP events."""
+    import numpy as np
+    import torch
+
+    import rotated_int2_kv_kvq_amd as kvq
+    from workload import kv_for_sequence
+
+    n = int(st.ctx_lens.min())
+    if n != int(st.ctx_lens.max()):
+        return None  # one call per shared prompt length: the stream workload has one
+    kv = [kv_for_sequence(w, st, 0, b, 0, n, dev) for b in range(w.batch)]
+    k = torch.stack([x[0] for x in kv]).contiguous()
+    v = torch.stack([x[1] for x in kv]).contiguous()
+    del kv
+    scratch = torch.empty_like(pages0)
+    sp = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    modes = {"rotated": (rk, rv), "value_rotation_folded": (rk, None), "unrotated": (None, None)}
+    ms = {}
+    for name, (a, b_) in modes.items():
+        kvq.append(scratch, table, sp, k, v, mu, a, b_, w.group, w.clip_k, w.clip_v)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            kvq.append(scratch, table, sp, k, v, mu, a, b_, w.group, w.clip_k, w.clip_v)
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / reps
+    del k, v, scratch
+    tokens = w.batch * n
+    base = ms["unrotated"]
+    return {
+        "call": "kvq_append of the whole prompt, one layer",
+        "batch": w.batch, "prompt_tokens": n, "kv_heads": w.num_kv_heads,
+        "ms": {k_: round(t, 4) for k_, t in ms.items()},
+        "mtok_s": {k_: round(tokens / (t * 1e-3) / 1e6, 3) for k_, t in ms.items()},
+        "overhead_pct": {
+            "both_rotations_vs_none": round((ms["rotated"] / base - 1) * 100, 2),
+            "key_rotation_only_vs_none": round((ms["value_rotation_folded"] / base - 1) * 100, 2),
+        },
+        "rotation_tflops": round(tokens * w.num_kv_heads * 65536 / (ms["rotated"] * 1e-3) / 1e12, 2),
+    }
 
 
 # Long-context decode workloads, timed cold with the automatic split plan:
@@ -526,7 +637,8 @@ def _cpu_baseline(O, w, st, pages_l0, table, ctx_t, q_l0, per_tok_head, budget_s
 # Infinity Cache several times, so that each call reads its cache from HBM
 # (a flushing write between calls would leave dirty lines whose write-back
 # competes with the reads).
-LONG_WORKLOADS = ("qwen3_8b_b1_ctx128k_sinks", "qwen3_8b_b64_ctx1k_32k_g64")
+LONG_WORKLOADS = ("qwen3_8b_b1_ctx128k_sinks", "qwen3_8b_b64_ctx1k_32k_g64",
+                  "qwen3_8b_b4_ctx8k")
 COLD_BYTES = 1200 << 20
 
 

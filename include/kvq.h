@@ -28,6 +28,11 @@
  *    of the output is o = o_rot * R_V^T.
  *  - head_dim must be 128; group (channels sharing one fp16 scale/zero) is 64
  *    or 128; a block (page) holds 16 tokens.
+ *  - Alignment: the cache, window store, k, v, q, out, mu and rotation
+ *    pointers must be 16-byte aligned, the int32 arrays (block table, start
+ *    positions, context lengths) 4-byte aligned and the workspace 256-byte
+ *    aligned; a misaligned pointer is KVQ_ERR_INVALID_ARG (the workspace's,
+ *    KVQ_ERR_WORKSPACE).
  *  - Return values are kvq_status codes.  Arguments are validated on the host
  *    before anything is launched; a failing check launches nothing.  A launch
  *    failure reported by the HIP runtime returns KVQ_ERR_HIP.  Values that
@@ -104,7 +109,10 @@ size_t kvq_page_bytes(int32_t head_dim, int32_t group);
  *                          caller's W_V and W_O (the OptR review page, "If this
  *                          is right": value-side rotations are folded into the
  *                          projection weights), so v arrives already rotated and
- *                          is encoded as given (y = v)
+ *                          is encoded as given (y = v).  rot_k may be NULL: the
+ *                          centred key is encoded unrotated (x = k - mu); with
+ *                          both NULL the cache is plain per-group INT2, the
+ *                          unrotated baseline of the rotation methods
  *   clip_k, clip_v host    clipping ratios in (0, 1]
  * Only the written tokens' codes, scales and zeros change; other tokens in the
  * same pages keep their contents.  Two sequences must not share a physical
@@ -145,7 +153,9 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *   rot_k, rot_v   device  float32 [num_kv_heads][head_dim][head_dim]; rot_v
  *                          may be NULL (value rotation folded into W_V and W_O):
  *                          out is then sum_t p_t v_hat_t, left in the rotated
- *                          value basis for the caller's folded W_O
+ *                          value basis for the caller's folded W_O.  rot_k may
+ *                          be NULL for a cache whose keys were encoded
+ *                          unrotated: q_r = q
  *   sm_scale       host    softmax scale (1/sqrt(head_dim) for standard attention)
  *   out            device  float32 [batch][num_q_heads][head_dim] (written)
  *   workspace      device  at least kvq_decode_workspace_bytes(...) bytes,

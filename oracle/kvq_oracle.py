@@ -57,7 +57,7 @@ __all__ = [
     "sz_site", "write_tokens", "read_tokens", "dequant", "attend", "decode",
     "append", "plain_attention", "SINK", "RECENT", "WINDOW", "window_slot", "window_parts",
     "bf16_round", "window_write", "append_windowed", "decode_windowed", "dequantized_kv",
-    "eq8_decomposition", "value_rotation",
+    "eq8_decomposition", "value_rotation", "key_rotation",
 ]
 
 
@@ -87,8 +87,12 @@ def bits_per_element(head_dim: int = HEAD_DIM, group: int = 128) -> float:
 # --------------------------------------------------------------------------- append
 def rotate(x, R):
     """Row-vector rotation x @ R for x [..., Hkv, d] and R [Hkv, d, d]
-    ([OptR] "Core claim": one orthogonal rotation per KV head)."""
+    ([OptR] "Core claim": one orthogonal rotation per KV head).  R None is the
+    identity: no rotation (the unrotated INT2 cache the rotations are
+    compared against)."""
     x = np.asarray(x, np.float64)
+    if R is None:
+        return x.copy()
     R = np.asarray(R, np.float64)
     return np.einsum("...hi,hij->...hj", x, R)
 
@@ -137,6 +141,14 @@ def quantize_on_grid(x, s16, z16, group: int):
     return codes.reshape(x.shape)
 
 
+def key_rotation(rot_k, h, d: int = HEAD_DIM):
+    """R_K of KV head h as float64; rot_k None (keys encoded unrotated) is the
+    identity."""
+    if rot_k is None:
+        return np.eye(d)
+    return np.asarray(rot_k[h], np.float64)
+
+
 def value_rotation(rot_v, h, d: int = HEAD_DIM):
     """R_V of KV head h as float64; rot_v None is the folded form ([OptR]
     "If this is right": the value rotations are folded into W_V and W_O), where
@@ -151,12 +163,12 @@ def encode_tokens(k, v, mu, rot_k, rot_v, group: int, clip_k: float, clip_v: flo
     """Centre, rotate and quantise new tokens.
 
     k, v: [..., Hkv, d]; mu: [Hkv, d]; rot_k, rot_v: [Hkv, d, d] (rot_v None:
-    values folded, encoded as given).
+    values folded, encoded as given; rot_k None: centred keys unrotated).
     Key centring subtracts mu before rotation ([OptR] "What carries the
     argument", mechanism 2); values are not centred.
     """
     x = rotate(np.asarray(k, np.float64) - np.asarray(mu, np.float64), rot_k)
-    y = np.asarray(v, np.float64) if rot_v is None else rotate(v, rot_v)
+    y = rotate(v, rot_v)
     ks, kz, kc, ks_raw, kz_raw = encode_groups(x, group, clip_k)
     vs, vz, vc, vs_raw, vz_raw = encode_groups(y, group, clip_v)
     return dict(x=x, y=y, k_s=ks, k_z=kz, k_codes=kc, v_s=vs, v_z=vz, v_codes=vc,
@@ -306,7 +318,7 @@ def decode(cache, block_table, ctx_len, q, rot_k, rot_v, sm_scale: float, num_kv
             tok = read_tokens(cache, block_table, b, np.arange(n), h, num_kv_heads, group)
             k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
             v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
-            Rk = np.asarray(rot_k[h], np.float64)
+            Rk = key_rotation(rot_k, h, d)
             Rv = value_rotation(rot_v, h, d)
             for hq in heads:
                 q_r = q[b, hq] @ Rk
@@ -331,7 +343,7 @@ def dequantized_kv(cache, block_table, b, n, h, num_kv_heads, group, mu, rot_k, 
     tok = read_tokens(cache, block_table, b, np.arange(n), h, num_kv_heads, group)
     k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
     v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
-    Rk = np.asarray(rot_k[h], np.float64)
+    Rk = key_rotation(rot_k, h)
     Rv = value_rotation(rot_v, h)
     return k_hat @ Rk.T + np.asarray(mu[h], np.float64), v_hat @ Rv.T
 
@@ -462,7 +474,7 @@ def decode_windowed(cache, block_table, ctx_len, q, rot_k, rot_v, mu, win_k, win
             tok = read_tokens(cache, block_table, b, bpos, h, num_kv_heads, group)
             k_hat = dequant(tok["k_s"], tok["k_z"], tok["k_codes"], group)
             v_hat = dequant(tok["v_s"], tok["v_z"], tok["v_codes"], group)
-            Rk = np.asarray(rot_k[h], np.float64)
+            Rk = key_rotation(rot_k, h)
             Rv = value_rotation(rot_v, h)
             for hq in heads:
                 if len(wpos) + len(bpos) == 0:

@@ -49,12 +49,13 @@ int check_append(const void* pages, int64_t num_blocks, int32_t num_kv_heads, in
   if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
     return KVQ_ERR_INVALID_ARG;
   if (batch == 0 || num_new == 0) return KVQ_OK;
-  // rot_v may be null: the value rotation is folded into the caller's weights
-  if (!pages || !block_table || !start_pos || !k || !v || !mu || !rot_k)
-    return KVQ_ERR_INVALID_ARG;
+  // rot_v may be null: the value rotation is folded into the caller's weights;
+  // rot_k may be null: keys are centred but not rotated
+  if (!pages || !block_table || !start_pos || !k || !v || !mu) return KVQ_ERR_INVALID_ARG;
   if (!aligned(pages, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(mu, 16) ||
-      !aligned(rot_k, 16) || (rot_v && !aligned(rot_v, 16)))
+      (rot_k && !aligned(rot_k, 16)) || (rot_v && !aligned(rot_v, 16)))
     return KVQ_ERR_INVALID_ARG;
+  if (!aligned(block_table, 4) || !aligned(start_pos, 4)) return KVQ_ERR_INVALID_ARG;
   return KVQ_OK;
 }
 }  // namespace
@@ -103,7 +104,7 @@ int check_decode(const void* pages, int64_t num_blocks, int32_t num_kv_heads, in
                  const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
                  const void* q, int32_t q_dtype, const float* rot_k, const float* rot_v,
                  float sm_scale, const float* out, const void* workspace, size_t workspace_bytes,
-                 int32_t split_pages, kvq::DecodePlan* plan) {
+                 int32_t split_pages, kvq::DecodePlan* plan, bool own_workspace = true) {
   if (!valid_geometry(head_dim, group)) return KVQ_ERR_INVALID_ARG;
   if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
   if (!valid_decode_shape(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages))
@@ -115,12 +116,16 @@ int check_decode(const void* pages, int64_t num_blocks, int32_t num_kv_heads, in
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KVQ_ERR_INVALID_ARG;
   if (batch == 0) return KVQ_OK;
-  // rot_v may be null: the output stays in the rotated value basis
-  if (!pages || !block_table || !ctx_len || !q || !rot_k || !out)
-    return KVQ_ERR_INVALID_ARG;
-  if (!aligned(pages, 16) || !aligned(rot_k, 16) || (rot_v && !aligned(rot_v, 16)))
+  // rot_v may be null: the output stays in the rotated value basis; rot_k may
+  // be null: the keys were encoded unrotated and the query is not rotated
+  if (!pages || !block_table || !ctx_len || !q || !out) return KVQ_ERR_INVALID_ARG;
+  // q is read as 32- and 64-bit words and out written as 32-bit words: both
+  // must be 16-byte aligned (as every tensor allocation is)
+  if (!aligned(pages, 16) || (rot_k && !aligned(rot_k, 16)) || (rot_v && !aligned(rot_v, 16)) ||
+      !aligned(q, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(ctx_len, 4))
     return KVQ_ERR_INVALID_ARG;
   *plan = kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
+  if (!own_workspace) return KVQ_OK;  // the library's static scratch; its size is checked apart
   if (!workspace || workspace_bytes < plan->total || !aligned(workspace, 256))
     return KVQ_ERR_WORKSPACE;
   return KVQ_OK;
@@ -203,7 +208,8 @@ KVQ_API int kvq_window_write(void* window, int32_t num_kv_heads, int32_t head_di
   if (kv_dtype != KVQ_F32 && kv_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
   if (batch == 0 || num_new == 0) return KVQ_OK;
   if (!window || !start_pos || !k || !v) return KVQ_ERR_INVALID_ARG;
-  if (!aligned(window, 16) || !aligned(k, 16) || !aligned(v, 16)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(window, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(start_pos, 4))
+    return KVQ_ERR_INVALID_ARG;
   const int rc = kvq::launch_window_write(static_cast<uint16_t*>(window), num_kv_heads, batch,
                                           start_pos, num_new, k, v, kv_dtype == KVQ_BF16,
                                           static_cast<hipStream_t>(stream));

@@ -121,11 +121,14 @@ __global__ __launch_bounds__(512) void append_kernel(
   const int wg_last = min(last_page, wg_first + pages_per_wg - 1);
 
   // rot_v null: the value rotation is folded into the caller's weights and
-  // values are encoded as given (no products for them).
+  // values are encoded as given (no products for them); rot_k null: keys are
+  // centred but not rotated (plain INT2 of the centred key).
   const bool v_ident = rot_v == nullptr;
+  const bool k_ident = rot_k == nullptr;
   // Stage R_K and R_V: LDS row r = 16*(c%8) + c/8 holds column c of R, so the
   // MFMA output column (tile nt, lane n) is rotated channel 8*n + nt.
-  for (int mat = 0; mat < (v_ident ? 1 : 2); ++mat) {
+  for (int mat = 0; mat < 2; ++mat) {
+    if (mat ? v_ident : k_ident) continue;
     const float* R = (mat ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim;
     for (int idx = tid; idx < kHeadDim * kHeadDim / 4; idx += 512) {
       const int krow = idx >> 5;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(512) void append_kernel(
   float mr[32];
 #pragma unroll
   for (int s = 0; s < 32; ++s) mr[s] = 0.f;
-  if (mat == 0) {
+  if (mat == 0 && !k_ident) {
     const float4* m4 = reinterpret_cast<const float4*>(mu + h * kHeadDim + 32 * kg);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -168,7 +171,8 @@ __global__ __launch_bounds__(512) void append_kernel(
   }
   // Token row t of page pg (input channels 32kg..32kg+31) if that token is
   // one this call writes; false (nothing loaded) otherwise.
-  const bool direct = mat == 1 && v_ident;  // values read in the output layout below
+  // Unrotated rows are read in the output layout below instead.
+  const bool direct = mat == 1 ? v_ident : k_ident;
   auto fetch = [&](int pg, RawRow<kBf16>& r) {
     const int pos = pg * kBlock + t;
     const bool row_new = !direct && pg <= wg_last && pos >= s0 && pos < s0 + T;
@@ -181,6 +185,10 @@ __global__ __launch_bounds__(512) void append_kernel(
   };
   RawRow<kBf16> raw;
   bool cur_new = fetch(wg_first + w4, raw);
+  // unrotated keys: the mean of this lane's output channels 8n..8n+7
+  float m8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m8[e] = (direct && mat == 0) ? mu[h * kHeadDim + 8 * n + e] : 0.f;
 
   for (int pg = wg_first + w4; pg <= wg_last; pg += 4) {
     if (pg >= max_blocks) break;
@@ -203,6 +211,7 @@ __global__ __launch_bounds__(512) void append_kernel(
     for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (direct) {
       // lane holds tokens 4*r4 + i, channels 8n..8n+7 of the value as given
+      // (of the key less its mean)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tpos = pg * kBlock + 4 * r4 + i;
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(512) void append_kernel(
             x8[4] = f1.x; x8[5] = f1.y; x8[6] = f1.z; x8[7] = f1.w;
           }
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) acc[nt][i] = x8[nt];
+          for (int nt = 0; nt < 8; ++nt) acc[nt][i] = x8[nt] - m8[nt];
         }
       }
     } else {
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(512) void append_kernel(
           bits |= static_cast<uint32_t>(qv) << (2 * nt);
         }
       } else if (sf != 0.f) {
-        // values as given (bfloat16 ones often lie exactly on a rounding
+        // unrotated values (bfloat16 ones often lie exactly on a rounding
         // boundary): the correctly rounded quotient breaks ties to even
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {

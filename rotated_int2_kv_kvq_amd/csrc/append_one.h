@@ -63,10 +63,10 @@ __device__ __forceinline__ void append_one_body(
   // split-K partial products: thread -> (mat, quarter kq, column jc).  The
   // rotation loads go out first: nothing they need depends on another load.
   // rot_v null (value rotation folded into the caller's weights): the value
-  // is encoded as given.
+  // is encoded as given; rot_k null: the centred key is encoded unrotated.
   {
     const int pm = tid >> 9, kq = (tid >> 7) & 3, jc = tid & 127;
-    const bool ident = pm == 1 && rot_v == nullptr;
+    const bool ident = (pm ? rot_v : rot_k) == nullptr;
     float rcol[32];
     if (!ident) {
       const float* R = (pm ? rot_v : rot_k) + static_cast<size_t>(h) * kHeadDim * kHeadDim +

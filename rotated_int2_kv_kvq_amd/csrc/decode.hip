@@ -34,6 +34,8 @@
 //      through a last-workgroup counter needs device-scope release/acquire,
 //      i.e. an L2 writeback and invalidate per workgroup on this multi-XCD
 //      part, which costs far more than the launch.)
+#include <algorithm>
+
 #include "append_one.h"
 #include "kvq_common.h"
 #include "kvq_launch.h"
@@ -382,10 +384,11 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
 
   // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
   // first (before the query rows, whose store to LDS waits for them), one pass
-  // over R_K for the four heads
-  const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
+  // over R_K for the four heads.  rot_k null: the keys were not rotated, q_r = q.
+  const bool ident = rot_k == nullptr;
   float ra[32], rb[32];
-  if (act) {
+  if (act && !ident) {
+    const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       ra[i] = R[i * kHeadDim + lane];
@@ -412,7 +415,14 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
     qin[hh][c + 1] = v1;
   }
   __syncthreads();
-  if (act) {
+  if (act && ident) {
+    // quarter wv of the split-K sum holds channels 32wv..32wv+31 of q
+#pragma unroll
+    for (int hh = 0; hh < kHT; ++hh) {
+      red[wv][hh][lane] = (lane >> 5) == wv ? qin[hh][lane] : 0.f;
+      red[wv][hh][lane + 64] = ((lane + 64) >> 5) == wv ? qin[hh][lane + 64] : 0.f;
+    }
+  } else if (act) {
 #pragma unroll
     for (int hh = 0; hh < kHT; ++hh) {
       float a0 = 0.f, a1 = 0.f;
@@ -1525,19 +1535,23 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Pages per split, from the longest context (the lengths themselves stay on
-// the device): at least 128 pages (four 8-page blocks per wave), below which
-// per-workgroup start-up and the merge of many partials cost more than the
-// extra workgroups bring; above that, about 8192 workgroups for the longest
-// context in every sequence, in whole 32-page steps, so that a ragged batch
-// (whose actual work may be half of that) still leaves the dispatcher many
-// short workgroups to balance; at most 512 pages.  Measured cold on MI355X:
-// 128K context batch 1 and 16K batch 16 are fastest at 128 pages; a batch of
-// 64 with contexts of 1K-32K at 128 (230 us) against 512 (258 us).
+// the device).  A large grid takes at least 128 pages per split (four 8-page
+// blocks per wave), below which per-workgroup start-up and the merge of many
+// partials cost more than the extra workgroups bring; above that, about 8192
+// workgroups for the longest context in every sequence, in whole 32-page
+// steps, so that a ragged batch (whose actual work may be half of that) still
+// leaves the dispatcher many short workgroups to balance; at most 512 pages.
+// A small grid lowers the floor toward 32 pages (one block per wave) so that
+// the launch still has about 512 workgroups: 128 splits of 128 pages would
+// leave half of the 256 CUs idle.  Measured cold on MI355X: 128K context
+// batch 1 and 16K batch 16 are fastest at 128 pages; a batch of 64 with
+// contexts of 1K-32K at 128 (230 us) against 512 (258 us).
 int choose_split_pages(int B, int Hkv, int QG, int max_ctx) {
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
   const int64_t total = static_cast<int64_t>(B) * Hkv * QG * max_pages;
+  const int64_t floor = std::min<int64_t>(128, std::max<int64_t>(32, total / 512 / 8 * 8));
   int64_t spw = (total / 8192 + 16) / 32 * 32;
-  if (spw < 128) spw = 128;
+  if (spw < floor) spw = floor;
   if (spw > 512) spw = 512;
   return static_cast<int>(spw);
 }

@@ -28,6 +28,18 @@ class Case:
     written: dict = field(default_factory=dict)  # b -> number of positions written
     # value rotation folded into the caller's W_V / W_O: rot_v passed as None
     folded: bool = False
+    # no key rotation either (rot_k passed as None): plain per-group INT2
+    unrotated: bool = False
+
+    @property
+    def rk(self):
+        """R_K as the library takes it (None when unrotated)."""
+        return None if self.unrotated else self.rot_k
+
+    @property
+    def rk_host(self):
+        """R_K as the oracle takes it (None when unrotated)."""
+        return None if self.unrotated else self.st.rot_k[self.layer]
 
     @property
     def sm_scale(self) -> float:
@@ -73,7 +85,7 @@ def append_range(case: Case, seqs, start: int, count: int):
     idx = torch.as_tensor(list(seqs), device=case.device, dtype=torch.long)
     table = case.table.index_select(0, idx).contiguous()
     sp = torch.full((len(seqs),), start, dtype=torch.int32, device=case.device)
-    kvq.append(case.pages, table, sp, k, v, case.mu, case.rot_k, case.rv, w.group, w.clip_k,
+    kvq.append(case.pages, table, sp, k, v, case.mu, case.rk, case.rv, w.group, w.clip_k,
                w.clip_v)
     for b in seqs:
         case.written[b] = max(case.written.get(b, 0), start + count)
@@ -108,7 +120,7 @@ def oracle_encode(case: Case, b: int, start: int, count: int):
     k, v = kv_for_sequence(case.w, case.st, case.layer, b, start, count, case.device)
     k, v = k.cpu(), v.cpu()
     return O.encode_tokens(k.double().numpy(), v.double().numpy(), case.mu.cpu().double().numpy(),
-                           case.st.rot_k[case.layer], case.rv_host, case.w.group,
+                           case.rk_host, case.rv_host, case.w.group,
                            case.w.clip_k, case.w.clip_v)
 
 
@@ -117,7 +129,7 @@ def decode(case: Case, q: torch.Tensor, ctx: np.ndarray | None = None, split_pag
     ctx = case.ctx if ctx is None else ctx
     ctx_t = torch.from_numpy(np.asarray(ctx, np.int32)).to(case.device)
     max_ctx = int(max(ctx.max(), 0)) if max_ctx is None else max_ctx
-    return kvq.decode(case.pages, case.table, ctx_t, max_ctx, q, case.rot_k, case.rv,
+    return kvq.decode(case.pages, case.table, ctx_t, max_ctx, q, case.rk, case.rv,
                       case.w.group, case.sm_scale, split_pages=split_pages)
 
 
@@ -130,7 +142,7 @@ def oracle_decode(case: Case, q: torch.Tensor, pairs, ctx=None):
         n = int(ctx[b])
         cache, table = host_pages(case, b, n)
         heads = [hq for (bb, hq) in pairs if bb == b]
-        o = O.decode(cache, table, [n], qh[b:b + 1], case.st.rot_k[case.layer],
+        o = O.decode(cache, table, [n], qh[b:b + 1], case.rk_host,
                      case.rv_host, case.sm_scale, case.w.num_kv_heads, case.w.group,
                      pairs=[(0, hq) for hq in heads])
         for hq in heads:

@@ -1,13 +1,23 @@
 """Host-side checks of the C ABI: the library loads, exports every symbol the
 header declares, and rejects invalid arguments before launching anything
-(no GPU needed: every call here returns before the first HIP call)."""
+(no GPU needed: every call here returns before the first HIP call).
+
+The argument-validation tests pass made-up device addresses and rely on the
+host checks failing first; on a machine with a visible GPU a regression in a
+check would launch kernels on those addresses, so there they are skipped (the
+GPU tests exercise the same checks with real buffers)."""
 import ctypes
 import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="made-up device addresses: host-only test")
+
 HEADER = os.path.join(ROOT, "include", "kvq.h")
 
 
@@ -75,6 +85,7 @@ def _append(lib, **kw):
                           args["ck"], args["cv"], None)
 
 
+@no_gpu
 def test_append_rejects_invalid_arguments(lib):
     assert _append(lib, g=32) == -1
     assert _append(lib, d=64, g=64) == -2
@@ -84,6 +95,7 @@ def test_append_rejects_invalid_arguments(lib):
     assert _append(lib, hkv=0) == -1
     assert _append(lib, k=None) == -1
     assert _append(lib, pages=(1 << 20) + 4) == -1          # misaligned
+    assert _append(lib, start=(1 << 22) + 2) == -1           # int32 array alignment
     assert _append(lib, B=0) == 0 and _append(lib, T=0) == 0  # no-ops
 
 
@@ -98,6 +110,7 @@ def _decode(lib, **kw):
                                args["scale"], args["out"], args["ws"], args["wsb"], args["sp"], None)
 
 
+@no_gpu
 def test_decode_rejects_invalid_arguments(lib):
     assert _decode(lib, hq=30) == -1
     assert _decode(lib, maxctx=65) == -1                     # beyond the block table
@@ -110,6 +123,10 @@ def test_decode_rejects_invalid_arguments(lib):
     assert _decode(lib, wsb=16) == -3
     assert _decode(lib, ws=None) == -3
     assert _decode(lib, ws=(1 << 27) + 16) == -3             # workspace alignment
+    assert _decode(lib, q=(1 << 23) + 4) == -1               # q read as 64-bit words
+    assert _decode(lib, out=(1 << 26) + 8) == -1             # out alignment
+    assert _decode(lib, ctx=(1 << 22) + 2) == -1             # int32 array alignment
+    assert _decode(lib, table=(1 << 21) + 1) == -1
     assert _decode(lib, B=0) == 0
     # staged variant: stage mask is validated first
     base = [1 << 20, 4, 8, 128, 128, 1 << 21, 4, 1 << 22, 64, 1, 32, 1 << 23, 1, 1 << 24, 1 << 25,
@@ -135,6 +152,7 @@ def _append_decode(lib, **kw):
                                  a["wsb"], a["sp"], None)
 
 
+@no_gpu
 def test_append_decode_rejects_invalid_arguments(lib):
     # the append's checks
     assert _append_decode(lib, ck=0.0) == -1
@@ -152,6 +170,7 @@ def test_append_decode_rejects_invalid_arguments(lib):
     assert _append_decode(lib, B=0) == 0
 
 
+@no_gpu
 def test_window_entry_points_reject_invalid_arguments(lib):
     import rotated_int2_kv_kvq_amd as kvq
     assert kvq.window_bytes(16, 8) == 16 * 8 * 2 * 320 * 128 * 2
@@ -199,3 +218,4 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
         L.lib()
     with pytest.raises(RuntimeError, match="not built"):
         L.page_bytes(128, 128)
+

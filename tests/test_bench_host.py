@@ -30,11 +30,27 @@ def _tiny_cache(batch=2, n=40, hkv=2, hq=8, group=64, seed=5):
 def test_cpu_baseline_fields():
     w, st, pages, table, ctx, q = _tiny_cache()
     per = bench.cache_bytes_per_token_head(w.group)
-    res = bench.cpu_baseline(w, st, pages, table, ctx, q, per, 0.3, 1.0 / np.sqrt(O.HEAD_DIM))
+    # two (layer, step) samples of the same layer-0 cache
+    samples = [(0, 5, pages, ctx, q), (0, 7, pages, ctx - 3, q)]
+    res = bench.cpu_baseline(w, st, samples, table, per, 0.3, 1.0 / np.sqrt(O.HEAD_DIM))
     assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["cores"] == 1
-    assert res["value"] > 0 and "1 thread," in res["sample"]
+    assert res["value"] > 0 and "1 thread;" in res["sample"]
+    assert "layer 0 step 5, layer 0 step 7" in res["sample"]
     assert isinstance(res["cpu_model"], str) and res["cpu_model"]
     import os
     if (os.cpu_count() or 1) > 1:
         allc = res["all_cores"]
         assert allc["cores"] == min(os.cpu_count(), 16) and allc["value"] > 0
+
+
+def test_bits_and_context_fields():
+    assert bench.bits_per_element(128) == 2.25 and bench.bits_per_element(64) == 2.5
+    w = SimpleNamespace(group=128)
+    ctx = bench.pages_context(w, np.array([16384]), 72, {"overhead_pct": {"x": 1.0}})
+    figs = {f["figure"]: f["value"] for f in ctx["pages"]}
+    assert figs["decode speed-up vs BF16 FlashDecoding-v2"] == "up to 3.0x"
+    assert figs["effective bits per cache element"] == 2.32
+    tb = ctx["this_build"]
+    assert tb["bits_per_element"] == 2.25 and tb["prefill_overhead_pct"] == {"x": 1.0}
+    # 16,064 body tokens at 2.25 bits and 320 window tokens at 16 bits over 16,384
+    assert abs(tb["bits_per_element_with_bf16_windows"] - (16064 * 2.25 + 320 * 16) / 16384) < 1e-4

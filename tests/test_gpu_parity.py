@@ -18,7 +18,8 @@ from workload import WORKLOADS, kv_for_sequence, scaled
 
 from cases import (append_range, decode, fill_context, host_pages, new_case, oracle_decode,
                    oracle_encode, query)
-from parity import ATTN_TOL, EXEMPT_FRACTION, attention_error, check_codes, check_scale_zero
+from parity import (ATTN_TOL, EXEMPT_FRACTION, TALLY, attention_error, check_scale_zero,
+                    code_parity, gate_exempt)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +34,12 @@ TIGHT = 5e-5
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def report(line: str) -> None:
+    """A line for the test log even when pytest captures output."""
+    sys.__stdout__.write(line + "\n")
+    sys.__stdout__.flush()
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,18 +65,30 @@ SMALL = {
     # value rotation folded into W_V / W_O (rot_v passed as None)
     "cfg1_b3_ctx700_folded": scaled(W1, batch=3, ctx_min=700, ctx_max=700),
     "cfg0_g64_folded": scaled(W0, group=64),
+    # no rotation at all (rot_k and rot_v None): the plain INT2 baseline
+    "cfg1_b3_ctx700_unrotated": scaled(W1, batch=3, ctx_min=700, ctx_max=700),
+    "cfg2_b4_ragged_g64_unrotated": scaled(W2, batch=4, ctx_min=1, ctx_max=500),
 }
 
 
 def _folded(name: str) -> bool:
-    return name.endswith("_folded")
+    return name.endswith("_folded") or name.endswith("_unrotated")
+
+
+def _mark(case, name: str):
+    """rot_v None for folded cases; rot_k None too for unrotated ones."""
+    case.folded = _folded(name)
+    case.unrotated = name.endswith("_unrotated")
+    return case
 
 
 def _append_parity(case, b, start, count):
+    """P1-P3 for tokens [start, start + count) of sequence b; returns
+    (exempt elements, elements, boundary groups)."""
     enc = oracle_encode(case, b, start, count)
     cache, table = host_pages(case, b, start + count)
     w = case.w
-    tot_bad = tot_near = tot_n = tot_bnd = 0
+    tot_near = tot_n = tot_bnd = 0
     for h in range(w.num_kv_heads):
         got = O.read_tokens(cache, table, 0, np.arange(start, start + count), h,
                             w.num_kv_heads, w.group)
@@ -78,14 +97,12 @@ def _append_parity(case, b, start, count):
                                            enc[kind + "_z"][:, h], enc[kind + "_s_raw"][:, h],
                                            enc[kind + "_z_raw"][:, h])
             assert bad_sz == 0, f"{kind} scale/zero mismatch outside boundary groups (h={h})"
-            bad, near, n, near_bad = check_codes(got[kind + "_codes"], enc[xkey][:, h],
-                                                 got[kind + "_s"], got[kind + "_z"], w.group,
-                                                 with_exempt_mismatches=True)
-            assert bad == 0, f"{kind} code mismatches outside exemptions: {bad} (h={h})"
-            # values encoded as given (folded): exact ties are an input property;
-            # the exempt elements that differ are counted instead (P2)
-            tot_near += near_bad if (case.folded and kind == "v") else near
-            tot_n += n
+            # values encoded as given (folded) hold exact ties to round half even
+            r = code_parity(got[kind + "_codes"], enc[xkey][:, h], got[kind + "_s"],
+                            got[kind + "_z"], w.group, oracle_codes=enc[kind + "_codes"][:, h],
+                            given=case.folded and kind == "v")
+            tot_near += r["exempt"]
+            tot_n += r["elements"]
             tot_bnd += bnd
     return tot_near, tot_n, tot_bnd
 
@@ -122,8 +139,7 @@ def _unwritten_unchanged(case):
 def test_append_parity_small(name):
     w = SMALL[name]
     say(f"[append] {name}")
-    case = new_case(w)
-    case.folded = _folded(name)
+    case = _mark(new_case(w), name)
     fill_context(case, pieces=[5, 11, 1, 16, 37, 200, 64, 1000])
     torch.cuda.synchronize()
     near = n = bnd = 0
@@ -134,8 +150,8 @@ def test_append_parity_small(name):
         near += a
         n += c
         bnd += d
-    say(f"  elements {n}  exempt {near}  boundary groups {bnd}")
-    assert near <= max(EXEMPT_FRACTION * n, 1)
+    say(f"  boundary groups {bnd}")
+    gate_exempt(near, n)
     _unwritten_unchanged(case)
 
 
@@ -143,8 +159,7 @@ def test_append_parity_small(name):
 def test_decode_parity_small(name):
     w = SMALL[name]
     say(f"[decode] {name}")
-    case = new_case(w, keep_initial=False)
-    case.folded = _folded(name)
+    case = _mark(new_case(w, keep_initial=False), name)
     fill_context(case)
     q = query(case)
     out = decode(case, q).cpu().numpy()
@@ -258,7 +273,7 @@ def test_cache_beyond_4gib():
             a, c, _ = _append_parity(case, b, 0, int(case.ctx[b]))
             near += a
             n += c
-        assert near <= max(EXEMPT_FRACTION * n, 1)
+        gate_exempt(near, n)
     finally:
         case.pages = None
         del big
@@ -322,13 +337,14 @@ def test_stream_append_then_decode():
         say(f"  step {step} max rel err {err:.3e}")
         assert err <= TIGHT
     near, n, _ = _append_parity(case, 1, int(case.ctx[1]), w.steps)
-    assert near <= max(EXEMPT_FRACTION * n, 1)
+    gate_exempt(near, n)
 
 
 STEP_CASES = {
     "cfg4_b3_layer5": SMALL["cfg4_b3_layer5"],
     "cfg2_b5_ragged_g64": scaled(W2, batch=5, ctx_min=1, ctx_max=300, steps=3),
     "cfg4_b3_layer5_folded": SMALL["cfg4_b3_layer5"],
+    "cfg4_b3_layer5_unrotated": SMALL["cfg4_b3_layer5"],
 }
 
 
@@ -342,7 +358,8 @@ def test_append_decode_step(name):
     layer = min(1, w.layers - 1)
     a = new_case(w, layer=layer, keep_initial=False)
     b = new_case(w, layer=layer, keep_initial=False)
-    a.folded = b.folded = _folded(name)
+    _mark(a, name)
+    _mark(b, name)
     fill_context(a)
     fill_context(b)
     ctx = a.ctx.copy()
@@ -352,14 +369,14 @@ def test_append_decode_step(name):
         k = torch.stack([x[0] for x in kv]).contiguous()
         v = torch.stack([x[1] for x in kv]).contiguous()
         sp = torch.from_numpy(ctx.astype(np.int32)).to(dev)
-        kvq.append(a.pages, a.table, sp, k, v, a.mu, a.rot_k, a.rv, w.group, w.clip_k,
+        kvq.append(a.pages, a.table, sp, k, v, a.mu, a.rk, a.rv, w.group, w.clip_k,
                    w.clip_v)
         ctx = ctx + 1
         q = query(a, step)
         out_a = decode(a, q, ctx=ctx)
         ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
         out_b = kvq.append_decode(b.pages, b.table, sp, ctx_t, int(ctx.max()), k, v, b.mu, q,
-                                  b.rot_k, b.rv, w.group, w.clip_k, w.clip_v, b.sm_scale)
+                                  b.rk, b.rv, w.group, w.clip_k, w.clip_v, b.sm_scale)
         torch.cuda.synchronize()
         assert torch.equal(a.pages, b.pages), step
         assert torch.equal(out_a, out_b), step
@@ -488,14 +505,14 @@ def test_windows_prefill_decode_and_stream(name):
                                              enc[kind + "_s_raw"][:, h],
                                              enc[kind + "_z_raw"][:, h])
                 assert bad_sz == 0
-                bad, nr, n, nr_bad = check_codes(got[kind + "_codes"], enc[xkey][:, h],
-                                                 got[kind + "_s"], got[kind + "_z"], w.group,
-                                                 with_exempt_mismatches=True)
-                assert bad == 0
                 # the BF16 window copies are encoded as given when folded (P2)
-                near += nr_bad if (case.folded and kind == "v") else nr
-                n_el += n
-    assert n_el > 0 and near <= max(EXEMPT_FRACTION * n_el, 1)
+                r = code_parity(got[kind + "_codes"], enc[xkey][:, h], got[kind + "_s"],
+                                got[kind + "_z"], w.group, oracle_codes=enc[kind + "_codes"][:, h],
+                                given=case.folded and kind == "v")
+                near += r["exempt"]
+                n_el += r["elements"]
+    assert n_el > 0
+    gate_exempt(near, n_el, "displaced tokens: ")
 
 
 def test_corrected_rotations_and_eq8_decomposition():
@@ -520,7 +537,7 @@ def test_corrected_rotations_and_eq8_decomposition():
         a, c, _ = _append_parity(case, b, 0, 600)
         near += a
         n += c
-    assert near <= max(EXEMPT_FRACTION * n, 1)
+    gate_exempt(near, n)
 
     rng = np.random.default_rng(31)
     D = 256  # width of the synthetic output projection of one head
@@ -575,8 +592,7 @@ def test_full_size_sampled(name):
             a, c, _ = _append_parity(case, b, s, min(40, L - s))
             near += a
             n += c
-    say(f"  sampled elements {n} exempt {near}")
-    assert near <= max(EXEMPT_FRACTION * n, 1)
+    gate_exempt(near, n, "sampled ")
 
 
 @pytest.mark.gpu
@@ -738,4 +754,19 @@ def test_full_size_decode_step_sampled(folded):
     say(f"  sampled max rel err {err:.3e}")
     assert err <= TIGHT
     near, n, _ = _append_parity(case, 7, int(case.ctx[7]), 2)
-    assert near <= max(EXEMPT_FRACTION * n, 1)
+    gate_exempt(near, n)
+
+
+def test_zz_exempt_rate_over_the_module():
+    """P2's exempt bound as a rate over every append check of this module
+    (small samples are only tallied); the raw agreement with the oracle's codes
+    on its own scale/zero is reported beside it."""
+    t = dict(TALLY)
+    if t["elements"] == 0:
+        pytest.skip("no append check ran in this session")
+    report(f"[P2 tally] elements {t['elements']}  exempt {t['exempt']} "
+        f"({t['exempt'] / t['elements']:.2e})  exact ties of values as given {t['ties']} "
+        f"(mismatched {t['tie_bad']})  codes differing from the oracle's own grid "
+        f"{t['raw_bad']} ({t['raw_bad'] / t['elements']:.2e})")
+    assert t["tie_bad"] == 0
+    assert t["exempt"] <= EXEMPT_FRACTION * t["elements"]

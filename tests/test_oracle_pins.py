@@ -631,3 +631,46 @@ def test_folded_value_rotation_writes_the_same_cache_and_output_through_the_weig
         y = o_unf[0, hq] @ w_o.T
         y_fold = o_fold[0, hq] @ (w_o @ R_v[kv]).T
         assert np.allclose(y_fold, y, rtol=1e-12, atol=1e-12)
+
+
+def test_unrotated_cache_is_textbook_per_group_rtn_and_decodes_with_the_plain_query():
+    """rot_k = rot_v = None (the cache the rotations are compared against):
+    the keys less their mean and the values as given are coded by the
+    exhaustive nearest grid point of per-token, per-group asymmetric min/max
+    INT2 (c = 1, fp16 scale (max - min)/3 and zero min), and the decode of an
+    on-grid cache with one token returns that token's value, scoring with the
+    unrotated query."""
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((1, 9, 2, 128)) * 3
+    v = rng.standard_normal((1, 9, 2, 128))
+    mu = rng.standard_normal((2, 128))
+    enc = O.encode_tokens(k, v, mu, None, None, 64, 1.0, 1.0)
+    for x, key in ((k[0] - mu[None], "k"), (v[0], "v")):
+        xg = x.reshape(9, 2, 2, 64)                       # [token][head][group][64]
+        s = np.float16((xg.max(-1) - xg.min(-1)) / 3).astype(np.float64)
+        z = np.float16(xg.min(-1)).astype(np.float64)
+        assert np.array_equal(enc[key + "_s"][0], s) and np.array_equal(enc[key + "_z"][0], z)
+        grid = z[..., None, None] + s[..., None, None] * np.arange(4)
+        dist = np.abs(xg[..., None] - grid)
+        srt = np.sort(dist, axis=-1)
+        clear = (srt[..., 1] - srt[..., 0] > 1e-9).reshape(9, 2, 128)
+        best = dist.argmin(-1).reshape(9, 2, 128)
+        assert clear.mean() > 0.99
+        assert np.array_equal(enc[key + "_codes"][0][clear], best[clear])
+    # one cached token on the grid: the output is its value; a rotation given
+    # explicitly as the identity is the same cache and output
+    cache = np.zeros((1, 2, O.page_bytes(128, 128)), np.uint8)
+    tab = np.zeros((1, 1), np.int32)
+    kk = (rng.integers(0, 4, (1, 1, 2, 128)) * 0.5 - 1.0)
+    vv = (rng.integers(0, 4, (1, 1, 2, 128)) * 0.25 + 0.5)
+    kk[..., 0], kk[..., 1] = -1.0, 0.5                    # both end points in the group
+    vv[..., 0], vv[..., 1] = 0.5, 1.25
+    O.append(cache, tab, [0], kk, vv, np.zeros((2, 128)), None, None, 128, 1.0, 1.0)
+    eye = np.broadcast_to(np.eye(128), (2, 128, 128))
+    cache2 = np.zeros_like(cache)
+    O.append(cache2, tab, [0], kk, vv, np.zeros((2, 128)), eye, eye, 128, 1.0, 1.0)
+    assert np.array_equal(cache, cache2)
+    q = rng.standard_normal((1, 4, 128))
+    o = O.decode(cache, tab, [1], q, None, None, 1 / math.sqrt(128), 2, 128)
+    assert np.array_equal(o[0, :2], np.broadcast_to(vv[0, 0, 0], (2, 128)))
+    assert np.array_equal(o[0, 2:], np.broadcast_to(vv[0, 0, 1], (2, 128)))
