@@ -69,7 +69,8 @@ typedef enum {
   KVQ_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad dtype, bad clip   */
   KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim != 128)   */
   KVQ_ERR_WORKSPACE = -3,   /* workspace pointer null or too small           */
-  KVQ_ERR_HIP = -4          /* the HIP runtime reported a launch error       */
+  KVQ_ERR_HIP = -4,         /* the HIP runtime reported a launch error       */
+  KVQ_ERR_SCRATCH = -5      /* larger than the static scratch (no-allocation) */
 } kvq_status;
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -289,6 +290,30 @@ int kvq_append_decode_window(void *pages, int64_t num_blocks, int32_t num_kv_hea
                              int32_t q_dtype, const float *rot_k, const float *rot_v,
                              float sm_scale, float *out, void *workspace, size_t workspace_bytes,
                              int32_t split_pages, void *stream);
+
+/*
+ * kvq_decode_attn_noalloc -- kvq_decode_attn without a workspace argument, for
+ * callers that cannot allocate device memory or pass one (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  It
+ * allocates nothing: the workspace is a static device array of
+ * KVQ_SCRATCH_BYTES inside the library, one per GPU, held until the process
+ * ends (its address is looked up once per device, on the first call there).
+ * Arguments, semantics and errors are those of kvq_decode_attn, plus
+ * KVQ_ERR_SCRATCH, returned before anything is launched, when the shape needs
+ * more than KVQ_SCRATCH_BYTES (kvq_decode_workspace_bytes() tells).  Every
+ * call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ * (several streams, several host threads) race and must be serialised by the
+ * caller.  The array keeps the previous call's contents; nothing in it needs
+ * to start at zero.
+ */
+#define KVQ_SCRATCH_BYTES (32u << 20)
+int kvq_decode_attn_noalloc(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t group, const int32_t *block_table,
+                            int32_t max_blocks_per_seq, const int32_t *ctx_len,
+                            int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                            const void *q, int32_t q_dtype, const float *rot_k,
+                            const float *rot_v, float sm_scale, float *out, int32_t split_pages,
+                            void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     append_decode,
     append_decode_window,
     decode,
+    decode_noalloc,
+    SCRATCH_BYTES,
     decode_window,
     decode_workspace_bytes,
     lib,

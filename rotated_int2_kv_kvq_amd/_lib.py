@@ -45,6 +45,9 @@ SIGNATURES = {
     "kvq_append_decode": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32,
                            c_i32, c_vp, c_vp, c_i32, c_vp, c_f32, c_f32, c_i32, c_vp, c_i32,
                            c_vp, c_vp, c_f32, c_vp, c_vp, c_sz, c_i32, c_vp], c_i32),
+    "kvq_decode_attn_noalloc": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32,
+                                 c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp],
+                                c_i32),
     "kvq_window_bytes": ([c_i32, c_i32, c_i32], c_sz),
     "kvq_window_write": ([c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp], c_i32),
     "kvq_decode_attn_window": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp,
@@ -293,6 +296,27 @@ def append_decode(pages: torch.Tensor, block_table: torch.Tensor, start_pos: tor
         _ptr(mu), clip_k, clip_v, Hq, _ptr(q), _DTYPES[q.dtype], _ptr(rot_k), _ptr(rot_v),
         sm_scale, _ptr(out), _ptr(workspace), workspace.numel(), split_pages, _stream(stream)),
         "kvq_append_decode")
+    return out
+
+
+SCRATCH_BYTES = 32 << 20  # KVQ_SCRATCH_BYTES of include/kvq.h
+
+
+def decode_noalloc(pages: torch.Tensor, block_table: torch.Tensor, ctx_len: torch.Tensor,
+                   max_ctx_len: int, q: torch.Tensor, rot_k: torch.Tensor | None,
+                   rot_v: torch.Tensor | None, group: int, sm_scale: float, out: torch.Tensor,
+                   split_pages: int = 0, stream=None) -> torch.Tensor:
+    """kvq_decode_attn_noalloc: kvq_decode_attn with the library's static
+    scratch as its workspace; `out` must be given (nothing is allocated)."""
+    _need("out", out, torch.float32)
+    num_blocks, hkv, B, Hq, sm_scale, out, _ = _decode_common(
+        pages, block_table, ctx_len, max_ctx_len, q, rot_k, rot_v, group, sm_scale, out,
+        None, split_pages, workspace_needed=False)
+    _check(lib().kvq_decode_attn_noalloc(
+        _ptr(pages), num_blocks, hkv, q.shape[-1], group, _ptr(block_table),
+        block_table.shape[1], _ptr(ctx_len), max_ctx_len, B, Hq, _ptr(q), _DTYPES[q.dtype],
+        _ptr(rot_k), _ptr(rot_v), sm_scale, _ptr(out), split_pages, _stream(stream)),
+        "kvq_decode_attn_noalloc")
     return out
 
 

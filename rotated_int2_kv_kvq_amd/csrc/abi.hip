@@ -2,6 +2,8 @@
 // kernel launches.  No allocation, no synchronisation, no global state.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kvq.h"
 #include "kvq_common.h"
 
@@ -23,6 +25,8 @@ KVQ_API const char* kvq_status_string(int status) {
     case KVQ_ERR_UNSUPPORTED: return "unsupported configuration (head_dim must be 128)";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_HIP: return "HIP runtime error at launch";
+    case KVQ_ERR_SCRATCH:
+      return "decode needs more than the library's static scratch (KVQ_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -265,5 +269,57 @@ KVQ_API int kvq_append_decode_window(void* pages, int64_t num_blocks, int32_t nu
       max_blocks_per_seq, start_pos, k, v, kv_dtype == KVQ_BF16, mu, clip_k, clip_v, ctx_len,
       max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k, rot_v, sm_scale, out,
       workspace, plan, static_cast<hipStream_t>(stream), static_cast<uint16_t*>(window));
+  return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+// ----------------------------------------------------------------- no allocation
+// The decode's workspace (query operands, split partials) in a file-scope
+// device array, for callers that cannot allocate.  In host code `scratch` is
+// only a stand-in symbol: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and that address, never the
+// symbol, is what the kernels get.  Every call on a GPU shares that GPU's
+// array; it keeps the last call's contents, and nothing in it needs to start
+// at zero (each call writes every entry it later reads).
+namespace {
+__device__ __align__(256) uint8_t scratch[KVQ_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch array, or null on a HIP error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+KVQ_API int kvq_decode_attn_noalloc(const void* pages, int64_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t group, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, const int32_t* ctx_len,
+                                    int32_t max_ctx_len, int32_t batch, int32_t num_q_heads,
+                                    const void* q, int32_t q_dtype, const float* rot_k,
+                                    const float* rot_v, float sm_scale, float* out,
+                                    int32_t split_pages, void* stream) {
+  kvq::DecodePlan plan{};
+  const int st = check_decode(pages, num_blocks, num_kv_heads, head_dim, group, block_table,
+                              max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q,
+                              q_dtype, rot_k, rot_v, sm_scale, out, nullptr, 0, split_pages, &plan,
+                              /*own_workspace=*/false);
+  if (st != KVQ_OK || batch == 0) return st;
+  if (plan.total > static_cast<size_t>(KVQ_SCRATCH_BYTES)) return KVQ_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return KVQ_ERR_HIP;
+  const int rc = kvq::launch_decode(
+      static_cast<const uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
+      max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k,
+      rot_v, sm_scale, out, ws, plan, KVQ_STAGE_ALL, static_cast<hipStream_t>(stream));
   return rc == 0 ? KVQ_OK : KVQ_ERR_HIP;
 }

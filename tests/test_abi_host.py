@@ -38,7 +38,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "kvq_append", "kvq_append_decode", "kvq_append_decode_window", "kvq_decode_attn",
-        "kvq_decode_attn_staged", "kvq_decode_attn_window", "kvq_decode_workspace_bytes",
+        "kvq_decode_attn_noalloc", "kvq_decode_attn_staged", "kvq_decode_attn_window",
+        "kvq_decode_workspace_bytes",
         "kvq_page_bytes", "kvq_status_string", "kvq_window_bytes", "kvq_window_write"])
 
 
@@ -50,8 +51,9 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_page_bytes(lib):
     import rotated_int2_kv_kvq_amd as kvq
     assert kvq.status_string(0) == "ok"
-    for s in (-1, -2, -3, -4, 7):
+    for s in (-1, -2, -3, -4, -5, 7):
         assert kvq.status_string(s)
+    assert "scratch" in kvq.status_string(-5)
     assert kvq.page_bytes(128, 128) == 1152
     assert kvq.page_bytes(128, 64) == 1280
     assert kvq.page_bytes(128, 32) == 0
@@ -219,3 +221,26 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         L.page_bytes(128, 128)
 
+
+@no_gpu
+def test_noalloc_validates_before_touching_the_device(lib):
+    """Invalid arguments are rejected first (no device lookup, no launch); a
+    plan larger than the static scratch is KVQ_ERR_SCRATCH."""
+    f = lib.kvq_decode_attn_noalloc
+    base = [1 << 20, 4, 8, 128, 128, 1 << 21, 4, 1 << 22, 64, 1, 32, 1 << 23, 1, 1 << 24, 1 << 25,
+            0.088, 1 << 26, 0, None]
+    bad = list(base)
+    bad[10] = 30                                              # Hq % Hkv
+    assert f(*bad) == -1
+    bad = list(base)
+    bad[16] = None                                            # out
+    assert f(*bad) == -1
+    bad = list(base)
+    bad[11] = (1 << 23) + 4                                   # q alignment
+    assert f(*bad) == -1
+    bad = list(base)
+    bad[9] = 0                                                # batch 0: no-op
+    assert f(*bad) == 0
+    big = [1 << 20, 4, 8, 128, 128, 1 << 21, 8192, 1 << 22, 131072, 64, 32, 1 << 23, 1, 1 << 24,
+           1 << 25, 0.088, 1 << 26, 8, None]
+    assert f(*big) == -5
