@@ -62,16 +62,18 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per scan launch from the committed counter summary, or None if
-    it was taken on another workload or the kernel's sources changed since."""
+    it was taken on another workload or kernel, or the kernel's sources changed
+    since."""
     from rotated_int2_kv_kvq_amd.traffic import kernel_source_hash
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+    if (rec.get("workload") != workload or rec.get("kernel") != kernel
+            or rec.get("source_sha256") != kernel_source_hash()):
         return None
     return round(float(rec["traffic_bytes"]))
 
@@ -227,23 +229,29 @@ def main():
     # workspace; the split kernels of all layers run back to back between one
     # pair of events, and so do the single-token appends.  Every launch is
     # queued behind a GPU sleep so that host launch latency never falls inside
-    # an event interval.
+    # an event interval.  Where the plan builds the query operand inside the
+    # scan (as the step does), PREPARE and SPLITS together are that one launch.
     last = total_steps - 1
+    plan = kvq.decode_plan(B, Hq, Hkv, maxc[last])
+    scan_stages = (kvq.STAGE_PREPARE | kvq.STAGE_SPLITS if plan["operand_in_scan"]
+                   else kvq.STAGE_SPLITS)
+    scan_kernel = scan_kernel_name(w.group, plan["operand_in_scan"])
     wss = [ws] + [torch.empty_like(ws) for _ in range(L - 1)]
     split_ms, app_ms = [], []
     for rep in range(4):
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)
         s0, s1, a0, a1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-        for layer in range(L):
-            kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
-                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
-                       stages=kvq.STAGE_PREPARE)
+        if not plan["operand_in_scan"]:
+            for layer in range(L):
+                kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer],
+                           rks[layer], rvs[layer], w.group, sm_scale, out=outs[layer],
+                           workspace=wss[layer], stages=kvq.STAGE_PREPARE)
         s0.record()
         for layer in range(L):
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
                        rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
-                       stages=kvq.STAGE_SPLITS)
+                       stages=scan_stages)
         s1.record()
         for layer in range(L):
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
@@ -452,13 +460,13 @@ def main():
         "split_kernel_avg_us": round(split_avg_ms * 1e3, 2),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "split_kernel<1, false, false> (decode split-K scan)",
+            "kernel": f"{scan_kernel} (decode split-K scan)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w0.name),
+            "traffic": measured_traffic(w0.name, scan_kernel),
             "algorithmic_bytes": split_bytes,
         },
         "cpu_baseline": cpu,
@@ -470,6 +478,14 @@ def main():
         "long_context": long_line,
     }
     print(json.dumps(line), flush=True)
+
+
+def scan_kernel_name(group, operand_in_scan, windows=False, wide=False):
+    """The scan kernel's name as rocprofv3 prints it: split_kernel<G, wide
+    descriptor, windows, operand built in the scan>."""
+    b = lambda x: "true" if x else "false"  # noqa: E731
+    return (f"split_kernel<{1 if group == 128 else 2}, {b(wide)}, {b(windows)}, "
+            f"{b(operand_in_scan)}>")
 
 
 def cpu_baseline(w, st, samples, table, per_tok_head, budget_s, sm_scale):
@@ -695,6 +711,11 @@ def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
     wss = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
     out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
     calls = max(reps, ncopy)
+    # the scan alone: PREPARE and SPLITS together where the plan builds the
+    # operand inside the scan (one launch, as in the whole call)
+    plan = kvq.decode_plan(B, Hq, Hkv, max_ctx, d, split_pages)
+    scan_stages = (kvq.STAGE_PREPARE | kvq.STAGE_SPLITS if plan["operand_in_scan"]
+                   else kvq.STAGE_SPLITS)
 
     def call(i, stages):
         kvq.decode(copies[i % ncopy], table, ctx, max_ctx, q, rk, rv, w.group, sm, out=out,
@@ -709,14 +730,15 @@ def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
         for i in range(calls):
             call(i, kvq.STAGE_ALL)
         e1.record()
-        for i in range(ncopy):
-            call(i, kvq.STAGE_PREPARE)
+        if not plan["operand_in_scan"]:
+            for i in range(ncopy):
+                call(i, kvq.STAGE_PREPARE)
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e2.record()
         for i in range(calls):
-            call(i, kvq.STAGE_SPLITS)
+            call(i, scan_stages)
         e3.record()
         torch.cuda.synchronize()
         if rep:
@@ -756,6 +778,8 @@ def long_context_leg(name: str, reps: int, split_pages: int = 0, cache=None):
         "scan_frac": round(nbytes / (scan_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(B / (full_us * 1e-6), 1),
         "split_pages": split_pages or "auto",
+        "splits": plan["num_splits"],
+        "scan_kernel": scan_kernel_name(w.group, plan["operand_in_scan"]),
     }
 
 

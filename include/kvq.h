@@ -133,6 +133,25 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
                                   int32_t head_dim, int32_t max_ctx_len, int32_t split_pages);
 
 /*
+ * kvq_decode_plan -- how kvq_decode_attn cuts this shape (host query, no
+ * device access).  Arguments as for kvq_decode_workspace_bytes; each output
+ * pointer may be NULL:
+ *   *num_splits        splits (workgroups per query tile of four heads) of the
+ *                      longest context; 0 when max_ctx_len is 0
+ *   *split_pages_out   pages per split (the automatic choice when split_pages
+ *                      is 0)
+ *   *operand_in_scan   1 when a call that launches the PREPARE and SPLITS
+ *                      stages together (kvq_decode_attn among them) builds the
+ *                      query operand inside the split workgroups, in one
+ *                      launch, leaving no operand in the workspace; 0 when it
+ *                      launches the PREPARE stage's kernel first
+ * Returns KVQ_OK, KVQ_ERR_INVALID_ARG or KVQ_ERR_UNSUPPORTED.
+ */
+int kvq_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_ctx_len, int32_t split_pages, int32_t *num_splits,
+                    int32_t *split_pages_out, int32_t *operand_in_scan);
+
+/*
  * kvq_decode_attn -- single-token attention over the paged INT2 cache.
  *
  * Defined by the OptR review page ("What carries the argument":
@@ -187,9 +206,12 @@ int kvq_decode_attn(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
 #define KVQ_STAGE_ALL 7
 /* A stage reads what the previous stage left in the workspace, so the calls
  * that make up one decode must pass identical arguments and workspace, on one
- * stream (or with the caller ordering them).  stages outside 1..7 is
- * KVQ_ERR_INVALID_ARG.  kvq_decode_attn(...) == kvq_decode_attn_staged(...,
- * KVQ_STAGE_ALL, stream). */
+ * stream (or with the caller ordering them).  When kvq_decode_plan reports
+ * operand_in_scan, PREPARE and SPLITS launched together are one launch that
+ * leaves only the partials: a later SPLITS-only call then needs a PREPARE of
+ * its own.  Every way of splitting the stages gives the same output, bit for
+ * bit.  stages outside 1..7 is KVQ_ERR_INVALID_ARG.  kvq_decode_attn(...) ==
+ * kvq_decode_attn_staged(..., KVQ_STAGE_ALL, stream). */
 int kvq_decode_attn_staged(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
                            int32_t head_dim, int32_t group, const int32_t *block_table,
                            int32_t max_blocks_per_seq, const int32_t *ctx_len,
@@ -205,9 +227,15 @@ int kvq_decode_attn_staged(const void *pages, int64_t num_blocks, int32_t num_kv
  * The same computation as kvq_append with num_new = 1 followed by
  * kvq_decode_attn on the same stream (the two steps of the OptR review page,
  * "What carries the argument": encode the new key and value, then attention
- * over the quantised cache and the inverse value rotation), with the append
- * and the decode's query rotation sharing one launch.  Arguments are those
- * of the two calls:
+ * over the quantised cache and the inverse value rotation), in fewer
+ * launches.  When kvq_decode_plan reports operand_in_scan and num_q_heads is
+ * at most 4 * num_kv_heads, the scan leaves each new token's slot out and the
+ * merge launch encodes the token and adds it to the softmax as one more
+ * partial (two launches); otherwise the append shares a launch with the query
+ * rotation (three).  The cache bytes written are those of kvq_append either
+ * way; the output is that of the two calls up to float32 rounding (the new
+ * token's term joins the sum in another order).  Arguments are those of the
+ * two calls:
  *   start_pos      device  int32 [batch]: position of the new token
  *   k, v           device  [batch][1][num_kv_heads][head_dim] of kv_dtype
  *   ctx_len        device  int32 [batch]: tokens attended, normally

@@ -36,6 +36,7 @@ SIGNATURES = {
     "kvq_append": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp,
                     c_vp, c_i32, c_vp, c_vp, c_vp, c_f32, c_f32, c_vp], c_i32),
     "kvq_decode_workspace_bytes": ([c_i32, c_i32, c_i32, c_i32, c_i32, c_i32], c_sz),
+    "kvq_decode_plan": ([c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp], c_i32),
     "kvq_decode_attn": ([c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32,
                          c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_sz, c_i32, c_vp],
                         c_i32),
@@ -216,6 +217,16 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_
                            head_dim: int = 128, split_pages: int = 0) -> int:
     return int(lib().kvq_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                                 max_ctx_len, split_pages))
+
+
+def decode_plan(batch: int, num_q_heads: int, num_kv_heads: int, max_ctx_len: int,
+                head_dim: int = 128, split_pages: int = 0) -> dict:
+    """kvq_decode_plan: {"num_splits", "split_pages", "operand_in_scan"}."""
+    ns, sp, ins = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().kvq_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_ctx_len,
+                                 split_pages, ctypes.byref(ns), ctypes.byref(sp),
+                                 ctypes.byref(ins)), "kvq_decode_plan")
+    return {"num_splits": ns.value, "split_pages": sp.value, "operand_in_scan": bool(ins.value)}
 
 
 def _decode_common(pages, block_table, ctx_len, max_ctx_len, q, rot_k, rot_v, group, sm_scale,

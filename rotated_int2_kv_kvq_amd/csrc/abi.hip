@@ -100,6 +100,22 @@ KVQ_API size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
   return kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages).total;
 }
 
+KVQ_API int kvq_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_ctx_len, int32_t split_pages,
+                            int32_t* num_splits, int32_t* split_pages_out,
+                            int32_t* operand_in_scan) {
+  if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (!valid_decode_shape(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages))
+    return KVQ_ERR_INVALID_ARG;
+  const kvq::DecodePlan p = kvq::make_plan(batch, num_q_heads, num_kv_heads, max_ctx_len,
+                                           split_pages);
+  if (num_splits) *num_splits = p.S;
+  if (split_pages_out) *split_pages_out = p.spw;
+  if (operand_in_scan)
+    *operand_in_scan = p.S > 0 && kvq::operand_in_scan(p, num_kv_heads, batch, KVQ_STAGE_ALL);
+  return KVQ_OK;
+}
+
 namespace {
 // Host-side checks of the decode arguments; on KVQ_OK with batch > 0, *plan
 // is the workspace carve-up.

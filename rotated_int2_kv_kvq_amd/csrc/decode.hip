@@ -34,6 +34,8 @@
 //      through a last-workgroup counter needs device-scope release/acquire,
 //      i.e. an L2 writeback and invalidate per workgroup on this multi-XCD
 //      part, which costs far more than the launch.)
+#include <stddef.h>
+
 #include <algorithm>
 
 #include "append_one.h"
@@ -53,6 +55,10 @@ constexpr float kLazy = 8.0f;        // log2 headroom before the running maximum
 // low-digit operands.
 constexpr int kQaDwords = 32;
 constexpr int kQaScale = 28;
+// The same operand in LDS (built by a split workgroup itself): 20 dwords per
+// lane, the row scales at 18 and 19.
+constexpr int kQaLds = 20;
+constexpr int kQaLdsScale = 18;
 constexpr int kFmtFp8 = 0;           // f8f6f4 MFMA operand formats
 constexpr int kFmtFp6 = 2;
 constexpr int kScaleOne = 127;  // E8M0 2^0
@@ -129,11 +135,11 @@ __host__ __device__ inline int num_splits(int n_pages, int spw) {
 // Wave hl of the first 256 threads: the digits of query head hl of the tile
 // into dig, its exponent into qe and its per-group sums into qf.
 template <int G>
-__device__ __forceinline__ void prologue_digits(int h, int qg, int b, int Hkv, int QG,
-                                                float qscale,
+__device__ __forceinline__ void prologue_digits(float qscale,
                                                 const float (&red)[4][kHT][kHeadDim],
                                                 uint8_t (&dig)[kHT][kHeadDim][8],
-                                                int (&qe)[kHT], float4* __restrict__ qf) {
+                                                int (&qe)[kHT], float4* __restrict__ qf_tile,
+                                                float* __restrict__ qr_tile) {
   const int lane = threadIdx.x & 63;
   const int wv = (threadIdx.x >> 6) & 3;
   // wave hl: x = qscale * q_r of head hl, channels lane and lane + 64
@@ -143,6 +149,10 @@ __device__ __forceinline__ void prologue_digits(int h, int qg, int b, int Hkv, i
               (red[2][hl][lane + 64] + red[3][hl][lane + 64]));
   r0 *= qscale;  // logits in log2 units
   r1 *= qscale;
+  if (qr_tile) {  // the rotated, scaled query in float32 (for the fused step's new token)
+    qr_tile[hl * kHeadDim + lane] = r0;
+    qr_tile[hl * kHeadDim + lane + 64] = r1;
+  }
   const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
   const float s0 = wave_sum(r0), s1 = wave_sum(r1);
   // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest; digit d
@@ -163,15 +173,15 @@ __device__ __forceinline__ void prologue_digits(int h, int qg, int b, int Hkv, i
   if (lane == 0) {
     qe[hl] = e;
     // per-group sums of x for the zero-point term (channels < 64, >= 64)
-    qf[((static_cast<size_t>(b) * Hkv + h) * QG + qg) * kHT + hl] = make_float4(0.f, s0, s1, 0.f);
+    qf_tile[hl] = make_float4(0.f, s0, s1, 0.f);
   }
 }
 
 // The A operands, one thread per (operand, lane).
 template <int G>
-__device__ __forceinline__ void prologue_pack(int h, int qg, int b, int Hkv, int QG,
-                                              const uint8_t (&dig)[kHT][kHeadDim][8],
-                                              const int (&qe)[kHT], uint32_t* __restrict__ qa) {
+__device__ __forceinline__ void prologue_pack(const uint8_t (&dig)[kHT][kHeadDim][8],
+                                              const int (&qe)[kHT], uint32_t* __restrict__ qa_tile,
+                                              int lane_stride, int scale_off) {
   const int lane = threadIdx.x & 63;
   const int wv = (threadIdx.x >> 6) & 3;
   // thread (operand, lane L): FP6 field j of lane L (row r = L%16, lane group
@@ -207,17 +217,17 @@ __device__ __forceinline__ void prologue_pack(int h, int qg, int b, int Hkv, int
         if ((bit & 63) > 58) bits[(bit >> 6) + 1] |= field >> (64 - (bit & 63));
       }
     }
-    uint32_t* dst = qa + (((static_cast<size_t>(b) * Hkv + h) * QG + qg) * 64 + L) * kQaDwords;
+    uint32_t* dst = qa_tile + L * lane_stride;
 #pragma unroll
     for (int d = 0; d < 6; ++d)
       dst[6 * op + d] = static_cast<uint32_t>(bits[d >> 1] >> (32 * (d & 1)));
     if (op == 0)
-      dst[kQaScale] =
+      dst[scale_off] =
           static_cast<uint32_t>(min(max(kScaleOne + qe[head] + 2 - 4 * (r & 3), 1), 254));
     if (op == kOps - 1) {
       // low-digit operand: digit 4 + r%4 (group 128) or 4 + r%2 (group 64)
       const int dlo = G == 1 ? 4 + (r & 3) : 4 + (r & 1);
-      dst[kQaScale + 1] =
+      dst[scale_off + 1] =
           static_cast<uint32_t>(min(max(kScaleOne + qe[head] + 2 - 4 * dlo, 1), 254));
     }
   }
@@ -232,12 +242,12 @@ __device__ __forceinline__ void prologue_pack(int h, int qg, int b, int Hkv, int
 // basis; the merge folds it in after the inverse value rotation.  The window
 // store already holds every token of the context when the scan runs.
 //
-// By 256 threads (all call it).  Logits: one thread per window token, its
-// key row read once for the four heads.  Softmax: one wave per head.  P.V:
-// four groups of 64 threads take every fourth token (a group's loads in
-// flight together), a lane two channels of all four heads; the groups' sums
-// meet in LDS.  lds: kWinLds floats of scratch; qin: the tile's raw query
-// rows (zero past nh).
+// By the first 256 threads (further threads of a larger workgroup only pass
+// the barriers).  Logits: one thread per window token, its key row read once for
+// the four heads.  Softmax: one wave per head.  P.V: four groups of 64
+// threads take every fourth token (a group's loads in flight together), a
+// lane two channels of all four heads; the groups' sums meet in LDS.  lds:
+// kWinLds floats of scratch; qin: the tile's raw query rows (zero past nh).
 constexpr int kWinLds = kHT * kWindow + 4 * kHT * kHeadDim + 3 * kHT;
 __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
                                              const float* __restrict__ mu, int n, int b, int h,
@@ -248,8 +258,9 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
   float(*acc)[kHT][kHeadDim] = reinterpret_cast<float(*)[kHT][kHeadDim]>(lds + kHT * kWindow);
   float(*hs)[kHT] = reinterpret_cast<float(*)[kHT]>(lds + kHT * kWindow + 4 * kHT * kHeadDim);
   const int tid = threadIdx.x;
+  const bool act = tid < 256;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = (tid >> 6) & 3;
   const uint16_t* wk = win + (static_cast<size_t>(b) * Hkv + h) * 2 * kWindow * kHeadDim;
   const uint16_t* wvs = wk + kWindow * kHeadDim;
   const int nsk = min(kSink, n);
@@ -257,50 +268,55 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
   const int nw = nsk + max(0, n - rlo);
   auto slot_of = [&](int i) { return window_slot(i < nsk ? i : rlo + (i - nsk)); };
 
-  {  // q . mu per head (wave wv)
+  if (act) {  // q . mu per head (wave wv)
     const float* muh = mu + static_cast<size_t>(h) * kHeadDim;
     float qm = qin[wv][lane] * muh[lane] + qin[wv][lane + 64] * muh[lane + 64];
     qm = wave_sum(qm);
     if (lane == 0) hs[0][wv] = qm;
   }
   __syncthreads();
-  for (int i = tid; i < nw; i += 256) {
+  for (int i = tid; act && i < nw; i += 256) {
     // the query values are re-read from LDS for every token rather than held
     // in registers across the loop (512 of them)
     asm volatile("" ::: "memory");
     const uint4* kr = reinterpret_cast<const uint4*>(wk + slot_of(i) * kHeadDim);
-    uint4 kw[16];
-#pragma unroll
-    for (int c8 = 0; c8 < 16; ++c8) kw[c8] = kr[c8];
     float dot[kHT] = {0.f, 0.f, 0.f, 0.f};
+    // the key row in two halves of 64 channels
 #pragma unroll
-    for (int c8 = 0; c8 < 16; ++c8) {
-      const uint32_t w4[4] = {kw[c8].x, kw[c8].y, kw[c8].z, kw[c8].w};
-      float kf[8];
+    for (int half = 0; half < 2; ++half) {
+      uint4 kw[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float(w4[e] << 16);
-        kf[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
-      }
+      for (int e = 0; e < 8; ++e) kw[e] = kr[8 * half + e];
 #pragma unroll
-      for (int u = 0; u < kHT; ++u) {
-        const float4 qa4 = *reinterpret_cast<const float4*>(&qin[u][8 * c8]);
-        const float4 qb4 = *reinterpret_cast<const float4*>(&qin[u][8 * c8 + 4]);
-        dot[u] = fmaf(qa4.x, kf[0], dot[u]);
-        dot[u] = fmaf(qa4.y, kf[1], dot[u]);
-        dot[u] = fmaf(qa4.z, kf[2], dot[u]);
-        dot[u] = fmaf(qa4.w, kf[3], dot[u]);
-        dot[u] = fmaf(qb4.x, kf[4], dot[u]);
-        dot[u] = fmaf(qb4.y, kf[5], dot[u]);
-        dot[u] = fmaf(qb4.z, kf[6], dot[u]);
-        dot[u] = fmaf(qb4.w, kf[7], dot[u]);
+      for (int c = 0; c < 8; ++c) {
+        const int c8 = 8 * half + c;
+        const uint32_t w4[4] = {kw[c].x, kw[c].y, kw[c].z, kw[c].w};
+        float kf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[2 * e] = __uint_as_float(w4[e] << 16);
+          kf[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int u = 0; u < kHT; ++u) {
+          const float4 qa4 = *reinterpret_cast<const float4*>(&qin[u][8 * c8]);
+          const float4 qb4 = *reinterpret_cast<const float4*>(&qin[u][8 * c8 + 4]);
+          dot[u] = fmaf(qa4.x, kf[0], dot[u]);
+          dot[u] = fmaf(qa4.y, kf[1], dot[u]);
+          dot[u] = fmaf(qa4.z, kf[2], dot[u]);
+          dot[u] = fmaf(qa4.w, kf[3], dot[u]);
+          dot[u] = fmaf(qb4.x, kf[4], dot[u]);
+          dot[u] = fmaf(qb4.y, kf[5], dot[u]);
+          dot[u] = fmaf(qb4.z, kf[6], dot[u]);
+          dot[u] = fmaf(qb4.w, kf[7], dot[u]);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kHT; ++u) lg[u][i] = qscale * (dot[u] - hs[0][u]);
   }
   __syncthreads();
-  {  // softmax of head wv
+  if (act) {  // softmax of head wv
     float m = -INFINITY;
     for (int i = lane; i < nw; i += 64) m = fmaxf(m, lg[wv][i]);
     m = wave_max(m);
@@ -317,7 +333,7 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
     }
   }
   __syncthreads();
-  {  // P.V: group wv takes tokens wv, wv + 4, ... (80 at most), 20 loads at a time
+  if (act) {  // P.V: group wv takes tokens wv, wv + 4, ... (80 at most), 20 loads at a time
     constexpr int kChunk = 20;
     float a[kHT][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
     for (int i0 = wv; i0 < nw; i0 += 4 * kChunk) {
@@ -348,7 +364,7 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
     }
   }
   __syncthreads();
-  if (wv < nh) {  // head wv: the four groups' sums, normalised
+  if (act && wv < nh) {  // head wv: the four groups' sums, normalised
     const int hq = h * (Hq / Hkv) + qg * kHT + wv;
     float* dst = wpart + (static_cast<size_t>(b) * Hq + hq) * kPartStride;
     const float inv = nw > 0 ? 1.0f / hs[2][wv] : 0.f;
@@ -361,20 +377,27 @@ __device__ __forceinline__ void window_block(const uint16_t* __restrict__ win,
   }
 }
 
-// The body is a device function of (query tile hx = h*QG + qg, sequence b):
-// threads 0-255 do the work; further threads of a larger workgroup only pass
-// the barriers (the fused decode step runs it in 1024-thread workgroups).
-template <bool kBf16, int G>
-__device__ __forceinline__ void prologue_body(int hx, int b, const void* __restrict__ q,
-                                              const float* __restrict__ rot_k, int Hq, int Hkv,
-                                              int QG, float qscale, uint32_t* __restrict__ qa,
-                                              float4* __restrict__ qf) {
-  __shared__ __attribute__((aligned(16))) float qin[kHT][kHeadDim];
-  __shared__ float red[4][kHT][kHeadDim];  // split-K partial products
-  __shared__ uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
-  __shared__ int qe[kHT];
-  const int h = hx / QG;
-  const int qg = hx % QG;
+// LDS the query-operand computation works in.
+struct QScratch {
+  float qin[kHT][kHeadDim];       // the tile's query rows
+  float red[4][kHT][kHeadDim];    // split-K partial products
+  uint8_t dig[kHT][kHeadDim][8];  // FP6 digit fields (sign | nibble)
+  int qe[kHT];                    // per-head exponents
+};
+
+// The operand of query tile (h, qg) of sequence b: threads 0-255 do the work;
+// further threads of a larger workgroup only pass the barriers (the fused
+// decode step runs it in 1024-thread workgroups).  The A operands of lane L go
+// to qa_tile + L * lane_stride (dwords 0-17, row scales at scale_off and
+// scale_off + 1), the per-head group sums to qf_tile[0..3].  q_bf16: the
+// query is bfloat16, else float32.
+template <int G>
+__device__ __forceinline__ void prologue_compute(int h, int qg, int b, const void* __restrict__ q,
+                                                 bool q_bf16, const float* __restrict__ rot_k,
+                                                 int Hq, int Hkv, float qscale, QScratch& ls,
+                                                 uint32_t* qa_tile, int lane_stride,
+                                                 int scale_off, float4* qf_tile,
+                                                 float* qr_tile = nullptr) {
   const int Hg = Hq / Hkv;
   const int tid = threadIdx.x;
   const bool act = tid < 256;
@@ -401,7 +424,7 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
     float v0 = 0.f, v1 = 0.f;
     if (hh < nh) {
       const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + hh) * kHeadDim + c;
-      if constexpr (kBf16) {
+      if (q_bf16) {
         const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + qrow);
         v0 = bf16_to_f32(static_cast<uint16_t>(u & 0xffffu));
         v1 = bf16_to_f32(static_cast<uint16_t>(u >> 16));
@@ -411,16 +434,16 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
         v1 = f.y;
       }
     }
-    qin[hh][c] = v0;
-    qin[hh][c + 1] = v1;
+    ls.qin[hh][c] = v0;
+    ls.qin[hh][c + 1] = v1;
   }
   __syncthreads();
   if (act && ident) {
     // quarter wv of the split-K sum holds channels 32wv..32wv+31 of q
 #pragma unroll
     for (int hh = 0; hh < kHT; ++hh) {
-      red[wv][hh][lane] = (lane >> 5) == wv ? qin[hh][lane] : 0.f;
-      red[wv][hh][lane + 64] = ((lane + 64) >> 5) == wv ? qin[hh][lane + 64] : 0.f;
+      ls.red[wv][hh][lane] = (lane >> 5) == wv ? ls.qin[hh][lane] : 0.f;
+      ls.red[wv][hh][lane + 64] = ((lane + 64) >> 5) == wv ? ls.qin[hh][lane + 64] : 0.f;
     }
   } else if (act) {
 #pragma unroll
@@ -428,18 +451,30 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const float qi = qin[hh][32 * wv + i];
+        const float qi = ls.qin[hh][32 * wv + i];
         a0 = fmaf(qi, ra[i], a0);
         a1 = fmaf(qi, rb[i], a1);
       }
-      red[wv][hh][lane] = a0;
-      red[wv][hh][lane + 64] = a1;
+      ls.red[wv][hh][lane] = a0;
+      ls.red[wv][hh][lane + 64] = a1;
     }
   }
   __syncthreads();
-  if (act) prologue_digits<G>(h, qg, b, Hkv, QG, qscale, red, dig, qe, qf);
+  if (act) prologue_digits<G>(qscale, ls.red, ls.dig, ls.qe, qf_tile, qr_tile);
   __syncthreads();
-  if (act) prologue_pack<G>(h, qg, b, Hkv, QG, dig, qe, qa);
+  if (act) prologue_pack<G>(ls.dig, ls.qe, qa_tile, lane_stride, scale_off);
+}
+
+// The prologue kernel's view: its own LDS, the operand to the workspace.
+template <bool kBf16, int G>
+__device__ __forceinline__ void prologue_body(int hx, int b, const void* __restrict__ q,
+                                              const float* __restrict__ rot_k, int Hq, int Hkv,
+                                              int QG, float qscale, uint32_t* __restrict__ qa,
+                                              float4* __restrict__ qf) {
+  __shared__ __attribute__((aligned(16))) QScratch ls;
+  const size_t tile = (static_cast<size_t>(b) * Hkv + hx / QG) * QG + hx % QG;
+  prologue_compute<G>(hx / QG, hx % QG, b, q, kBf16, rot_k, Hq, Hkv, qscale, ls,
+                      qa + tile * 64 * kQaDwords, kQaDwords, kQaScale, qf + tile * kHT);
 }
 
 template <bool kBf16, int G>
@@ -838,29 +873,40 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
 }
 
 // 1-D grid of n_win + S * Hkv * QG * B workgroups of 256 threads.  With BF16
-// windows (kWin; n_win = 0 otherwise) the first n_win = Hkv * QG * B workgroups each
-// score the window of one (query tile, sequence) and write its partial to
-// wpart (q: the raw queries, bf16 when q_bf16); they are dispatched first and
-// run beside the splits.  The rest are the splits: split x of a query tile
-// covers body pages [x*spw, (x+1)*spw) (after the sink pages with windows),
-// cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
+// windows (kWin; n_win = 0 otherwise) the first n_win = Hkv * QG * B
+// workgroups each score the window of one (query tile, sequence) and write its
+// partial to wpart (q: the raw queries, bf16 when q_bf16); they are dispatched
+// first and run beside the splits.  The rest are the splits: split x of a
+// query tile covers body pages [x*spw, (x+1)*spw) (after the sink pages with
+// windows), cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
 // 128 VGPRs (four waves per SIMD); group 64, with a third q.K operand and a
 // second value group, gets up to 168 (three waves per SIMD) rather than spill
 // inside the loop (a spill reload waits for every outstanding DMA).  kWide
 // builds a buffer descriptor per page for caches of 4 GiB and more.
-template <int G, bool kWide, bool kWin>
+//
+// kSelfQ: every split workgroup builds its query operand itself (from q and
+// rot_k, with the prologue's arithmetic, so bit for bit the same operand)
+// while its first slices are in flight, in the ring slots 2-3 that the loop
+// has not reached yet; otherwise the operand comes from qa/qf, written by the
+// prologue (or the fused step's preparation) launch.
+template <int G, bool kWide, bool kWin, bool kSelfQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
              int max_ctx, int Hq, int QG, int spw, const uint32_t* __restrict__ qa,
              const float4* __restrict__ qf, float* __restrict__ part, int S,
              const uint16_t* __restrict__ wstore, int n_win, const void* __restrict__ q,
-             int q_bf16, const float* __restrict__ mu, float qscale, float* __restrict__ wpart) {
+             int q_bf16, const float* __restrict__ mu, float qscale, float* __restrict__ wpart,
+             const float* __restrict__ rot_k, const int* __restrict__ new_pos,
+             float* __restrict__ qr) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
+  // slot s of wave w at ring[s][w]: the slots 2-3 of all four waves are one
+  // contiguous region, free from the start until the first block's loop
+  constexpr int kSlotStride = 4 * kSlot;
   static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
   static_assert(kRing == 4 && kDepth == 2, "slots are the slices of a block; two in flight");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kSlot];
   __shared__ __attribute__((aligned(16))) int wids[kMaxSplitPages];  // block ids of the pages
   __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
   __shared__ float cm[4][kHT], cl[4][kHT];
@@ -944,17 +990,30 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   // (they complete in order and the slices stay in flight) and the loop never
   // waits on it again.
   const size_t hgi = (static_cast<size_t>(b) * Hkv + h) * QG + qg;
-  const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
-  const uint4 q0 = qap[0], q1 = qap[1], q2 = qap[2];
-  const uint4 q3 = G == 2 ? qap[3] : make_uint4(0u, 0u, 0u, 0u);
-  const uint4 q4 = G == 2 ? qap[4] : make_uint4(0u, 0u, 0u, 0u);
-  const uint4 qsv = qap[kQaScale / 4];
   const int t = lane & 15;
   const int hl = lane >> 4;
-  const float4 fq = qf[hgi * kHT + hl];
+  uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0, q2 = q0, q3 = q0, q4 = q0, qsv = q0;
+  float4 fq = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (!kSelfQ) {
+    const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
+    q0 = qap[0];
+    q1 = qap[1];
+    q2 = qap[2];
+    if (G == 2) {
+      q3 = qap[3];
+      q4 = qap[4];
+    }
+    qsv = qap[kQaScale / 4];
+    fq = qf[hgi * kHT + hl];
+  }
 
   const int ctx = min(max(ctx_in, 0), max_ctx);
   const int hi_tok = win ? body_end(ctx) : ctx;  // tokens scanned: [lo_pages * 16, hi_tok)
+  // The fused decode step (new_pos: the new tokens' positions) appends in the
+  // merge, after this launch: the scan leaves the new token's slot out (the
+  // merge adds the token itself), and the block holding it takes the masked
+  // path.
+  const int pex = new_pos ? new_pos[b] : -1;
   const int n_pages = (hi_tok + kBlock - 1) / kBlock;
   const int ns_b = num_splits(n_pages - lo_pages, spw);
   if (wgs >= ns_b) return;
@@ -983,7 +1042,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     }
   };
 
-  uint8_t* myring = &ring[wave][0][0];
+  uint8_t* myring = &ring[0][wave][0];
   // DMA lane offsets: 16 code bytes per lane; one (scale, zero) word per lane
   // (group 128: lanes 0-31 and 32-63 take the same words of the two pages)
   const uint32_t off16 = 16u * lane;
@@ -1020,7 +1079,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
                  "+v"(fqz))
   if (nsl >= 2) {
     issue(myring, idc[0], idc[1]);
-    issue(myring + kSlot, idc[2], idc[3]);
+    issue(myring + kSlotStride, idc[2], idc[3]);
     fill_table();
     KVQ_HOLD_Q("after two slices");
   } else if (nsl == 1) {
@@ -1032,7 +1091,36 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     KVQ_HOLD_Q("alone");
   }
 #undef KVQ_HOLD_Q
-  __syncthreads();  // the id table is complete
+  if constexpr (kSelfQ) {
+    // slots 2-3 of every wave: the prologue's scratch, then the operand of
+    // lane L at dwords 20L.. (over the partial products, dead by then), the
+    // per-head group sums after the scratch
+    uint8_t* free_lds = &ring[2][0][0];
+    static_assert(sizeof(QScratch) + kHT * sizeof(float4) <= 2 * kSlotStride,
+                  "the operand's scratch fits in slots 2-3");
+    static_assert(offsetof(QScratch, red) + 64 * kQaLds * 4 <= offsetof(QScratch, dig),
+                  "the operand overwrites only the partial products");
+    QScratch& ls = *reinterpret_cast<QScratch*>(free_lds);
+    uint32_t* qa_s = reinterpret_cast<uint32_t*>(free_lds + offsetof(QScratch, red));
+    float4* qf_s = reinterpret_cast<float4*>(free_lds + sizeof(QScratch));
+    prologue_compute<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qscale, ls, qa_s, kQaLds,
+                        kQaLdsScale, qf_s,
+                        (qr && wgs == 0) ? qr + hgi * kHT * kHeadDim : nullptr);
+    __syncthreads();  // the operand is packed
+    const uint32_t* mine = qa_s + lane * kQaLds;
+    qv0 = u32x4{mine[0], mine[1], mine[2], mine[3]};
+    qv1 = u32x4{mine[4], mine[5], mine[6], mine[7]};
+    qv2 = u32x4{mine[8], mine[9], mine[10], mine[11]};
+    if (G == 2) {
+      qv3 = u32x4{mine[12], mine[13], mine[14], mine[15]};
+      qv4 = u32x4{mine[16], mine[17], 0u, 0u};
+    }
+    qvs = u32x4{mine[kQaLdsScale], mine[kQaLdsScale + 1], 0u, 0u};
+    fqy = qf_s[hl].y;
+    fqz = qf_s[hl].z;
+  }
+  // the id table is complete (and the operand read before slots 2-3 refill)
+  __syncthreads();
 
   auto op6 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
     return v8i{static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
@@ -1077,9 +1165,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         // slice i + 2: slices 2, 3 of this block, then 0, 1 of the next
         if (kFast || i + kDepth < nsl) {
           if constexpr (s < 2)
-            issue(myring + (s + 2) * kSlot, idc[2 * s + 4], idc[2 * s + 5]);
+            issue(myring + (s + 2) * kSlotStride, idc[2 * s + 4], idc[2 * s + 5]);
           else
-            issue(myring + (s - 2) * kSlot, idn[2 * s - 4], idn[2 * s - 3]);
+            issue(myring + (s - 2) * kSlotStride, idn[2 * s - 4], idn[2 * s - 3]);
         }
         // slice i has landed once at most the DMAs of the slices behind it are pending
         if (kFast || i + kDepth < nsl)
@@ -1091,10 +1179,10 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         Slice c;
         // the next block's ids (two slices before its first DMA) with slice 0
         if constexpr (kFast && s == 0)
-          read_slice_ids<G, s * kSlot>(c, ak, as, ids_addr(bi + 1), idn);
+          read_slice_ids<G, s * kSlotStride>(c, ak, as, ids_addr(bi + 1), idn);
         else
-          read_slice<G, s * kSlot>(c, ak, as);
-        if (hl == s) read_vwords<s * kSlot>(vw, av);
+          read_slice<G, s * kSlotStride>(c, ak, as);
+        if (hl == s) read_vwords<s * kSlotStride>(vw, av);
         if (!kFast && s == 0 && bi + 1 < nbw) read_ids8(ids_addr(bi + 1), idn);
 
         // q.K: D[4*head + digit][token t]; the digit rows add up in-lane
@@ -1139,8 +1227,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         } else {
           const int pg = pblk + 2 * s;
           const int pos = pg * kBlock + t;
-          const bool v0 = pos < hi_tok;
-          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok;
+          const bool v0 = pos < hi_tok && pos != pex;
+          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok && pos + kBlock != pex;
           lg[2 * s] = v0 ? l0 : -INFINITY;
           lg[2 * s + 1] = v1 ? l1 : -INFINITY;
           // slots past the context hold arbitrary bytes (possibly NaN as fp16):
@@ -1200,7 +1288,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     st.zs0 += z0;
     st.zs1 += z1;
     // slot 3: read above; the DMAs in flight target slots 0 and 1
-    uint8_t* ptile = myring + 3 * kSlot;
+    uint8_t* ptile = myring + 3 * kSlotStride;
     if constexpr (G == 1) {
       block_pv<0, 8>(st, p, sz0, ptile, pexp[wave], vw, lane);
     } else {
@@ -1210,7 +1298,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 #pragma unroll
     for (int k = 0; k < 8; ++k) idc[k] = idn[k];
   };
-  const int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
+  int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
+  if (pex >= 0) {
+    const int rel = pex / kBlock - p_begin;  // page of the new token in this range
+    if (rel >= 0 && rel < np && ((rel >> 3) & 3) == wave) nfast = min(nfast, (rel >> 3) >> 2);
+  }
   int bi = 0;
   for (; bi < nfast; ++bi) run_block(Const<bool, true>{}, bi);
   for (; bi < nbw; ++bi) run_block(Const<bool, false>{}, bi);
@@ -1254,10 +1346,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     }
     const int hq = h * Hg + hloc;
     float* dst = part + ((static_cast<size_t>(b) * Hq + hq) * S + wgs) * kPartStride;
-    const float inv = 1.0f / L;
+    // a split whose only token is the fused step's new one saw nothing
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
     dst[4 + cc] = o0 * inv;
     dst[4 + cc + 64] = o1 * inv;
-    if (cc == 0) dst[0] = M + __log2f(L);
+    if (cc == 0) dst[0] = L > 0.f ? M + __log2f(L) : kNegBig;
   }
 }
 
@@ -1276,15 +1369,40 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // separates the merge from the rotation.
 constexpr int kMergeSplits = 16;  // splits per thread and round (two halves: 32 per round)
 
+// The fused decode step (kApp = 1: bfloat16 k/v, 2: float32) also encodes
+// the step's new token of (sequence, KV head) into the cache, with the
+// single-token append's arithmetic (the same bytes), and merges the token
+// itself as one more partial: its logit is the scan's float32 rotated query
+// (qr) against the dequantised new key, its output the dequantised new value.
+// The scan left the token's slot out.  One query tile per KV head (QG == 1).
+struct StepArgs {
+  uint8_t* pages;
+  int64_t num_blocks;
+  const int* block_table;
+  int max_blocks;
+  const int* start_pos;
+  const void* k;
+  const void* v;
+  const float* mu;
+  const float* rot_k;
+  float clip_k, clip_v;
+  int G;            // groups per head_dim (1: group 128, 2: group 64)
+  const float* qr;  // [B][Hkv][4][128] scaled rotated query from the scan
+};
+
+template <int kApp>
 __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ part,
                                                      const int* __restrict__ ctx_len, int max_ctx,
                                                      int Hq, int Hkv, int QG, int spw, int S,
                                                      const float* __restrict__ rot_v,
                                                      float* __restrict__ out,
-                                                     const float* __restrict__ wpart) {
+                                                     const float* __restrict__ wpart,
+                                                     StepArgs st) {
   __shared__ __attribute__((aligned(16))) float osum[2][kHT][kHeadDim];
   __shared__ float hinv[kHT];  // 1 / (weight sum) per head
   __shared__ float hwin[kHT];  // the window partial's share of each head's output
+  __shared__ float deq[2][kHeadDim];   // fused step: the new key and value, dequantised
+  __shared__ float nlog[kHT][2];      // fused step: halves of the new token's logits
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
@@ -1320,10 +1438,29 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   };
   load_x(0, xv);
   if (S > 2 * kMergeSplits) load_x(1, xw);  // S: the same in every thread
+  const int ctx = min(max(ctx_in, 0), max_ctx);
+  // fused step: encode the new token (all 1024 threads), then its logits
+  float lse_n = kNegBig;  // head u's new-token logit (log2 units); kNegBig: not attended
+  if constexpr (kApp != 0) {
+    constexpr bool kKvBf16 = kApp == 1;
+    const float qrv = st.qr[((static_cast<size_t>(b) * Hkv + h) * kHT + u) * kHeadDim + c];
+    append_one_body<kKvBf16>(h, b, st.pages, st.num_blocks, Hkv, st.G,
+                             st.block_table, st.max_blocks, st.start_pos, 0,
+                             token_row<kKvBf16>(st.k, b, h, Hkv),
+                             token_row<kKvBf16>(st.v, b, h, Hkv), st.mu, st.rot_k, rot_v,
+                             st.clip_k, st.clip_v, &deq[0][0]);
+    __syncthreads();
+    const int pn = st.start_pos[b];
+    if (half == 0) {
+      float x = wave_sum(qrv * deq[0][c]);
+      if (lane == 0) nlog[u][c >> 6] = x;
+    }
+    __syncthreads();
+    if (pn >= 0 && pn < ctx) lse_n = nlog[u][0] + nlog[u][1];
+  }
   // the window partial's lse, and the window output this thread adds
   const float lse_w = wpart ? wpart[(row0 + min(u, nh - 1)) * kPartStride] : kNegBig;
   const float wv = wpart ? wpart[(row0 + min(part8 & 3, nh - 1)) * kPartStride + 4 + j] : 0.f;
-  const int ctx = min(max(ctx_in, 0), max_ctx);
   // with BF16 windows (wpart != null) the splits cover the body only
   const int lo_pages = wpart ? kSink / kBlock : 0;
   const int hi_tok = wpart ? body_end(ctx) : ctx;
@@ -1342,11 +1479,15 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
   M = wave_max(M);
   M = fmaxf(M, lse_w);
+  M = fmaxf(M, lse_n);
   float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
   for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
   W = wave_sum(W);
   const float a_w = exp2_hw(lse_w - M);  // 0 without windows
   W += a_w;
+  // the fused step's new token: weight 0 when it is not attended
+  const float a_n = (kApp != 0 && lse_n > kNegBig) ? exp2_hw(lse_n - M) : 0.f;
+  W += a_n;
 
   // channel c over this half's splits, a round at a time (one round covers
   // 32 splits); a split past the count contributes nothing (its stale values
@@ -1381,6 +1522,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
       if (s < ns) acc = fmaf(exp2_hw(lv[k] - M), xv[k], acc);
     }
   }
+  if (kApp != 0 && half == 0 && a_n > 0.f) acc = fmaf(a_n, deq[1][c], acc);
   osum[half][u][c] = acc;
   if ((tid & 255) == 0) {
     const float inv = 1.0f / W;
@@ -1569,22 +1711,43 @@ DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages) {
   p.part_off = p.qf_off + align256(hg * kHT * 16);
   p.wpart_off =
       p.part_off + align256(static_cast<size_t>(B) * Hq * (p.S ? p.S : 1) * kPartStride * 4);
-  p.total = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
+  p.qr_off = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
+  p.total = p.qr_off + align256(hg * kHT * kHeadDim * 4);
   return p;
 }
 
-int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
-                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
-                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
-                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
-                  hipStream_t stream, const uint16_t* win, const float* mu) {
+// A call that launches the PREPARE and SPLITS stages together builds the
+// query operand inside the split workgroups, with no prologue launch, when
+// the grid is one round of workgroups (at most 1024): the CUs have time to
+// spare while the first slices land (16K batch 16: 46.5 -> 42.9 us per call;
+// 128K batch 1: 31.1 -> 29.7 us).  On larger grids every workgroup repeating
+// the rotation costs more than the launch (the ragged batch of 64: 231 -> 256
+// us).  A PREPARE-only call still writes the operand to the workspace for a
+// later SPLITS-only call.
+bool operand_in_scan(const DecodePlan& p, int Hkv, int B, int stages) {
+  return (stages & 3) == 3 && static_cast<int64_t>(p.S) * Hkv * p.QG * B <= 1024;
+}
+
+// The decode launches; `step` (the fused decode step, non-null only with the
+// operand built in the scan, one query tile per KV head and no windows) makes
+// the scan leave the new tokens' slots out and the merge append them.
+static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                              const int* block_table, int max_blocks, const int* ctx_len,
+                              int max_ctx, int B, int Hq, const void* q, bool q_bf16,
+                              const float* rot_k, const float* rot_v, float sm_scale, float* out,
+                              void* workspace, const DecodePlan& p, int stages,
+                              hipStream_t stream, const uint16_t* win, const float* mu,
+                              const StepArgs* step, bool kv_bf16) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
   float* part = reinterpret_cast<float*>(ws + p.part_off);
   float* wpart = win ? reinterpret_cast<float*>(ws + p.wpart_off) : nullptr;
   const float qscale = sm_scale * kLog2e;
-  if (p.S > 0 && (stages & 1)) {
+  const bool self_q = operand_in_scan(p, Hkv, B, stages);
+  const int* new_pos = step ? step->start_pos : nullptr;
+  float* qr = step ? reinterpret_cast<float*>(ws + p.qr_off) : nullptr;
+  if (p.S > 0 && (stages & 1) && !self_q) {
     const dim3 g1(Hkv * p.QG, B);
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv, p.QG, qscale, qa,
@@ -1604,12 +1767,15 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
                          max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S, win,
-                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart);
+                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, new_pos, qr);
     };
     auto pick = [&](auto g, auto wd) {
       constexpr int GG = decltype(g)::value;
       constexpr bool WD = decltype(wd)::value;
-      win ? go(split_kernel<GG, WD, true>) : go(split_kernel<GG, WD, false>);
+      if (win)
+        self_q ? go(split_kernel<GG, WD, true, true>) : go(split_kernel<GG, WD, true, false>);
+      else
+        self_q ? go(split_kernel<GG, WD, false, true>) : go(split_kernel<GG, WD, false, false>);
     };
     auto pick_w = [&](auto g) {
       wide ? pick(g, Const<bool, true>{}) : pick(g, Const<bool, false>{});
@@ -1617,15 +1783,37 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
     G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
   // fewer than 64 query tiles without windows: a workgroup per query head
-  const bool per_head = !win && static_cast<int64_t>(B) * Hkv * p.QG < 64;
-  if ((stages & 4) && per_head)
+  const bool per_head = !win && !step && static_cast<int64_t>(B) * Hkv * p.QG < 64;
+  StepArgs sa{};
+  if (step) {
+    sa = *step;
+    sa.qr = qr;
+  }
+  if ((stages & 4) && per_head) {
     hipLaunchKernelGGL(merge_head_kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len,
                        max_ctx, Hq, Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
-  else if (stages & 4)
-    hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
-                       max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
-                       static_cast<const float*>(wpart));
+  } else if (stages & 4) {
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
+                         max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
+                         static_cast<const float*>(wpart), sa);
+    };
+    if (!step)
+      go(merge_kernel<0>);
+    else
+      kv_bf16 ? go(merge_kernel<1>) : go(merge_kernel<2>);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
+                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
+                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
+                  hipStream_t stream, const uint16_t* win, const float* mu) {
+  return launch_decode_impl(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len, max_ctx,
+                            B, Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace, p, stages,
+                            stream, win, mu, nullptr, false);
 }
 
 int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
@@ -1635,6 +1823,17 @@ int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          int Hq, const void* q, bool q_bf16, const float* rot_k,
                          const float* rot_v, float sm_scale, float* out, void* workspace,
                          const DecodePlan& p, hipStream_t stream, uint16_t* win) {
+  // Fused: when the scan builds its own query operand (one round of
+  // workgroups), with one query tile per KV head and no windows, the append
+  // moves into the merge and the step is two launches; otherwise the append
+  // and the query rotation share the first of three.
+  if (!win && p.QG == 1 && operand_in_scan(p, Hkv, B, 7)) {
+    StepArgs sa{pages, num_blocks, block_table, max_blocks, start_pos, k, v, mu, rot_k,
+                clip_k, clip_v, G, nullptr};
+    return launch_decode_impl(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len,
+                              max_ctx, B, Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace,
+                              p, 7, stream, nullptr, mu, &sa, kv_bf16);
+  }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);

@@ -17,10 +17,14 @@ struct DecodePlan {
   int QG;    // query-head tiles of 4 per KV head
   int spw;   // pages per workgroup split
   int S;     // splits for the longest context
-  size_t qa_off, qf_off, part_off, wpart_off, total;
+  size_t qa_off, qf_off, part_off, wpart_off, qr_off, total;
 };
 
 DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages);
+
+// Whether a call launching the PREPARE and SPLITS stages together builds the
+// query operand inside the split workgroups (no prologue launch).
+bool operand_in_scan(const DecodePlan& p, int Hkv, int B, int stages);
 
 int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                   const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,

@@ -25,8 +25,6 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/decode.hip", "csrc/kvq_common.h", "csrc/kvq_launch.h")
-# the scan without windows, group 128, one buffer descriptor over the cache
-SCAN_KERNEL = "split_kernel<1, false, false>"
 COPY_KERNEL = "neg_kernel"
 
 
@@ -49,9 +47,12 @@ def _per_dispatch(path: str, counter: str, name_part: str) -> list[float]:
     return vals
 
 
-def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes: float) -> dict:
-    sf = _per_dispatch(fetch_csv, "FETCH_SIZE", SCAN_KERNEL)
-    sw = _per_dispatch(write_csv, "WRITE_SIZE", SCAN_KERNEL)
+def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes: float,
+              kernel: str) -> dict:
+    """kernel: the scan kernel's name as rocprofv3 prints it (bench.py's
+    roofline.kernel), e.g. split_kernel<1, false, false, true>."""
+    sf = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
+    sw = _per_dispatch(write_csv, "WRITE_SIZE", kernel)
     cf = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL)
     cw = _per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL)
     mean = lambda v: sum(v) / len(v)  # noqa: E731
@@ -60,7 +61,7 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes
     fetch = mean(sf) * 1024.0 * k_fetch
     write = mean(sw) * 1024.0 * k_write
     return {
-        "kernel": SCAN_KERNEL,
+        "kernel": kernel,
         "source_sha256": kernel_source_hash(),
         "dispatches": {"fetch": len(sf), "write": len(sw), "copy_fetch": len(cf),
                        "copy_write": len(cw)},
@@ -98,7 +99,8 @@ def main():
     if line is None:
         raise SystemExit(f"{a.bench_json}: no bench JSON line")
     res = summarize(a.fetch_csv, a.write_csv, a.copy_bytes,
-                    float(line["roofline"]["algorithmic_bytes"]))
+                    float(line["roofline"]["algorithmic_bytes"]),
+                    line["roofline"]["kernel"].split(" (")[0])
     res["workload"] = line["config"]["workload"]
     res["command"] = a.command
     with open(a.out, "w") as f:

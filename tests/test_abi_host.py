@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "kvq_append", "kvq_append_decode", "kvq_append_decode_window", "kvq_decode_attn",
         "kvq_decode_attn_noalloc", "kvq_decode_attn_staged", "kvq_decode_attn_window",
-        "kvq_decode_workspace_bytes",
+        "kvq_decode_plan", "kvq_decode_workspace_bytes",
         "kvq_page_bytes", "kvq_status_string", "kvq_window_bytes", "kvq_window_write"])
 
 
@@ -74,6 +74,31 @@ def test_workspace_bytes(lib):
     # workspace grows with the number of splits
     assert kvq.decode_workspace_bytes(1, 32, 8, 131072, split_pages=8) > \
         kvq.decode_workspace_bytes(1, 32, 8, 131072, split_pages=64)
+
+
+def test_decode_plan(lib):
+    """The host plan query: splits of round(pages / split_pages), at least one
+    for a non-empty context; the operand built in the scan only while the grid
+    (splits x KV heads x query tiles x batch) is at most 1024 workgroups."""
+    import rotated_int2_kv_kvq_amd as kvq
+    p = kvq.decode_plan(16, 32, 8, 16384 + 64)
+    assert p == {"num_splits": 8, "split_pages": 128, "operand_in_scan": True}   # 1024 WGs
+    p = kvq.decode_plan(32, 32, 8, 16384)
+    assert p["num_splits"] * 8 * 32 > 1024 and not p["operand_in_scan"]
+    p = kvq.decode_plan(4, 32, 8, 1000, split_pages=64)    # 63 pages: one split of 64
+    assert p["num_splits"] == 1 and p["split_pages"] == 64 and p["operand_in_scan"]
+    p = kvq.decode_plan(4, 32, 8, 1000, split_pages=8)     # 63 / 8 -> 8 splits
+    assert p["num_splits"] == 8
+    p = kvq.decode_plan(1, 64, 8, 131072)                  # two query tiles per KV head
+    assert p["num_splits"] * 8 * 2 <= 1024 and p["operand_in_scan"]
+    assert kvq.decode_plan(4, 32, 8, 0)["num_splits"] == 0
+    assert not kvq.decode_plan(4, 32, 8, 0)["operand_in_scan"]
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_plan(4, 30, 8, 8192)                    # Hq % Hkv
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_plan(4, 32, 8, 8192, head_dim=64)
+    # null outputs are allowed
+    assert lib.kvq_decode_plan(4, 32, 8, 128, 8192, 0, None, None, None) == 0
 
 
 def _append(lib, **kw):
@@ -244,3 +269,14 @@ def test_noalloc_validates_before_touching_the_device(lib):
     big = [1 << 20, 4, 8, 128, 128, 1 << 21, 8192, 1 << 22, 131072, 64, 32, 1 << 23, 1, 1 << 24,
            1 << 25, 0.088, 1 << 26, 8, None]
     assert f(*big) == -5
+
+
+def test_build_rejects_kernels_with_a_private_segment():
+    """build.py's check of the compiler's resource-usage remarks."""
+    from rotated_int2_kv_kvq_amd.build import scratch_users
+    remarks = """x.hip:1:1: remark: Function Name: _ZN3kvq1aEv [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:9:1: remark: Function Name: _ZN3kvq1bEv [-Rpass-analysis=kernel-resource-usage]
+x.hip:9:1: remark:     ScratchSize [bytes/lane]: 120 [-Rpass-analysis=kernel-resource-usage]
+"""
+    assert scratch_users(remarks) == ["_ZN3kvq1bEv: 120 bytes/lane"]

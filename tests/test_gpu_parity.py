@@ -36,10 +36,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def report(line: str) -> None:
-    """A line for the test log even when pytest captures output."""
-    sys.__stdout__.write(line + "\n")
-    sys.__stdout__.flush()
+def report(request, line: str) -> None:
+    """A line for the test log even when pytest captures output (through the
+    terminal reporter)."""
+    tr = request.config.pluginmanager.getplugin("terminalreporter")
+    if tr is not None:
+        tr.write_line(line)
+    print(line, flush=True)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -211,19 +214,32 @@ def test_gqa_ratios(hg):
     assert err <= TIGHT
 
 
-@pytest.mark.parametrize("name", ["cfg1_b4_ctx1000", "cfg2_b6_ragged_g64"])
+# (workload, split pages, whether the whole call builds the operand in the scan)
+STAGED = {
+    "cfg1_b4_ctx1000": (SMALL["cfg1_b4_ctx1000"], 0, True),
+    "cfg2_b6_ragged_g64": (SMALL["cfg2_b6_ragged_g64"], 0, True),
+    # 8 splits x 8 KV heads x 24 sequences: more than one round of workgroups
+    "cfg1_b24_ctx1000_split8": (scaled(W1, batch=24, ctx_min=1000, ctx_max=1000), 8, False),
+}
+
+
+@pytest.mark.parametrize("name", list(STAGED))
 def test_staged_decode_matches_whole_call(name):
     """kvq_decode_attn_staged: the three stages launched one at a time, or two
-    together, leave the same output as kvq_decode_attn, bit for bit."""
+    together, leave the same output as kvq_decode_attn, bit for bit (the
+    operand built by the prologue kernel or inside the scan rounds alike)."""
     import rotated_int2_kv_kvq_amd as kvq
-    w = SMALL[name]
+    w, split_pages, in_scan = STAGED[name]
     say(f"[staged] {name}")
     case = new_case(w, keep_initial=False)
     fill_context(case)
     q = query(case)
     ctx_t = torch.from_numpy(case.ctx.astype(np.int32)).to(case.device)
     max_ctx = int(case.ctx.max())
-    ws = torch.empty(kvq.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx),
+    assert kvq.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx,
+                           split_pages=split_pages)["operand_in_scan"] == in_scan
+    ws = torch.empty(kvq.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx,
+                                                split_pages=split_pages),
                      dtype=torch.uint8, device=case.device)
 
     def run(stage_list):
@@ -231,7 +247,8 @@ def test_staged_decode_matches_whole_call(name):
                          device=case.device)
         for st in stage_list:
             kvq.decode(case.pages, case.table, ctx_t, max_ctx, q, case.rot_k, case.rot_v, w.group,
-                       case.sm_scale, out=out, workspace=ws, stages=st)
+                       case.sm_scale, out=out, workspace=ws, stages=st,
+                       split_pages=split_pages)
         torch.cuda.synchronize()
         return out
 
@@ -350,8 +367,10 @@ STEP_CASES = {
 
 @pytest.mark.parametrize("name", list(STEP_CASES))
 def test_append_decode_step(name):
-    """kvq_append_decode equals kvq_append + kvq_decode_attn bit for bit (cache
-    and output) and matches the oracle on the cache it wrote."""
+    """kvq_append_decode writes the cache kvq_append writes, bit for bit, and
+    its output equals kvq_decode_attn's after kvq_append to float32 rounding
+    (the fused step scores the new token in float32 instead of through the
+    scan's digit products); it matches the oracle on the cache it wrote."""
     import rotated_int2_kv_kvq_amd as kvq
     w = STEP_CASES[name]
     say(f"[step] {name}")
@@ -379,7 +398,8 @@ def test_append_decode_step(name):
                                   b.rk, b.rv, w.group, w.clip_k, w.clip_v, b.sm_scale)
         torch.cuda.synchronize()
         assert torch.equal(a.pages, b.pages), step
-        assert torch.equal(out_a, out_b), step
+        diff = attention_error(out_b.cpu().numpy(), out_a.cpu().numpy())
+        assert diff <= 2e-5, (step, diff)
     for s in range(w.batch):
         b.written[s] = int(ctx[s])
     pairs = [(s, hq) for s in range(w.batch) for hq in (0, 9, 31)]
@@ -401,6 +421,8 @@ WIN_CASES = {
                          [40, 317, 600]),
     # one layer of the stream workload at full size: batch 16, 16K prompts
     "bf16_g128_full": (scaled(W4, steps=2), [16384] * 16),
+    # the ragged decode batch at full size, group 64: batch 64, 1K-32K (its own lengths)
+    "bf16_g64_ragged_full": (scaled(W2, steps=2), None),
 }
 
 
@@ -437,7 +459,7 @@ def test_windows_prefill_decode_and_stream(name):
     case.folded = _folded(name)
     dev = case.device
     B, Hkv = w.batch, w.num_kv_heads
-    ctx = np.array(ctx_list, np.int64)
+    ctx = np.array(case.ctx if ctx_list is None else ctx_list, np.int64)
     win = kvq.new_window(B, Hkv, dev)
     win.zero_()
     for b in range(B):
@@ -459,7 +481,11 @@ def test_windows_prefill_decode_and_stream(name):
         kk = torch.as_tensor(keep, device=dev)
         assert torch.equal(win[b, :, 0, slots].transpose(0, 1), k[kk].to(torch.bfloat16))
         assert torch.equal(win[b, :, 1, slots].transpose(0, 1), v[kk].to(torch.bfloat16))
-    pairs = [(b, hq) for b in range(B) for hq in (0, w.num_q_heads // 2, w.num_q_heads - 1)]
+    # large batches: the oracle checks a sample of the sequences (every eighth,
+    # the shortest and the longest); the GPU decodes them all
+    seqs = range(B) if B <= 16 else sorted(set(range(0, B, 8)) | {int(ctx.argmin()),
+                                                                int(ctx.argmax())})
+    pairs = [(b, hq) for b in seqs for hq in (0, w.num_q_heads // 2, w.num_q_heads - 1)]
     q = query(case, 0)
     ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
     out = kvq.decode_window(case.pages, case.table, win, case.mu, ctx_t, int(ctx.max()), q,
@@ -757,14 +783,14 @@ def test_full_size_decode_step_sampled(folded):
     gate_exempt(near, n)
 
 
-def test_zz_exempt_rate_over_the_module():
+def test_zz_exempt_rate_over_the_module(request):
     """P2's exempt bound as a rate over every append check of this module
     (small samples are only tallied); the raw agreement with the oracle's codes
     on its own scale/zero is reported beside it."""
     t = dict(TALLY)
     if t["elements"] == 0:
         pytest.skip("no append check ran in this session")
-    report(f"[P2 tally] elements {t['elements']}  exempt {t['exempt']} "
+    report(request, f"[P2 tally] elements {t['elements']}  exempt {t['exempt']} "
         f"({t['exempt'] / t['elements']:.2e})  exact ties of values as given {t['ties']} "
         f"(mismatched {t['tie_bad']})  codes differing from the oracle's own grid "
         f"{t['raw_bad']} ({t['raw_bad'] / t['elements']:.2e})")
