@@ -227,15 +227,10 @@ int kvq_decode_attn_staged(const void *pages, int64_t num_blocks, int32_t num_kv
  * The same computation as kvq_append with num_new = 1 followed by
  * kvq_decode_attn on the same stream (the two steps of the OptR review page,
  * "What carries the argument": encode the new key and value, then attention
- * over the quantised cache and the inverse value rotation), in fewer
- * launches.  When kvq_decode_plan reports operand_in_scan and num_q_heads is
- * at most 4 * num_kv_heads, the scan leaves each new token's slot out and the
- * merge launch encodes the token and adds it to the softmax as one more
- * partial (two launches); otherwise the append shares a launch with the query
- * rotation (three).  The cache bytes written are those of kvq_append either
- * way; the output is that of the two calls up to float32 rounding (the new
- * token's term joins the sum in another order).  Arguments are those of the
- * two calls:
+ * over the quantised cache and the inverse value rotation), with the append
+ * and the decode's query rotation sharing the first of three launches (the
+ * scan and the merge follow).  The cache bytes and the output are those of
+ * the two calls, bit for bit.  Arguments are those of the two calls:
  *   start_pos      device  int32 [batch]: position of the new token
  *   k, v           device  [batch][1][num_kv_heads][head_dim] of kv_dtype
  *   ctx_len        device  int32 [batch]: tokens attended, normally

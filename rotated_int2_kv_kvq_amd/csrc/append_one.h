@@ -26,16 +26,14 @@ namespace kvq {
 // step can run it in the same launch as the query rotation.  It needs all
 // 1024 threads of the workgroup.  k_row, v_row are the token's 128 key and
 // value elements (kBf16: bfloat16, else float32); it goes to position
-// start_pos[b] + pos_delta.  deq (optional, LDS or global [2][128]) receives
-// the token's dequantised key and value in the rotated basis.
+// start_pos[b] + pos_delta.
 template <bool kBf16>
 __device__ __forceinline__ void append_one_body(
     int h, int b, uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv, int G,
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
     int pos_delta, const void* __restrict__ k_row, const void* __restrict__ v_row,
     const float* __restrict__ mu, const float* __restrict__ rot_k,
-    const float* __restrict__ rot_v, float clip_k, float clip_v,
-    float* __restrict__ deq = nullptr) {
+    const float* __restrict__ rot_v, float clip_k, float clip_v) {
   __shared__ float a_s[2][kHeadDim];
   __shared__ float part[2][4][kHeadDim];
   __shared__ float red[4][2];
@@ -127,8 +125,6 @@ __device__ __forceinline__ void append_one_body(
   const float zf = static_cast<float>(z16);
   uint32_t code = 0;
   if (sf != 0.f) code = static_cast<uint32_t>(fminf(fmaxf(rintf((x - zf) / sf), 0.f), 3.f));
-  // the dequantised value (deq: [K, V][128]), for a caller that attends the token
-  if (deq) deq[mat * kHeadDim + j] = fmaf(sf, static_cast<float>(code), zf);
 
   if (mat == 0) {
     uint32_t byte = code << (2 * (j & 3));

@@ -138,8 +138,7 @@ template <int G>
 __device__ __forceinline__ void prologue_digits(float qscale,
                                                 const float (&red)[4][kHT][kHeadDim],
                                                 uint8_t (&dig)[kHT][kHeadDim][8],
-                                                int (&qe)[kHT], float4* __restrict__ qf_tile,
-                                                float* __restrict__ qr_tile) {
+                                                int (&qe)[kHT], float4* __restrict__ qf_tile) {
   const int lane = threadIdx.x & 63;
   const int wv = (threadIdx.x >> 6) & 3;
   // wave hl: x = qscale * q_r of head hl, channels lane and lane + 64
@@ -149,10 +148,6 @@ __device__ __forceinline__ void prologue_digits(float qscale,
               (red[2][hl][lane + 64] + red[3][hl][lane + 64]));
   r0 *= qscale;  // logits in log2 units
   r1 *= qscale;
-  if (qr_tile) {  // the rotated, scaled query in float32 (for the fused step's new token)
-    qr_tile[hl * kHeadDim + lane] = r0;
-    qr_tile[hl * kHeadDim + lane + 64] = r1;
-  }
   const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
   const float s0 = wave_sum(r0), s1 = wave_sum(r1);
   // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest; digit d
@@ -385,57 +380,71 @@ struct QScratch {
   int qe[kHT];                    // per-head exponents
 };
 
-// The operand of query tile (h, qg) of sequence b: threads 0-255 do the work;
-// further threads of a larger workgroup only pass the barriers (the fused
-// decode step runs it in 1024-thread workgroups).  The A operands of lane L go
-// to qa_tile + L * lane_stride (dwords 0-17, row scales at scale_off and
-// scale_off + 1), the per-head group sums to qf_tile[0..3].  q_bf16: the
-// query is bfloat16, else float32.
+// What a thread of the operand computation loads: R_K rows [32 wv, 32 wv + 32)
+// at columns 2 lane and 2 lane + 1 (one 8-byte load per row), and two
+// channels of one query row.  Split from the arithmetic so that a split
+// workgroup can issue these loads ahead of its cache DMAs (a wave's loads
+// complete in order).
+struct QLoads {
+  float2 r[32];
+  float v0, v1;
+};
+
+// The loads of query tile (h, qg) of sequence b (threads 0-255; further
+// threads load nothing).  rot_k null: the keys were not rotated, q_r = q.
 template <int G>
-__device__ __forceinline__ void prologue_compute(int h, int qg, int b, const void* __restrict__ q,
-                                                 bool q_bf16, const float* __restrict__ rot_k,
-                                                 int Hq, int Hkv, float qscale, QScratch& ls,
-                                                 uint32_t* qa_tile, int lane_stride,
-                                                 int scale_off, float4* qf_tile,
-                                                 float* qr_tile = nullptr) {
+__device__ __forceinline__ void prologue_load(int h, int qg, int b, const void* __restrict__ q,
+                                              bool q_bf16, const float* __restrict__ rot_k, int Hq,
+                                              int Hkv, QLoads& L) {
   const int Hg = Hq / Hkv;
   const int tid = threadIdx.x;
   const bool act = tid < 256;
   const int lane = tid & 63;
   const int wv = (tid >> 6) & 3;
   const int nh = min(kHT, Hg - qg * kHT);
-
-  // R_K rows [32*wv, 32*wv + 32), columns lane and lane + 64: all loads issued
-  // first (before the query rows, whose store to LDS waits for them), one pass
-  // over R_K for the four heads.  rot_k null: the keys were not rotated, q_r = q.
-  const bool ident = rot_k == nullptr;
-  float ra[32], rb[32];
-  if (act && !ident) {
-    const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim;
+  if (act && rot_k != nullptr) {
+    const float2* R = reinterpret_cast<const float2*>(
+        rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim + 2 * lane);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      ra[i] = R[i * kHeadDim + lane];
-      rb[i] = R[i * kHeadDim + lane + 64];
-    }
+    for (int i = 0; i < 32; ++i) L.r[i] = R[i * (kHeadDim / 2)];
   }
   // the tile's query rows (zero for rows past the KV head's query heads)
+  L.v0 = 0.f;
+  L.v1 = 0.f;
+  const int hh = tid >> 6, c = (tid & 63) * 2;
+  if (act && hh < nh) {
+    const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + hh) * kHeadDim + c;
+    if (q_bf16) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + qrow);
+      L.v0 = bf16_to_f32(static_cast<uint16_t>(u & 0xffffu));
+      L.v1 = bf16_to_f32(static_cast<uint16_t>(u >> 16));
+    } else {
+      const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(q) + qrow);
+      L.v0 = f.x;
+      L.v1 = f.y;
+    }
+  }
+}
+
+// The operand from the loads: threads 0-255 do the work; further threads of
+// a larger workgroup only pass the barriers (the fused decode step runs it in
+// 1024-thread workgroups).  q.R_K as a split-K product (quarter wv of the
+// input channels, output channels 2 lane and 2 lane + 1, the four heads in
+// one pass).  The A operands of lane L go to qa_tile + L * lane_stride (dwords
+// 0-17, row scales at scale_off and scale_off + 1), the per-head group sums
+// to qf_tile[0..3].
+template <int G>
+__device__ __forceinline__ void prologue_finish(const QLoads& L, bool ident, float qscale,
+                                                QScratch& ls, uint32_t* qa_tile, int lane_stride,
+                                                int scale_off, float4* qf_tile) {
+  const int tid = threadIdx.x;
+  const bool act = tid < 256;
+  const int lane = tid & 63;
+  const int wv = (tid >> 6) & 3;
   if (act) {
     const int hh = tid >> 6, c = (tid & 63) * 2;
-    float v0 = 0.f, v1 = 0.f;
-    if (hh < nh) {
-      const size_t qrow = (static_cast<size_t>(b) * Hq + h * Hg + qg * kHT + hh) * kHeadDim + c;
-      if (q_bf16) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + qrow);
-        v0 = bf16_to_f32(static_cast<uint16_t>(u & 0xffffu));
-        v1 = bf16_to_f32(static_cast<uint16_t>(u >> 16));
-      } else {
-        const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(q) + qrow);
-        v0 = f.x;
-        v1 = f.y;
-      }
-    }
-    ls.qin[hh][c] = v0;
-    ls.qin[hh][c + 1] = v1;
+    ls.qin[hh][c] = L.v0;
+    ls.qin[hh][c + 1] = L.v1;
   }
   __syncthreads();
   if (act && ident) {
@@ -452,17 +461,29 @@ __device__ __forceinline__ void prologue_compute(int h, int qg, int b, const voi
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const float qi = ls.qin[hh][32 * wv + i];
-        a0 = fmaf(qi, ra[i], a0);
-        a1 = fmaf(qi, rb[i], a1);
+        a0 = fmaf(qi, L.r[i].x, a0);
+        a1 = fmaf(qi, L.r[i].y, a1);
       }
-      ls.red[wv][hh][lane] = a0;
-      ls.red[wv][hh][lane + 64] = a1;
+      ls.red[wv][hh][2 * lane] = a0;
+      ls.red[wv][hh][2 * lane + 1] = a1;
     }
   }
   __syncthreads();
-  if (act) prologue_digits<G>(qscale, ls.red, ls.dig, ls.qe, qf_tile, qr_tile);
+  if (act) prologue_digits<G>(qscale, ls.red, ls.dig, ls.qe, qf_tile);
   __syncthreads();
   if (act) prologue_pack<G>(ls.dig, ls.qe, qa_tile, lane_stride, scale_off);
+}
+
+// Both parts back to back.
+template <int G>
+__device__ __forceinline__ void prologue_compute(int h, int qg, int b, const void* __restrict__ q,
+                                                 bool q_bf16, const float* __restrict__ rot_k,
+                                                 int Hq, int Hkv, float qscale, QScratch& ls,
+                                                 uint32_t* qa_tile, int lane_stride,
+                                                 int scale_off, float4* qf_tile) {
+  QLoads L;
+  prologue_load<G>(h, qg, b, q, q_bf16, rot_k, Hq, Hkv, L);
+  prologue_finish<G>(L, rot_k == nullptr, qscale, ls, qa_tile, lane_stride, scale_off, qf_tile);
 }
 
 // The prologue kernel's view: its own LDS, the operand to the workspace.
@@ -543,11 +564,14 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(
 // page 0 (128G B)][pairs of page 1], each part as laid out in the cache, so
 // that for group 128 one 64-lane DMA fetches both pages' pairs: a slice is
 // dma_per_slice<G>() DMA instructions, with no lane-dependent branch for the
-// compiler to duplicate (the waits count them exactly).  Two slices in flight
-// per wave.  Four slots, one per slice of an 8-page block, so that every slot
-// address is a compile-time offset; the P tile lives in the slot of the
-// block's last slice.
-constexpr int kDepth = 2;
+// compiler to duplicate (the waits count them exactly).  Four slots, one per
+// slice of an 8-page block, so that every slot address is a compile-time
+// offset.  A slot is free once its slice has been read into registers, so
+// three slices are in flight per wave: slice s of a block issues the slice
+// three ahead into the slot read one slice before.  The P tile lives in the
+// slot of the block's last slice, whose next DMA is issued by the next
+// block's first slice, after the P.V products.
+constexpr int kDepth = 3;
 constexpr int kRing = 4;
 constexpr int kSlotCodes1 = 1024;  // codes of a slot's second page
 constexpr int kSlotPairs = 2048;   // (scale, zero) pairs of its first page
@@ -897,15 +921,14 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const float4* __restrict__ qf, float* __restrict__ part, int S,
              const uint16_t* __restrict__ wstore, int n_win, const void* __restrict__ q,
              int q_bf16, const float* __restrict__ mu, float qscale, float* __restrict__ wpart,
-             const float* __restrict__ rot_k, const int* __restrict__ new_pos,
-             float* __restrict__ qr) {
+             const float* __restrict__ rot_k) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
   // slot s of wave w at ring[s][w]: the slots 2-3 of all four waves are one
   // contiguous region, free from the start until the first block's loop
   constexpr int kSlotStride = 4 * kSlot;
   static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
-  static_assert(kRing == 4 && kDepth == 2, "slots are the slices of a block; two in flight");
+  static_assert(kRing == 4 && kDepth == 3, "slots are the slices of a block; three in flight");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kSlot];
   __shared__ __attribute__((aligned(16))) int wids[kMaxSplitPages];  // block ids of the pages
   __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
@@ -994,6 +1017,13 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int hl = lane >> 4;
   uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0, q2 = q0, q3 = q0, q4 = q0, qsv = q0;
   float4 fq = make_float4(0.f, 0.f, 0.f, 0.f);
+  // kSelfQ: R_K and the query rows for the operand, loaded here so that they
+  // land ahead of the cache DMAs issued below (with the wide descriptor or the
+  // window role the registers are short: loaded after the DMAs)
+  constexpr bool kEarlyQ = kSelfQ && !kWide && !kWin;
+  QLoads qload;
+  if constexpr (kEarlyQ)
+    prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qload);
   if constexpr (!kSelfQ) {
     const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
     q0 = qap[0];
@@ -1009,11 +1039,6 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 
   const int ctx = min(max(ctx_in, 0), max_ctx);
   const int hi_tok = win ? body_end(ctx) : ctx;  // tokens scanned: [lo_pages * 16, hi_tok)
-  // The fused decode step (new_pos: the new tokens' positions) appends in the
-  // merge, after this launch: the scan leaves the new token's slot out (the
-  // merge adds the token itself), and the block holding it takes the masked
-  // path.
-  const int pex = new_pos ? new_pos[b] : -1;
   const int n_pages = (hi_tok + kBlock - 1) / kBlock;
   const int ns_b = num_splits(n_pages - lo_pages, spw);
   if (wgs >= ns_b) return;
@@ -1103,9 +1128,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     QScratch& ls = *reinterpret_cast<QScratch*>(free_lds);
     uint32_t* qa_s = reinterpret_cast<uint32_t*>(free_lds + offsetof(QScratch, red));
     float4* qf_s = reinterpret_cast<float4*>(free_lds + sizeof(QScratch));
-    prologue_compute<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qscale, ls, qa_s, kQaLds,
-                        kQaLdsScale, qf_s,
-                        (qr && wgs == 0) ? qr + hgi * kHT * kHeadDim : nullptr);
+    if constexpr (!kEarlyQ) prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qload);
+    prologue_finish<G>(qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s);
     __syncthreads();  // the operand is packed
     const uint32_t* mine = qa_s + lane * kQaLds;
     qv0 = u32x4{mine[0], mine[1], mine[2], mine[3]};
@@ -1121,6 +1145,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   }
   // the id table is complete (and the operand read before slots 2-3 refill)
   __syncthreads();
+  if (nsl >= 3) issue(myring + 2 * kSlotStride, idc[4], idc[5]);
 
   auto op6 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
     return v8i{static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
@@ -1162,16 +1187,20 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
       constexpr int s = decltype(sc)::value;
       const int i = 4 * bi + s;
       if (kFast || i < nsl) {
-        // slice i + 2: slices 2, 3 of this block, then 0, 1 of the next
+        // slice i + 3: slice 3 of this block, then 0-2 of the next (into the
+        // slot that slice i - 1 was read from)
+        static_assert(kDepth == 3, "the slot schedule assumes three slices in flight");
         if (kFast || i + kDepth < nsl) {
-          if constexpr (s < 2)
-            issue(myring + (s + 2) * kSlotStride, idc[2 * s + 4], idc[2 * s + 5]);
+          if constexpr (s == 0)
+            issue(myring + 3 * kSlotStride, idc[6], idc[7]);
           else
-            issue(myring + (s - 2) * kSlotStride, idn[2 * s - 4], idn[2 * s - 3]);
+            issue(myring + (s - 1) * kSlotStride, idn[2 * s - 2], idn[2 * s - 1]);
         }
         // slice i has landed once at most the DMAs of the slices behind it are pending
-        if (kFast || i + kDepth < nsl)
-          wait_vmem<kDepth * dma_per_slice<G>()>();
+        if (kFast || i + 3 < nsl)
+          wait_vmem<3 * dma_per_slice<G>()>();
+        else if (i + 2 < nsl)
+          wait_vmem<2 * dma_per_slice<G>()>();
         else if (i + 1 < nsl)
           wait_vmem<dma_per_slice<G>()>();
         else
@@ -1227,8 +1256,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         } else {
           const int pg = pblk + 2 * s;
           const int pos = pg * kBlock + t;
-          const bool v0 = pos < hi_tok && pos != pex;
-          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok && pos + kBlock != pex;
+          const bool v0 = pos < hi_tok;
+          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok;
           lg[2 * s] = v0 ? l0 : -INFINITY;
           lg[2 * s + 1] = v1 ? l1 : -INFINITY;
           // slots past the context hold arbitrary bytes (possibly NaN as fp16):
@@ -1287,7 +1316,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     st.l += lsum;
     st.zs0 += z0;
     st.zs1 += z1;
-    // slot 3: read above; the DMAs in flight target slots 0 and 1
+    // slot 3: read above; the DMAs in flight target slots 0-2
     uint8_t* ptile = myring + 3 * kSlotStride;
     if constexpr (G == 1) {
       block_pv<0, 8>(st, p, sz0, ptile, pexp[wave], vw, lane);
@@ -1298,11 +1327,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 #pragma unroll
     for (int k = 0; k < 8; ++k) idc[k] = idn[k];
   };
-  int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
-  if (pex >= 0) {
-    const int rel = pex / kBlock - p_begin;  // page of the new token in this range
-    if (rel >= 0 && rel < np && ((rel >> 3) & 3) == wave) nfast = min(nfast, (rel >> 3) >> 2);
-  }
+  const int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
   int bi = 0;
   for (; bi < nfast; ++bi) run_block(Const<bool, true>{}, bi);
   for (; bi < nbw; ++bi) run_block(Const<bool, false>{}, bi);
@@ -1346,11 +1371,10 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     }
     const int hq = h * Hg + hloc;
     float* dst = part + ((static_cast<size_t>(b) * Hq + hq) * S + wgs) * kPartStride;
-    // a split whose only token is the fused step's new one saw nothing
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    const float inv = 1.0f / L;
     dst[4 + cc] = o0 * inv;
     dst[4 + cc + 64] = o1 * inv;
-    if (cc == 0) dst[0] = L > 0.f ? M + __log2f(L) : kNegBig;
+    if (cc == 0) dst[0] = M + __log2f(L);
   }
 }
 
@@ -1369,40 +1393,15 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // separates the merge from the rotation.
 constexpr int kMergeSplits = 16;  // splits per thread and round (two halves: 32 per round)
 
-// The fused decode step (kApp = 1: bfloat16 k/v, 2: float32) also encodes
-// the step's new token of (sequence, KV head) into the cache, with the
-// single-token append's arithmetic (the same bytes), and merges the token
-// itself as one more partial: its logit is the scan's float32 rotated query
-// (qr) against the dequantised new key, its output the dequantised new value.
-// The scan left the token's slot out.  One query tile per KV head (QG == 1).
-struct StepArgs {
-  uint8_t* pages;
-  int64_t num_blocks;
-  const int* block_table;
-  int max_blocks;
-  const int* start_pos;
-  const void* k;
-  const void* v;
-  const float* mu;
-  const float* rot_k;
-  float clip_k, clip_v;
-  int G;            // groups per head_dim (1: group 128, 2: group 64)
-  const float* qr;  // [B][Hkv][4][128] scaled rotated query from the scan
-};
-
-template <int kApp>
 __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ part,
                                                      const int* __restrict__ ctx_len, int max_ctx,
                                                      int Hq, int Hkv, int QG, int spw, int S,
                                                      const float* __restrict__ rot_v,
                                                      float* __restrict__ out,
-                                                     const float* __restrict__ wpart,
-                                                     StepArgs st) {
+                                                     const float* __restrict__ wpart) {
   __shared__ __attribute__((aligned(16))) float osum[2][kHT][kHeadDim];
   __shared__ float hinv[kHT];  // 1 / (weight sum) per head
   __shared__ float hwin[kHT];  // the window partial's share of each head's output
-  __shared__ float deq[2][kHeadDim];   // fused step: the new key and value, dequantised
-  __shared__ float nlog[kHT][2];      // fused step: halves of the new token's logits
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
@@ -1439,25 +1438,6 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   load_x(0, xv);
   if (S > 2 * kMergeSplits) load_x(1, xw);  // S: the same in every thread
   const int ctx = min(max(ctx_in, 0), max_ctx);
-  // fused step: encode the new token (all 1024 threads), then its logits
-  float lse_n = kNegBig;  // head u's new-token logit (log2 units); kNegBig: not attended
-  if constexpr (kApp != 0) {
-    constexpr bool kKvBf16 = kApp == 1;
-    const float qrv = st.qr[((static_cast<size_t>(b) * Hkv + h) * kHT + u) * kHeadDim + c];
-    append_one_body<kKvBf16>(h, b, st.pages, st.num_blocks, Hkv, st.G,
-                             st.block_table, st.max_blocks, st.start_pos, 0,
-                             token_row<kKvBf16>(st.k, b, h, Hkv),
-                             token_row<kKvBf16>(st.v, b, h, Hkv), st.mu, st.rot_k, rot_v,
-                             st.clip_k, st.clip_v, &deq[0][0]);
-    __syncthreads();
-    const int pn = st.start_pos[b];
-    if (half == 0) {
-      float x = wave_sum(qrv * deq[0][c]);
-      if (lane == 0) nlog[u][c >> 6] = x;
-    }
-    __syncthreads();
-    if (pn >= 0 && pn < ctx) lse_n = nlog[u][0] + nlog[u][1];
-  }
   // the window partial's lse, and the window output this thread adds
   const float lse_w = wpart ? wpart[(row0 + min(u, nh - 1)) * kPartStride] : kNegBig;
   const float wv = wpart ? wpart[(row0 + min(part8 & 3, nh - 1)) * kPartStride + 4 + j] : 0.f;
@@ -1479,15 +1459,11 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
   M = wave_max(M);
   M = fmaxf(M, lse_w);
-  M = fmaxf(M, lse_n);
   float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
   for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
   W = wave_sum(W);
   const float a_w = exp2_hw(lse_w - M);  // 0 without windows
   W += a_w;
-  // the fused step's new token: weight 0 when it is not attended
-  const float a_n = (kApp != 0 && lse_n > kNegBig) ? exp2_hw(lse_n - M) : 0.f;
-  W += a_n;
 
   // channel c over this half's splits, a round at a time (one round covers
   // 32 splits); a split past the count contributes nothing (its stale values
@@ -1522,7 +1498,6 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
       if (s < ns) acc = fmaf(exp2_hw(lv[k] - M), xv[k], acc);
     }
   }
-  if (kApp != 0 && half == 0 && a_n > 0.f) acc = fmaf(a_n, deq[1][c], acc);
   osum[half][u][c] = acc;
   if ((tid & 255) == 0) {
     const float inv = 1.0f / W;
@@ -1711,8 +1686,7 @@ DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages) {
   p.part_off = p.qf_off + align256(hg * kHT * 16);
   p.wpart_off =
       p.part_off + align256(static_cast<size_t>(B) * Hq * (p.S ? p.S : 1) * kPartStride * 4);
-  p.qr_off = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
-  p.total = p.qr_off + align256(hg * kHT * kHeadDim * 4);
+  p.total = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
   return p;
 }
 
@@ -1728,16 +1702,11 @@ bool operand_in_scan(const DecodePlan& p, int Hkv, int B, int stages) {
   return (stages & 3) == 3 && static_cast<int64_t>(p.S) * Hkv * p.QG * B <= 1024;
 }
 
-// The decode launches; `step` (the fused decode step, non-null only with the
-// operand built in the scan, one query tile per KV head and no windows) makes
-// the scan leave the new tokens' slots out and the merge append them.
-static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
-                              const int* block_table, int max_blocks, const int* ctx_len,
-                              int max_ctx, int B, int Hq, const void* q, bool q_bf16,
-                              const float* rot_k, const float* rot_v, float sm_scale, float* out,
-                              void* workspace, const DecodePlan& p, int stages,
-                              hipStream_t stream, const uint16_t* win, const float* mu,
-                              const StepArgs* step, bool kv_bf16) {
+int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
+                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
+                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
+                  hipStream_t stream, const uint16_t* win, const float* mu) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
@@ -1745,8 +1714,6 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
   float* wpart = win ? reinterpret_cast<float*>(ws + p.wpart_off) : nullptr;
   const float qscale = sm_scale * kLog2e;
   const bool self_q = operand_in_scan(p, Hkv, B, stages);
-  const int* new_pos = step ? step->start_pos : nullptr;
-  float* qr = step ? reinterpret_cast<float*>(ws + p.qr_off) : nullptr;
   if (p.S > 0 && (stages & 1) && !self_q) {
     const dim3 g1(Hkv * p.QG, B);
     auto go = [&](auto kernel) {
@@ -1767,7 +1734,7 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
                          max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S, win,
-                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, new_pos, qr);
+                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k);
     };
     auto pick = [&](auto g, auto wd) {
       constexpr int GG = decltype(g)::value;
@@ -1783,37 +1750,16 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
     G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
   // fewer than 64 query tiles without windows: a workgroup per query head
-  const bool per_head = !win && !step && static_cast<int64_t>(B) * Hkv * p.QG < 64;
-  StepArgs sa{};
-  if (step) {
-    sa = *step;
-    sa.qr = qr;
-  }
+  const bool per_head = !win && static_cast<int64_t>(B) * Hkv * p.QG < 64;
   if ((stages & 4) && per_head) {
     hipLaunchKernelGGL(merge_head_kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len,
                        max_ctx, Hq, Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
   } else if (stages & 4) {
-    auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
-                         max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
-                         static_cast<const float*>(wpart), sa);
-    };
-    if (!step)
-      go(merge_kernel<0>);
-    else
-      kv_bf16 ? go(merge_kernel<1>) : go(merge_kernel<2>);
+    hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
+                       max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
+                       static_cast<const float*>(wpart));
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
-                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
-                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
-                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
-                  hipStream_t stream, const uint16_t* win, const float* mu) {
-  return launch_decode_impl(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len, max_ctx,
-                            B, Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace, p, stages,
-                            stream, win, mu, nullptr, false);
 }
 
 int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
@@ -1823,17 +1769,6 @@ int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          int Hq, const void* q, bool q_bf16, const float* rot_k,
                          const float* rot_v, float sm_scale, float* out, void* workspace,
                          const DecodePlan& p, hipStream_t stream, uint16_t* win) {
-  // Fused: when the scan builds its own query operand (one round of
-  // workgroups), with one query tile per KV head and no windows, the append
-  // moves into the merge and the step is two launches; otherwise the append
-  // and the query rotation share the first of three.
-  if (!win && p.QG == 1 && operand_in_scan(p, Hkv, B, 7)) {
-    StepArgs sa{pages, num_blocks, block_table, max_blocks, start_pos, k, v, mu, rot_k,
-                clip_k, clip_v, G, nullptr};
-    return launch_decode_impl(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len,
-                              max_ctx, B, Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace,
-                              p, 7, stream, nullptr, mu, &sa, kv_bf16);
-  }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
