@@ -810,6 +810,16 @@ __device__ __forceinline__ void put_digits(uint32_t wbase, uint32_t d0, uint32_t
         "i"(16 * kJ + 2 * kPRow), "i"(16 * kJ + 3 * kPRow)
       : "memory");
 }
+// The same for two digits (rows 0 and 1 of the head).
+template <int kJ>
+__device__ __forceinline__ void put_digits2(uint32_t wbase, uint32_t d0, uint32_t d1) {
+  asm volatile(
+      "ds_write_b8 %0, %1 offset:%3\n"
+      "ds_write_b8 %0, %2 offset:%4"
+      :
+      : "v"(wbase), "v"(d0), "v"(d1), "i"(16 * kJ), "i"(16 * kJ + kPRow)
+      : "memory");
+}
 
 struct ScanState {
   float m, l, zs0, zs1;
@@ -821,10 +831,11 @@ struct ScanState {
 // (per head and block, rounded to nearest); digit d (0 = most significant) is worth
 // b * 2^(e - 4 - 4d), an FP8 byte b * 2^-9 under the row scale
 // 2^(e + 8 - 4d) (which also cancels the code operand's code/8).  Digits 0-3,
-// then 4-5 (rows 2 and 3 of each head zero), go through the one P tile (the
-// second set overwrites rows the first has already read back), each read back
-// as an A operand (row r = lane%16, pages g and g + 4 of lane group
-// g = lane/16); then two MFMAs per 16 output channels on one code operand.
+// then 4-5 (into rows 0 and 1 of each head; rows 2 and 3 keep digits 2-3,
+// scaled by 2^-127 to nothing), go through the one P tile (the second set
+// overwrites rows the first has already read back), each read back as an A
+// operand (row r = lane%16, pages g and g + 4 of lane group g = lane/16);
+// then two MFMAs per 16 output channels on one code operand.
 template <int kT0, int kT1>
 __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
                                          const uint32_t (&szv)[8], uint8_t* ptile, int* pexp,
@@ -868,7 +879,7 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
       : "memory");
   static_for<0, 8>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    put_digits<j>(wbase, (W[j] >> 4) & 15u, W[j] & 15u, 0u, 0u);
+    put_digits2<j>(wbase, (W[j] >> 4) & 15u, W[j] & 15u);
   });
   asm volatile(
       "ds_read_b128 %0, %2\n"
@@ -878,7 +889,9 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
       : "v"(ra)
       : "memory");
   const int sa_hi = min(max(kScaleOne + er + 8 - 4 * (r & 3), 1), 254);
-  const int sa_lo = min(max(kScaleOne + er - 8 - 4 * (r & 3), 1), 254);
+  // rows 2 and 3 of a head still hold digits 2 and 3: the smallest E8M0
+  // scale (2^-127) takes their products below every accumulated value
+  const int sa_lo = (r & 3) < 2 ? min(max(kScaleOne + er - 8 - 4 * (r & 3), 1), 254) : 0;
   const v8i Ahi = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
                    static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
                    static_cast<int>(h1.z), static_cast<int>(h1.w)};
