@@ -583,12 +583,11 @@ __host__ __device__ constexpr int dma_per_slice() {
 // of a context taking up to half a split more.
 constexpr int kMaxSplitPages = 768;
 // P tile: 16 rows (4 heads x 4 digits) x 8 pages x 16 tokens of FP8 digit
-// bytes; the row stride is padded to 144 bytes so that the A-operand reads
-// (16 rows at one page) and the digit writes spread over all LDS banks.  It
-// lives in the ring slot of the block's last slice, which is free from the
-// moment that slice is read until the next slice's DMA is issued.
-constexpr int kPRow = 144;
-constexpr int kPTile = 16 * kPRow;
+// bytes, stored by token column (16 bytes per column: 8 rows of each half of
+// the heads).  It lives in the ring slot of the block's last slice, which is
+// free from the moment that slice is read until the next slice's DMA is
+// issued.
+constexpr int kPTile = 2048;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -797,28 +796,15 @@ __device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av) {
 
 // Write four digit bytes to rows 4*hl + 0..3 of the P tile at this lane's
 // (page kJ, token) column.
+// A lane's P-tile store for page kJ: the four digit bytes of its head, or
+// the low two.
 template <int kJ>
-__device__ __forceinline__ void put_digits(uint32_t wbase, uint32_t d0, uint32_t d1, uint32_t d2,
-                                           uint32_t d3) {
-  asm volatile(
-      "ds_write_b8 %0, %1 offset:%5\n"
-      "ds_write_b8 %0, %2 offset:%6\n"
-      "ds_write_b8 %0, %3 offset:%7\n"
-      "ds_write_b8 %0, %4 offset:%8"
-      :
-      : "v"(wbase), "v"(d0), "v"(d1), "v"(d2), "v"(d3), "i"(16 * kJ), "i"(16 * kJ + kPRow),
-        "i"(16 * kJ + 2 * kPRow), "i"(16 * kJ + 3 * kPRow)
-      : "memory");
+__device__ __forceinline__ void put_p32(uint32_t wbase, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(wbase), "v"(v), "i"(256 * kJ) : "memory");
 }
-// The same for two digits (rows 0 and 1 of the head).
 template <int kJ>
-__device__ __forceinline__ void put_digits2(uint32_t wbase, uint32_t d0, uint32_t d1) {
-  asm volatile(
-      "ds_write_b8 %0, %1 offset:%3\n"
-      "ds_write_b8 %0, %2 offset:%4"
-      :
-      : "v"(wbase), "v"(d0), "v"(d1), "i"(16 * kJ), "i"(16 * kJ + kPRow)
-      : "memory");
+__device__ __forceinline__ void put_p16(uint32_t wbase, uint32_t v) {
+  asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(wbase), "v"(v), "i"(256 * kJ) : "memory");
 }
 
 struct ScanState {
@@ -828,14 +814,18 @@ struct ScanState {
 
 // The P.V products of one 128-token block for output channel tiles
 // [kT0, kT1).  w = p * s_V is fixed-point with 24 fraction bits under 2^e
-// (per head and block, rounded to nearest); digit d (0 = most significant) is worth
-// b * 2^(e - 4 - 4d), an FP8 byte b * 2^-9 under the row scale
-// 2^(e + 8 - 4d) (which also cancels the code operand's code/8).  Digits 0-3,
-// then 4-5 (into rows 0 and 1 of each head; rows 2 and 3 keep digits 2-3,
-// scaled by 2^-127 to nothing), go through the one P tile (the second set
-// overwrites rows the first has already read back), each read back as an A
-// operand (row r = lane%16, pages g and g + 4 of lane group g = lane/16);
-// then two MFMAs per 16 output channels on one code operand.
+// (per head and block, rounded to nearest), six 4-bit digits D0 (most
+// significant) .. D5, an FP8 byte b being worth b * 2^-9.  The P tile holds,
+// for each token column c (16 page + token) and half h of the heads, the
+// eight bytes of rows 8h .. 8h + 7 (row 4 * head + k), 16 bytes per column:
+// a lane writes its token's four digit bytes of one head with one 32-bit
+// store, and each A operand (row r = lane%16; lane group g = lane/16 takes
+// pages g and g + 4) comes back with four 8-byte transposing reads, which
+// hand lane r byte r%8 of eight column chunks.  Row 4 * head + k holds D(3-k)
+// in the first pass (row scale 2^(e - 4 + 4k), which also cancels the code
+// operand's code/8) and D(5-k) for k < 2 in the second (2^(e - 12 + 4k));
+// rows k = 2, 3 then still hold D1, D0, scaled by 2^-127 to nothing.  Two
+// MFMAs per 16 output channels on one code operand.
 template <int kT0, int kT1>
 __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
                                          const uint32_t (&szv)[8], uint8_t* ptile, int* pexp,
@@ -854,50 +844,62 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
   uint32_t W[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) W[j] = static_cast<uint32_t>(fmaf(w[j], sc, 0.5f));
-  // kept opaque: computed here, not held across the scan loop
-  uint32_t wbase = lds_addr(ptile) + 4 * hl * kPRow + t;
+  // kept opaque: computed here, not held across the scan loop.  This lane's
+  // dword of page 0: column t, half hl/2, bytes 4(hl%2) ..; page j at + 256 j
+  uint32_t wbase = lds_addr(ptile) + 16 * t + 4 * hl;
   uint32_t hdr = lds_addr(reinterpret_cast<const uint8_t*>(pexp));
   asm volatile("" : "+v"(wbase), "+v"(hdr));
   if (t == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(hdr + 4 * hl), "v"(e) : "memory");
   const int r = lane & 15, g = lane >> 4;
-  uint32_t ra = lds_addr(ptile) + r * kPRow + 16 * g;
+  // transposing reads: lane (r, g) addresses the chunk of column 16g + r/2
+  // (+ 8, + 64, + 72 for the other three), half r%2
+  uint32_t ra = lds_addr(ptile) + 16 * (16 * g + (r >> 1)) + 8 * (r & 1);
   asm volatile("" : "+v"(ra));
-  u32x4 h0, h1, l0, l1;
+  u32x2 h0, h1, h2, h3, l0, l1, l2, l3;
   int er;
   static_for<0, 8>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    put_digits<j>(wbase, (W[j] >> 20) & 15u, (W[j] >> 16) & 15u, (W[j] >> 12) & 15u,
-                  (W[j] >> 8) & 15u);
+    // bytes [D3, D2, D1, D0]: the two upper bytes of W spread to nibbles
+    const uint32_t t1 = __builtin_amdgcn_perm(W[j], W[j], 0x0C020C01u);
+    const uint32_t hi = (t1 & 0x000F000Fu) | ((t1 << 4) & 0x0F000F00u);
+    put_p32<j>(wbase, hi);
   });
   asm volatile(
-      "ds_read_b128 %0, %3\n"
-      "ds_read_b128 %1, %3 offset:64\n"
-      "ds_read_b32 %2, %4\n"
+      "ds_read_b64_tr_b8 %0, %4\n"
+      "ds_read_b64_tr_b8 %1, %4 offset:128\n"
+      "ds_read_b64_tr_b8 %2, %4 offset:1024\n"
+      "ds_read_b64_tr_b8 %3, %4 offset:1152\n"
+      "ds_read_b32 %5, %6\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(h0), "=&v"(h1), "=&v"(er)
-      : "v"(ra), "v"(hdr + 4 * (r >> 2))
+      : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "+v"(ra), "=&v"(er)
+      : "v"(hdr + 4 * (r >> 2))
       : "memory");
   static_for<0, 8>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    put_digits2<j>(wbase, (W[j] >> 4) & 15u, W[j] & 15u);
+    // bytes [D5, D4] over the first pass's [D3, D2]
+    const uint32_t lo = (W[j] & 0x0Fu) | ((W[j] << 4) & 0x0F00u);
+    put_p16<j>(wbase, lo);
   });
   asm volatile(
-      "ds_read_b128 %0, %2\n"
-      "ds_read_b128 %1, %2 offset:64\n"
+      "ds_read_b64_tr_b8 %0, %4\n"
+      "ds_read_b64_tr_b8 %1, %4 offset:128\n"
+      "ds_read_b64_tr_b8 %2, %4 offset:1024\n"
+      "ds_read_b64_tr_b8 %3, %4 offset:1152\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(l0), "=&v"(l1)
-      : "v"(ra)
+      : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3), "+v"(ra)
+      :
       : "memory");
-  const int sa_hi = min(max(kScaleOne + er + 8 - 4 * (r & 3), 1), 254);
-  // rows 2 and 3 of a head still hold digits 2 and 3: the smallest E8M0
-  // scale (2^-127) takes their products below every accumulated value
-  const int sa_lo = (r & 3) < 2 ? min(max(kScaleOne + er - 8 - 4 * (r & 3), 1), 254) : 0;
-  const v8i Ahi = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
-                   static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
-                   static_cast<int>(h1.z), static_cast<int>(h1.w)};
-  const v8i Alo = {static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
-                   static_cast<int>(l0.w), static_cast<int>(l1.x), static_cast<int>(l1.y),
-                   static_cast<int>(l1.z), static_cast<int>(l1.w)};
+  const int k = r & 3;
+  const int sa_hi = min(max(kScaleOne + er - 4 + 4 * k, 1), 254);
+  // rows k = 2, 3 of a head still hold D1, D0: the smallest E8M0 scale
+  // (2^-127) takes their products below every accumulated value
+  const int sa_lo = k < 2 ? min(max(kScaleOne + er - 12 + 4 * k, 1), 254) : 0;
+  const v8i Ahi = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h1.x),
+                   static_cast<int>(h1.y), static_cast<int>(h2.x), static_cast<int>(h2.y),
+                   static_cast<int>(h3.x), static_cast<int>(h3.y)};
+  const v8i Alo = {static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l1.x),
+                   static_cast<int>(l1.y), static_cast<int>(l2.x), static_cast<int>(l2.y),
+                   static_cast<int>(l3.x), static_cast<int>(l3.y)};
   // value words: vw[0..1] = page 2g, tiles 0-7; vw[2..3] = page 2g + 1
   const uint32_t p0[8] = {vw[0].x, vw[0].y, vw[0].z, vw[0].w, vw[1].x, vw[1].y, vw[1].z, vw[1].w};
   const uint32_t p1[8] = {vw[2].x, vw[2].y, vw[2].z, vw[2].w, vw[3].x, vw[3].y, vw[3].z, vw[3].w};
