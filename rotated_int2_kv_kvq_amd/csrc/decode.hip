@@ -794,8 +794,6 @@ __device__ __forceinline__ void read_vwords(u32x4 (&vw)[4], uint32_t av) {
       : "memory");
 }
 
-// Write four digit bytes to rows 4*hl + 0..3 of the P tile at this lane's
-// (page kJ, token) column.
 // A lane's P-tile store for page kJ: the four digit bytes of its head, or
 // the low two.
 template <int kJ>
