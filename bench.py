@@ -229,26 +229,32 @@ def main():
     # workspace; the split kernels of all layers run back to back between one
     # pair of events, and so do the single-token appends.  Every launch is
     # queued behind a GPU sleep so that host launch latency never falls inside
-    # an event interval.  The step (kvq_append_decode) rotates the query in
-    # its first launch, so its scan reads the operand from the workspace: the
-    # PREPARE stage runs untimed and SPLITS alone is timed, the step's kernel.
+    # an event interval.  Where the plan builds the query operand inside the
+    # scan, PREPARE and SPLITS together are that one launch, the step's scan
+    # kernel (whose launch in the step also encodes the new tokens, in 128
+    # workgroups after the splits); otherwise PREPARE runs untimed and SPLITS
+    # alone is timed.
     last = total_steps - 1
-    scan_kernel = scan_kernel_name(w.group, False)
+    plan = kvq.decode_plan(B, Hq, Hkv, maxc[last])
+    scan_stages = (kvq.STAGE_PREPARE | kvq.STAGE_SPLITS if plan["operand_in_scan"]
+                   else kvq.STAGE_SPLITS)
+    scan_kernel = scan_kernel_name(w.group, plan["operand_in_scan"])
     wss = [ws] + [torch.empty_like(ws) for _ in range(L - 1)]
     split_ms, app_ms = [], []
     for rep in range(4):
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)
         s0, s1, a0, a1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-        for layer in range(L):
-            kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
-                       rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
-                       stages=kvq.STAGE_PREPARE)
+        if not plan["operand_in_scan"]:
+            for layer in range(L):
+                kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer],
+                           rks[layer], rvs[layer], w.group, sm_scale, out=outs[layer],
+                           workspace=wss[layer], stages=kvq.STAGE_PREPARE)
         s0.record()
         for layer in range(L):
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],
                        rvs[layer], w.group, sm_scale, out=outs[layer], workspace=wss[layer],
-                       stages=kvq.STAGE_SPLITS)
+                       stages=scan_stages)
         s1.record()
         for layer in range(L):
             kvq.decode(pages[layer], table, ctxs[last], maxc[last], qs[last][layer], rks[layer],

@@ -227,10 +227,17 @@ int kvq_decode_attn_staged(const void *pages, int64_t num_blocks, int32_t num_kv
  * The same computation as kvq_append with num_new = 1 followed by
  * kvq_decode_attn on the same stream (the two steps of the OptR review page,
  * "What carries the argument": encode the new key and value, then attention
- * over the quantised cache and the inverse value rotation), with the append
- * and the decode's query rotation sharing the first of three launches (the
- * scan and the merge follow).  The cache bytes and the output are those of
- * the two calls, bit for bit.  Arguments are those of the two calls:
+ * over the quantised cache and the inverse value rotation), in fewer
+ * launches.  When kvq_decode_plan reports operand_in_scan, num_q_heads is at
+ * most 4 * num_kv_heads and max_ctx_len > 0, it is two: the scan's launch also
+ * encodes the new tokens (in workgroups dispatched after its splits, which
+ * leave the new tokens' slots out) and the merge adds each new token as one
+ * more partial.  Otherwise three: the append shares a launch with the query
+ * rotation, then the scan and the merge.  The cache bytes written are those
+ * of kvq_append either way; the output is that of the two calls bit for bit
+ * in the three-launch form, to float32 rounding in the two-launch form (the
+ * new token's logit is taken in float32).  Arguments are those of the two
+ * calls:
  *   start_pos      device  int32 [batch]: position of the new token
  *   k, v           device  [batch][1][num_kv_heads][head_dim] of kv_dtype
  *   ctx_len        device  int32 [batch]: tokens attended, normally

@@ -138,7 +138,8 @@ template <int G>
 __device__ __forceinline__ void prologue_digits(float qscale,
                                                 const float (&red)[4][kHT][kHeadDim],
                                                 uint8_t (&dig)[kHT][kHeadDim][8],
-                                                int (&qe)[kHT], float4* __restrict__ qf_tile) {
+                                                int (&qe)[kHT], float4* __restrict__ qf_tile,
+                                                float* __restrict__ qr_tile) {
   const int lane = threadIdx.x & 63;
   const int wv = (threadIdx.x >> 6) & 3;
   // wave hl: x = qscale * q_r of head hl, channels lane and lane + 64
@@ -148,6 +149,10 @@ __device__ __forceinline__ void prologue_digits(float qscale,
               (red[2][hl][lane + 64] + red[3][hl][lane + 64]));
   r0 *= qscale;  // logits in log2 units
   r1 *= qscale;
+  if (qr_tile) {  // the rotated, scaled query in float32 (the decode step's new token)
+    qr_tile[hl * kHeadDim + lane] = r0;
+    qr_tile[hl * kHeadDim + lane + 64] = r1;
+  }
   const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
   const float s0 = wave_sum(r0), s1 = wave_sum(r1);
   // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest; digit d
@@ -436,7 +441,8 @@ __device__ __forceinline__ void prologue_load(int h, int qg, int b, const void* 
 template <int G>
 __device__ __forceinline__ void prologue_finish(const QLoads& L, bool ident, float qscale,
                                                 QScratch& ls, uint32_t* qa_tile, int lane_stride,
-                                                int scale_off, float4* qf_tile) {
+                                                int scale_off, float4* qf_tile,
+                                                float* qr_tile = nullptr) {
   const int tid = threadIdx.x;
   const bool act = tid < 256;
   const int lane = tid & 63;
@@ -469,7 +475,7 @@ __device__ __forceinline__ void prologue_finish(const QLoads& L, bool ident, flo
     }
   }
   __syncthreads();
-  if (act) prologue_digits<G>(qscale, ls.red, ls.dig, ls.qe, qf_tile);
+  if (act) prologue_digits<G>(qscale, ls.red, ls.dig, ls.qe, qf_tile, qr_tile);
   __syncthreads();
   if (act) prologue_pack<G>(ls.dig, ls.qe, qa_tile, lane_stride, scale_off);
 }
@@ -926,6 +932,24 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
 // while its first slices are in flight, in the ring slots 2-3 that the loop
 // has not reached yet; otherwise the operand comes from qa/qf, written by the
 // prologue (or the fused step's preparation) launch.
+// The decode step's single-token append run in the scan launch (see
+// split_kernel): the new tokens, and where the scan leaves what the merge
+// needs to add them.  n_app == 0: no step.
+struct StepTail {
+  uint8_t* pages;        // the cache, written by the append workgroups
+  const int* start_pos;  // [B] positions of the new tokens
+  const void* k;         // [B][1][Hkv][128]
+  const void* v;
+  int kv_bf16;
+  const float* mu;
+  const float* rot_v;
+  float clip_k, clip_v;
+  float* deq;            // [B][Hkv][kDeqStride]: K, V dequantised (rotated), valid flag
+  float* qr;             // [B][Hkv][4][128] rotated query x sm_scale x log2(e)
+  int n_app;             // append workgroups at the end of the grid
+};
+constexpr int kDeqStride = 2 * kHeadDim + 4;
+
 template <int G, bool kWide, bool kWin, bool kSelfQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
@@ -934,7 +958,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const float4* __restrict__ qf, float* __restrict__ part, int S,
              const uint16_t* __restrict__ wstore, int n_win, const void* __restrict__ q,
              int q_bf16, const float* __restrict__ mu, float qscale, float* __restrict__ wpart,
-             const float* __restrict__ rot_k) {
+             const float* __restrict__ rot_k, StepTail step) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
   // slot s of wave w at ring[s][w]: the slots 2-3 of all four waves are one
@@ -984,8 +1008,43 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   // Within the run the query groups of one split come first, so the KV heads
   // of a sequence start on the same pages together and read neighbouring
   // slices of each block (the ragged group-64 batch of 64: 224-232 -> 214 us).
-  const int n_wg = static_cast<int>(gridDim.x) - n_win;
+  // The decode step's appends (kSelfQ without windows: the scan builds its own
+  // operand and needs no earlier launch) are the last n_app workgroups, one
+  // per (sequence, KV head).  Dispatched after every split, they start as the
+  // first splits finish, and the scan leaves the new tokens' slots out, so
+  // they run in the launch's tail.  A split may read a page while its new
+  // token's bytes change: it masks that slot, and the other codes in the
+  // bytes it shares are rewritten as they were.
+  const int n_app = (kSelfQ && !kWin) ? step.n_app : 0;
+  const int n_wg = static_cast<int>(gridDim.x) - n_win - n_app;
   const int lin = static_cast<int>(blockIdx.x) - n_win;
+  if constexpr (kSelfQ && !kWin) {
+    if (lin >= n_wg) {
+      const int a = lin - n_wg, hb = a / Hkv, ha = a % Hkv;
+      float* scratch = reinterpret_cast<float*>(&ring[0][0][0]);
+      float* dq = step.deq + (static_cast<size_t>(hb) * Hkv + ha) * kDeqStride;
+      const int pos = step.start_pos[hb];
+      if (step.kv_bf16)
+        append_one_256<true>(ha, hb, step.pages, num_blocks, Hkv, G, block_table, max_blocks, pos,
+                             token_row<true>(step.k, hb, ha, Hkv),
+                             token_row<true>(step.v, hb, ha, Hkv), step.mu, rot_k, step.rot_v,
+                             step.clip_k, step.clip_v, scratch, dq);
+      else
+        append_one_256<false>(ha, hb, step.pages, num_blocks, Hkv, G, block_table, max_blocks,
+                              pos, token_row<false>(step.k, hb, ha, Hkv),
+                              token_row<false>(step.v, hb, ha, Hkv), step.mu, rot_k, step.rot_v,
+                              step.clip_k, step.clip_v, scratch, dq);
+      // whether the token was stored (a position outside the table or a
+      // block id outside the cache stores nothing, and the merge skips it)
+      if (threadIdx.x == 0) {
+        const int bi = pos >= 0 && pos / kBlock < max_blocks
+                           ? block_table[static_cast<size_t>(hb) * max_blocks + pos / kBlock]
+                           : -1;
+        dq[2 * kHeadDim] = (bi >= 0 && bi < num_blocks) ? 1.f : 0.f;
+      }
+      return;
+    }
+  }
   const int xcd = lin & 7;
   const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
   const int hy = job % Y;
@@ -1052,6 +1111,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 
   const int ctx = min(max(ctx_in, 0), max_ctx);
   const int hi_tok = win ? body_end(ctx) : ctx;  // tokens scanned: [lo_pages * 16, hi_tok)
+  // with the step's appends in this launch the new token's slot is left out
+  // (the merge adds the token) and the block holding it takes the masked path
+  const int pex = n_app > 0 ? step.start_pos[b] : -1;
   const int n_pages = (hi_tok + kBlock - 1) / kBlock;
   const int ns_b = num_splits(n_pages - lo_pages, spw);
   if (wgs >= ns_b) return;
@@ -1142,7 +1204,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     uint32_t* qa_s = reinterpret_cast<uint32_t*>(free_lds + offsetof(QScratch, red));
     float4* qf_s = reinterpret_cast<float4*>(free_lds + sizeof(QScratch));
     if constexpr (!kEarlyQ) prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qload);
-    prologue_finish<G>(qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s);
+    prologue_finish<G>(qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s,
+                       (n_app > 0 && wgs == 0) ? step.qr + hgi * kHT * kHeadDim : nullptr);
     __syncthreads();  // the operand is packed
     const uint32_t* mine = qa_s + lane * kQaLds;
     qv0 = u32x4{mine[0], mine[1], mine[2], mine[3]};
@@ -1269,8 +1332,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
         } else {
           const int pg = pblk + 2 * s;
           const int pos = pg * kBlock + t;
-          const bool v0 = pos < hi_tok;
-          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok;
+          const bool v0 = pos < hi_tok && pos != pex;
+          const bool v1 = pg + 1 < p_end && pos + kBlock < hi_tok && pos + kBlock != pex;
           lg[2 * s] = v0 ? l0 : -INFINITY;
           lg[2 * s + 1] = v1 ? l1 : -INFINITY;
           // slots past the context hold arbitrary bytes (possibly NaN as fp16):
@@ -1340,7 +1403,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 #pragma unroll
     for (int k = 0; k < 8; ++k) idc[k] = idn[k];
   };
-  const int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
+  int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
+  if (pex >= 0) {
+    const int rel = pex / kBlock - p_begin;  // page of the new token in this range
+    if (rel >= 0 && rel < np && ((rel >> 3) & 3) == wave) nfast = min(nfast, (rel >> 3) >> 2);
+  }
   int bi = 0;
   for (; bi < nfast; ++bi) run_block(Const<bool, true>{}, bi);
   for (; bi < nbw; ++bi) run_block(Const<bool, false>{}, bi);
@@ -1384,10 +1451,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     }
     const int hq = h * Hg + hloc;
     float* dst = part + ((static_cast<size_t>(b) * Hq + hq) * S + wgs) * kPartStride;
-    const float inv = 1.0f / L;
+    // a split whose only token is the step's new one saw nothing
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
     dst[4 + cc] = o0 * inv;
     dst[4 + cc + 64] = o1 * inv;
-    if (cc == 0) dst[0] = M + __log2f(L);
+    if (cc == 0) dst[0] = L > 0.f ? M + __log2f(L) : kNegBig;
   }
 }
 
@@ -1406,15 +1474,24 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // separates the merge from the rotation.
 constexpr int kMergeSplits = 16;  // splits per thread and round (two halves: 32 per round)
 
+// kStep: the decode step's new token of (sequence, KV head), left out by the
+// scan and appended in its launch (one query tile per KV head), joins as one
+// more partial: its logit is the scan's float32 rotated query (qr) against the
+// dequantised new key, its output the dequantised new value (deq).
+template <bool kStep>
 __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ part,
                                                      const int* __restrict__ ctx_len, int max_ctx,
                                                      int Hq, int Hkv, int QG, int spw, int S,
                                                      const float* __restrict__ rot_v,
                                                      float* __restrict__ out,
-                                                     const float* __restrict__ wpart) {
+                                                     const float* __restrict__ wpart,
+                                                     const int* __restrict__ new_pos,
+                                                     const float* __restrict__ deq,
+                                                     const float* __restrict__ qr) {
   __shared__ __attribute__((aligned(16))) float osum[2][kHT][kHeadDim];
   __shared__ float hinv[kHT];  // 1 / (weight sum) per head
   __shared__ float hwin[kHT];  // the window partial's share of each head's output
+  __shared__ float nlog[kHT][2];  // kStep: halves of the new token's logits
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
@@ -1437,6 +1514,16 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   const size_t row0 = static_cast<size_t>(b) * Hq + h * Hg + qg * kHT;
   const float* p = part + (row0 + min(u, nh - 1)) * S * kPartStride;
   const int ctx_in = ctx_len[b];
+  float dk = 0.f, dv = 0.f, dflag = 0.f, qrv = 0.f;
+  int pn = -1;
+  if constexpr (kStep) {
+    const float* dq = deq + (static_cast<size_t>(b) * Hkv + h) * kDeqStride;
+    dk = dq[c];
+    dv = dq[kHeadDim + c];
+    dflag = dq[2 * kHeadDim];
+    qrv = qr[((static_cast<size_t>(b) * Hkv + h) * kHT + u) * kHeadDim + c];
+    pn = new_pos[b];
+  }
   // Loaded before the context length (and so the split count) is known, for
   // the S allocated splits; entries of splits past the count are never used.
   const float lse_l = p[min(lane, S - 1) * kPartStride];
@@ -1451,6 +1538,16 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   load_x(0, xv);
   if (S > 2 * kMergeSplits) load_x(1, xw);  // S: the same in every thread
   const int ctx = min(max(ctx_in, 0), max_ctx);
+  // kStep: head u's new-token logit (log2 units); kNegBig: not attended
+  float lse_n = kNegBig;
+  if constexpr (kStep) {
+    if (half == 0) {
+      const float x = wave_sum(qrv * dk);
+      if (lane == 0) nlog[u][c >> 6] = x;
+    }
+    __syncthreads();
+    if (pn >= 0 && pn < ctx && dflag != 0.f) lse_n = nlog[u][0] + nlog[u][1];
+  }
   // the window partial's lse, and the window output this thread adds
   const float lse_w = wpart ? wpart[(row0 + min(u, nh - 1)) * kPartStride] : kNegBig;
   const float wv = wpart ? wpart[(row0 + min(part8 & 3, nh - 1)) * kPartStride + 4 + j] : 0.f;
@@ -1472,11 +1569,14 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
   M = wave_max(M);
   M = fmaxf(M, lse_w);
+  M = fmaxf(M, lse_n);
   float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
   for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
   W = wave_sum(W);
   const float a_w = exp2_hw(lse_w - M);  // 0 without windows
   W += a_w;
+  const float a_n = (kStep && lse_n > kNegBig) ? exp2_hw(lse_n - M) : 0.f;
+  W += a_n;
 
   // channel c over this half's splits, a round at a time (one round covers
   // 32 splits); a split past the count contributes nothing (its stale values
@@ -1511,6 +1611,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
       if (s < ns) acc = fmaf(exp2_hw(lv[k] - M), xv[k], acc);
     }
   }
+  if (kStep && half == 0 && a_n > 0.f) acc = fmaf(a_n, dv, acc);
   osum[half][u][c] = acc;
   if ((tid & 255) == 0) {
     const float inv = 1.0f / W;
@@ -1699,7 +1800,9 @@ DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages) {
   p.part_off = p.qf_off + align256(hg * kHT * 16);
   p.wpart_off =
       p.part_off + align256(static_cast<size_t>(B) * Hq * (p.S ? p.S : 1) * kPartStride * 4);
-  p.total = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
+  p.deq_off = p.wpart_off + align256(static_cast<size_t>(B) * Hq * kPartStride * 4);
+  p.qr_off = p.deq_off + align256(static_cast<size_t>(B) * Hkv * kDeqStride * 4);
+  p.total = p.qr_off + align256(hg * kHT * kHeadDim * 4);
   return p;
 }
 
@@ -1715,11 +1818,17 @@ bool operand_in_scan(const DecodePlan& p, int Hkv, int B, int stages) {
   return (stages & 3) == 3 && static_cast<int64_t>(p.S) * Hkv * p.QG * B <= 1024;
 }
 
-int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
-                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
-                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
-                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
-                  hipStream_t stream, const uint16_t* win, const float* mu) {
+// The decode launches.  tail (the decode step with the operand built in the
+// scan, one query tile per KV head, no windows): the scan also appends the
+// new tokens in workgroups of its own, leaving their slots out, and the merge
+// adds them.
+static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                              const int* block_table, int max_blocks, const int* ctx_len,
+                              int max_ctx, int B, int Hq, const void* q, bool q_bf16,
+                              const float* rot_k, const float* rot_v, float sm_scale, float* out,
+                              void* workspace, const DecodePlan& p, int stages,
+                              hipStream_t stream, const uint16_t* win, const float* mu,
+                              const StepTail* tail) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);
@@ -1739,15 +1848,22 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
       G == 2 ? go(prologue_kernel<false, 2>) : go(prologue_kernel<false, 1>);
   }
   const int n_win = win ? B * Hkv * p.QG : 0;
+  StepTail st{};
+  if (tail) {
+    st = *tail;
+    st.deq = reinterpret_cast<float*>(ws + p.deq_off);
+    st.qr = reinterpret_cast<float*>(ws + p.qr_off);
+    st.n_app = B * Hkv;
+  }
   if ((p.S > 0 || win) && (stages & 2)) {
-    const dim3 g2(n_win + p.S * Hkv * p.QG * B);
+    const dim3 g2(n_win + p.S * Hkv * p.QG * B + st.n_app);
     // one buffer descriptor spans the cache when its byte size fits 32 bits
     const bool wide = static_cast<uint64_t>(num_blocks) * Hkv * page_bytes_for_groups(G) >
                       0xFFFFFFFFull;
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
                          max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S, win,
-                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k);
+                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, st);
     };
     auto pick = [&](auto g, auto wd) {
       constexpr int GG = decltype(g)::value;
@@ -1763,16 +1879,30 @@ int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
     G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
   // fewer than 64 query tiles without windows: a workgroup per query head
-  const bool per_head = !win && static_cast<int64_t>(B) * Hkv * p.QG < 64;
+  const bool per_head = !win && !tail && static_cast<int64_t>(B) * Hkv * p.QG < 64;
   if ((stages & 4) && per_head) {
     hipLaunchKernelGGL(merge_head_kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len,
                        max_ctx, Hq, Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
   } else if (stages & 4) {
-    hipLaunchKernelGGL(merge_kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
-                       max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
-                       static_cast<const float*>(wpart));
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
+                         max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
+                         static_cast<const float*>(wpart), st.start_pos,
+                         static_cast<const float*>(st.deq), static_cast<const float*>(st.qr));
+    };
+    tail ? go(merge_kernel<true>) : go(merge_kernel<false>);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_decode(const uint8_t* pages, int64_t num_blocks, int Hkv, int G,
+                  const int* block_table, int max_blocks, const int* ctx_len, int max_ctx, int B,
+                  int Hq, const void* q, bool q_bf16, const float* rot_k, const float* rot_v,
+                  float sm_scale, float* out, void* workspace, const DecodePlan& p, int stages,
+                  hipStream_t stream, const uint16_t* win, const float* mu) {
+  return launch_decode_impl(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len, max_ctx,
+                            B, Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace, p, stages,
+                            stream, win, mu, nullptr);
 }
 
 int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
@@ -1782,6 +1912,17 @@ int launch_append_decode(uint8_t* pages, int64_t num_blocks, int Hkv, int G,
                          int Hq, const void* q, bool q_bf16, const float* rot_k,
                          const float* rot_v, float sm_scale, float* out, void* workspace,
                          const DecodePlan& p, hipStream_t stream, uint16_t* win) {
+  // Two launches when the scan builds its own query operand (one round of
+  // workgroups), with one query tile per KV head and no windows: the appends
+  // run in the scan's launch (its tail) and the merge adds the new tokens.
+  // Otherwise three: the append and the query rotation share the first.
+  if (!win && p.QG == 1 && p.S > 0 && operand_in_scan(p, Hkv, B, 7)) {
+    const StepTail tail{pages, start_pos, k, v, kv_bf16 ? 1 : 0, mu, rot_v, clip_k, clip_v,
+                        nullptr, nullptr, 0};
+    return launch_decode_impl(pages, num_blocks, Hkv, G, block_table, max_blocks, ctx_len,
+                              max_ctx, B, Hq, q, q_bf16, rot_k, rot_v, sm_scale, out, workspace,
+                              p, 7, stream, nullptr, mu, &tail);
+  }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* qa = reinterpret_cast<uint32_t*>(ws + p.qa_off);
   float4* qf = reinterpret_cast<float4*>(ws + p.qf_off);

@@ -17,7 +17,7 @@ struct DecodePlan {
   int QG;    // query-head tiles of 4 per KV head
   int spw;   // pages per workgroup split
   int S;     // splits for the longest context
-  size_t qa_off, qf_off, part_off, wpart_off, total;
+  size_t qa_off, qf_off, part_off, wpart_off, deq_off, qr_off, total;
 };
 
 DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages);

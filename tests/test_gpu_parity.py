@@ -367,9 +367,10 @@ STEP_CASES = {
 
 @pytest.mark.parametrize("name", list(STEP_CASES))
 def test_append_decode_step(name):
-    """kvq_append_decode writes the cache kvq_append writes and leaves the
-    output kvq_decode_attn leaves after kvq_append, bit for bit (the query
-    operand from the shared first launch rounds as the scan's own); it
+    """kvq_append_decode writes the cache kvq_append writes, bit for bit, and
+    its output equals kvq_decode_attn's after kvq_append to float32 rounding
+    (where the step appends in the scan's launch, the merge scores the new
+    token in float32 instead of through the scan's digit products); it
     matches the oracle on the cache it wrote."""
     import rotated_int2_kv_kvq_amd as kvq
     w = STEP_CASES[name]
@@ -398,7 +399,8 @@ def test_append_decode_step(name):
                                   b.rk, b.rv, w.group, w.clip_k, w.clip_v, b.sm_scale)
         torch.cuda.synchronize()
         assert torch.equal(a.pages, b.pages), step
-        assert torch.equal(out_a, out_b), step
+        diff = attention_error(out_b.cpu().numpy(), out_a.cpu().numpy())
+        assert diff <= 2e-5, (step, diff)
     for s in range(w.batch):
         b.written[s] = int(ctx[s])
     pairs = [(s, hq) for s in range(w.batch) for hq in (0, 9, 31)]
