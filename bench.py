@@ -62,10 +62,10 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, kernel: str, workgroups: int):
     """HBM bytes per scan launch from the committed counter summary, or None if
-    it was taken on another workload or kernel, or the kernel's sources changed
-    since."""
+    it was taken on another workload, kernel or grid, or the kernel's sources
+    changed since."""
     from rotated_int2_kv_kvq_amd.traffic import kernel_source_hash
     try:
         with open(TRAFFIC_FILE) as f:
@@ -73,6 +73,7 @@ def measured_traffic(workload: str, kernel: str):
     except (OSError, ValueError):
         return None
     if (rec.get("workload") != workload or rec.get("kernel") != kernel
+            or rec.get("workgroups") != workgroups
             or rec.get("source_sha256") != kernel_source_hash()):
         return None
     return round(float(rec["traffic_bytes"]))
@@ -239,6 +240,7 @@ def main():
     scan_stages = (kvq.STAGE_PREPARE | kvq.STAGE_SPLITS if plan["operand_in_scan"]
                    else kvq.STAGE_SPLITS)
     scan_kernel = scan_kernel_name(w.group, plan["operand_in_scan"])
+    scan_wgs = plan["num_splits"] * Hkv * ((Hq // Hkv + 3) // 4) * B
     wss = [ws] + [torch.empty_like(ws) for _ in range(L - 1)]
     split_ms, app_ms = [], []
     for rep in range(4):
@@ -469,8 +471,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w0.name, scan_kernel),
+            "traffic": measured_traffic(w0.name, scan_kernel, scan_wgs),
             "algorithmic_bytes": split_bytes,
+            "workgroups": scan_wgs,
         },
         "cpu_baseline": cpu,
         "bits_per_element": bits_per_element(w.group),

@@ -36,23 +36,33 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def _per_dispatch(path: str, counter: str, name_part: str) -> list[float]:
+def _per_dispatch(path: str, counter: str, name_part: str, grid_threads: int = 0) -> list[float]:
+    """The counter's value per dispatch of kernels whose name contains
+    name_part (and, if grid_threads, whose grid has that many threads)."""
     vals = []
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
-            if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
-                vals.append(float(row["Counter_Value"]))
+            if row["Counter_Name"] != counter or name_part not in row["Kernel_Name"]:
+                continue
+            if grid_threads:
+                g = row.get("Grid_Size", row.get("Grid_Size_X"))
+                if g is None or int(g) != grid_threads:
+                    continue
+            vals.append(float(row["Counter_Value"]))
     if not vals:
-        raise SystemExit(f"{path}: no {counter} rows for kernels matching {name_part!r}")
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {name_part!r}"
+                         + (f" with {grid_threads} threads" if grid_threads else ""))
     return vals
 
 
 def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes: float,
-              kernel: str) -> dict:
+              kernel: str, workgroups: int = 0) -> dict:
     """kernel: the scan kernel's name as rocprofv3 prints it (bench.py's
-    roofline.kernel), e.g. split_kernel<1, false, false, true>."""
-    sf = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
-    sw = _per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    roofline.kernel), e.g. split_kernel<1, false, false, true>; workgroups:
+    the timed launch's workgroup count (256 threads each), which keeps
+    launches of the same kernel on other grids out of the mean (0: all)."""
+    sf = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel, 256 * workgroups)
+    sw = _per_dispatch(write_csv, "WRITE_SIZE", kernel, 256 * workgroups)
     cf = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL)
     cw = _per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL)
     mean = lambda v: sum(v) / len(v)  # noqa: E731
@@ -62,6 +72,7 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes
     write = mean(sw) * 1024.0 * k_write
     return {
         "kernel": kernel,
+        "workgroups": workgroups or None,
         "source_sha256": kernel_source_hash(),
         "dispatches": {"fetch": len(sf), "write": len(sw), "copy_fetch": len(cf),
                        "copy_write": len(cw)},
@@ -100,7 +111,8 @@ def main():
         raise SystemExit(f"{a.bench_json}: no bench JSON line")
     res = summarize(a.fetch_csv, a.write_csv, a.copy_bytes,
                     float(line["roofline"]["algorithmic_bytes"]),
-                    line["roofline"]["kernel"].split(" (")[0])
+                    line["roofline"]["kernel"].split(" (")[0],
+                    int(line["roofline"].get("workgroups") or 0))
     res["workload"] = line["config"]["workload"]
     res["command"] = a.command
     with open(a.out, "w") as f:

@@ -54,3 +54,36 @@ def test_bits_and_context_fields():
     assert tb["bits_per_element"] == 2.25 and tb["prefill_overhead_pct"] == {"x": 1.0}
     # 16,064 body tokens at 2.25 bits and 320 window tokens at 16 bits over 16,384
     assert abs(tb["bits_per_element_with_bf16_windows"] - (16064 * 2.25 + 320 * 16) / 16384) < 1e-4
+
+
+def test_traffic_summary_filters_kernel_and_grid(tmp_path):
+    """The counter summary averages only the named kernel's dispatches on the
+    timed grid, and scales each counter by the copy kernel's known bytes."""
+    from rotated_int2_kv_kvq_amd import traffic
+
+    def write(path, counter, rows):
+        with open(path, "w") as f:
+            f.write("Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+            for name, grid, val in rows:
+                f.write(f'"{name}",{grid},{counter},{val}\n')
+
+    scan = "void kvq::split_kernel<1, false, false, true>(int)"
+    other = "void kvq::split_kernel<1, false, false, false>(int)"
+    copy = "void at::native::neg_kernel(int)"
+    fetch, write_ = tmp_path / "f.csv", tmp_path / "w.csv"
+    # copy of 2048 bytes: FETCH reads 1 KiB (factor 2), WRITE 2 KiB (factor 1)
+    write(fetch, "FETCH_SIZE", [(copy, 4096, 1.0), (scan, 1024 * 256, 10.0),
+                                (scan, 1024 * 256, 14.0), (scan, 1152 * 256, 99.0),
+                                (other, 1024 * 256, 99.0)])
+    write(write_, "WRITE_SIZE", [(copy, 4096, 2.0), (scan, 1024 * 256, 3.0),
+                                 (scan, 1152 * 256, 99.0)])
+    res = traffic.summarize(str(fetch), str(write_), 2048, 1000.0,
+                            "split_kernel<1, false, false, true>", 1024)
+    assert res["dispatches"]["fetch"] == 2 and res["dispatches"]["write"] == 1
+    assert res["fetch_bytes"] == 12.0 * 1024 * 2
+    assert res["write_bytes"] == 3.0 * 1024
+    assert res["traffic_over_algorithmic"] == (12.0 * 2048 + 3.0 * 1024) / 1000.0
+    # no grid given: every dispatch of the kernel
+    res_all = traffic.summarize(str(fetch), str(write_), 2048, 1000.0,
+                                "split_kernel<1, false, false, true>")
+    assert res_all["dispatches"]["fetch"] == 3
