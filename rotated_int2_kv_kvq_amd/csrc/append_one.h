@@ -191,7 +191,9 @@ __device__ __forceinline__ void append_one_body(
 
 // 256 threads (a thread per rotated channel, the quarters in turn, the next
 // quarter's column loads in flight while one is summed); the token goes to
-// position pos.  scratch: 264 floats of LDS that the caller lends (the
+// position pos.  Threads 256 and up of a larger workgroup repeat the first
+// 256's loads and arithmetic (the same values to the same LDS words) and
+// store nothing.  scratch: 264 floats of LDS that the caller lends (the
 // token's inputs and the group reduction).  deq as for append_one_store.
 template <bool kBf16>
 __device__ __forceinline__ void append_one_256(
@@ -201,7 +203,7 @@ __device__ __forceinline__ void append_one_256(
     const float* __restrict__ rot_v, float clip_k, float clip_v, float* scratch,
     float* __restrict__ deq) {
   const int tid = threadIdx.x;
-  const int mat = tid >> 7, j = tid & 127;
+  const int mat = (tid >> 7) & 1, j = tid & 127;
   float* a_s = scratch;                 // [2][128]
   float* red = scratch + 2 * kHeadDim;  // [8]
   OneDst D;

@@ -950,8 +950,19 @@ struct StepTail {
 };
 constexpr int kDeqStride = 2 * kHeadDim + 4;
 
+// Waves per split workgroup.  A workgroup that builds its query operand
+// itself (group 128, no windows) takes two consecutive splits of its query
+// tile, four waves each, and builds the operand once for both: half the
+// workgroups load R_K (64 KB each, the largest read of the operand; every
+// workgroup of a CU loads it at the same moment, ahead of its cache slices).
+// Otherwise a workgroup is one split.
+__host__ __device__ constexpr int split_waves(int G, bool win, bool self_q) {
+  return (self_q && !win && G == 1) ? 8 : 4;
+}
+
 template <int G, bool kWide, bool kWin, bool kSelfQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
+__global__ __launch_bounds__(64 * split_waves(G, kWin, kSelfQ))
+__attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
 split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const int* __restrict__ block_table, int max_blocks, const int* __restrict__ ctx_len,
              int max_ctx, int Hq, int QG, int spw, const uint32_t* __restrict__ qa,
@@ -961,15 +972,18 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const float* __restrict__ rot_k, StepTail step) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
-  // slot s of wave w at ring[s][w]: the slots 2-3 of all four waves are one
+  constexpr int kW = split_waves(G, kWin, kSelfQ);  // waves
+  constexpr int kPair = kW / 4;                     // splits
+  // slot s of wave w at ring[s][w]: the slots 2-3 of all the waves are one
   // contiguous region, free from the start until the first block's loop
-  constexpr int kSlotStride = 4 * kSlot;
+  constexpr int kSlotStride = kW * kSlot;
   static_assert(kPTile <= kSlot, "the P tile must fit in a ring slot");
   static_assert(kRing == 4 && kDepth == 3, "slots are the slices of a block; three in flight");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kSlot];
-  __shared__ __attribute__((aligned(16))) int wids[kMaxSplitPages];  // block ids of the pages
-  __shared__ int pexp[4][kHT];  // per-head digit exponents of the P tile
-  __shared__ float cm[4][kHT], cl[4][kHT];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kW][kSlot];
+  // block ids of each split's pages
+  __shared__ __attribute__((aligned(16))) int wids[kPair][kMaxSplitPages];
+  __shared__ int pexp[kW][kHT];  // per-head digit exponents of the P tile
+  __shared__ float cm[kW][kHT], cl[kW][kHT];
   const int Y = Hkv * QG;
 
   if (kWin && static_cast<int>(blockIdx.x) < n_win) {  // a window workgroup
@@ -1048,12 +1062,18 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int xcd = lin & 7;
   const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
   const int hy = job % Y;
-  const int wgs = (job / Y) % S;
-  const int b = job / (S * Y);
+  const int SP = (S + kPair - 1) / kPair;  // workgroups per query tile
+  const int wgp = (job / Y) % SP;
+  const int b = job / (SP * Y);
   const int h = hy / QG;
   const int qg = hy % QG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // this wave's split of the workgroup, and its place among the split's four
+  const int half = kPair > 1 ? wave >> 2 : 0;
+  const int lw = kPair > 1 ? wave & 3 : wave;
+  const int ht = kPair > 1 ? threadIdx.x & 255 : threadIdx.x;
+  const int wgs = kPair * wgp + half;  // the split (may be past the last one)
   // with BF16 windows the body starts after the sinks (a whole number of pages)
   constexpr bool win = kWin;
   const int lo_pages = win ? kSink / kBlock : 0;
@@ -1072,12 +1092,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   auto clamp_id = [&](int id) {
     return static_cast<int>(min(static_cast<uint32_t>(id), static_cast<uint32_t>(max_block)));
   };
-  const int id_lane = row[min(p_begin + 8 * wave + (lane & 7), max_blocks - 1)];
-  static_assert(kMaxSplitPages == 3 * 256, "three table entries per thread");
+  const int id_lane = row[min(p_begin + 8 * lw + (lane & 7), max_blocks - 1)];
+  static_assert(kMaxSplitPages == 3 * 256, "three table entries per thread of a split");
   int idv[3];
 #pragma unroll
-  for (int k = 0; k < 3; ++k)
-    idv[k] = row[min(p_begin + static_cast<int>(threadIdx.x) + 256 * k, max_blocks - 1)];
+  for (int k = 0; k < 3; ++k) idv[k] = row[min(p_begin + ht + 256 * k, max_blocks - 1)];
 
   // The query operand is loaded next, and the ring's first slices are issued
   // once the context length is known; the operand is then waited for on each
@@ -1116,15 +1135,18 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int pex = n_app > 0 ? step.start_pos[b] : -1;
   const int n_pages = (hi_tok + kBlock - 1) / kBlock;
   const int ns_b = num_splits(n_pages - lo_pages, spw);
-  if (wgs >= ns_b) return;
-  if (p_begin >= n_pages) return;
-  const int p_end = (wgs == ns_b - 1) ? n_pages : p_begin + spw;
+  // a split past the tile's count, or starting past the context, has no pages
+  // (the splits of a workgroup are consecutive: if its first has none, neither
+  // has the second)
+  if (kPair * wgp >= ns_b || lo_pages + kPair * wgp * spw >= n_pages) return;
+  const bool has = kPair == 1 || (wgs < ns_b && p_begin < n_pages);
+  const int p_end = !has ? p_begin : (wgs == ns_b - 1) ? n_pages : p_begin + spw;
   const int np = p_end - p_begin;  // at most kMaxSplitPages - 1 (split_pages <= 512)
-  // 8-page blocks of this range; this wave's are wave, wave + 4, ...  Only the
+  // 8-page blocks of this range; this wave's are lw, lw + 4, ...  Only the
   // range's last block can be short; its slices past the range are skipped.
   const int nblk = (np + 7) >> 3;
-  const int nbw = wave < nblk ? (nblk - wave + 3) >> 2 : 0;
-  const bool owns_last = nbw > 0 && ((nblk - 1 - wave) & 3) == 0;
+  const int nbw = lw < nblk ? (nblk - lw + 3) >> 2 : 0;
+  const bool owns_last = nbw > 0 && ((nblk - 1 - lw) & 3) == 0;
   const int ns_last = owns_last ? min(4, (np - 8 * (nblk - 1) + 1) >> 1) : 4;
   const int nsl = nbw > 0 ? 4 * (nbw - 1) + ns_last : 0;
   // the table, padded with block 0 to whole 8-page blocks (padding pages are
@@ -1137,8 +1159,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   auto fill_table = [&]() {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      const int lp = threadIdx.x + 256 * k;
-      if (lp < np8) wids[lp] = lp < np ? clamp_id(idv[k]) : 0;
+      const int lp = ht + 256 * k;
+      if (lp < np8) wids[half][lp] = lp < np ? clamp_id(idv[k]) : 0;
     }
   };
 
@@ -1163,8 +1185,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
                       static_cast<uint32_t>(b1) * pstride + hoff, slot, off16, off4, lo_lane);
   };
   // LDS address of the ids of this wave's block m (the same in every lane)
-  const uint32_t ids_base = lds_addr(reinterpret_cast<const uint8_t*>(&wids[0]));
-  auto ids_addr = [&](int m) { return ids_base + 32u * static_cast<uint32_t>(wave + 4 * m); };
+  const uint32_t ids_base = lds_addr(reinterpret_cast<const uint8_t*>(&wids[half][0]));
+  auto ids_addr = [&](int m) { return ids_base + 32u * static_cast<uint32_t>(lw + 4 * m); };
 
   // The operand passes through an empty asm on each path: the compiler waits
   // for it there, and afterwards sees it as defined by the asm, not by a
@@ -1205,7 +1227,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     float4* qf_s = reinterpret_cast<float4*>(free_lds + sizeof(QScratch));
     if constexpr (!kEarlyQ) prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qload);
     prologue_finish<G>(qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s,
-                       (n_app > 0 && wgs == 0) ? step.qr + hgi * kHT * kHeadDim : nullptr);
+                       (n_app > 0 && wgp == 0) ? step.qr + hgi * kHT * kHeadDim : nullptr);
     __syncthreads();  // the operand is packed
     const uint32_t* mine = qa_s + lane * kQaLds;
     qv0 = u32x4{mine[0], mine[1], mine[2], mine[3]};
@@ -1256,7 +1278,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   // no per-slice conditions.
   auto run_block = [&](auto fast, int bi) {
     constexpr bool kFast = decltype(fast)::value;
-    const int pblk = p_begin + 8 * (wave + 4 * bi);
+    const int pblk = p_begin + 8 * (lw + 4 * bi);
     float lg[8];
     uint2 szv[8];
     auto slice = [&](auto sc) {
@@ -1406,7 +1428,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   int nfast = nsl >= 4 + kDepth ? (nsl - 4 - kDepth) / 4 + 1 : 0;
   if (pex >= 0) {
     const int rel = pex / kBlock - p_begin;  // page of the new token in this range
-    if (rel >= 0 && rel < np && ((rel >> 3) & 3) == wave) nfast = min(nfast, (rel >> 3) >> 2);
+    if (rel >= 0 && rel < np && ((rel >> 3) & 3) == lw) nfast = min(nfast, (rel >> 3) >> 2);
   }
   int bi = 0;
   for (; bi < nfast; ++bi) run_block(Const<bool, true>{}, bi);
@@ -1431,23 +1453,25 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   }
   __syncthreads();
 
-  // ---- combine the 4 waves: thread -> (head tid/64, channels c, c + 64)
-  const int ch = threadIdx.x >> 6;
+  // ---- combine each split's 4 waves: thread -> (split tid/256, head
+  // (tid/64)%4, channels c, c + 64)
+  const int ch = (threadIdx.x >> 6) & 3;
   const int cc = threadIdx.x & 63;
+  const int w0 = 4 * half;
   const int hloc = qg * kHT + ch;
   const int Hg = Hq / Hkv;
   const int nh = min(kHT, Hg - qg * kHT);
-  if (ch < nh) {
+  if (has && ch < nh) {
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w][ch]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w0 + w][ch]);
     float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float a = exp2_hw(cm[w][ch] - M);  // 0 for a wave that saw no token
-      L += a * cl[w][ch];
-      o0 += a * co[w][ch][cc];
-      o1 += a * co[w][ch][cc + 64];
+      const float a = exp2_hw(cm[w0 + w][ch] - M);  // 0 for a wave that saw no token
+      L += a * cl[w0 + w][ch];
+      o0 += a * co[w0 + w][ch][cc];
+      o1 += a * co[w0 + w][ch][cc + 64];
     }
     const int hq = h * Hg + hloc;
     float* dst = part + ((static_cast<size_t>(b) * Hq + hq) * S + wgs) * kPartStride;
@@ -1856,14 +1880,16 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
     st.n_app = B * Hkv;
   }
   if ((p.S > 0 || win) && (stages & 2)) {
-    const dim3 g2(n_win + p.S * Hkv * p.QG * B + st.n_app);
+    const int nw = split_waves(G, win != nullptr, self_q);
+    const int sp = (p.S + nw / 4 - 1) / (nw / 4);  // split workgroups per query tile
+    const dim3 g2(n_win + sp * Hkv * p.QG * B + st.n_app);
     // one buffer descriptor spans the cache when its byte size fits 32 bits
     const bool wide = static_cast<uint64_t>(num_blocks) * Hkv * page_bytes_for_groups(G) >
                       0xFFFFFFFFull;
     auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, g2, dim3(256), 0, stream, pages, num_blocks, Hkv, block_table,
-                         max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part, p.S, win,
-                         n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, st);
+      hipLaunchKernelGGL(kernel, g2, dim3(64 * nw), 0, stream, pages, num_blocks, Hkv,
+                         block_table, max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part,
+                         p.S, win, n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, st);
     };
     auto pick = [&](auto g, auto wd) {
       constexpr int GG = decltype(g)::value;
