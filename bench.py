@@ -62,7 +62,7 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
 
-def measured_traffic(workload: str, kernel: str, workgroups: int):
+def measured_traffic(workload: str, kernel: str, grid_threads: int):
     """HBM bytes per scan launch from the committed counter summary, or None if
     it was taken on another workload, kernel or grid, or the kernel's sources
     changed since."""
@@ -73,7 +73,7 @@ def measured_traffic(workload: str, kernel: str, workgroups: int):
     except (OSError, ValueError):
         return None
     if (rec.get("workload") != workload or rec.get("kernel") != kernel
-            or rec.get("workgroups") != workgroups
+            or rec.get("grid_threads") != grid_threads
             or rec.get("source_sha256") != kernel_source_hash()):
         return None
     return round(float(rec["traffic_bytes"]))
@@ -240,7 +240,12 @@ def main():
     scan_stages = (kvq.STAGE_PREPARE | kvq.STAGE_SPLITS if plan["operand_in_scan"]
                    else kvq.STAGE_SPLITS)
     scan_kernel = scan_kernel_name(w.group, plan["operand_in_scan"])
-    scan_wgs = plan["num_splits"] * Hkv * ((Hq // Hkv + 3) // 4) * B
+    # threads of the timed launch: a 256-thread workgroup per split, or, where
+    # the scan builds its own operand at group 128, 512 threads per pair of
+    # consecutive splits
+    S = plan["num_splits"]
+    pairs = plan["operand_in_scan"] and w.group == 128
+    scan_threads = 256 * (2 * ((S + 1) // 2) if pairs else S) * Hkv * ((Hq // Hkv + 3) // 4) * B
     wss = [ws] + [torch.empty_like(ws) for _ in range(L - 1)]
     split_ms, app_ms = [], []
     for rep in range(4):
@@ -471,9 +476,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w0.name, scan_kernel, scan_wgs),
+            "traffic": measured_traffic(w0.name, scan_kernel, scan_threads),
             "algorithmic_bytes": split_bytes,
-            "workgroups": scan_wgs,
+            "grid_threads": scan_threads,
         },
         "cpu_baseline": cpu,
         "bits_per_element": bits_per_element(w.group),

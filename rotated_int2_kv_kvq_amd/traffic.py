@@ -24,7 +24,8 @@ import json
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/decode.hip", "csrc/kvq_common.h", "csrc/kvq_launch.h")
+KERNEL_SOURCES = ("csrc/decode.hip", "csrc/append_one.h", "csrc/kvq_common.h",
+                  "csrc/kvq_launch.h")
 COPY_KERNEL = "neg_kernel"
 
 
@@ -56,13 +57,13 @@ def _per_dispatch(path: str, counter: str, name_part: str, grid_threads: int = 0
 
 
 def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes: float,
-              kernel: str, workgroups: int = 0) -> dict:
+              kernel: str, grid_threads: int = 0) -> dict:
     """kernel: the scan kernel's name as rocprofv3 prints it (bench.py's
-    roofline.kernel), e.g. split_kernel<1, false, false, true>; workgroups:
-    the timed launch's workgroup count (256 threads each), which keeps
-    launches of the same kernel on other grids out of the mean (0: all)."""
-    sf = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel, 256 * workgroups)
-    sw = _per_dispatch(write_csv, "WRITE_SIZE", kernel, 256 * workgroups)
+    roofline.kernel), e.g. split_kernel<1, false, false, true>; grid_threads:
+    the timed launch's grid size in threads, which keeps launches of the same
+    kernel on other grids out of the mean (0: all)."""
+    sf = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel, grid_threads)
+    sw = _per_dispatch(write_csv, "WRITE_SIZE", kernel, grid_threads)
     cf = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL)
     cw = _per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL)
     mean = lambda v: sum(v) / len(v)  # noqa: E731
@@ -72,7 +73,7 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int, algorithmic_bytes
     write = mean(sw) * 1024.0 * k_write
     return {
         "kernel": kernel,
-        "workgroups": workgroups or None,
+        "grid_threads": grid_threads or None,
         "source_sha256": kernel_source_hash(),
         "dispatches": {"fetch": len(sf), "write": len(sw), "copy_fetch": len(cf),
                        "copy_write": len(cw)},
@@ -112,7 +113,7 @@ def main():
     res = summarize(a.fetch_csv, a.write_csv, a.copy_bytes,
                     float(line["roofline"]["algorithmic_bytes"]),
                     line["roofline"]["kernel"].split(" (")[0],
-                    int(line["roofline"].get("workgroups") or 0))
+                    int(line["roofline"].get("grid_threads") or 0))
     res["workload"] = line["config"]["workload"]
     res["command"] = a.command
     with open(a.out, "w") as f:

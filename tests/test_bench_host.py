@@ -78,7 +78,7 @@ def test_traffic_summary_filters_kernel_and_grid(tmp_path):
     write(write_, "WRITE_SIZE", [(copy, 4096, 2.0), (scan, 1024 * 256, 3.0),
                                  (scan, 1152 * 256, 99.0)])
     res = traffic.summarize(str(fetch), str(write_), 2048, 1000.0,
-                            "split_kernel<1, false, false, true>", 1024)
+                            "split_kernel<1, false, false, true>", 1024 * 256)
     assert res["dispatches"]["fetch"] == 2 and res["dispatches"]["write"] == 1
     assert res["fetch_bytes"] == 12.0 * 1024 * 2
     assert res["write_bytes"] == 3.0 * 1024
