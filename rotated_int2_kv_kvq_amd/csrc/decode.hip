@@ -1488,21 +1488,28 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // Latency-bound, so every load is issued before the first one is used:
 //   - thread (j = tid/8, part = tid%8) loads its sixteen entries of row j of
 //     R_V for the rotation;
-//   - thread (head u = tid/256, half = (tid/128)%2, channel c = tid%128) loads
-//     channel c of splits half, half + 2, ... (kMergeSplits of them per round;
-//     the first two rounds at once), and lane l of each wave the lse of split
-//     l, which the wave's other lanes read from it (splits past 64 load their
-//     lse with the round).
+//   - thread (head u = tid/256, half = lane/32, channel c = 32 ((tid/64)%4) +
+//     lane%32) loads channel c of splits half, half + 2, ... (kMS of them
+//     per round, below; the first two rounds at once), and lane l of each
+//     wave the lse of split l.
 // Each wave of head u then reduces the head's maximum lse and weight sum over
-// the splits itself, so one barrier (the per-half channel sums into LDS)
-// separates the merge from the rotation.
-constexpr int kMergeSplits = 16;  // splits per thread and round (two halves: 32 per round)
+// the splits itself; lane l's term of the sum, the weight of split l, is what
+// the wave's other lanes read from it for that split (one exponential per
+// lane, not one per split).  The two halves of a channel meet by a lane swap,
+// so one barrier (the channel sums into LDS) separates the merge from the
+// rotation.
+// kMS: splits per thread and round (two halves: 2 kMS per round): 16, or 4
+// where a tile has at most 8 splits, so that a thread issues no loads that
+// only repeat the last split's (the loads are unconditional, the split index
+// clamped).  The sums are the same either way (each half's splits in order).
+constexpr int kMergeSplits = 16;
 
 // kStep: the decode step's new token of (sequence, KV head), left out by the
 // scan and appended in its launch (one query tile per KV head), joins as one
 // more partial: its logit is the scan's float32 rotated query (qr) against the
-// dequantised new key, its output the dequantised new value (deq).
-template <bool kStep>
+// dequantised new key (each wave forms it: channels lane and lane + 64, two
+// wave sums), its output the dequantised new value (deq).
+template <bool kStep, int kMS>
 __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ part,
                                                      const int* __restrict__ ctx_len, int max_ctx,
                                                      int Hq, int Hkv, int QG, int spw, int S,
@@ -1512,10 +1519,9 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
                                                      const int* __restrict__ new_pos,
                                                      const float* __restrict__ deq,
                                                      const float* __restrict__ qr) {
-  __shared__ __attribute__((aligned(16))) float osum[2][kHT][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float osum[kHT][kHeadDim];  // both halves
   __shared__ float hinv[kHT];  // 1 / (weight sum) per head
   __shared__ float hwin[kHT];  // the window partial's share of each head's output
-  __shared__ float nlog[kHT][2];  // kStep: halves of the new token's logits
   const int h = blockIdx.x / QG;
   const int qg = blockIdx.x % QG;
   const int b = blockIdx.y;
@@ -1534,43 +1540,44 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) rr[i4] = R[8 * i4];
   }
-  const int u = tid >> 8, half = (tid >> 7) & 1, c = tid & 127, lane = tid & 63;
+  const int u = tid >> 8, lane = tid & 63, half = lane >> 5;
+  const int c = 32 * ((tid >> 6) & 3) + (lane & 31);
   const size_t row0 = static_cast<size_t>(b) * Hq + h * Hg + qg * kHT;
   const float* p = part + (row0 + min(u, nh - 1)) * S * kPartStride;
   const int ctx_in = ctx_len[b];
-  float dk = 0.f, dv = 0.f, dflag = 0.f, qrv = 0.f;
+  float dk0 = 0.f, dk1 = 0.f, q0 = 0.f, q1 = 0.f, dv = 0.f, dflag = 0.f;
   int pn = -1;
   if constexpr (kStep) {
     const float* dq = deq + (static_cast<size_t>(b) * Hkv + h) * kDeqStride;
-    dk = dq[c];
+    const float* qq = qr + ((static_cast<size_t>(b) * Hkv + h) * kHT + u) * kHeadDim;
+    dk0 = dq[lane];
+    dk1 = dq[lane + 64];
+    q0 = qq[lane];
+    q1 = qq[lane + 64];
     dv = dq[kHeadDim + c];
     dflag = dq[2 * kHeadDim];
-    qrv = qr[((static_cast<size_t>(b) * Hkv + h) * kHT + u) * kHeadDim + c];
     pn = new_pos[b];
   }
   // Loaded before the context length (and so the split count) is known, for
   // the S allocated splits; entries of splits past the count are never used.
   const float lse_l = p[min(lane, S - 1) * kPartStride];
-  float xv[kMergeSplits], xw[kMergeSplits], lv[kMergeSplits];
+  float xv[kMS], xw[kMS], lv[kMS];
   // unconditional loads with the split index clamped (a guarded load becomes a
   // branch whose result copy waits for it, serialising the round)
-  auto load_x = [&](int r, float(&x)[kMergeSplits]) {
+  auto load_x = [&](int r, float(&x)[kMS]) {
 #pragma unroll
-    for (int k = 0; k < kMergeSplits; ++k)
-      x[k] = p[min(2 * (kMergeSplits * r + k) + half, S - 1) * kPartStride + 4 + c];
+    for (int k = 0; k < kMS; ++k)
+      x[k] = p[min(2 * (kMS * r + k) + half, S - 1) * kPartStride + 4 + c];
   };
   load_x(0, xv);
-  if (S > 2 * kMergeSplits) load_x(1, xw);  // S: the same in every thread
+  if (S > 2 * kMS) load_x(1, xw);  // S: the same in every thread
   const int ctx = min(max(ctx_in, 0), max_ctx);
   // kStep: head u's new-token logit (log2 units); kNegBig: not attended
   float lse_n = kNegBig;
   if constexpr (kStep) {
-    if (half == 0) {
-      const float x = wave_sum(qrv * dk);
-      if (lane == 0) nlog[u][c >> 6] = x;
-    }
-    __syncthreads();
-    if (pn >= 0 && pn < ctx && dflag != 0.f) lse_n = nlog[u][0] + nlog[u][1];
+    const float x0 = wave_sum(q0 * dk0);
+    const float x1 = wave_sum(q1 * dk1);
+    if (pn >= 0 && pn < ctx && dflag != 0.f) lse_n = x0 + x1;
   }
   // the window partial's lse, and the window output this thread adds
   const float lse_w = wpart ? wpart[(row0 + min(u, nh - 1)) * kPartStride] : kNegBig;
@@ -1594,7 +1601,8 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   M = wave_max(M);
   M = fmaxf(M, lse_w);
   M = fmaxf(M, lse_n);
-  float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
+  const float wl = lane < ns ? exp2_hw(lse_l - M) : 0.f;  // the weight of split `lane`
+  float W = wl;
   for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
   W = wave_sum(W);
   const float a_w = exp2_hw(lse_w - M);  // 0 without windows
@@ -1604,39 +1612,44 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 
   // channel c over this half's splits, a round at a time (one round covers
   // 32 splits); a split past the count contributes nothing (its stale values
-  // are never multiplied).  The lse of split s < 64 is lane s's lse_l.
+  // are never multiplied).  The weight of split s < 64 is lane s's wl.
   float acc = 0.f;
-  const int half_s = __builtin_amdgcn_readfirstlane(half);  // the same in the wave
-  auto lse_of = [&](int s) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_l), s));
+  auto wgt_of = [&](int s) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
   };
-  const int nr = (ns + 2 * kMergeSplits - 1) / (2 * kMergeSplits);
+  const int nr = (ns + 2 * kMS - 1) / (2 * kMS);
 #pragma unroll
-  for (int k = 0; k < kMergeSplits; ++k) {
-    const int s = 2 * k + half_s;
-    if (s < ns) acc = fmaf(exp2_hw(lse_of(s) - M), xv[k], acc);
+  for (int k = 0; k < kMS; ++k) {
+    // the two halves of the wave take splits 2k and 2k + 1
+    const int s0 = 2 * k;
+    const float w0 = wgt_of(s0), w1 = wgt_of(s0 + 1);
+    const int s = s0 + half;
+    if (s < ns) acc = fmaf(half ? w1 : w0, xv[k], acc);
   }
   if (nr > 1) {
 #pragma unroll
-    for (int k = 0; k < kMergeSplits; ++k) {
-      const int s = 2 * (kMergeSplits + k) + half_s;
-      if (s < ns) acc = fmaf(exp2_hw(lse_of(s) - M), xw[k], acc);
+    for (int k = 0; k < kMS; ++k) {
+      const int s0 = 2 * (kMS + k);
+      const float w0 = wgt_of(s0), w1 = wgt_of(s0 + 1);
+      const int s = s0 + half;
+      if (s < ns) acc = fmaf(half ? w1 : w0, xw[k], acc);
     }
   }
   for (int r = 2; r < nr; ++r) {
     load_x(r, xv);
 #pragma unroll
-    for (int k = 0; k < kMergeSplits; ++k)
-      lv[k] = p[min(2 * (kMergeSplits * r + k) + half_s, S - 1) * kPartStride];
+    for (int k = 0; k < kMS; ++k)
+      lv[k] = p[min(2 * (kMS * r + k) + half, S - 1) * kPartStride];
 #pragma unroll
-    for (int k = 0; k < kMergeSplits; ++k) {
-      const int s = 2 * (kMergeSplits * r + k) + half_s;
+    for (int k = 0; k < kMS; ++k) {
+      const int s = 2 * (kMS * r + k) + half;
       if (s < ns) acc = fmaf(exp2_hw(lv[k] - M), xv[k], acc);
     }
   }
   if (kStep && half == 0 && a_n > 0.f) acc = fmaf(a_n, dv, acc);
-  osum[half][u][c] = acc;
+  // the two halves of channel c: lanes l and l + 32 (the even splits' sum first)
+  const float other = shfl_xor(acc, 32);
+  if (half == 0) osum[u][c] = acc + other;
   if ((tid & 255) == 0) {
     const float inv = 1.0f / W;
     hinv[u] = inv;
@@ -1648,8 +1661,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
     // thread (j, part) with part = head < nh writes channel j of that head
     if (part8 < nh) {
       const size_t row = row0 + part8;
-      out[row * kHeadDim + j] =
-          fmaf(hwin[part8], wv, (osum[0][part8][j] + osum[1][part8][j]) * hinv[part8]);
+      out[row * kHeadDim + j] = fmaf(hwin[part8], wv, osum[part8][j] * hinv[part8]);
     }
     return;
   }
@@ -1662,10 +1674,8 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
     const int i = 4 * part8 + 32 * i4;
 #pragma unroll
     for (int uu = 0; uu < kHT; ++uu) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&osum[0][uu][i]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&osum[1][uu][i]);
-      o[uu] = fmaf(x0.x + x1.x, r.x,
-                   fmaf(x0.y + x1.y, r.y, fmaf(x0.z + x1.z, r.z, fmaf(x0.w + x1.w, r.w, o[uu]))));
+      const float4 x = *reinterpret_cast<const float4*>(&osum[uu][i]);
+      o[uu] = fmaf(x.x, r.x, fmaf(x.y, r.y, fmaf(x.z, r.z, fmaf(x.w, r.w, o[uu]))));
     }
   }
   // quad_perm [1,0,3,2], [2,3,0,1], then row_half_mirror (lane i and 7 - i
@@ -1689,7 +1699,8 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 // (batch-1 long contexts, where one workgroup per KV head would leave most
 // CUs idle).  grid (Hq, B), block 256.  Lane l of every wave loads the lse of
 // split l (more in a loop), so every wave forms the head's maximum and weight
-// sum; wave w adds up splits w, w + 4, ... for channels lane and lane + 64,
+// sum (lane l's term, the weight of split l, is read from it for that split);
+// wave w adds up splits w, w + 4, ... for channels lane and lane + 64,
 // all of its loads issued at once, and the four waves meet in LDS.  Then
 // thread (row j = tid / 2, half) takes 64 columns of R_V row j, loaded at the
 // start, and the two halves add by a DPP step.
@@ -1738,14 +1749,15 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
   float M = lane < ns ? lse_l : -INFINITY;
   for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
   M = wave_max(M);
-  float W = lane < ns ? exp2_hw(lse_l - M) : 0.f;
+  const float wl = lane < ns ? exp2_hw(lse_l - M) : 0.f;  // the weight of split `lane`
+  float W = wl;
   for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
   W = wave_sum(W);
-  // this wave's splits; the lse of split s < 64 is lane s's lse_l
-  auto lse_of = [&](int s) {
+  // this wave's splits; the weight of split s < 64 is lane s's wl
+  auto wgt_of = [&](int s) {
     return s < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                  __builtin_bit_cast(int, lse_l), s))
-                  : p[s * kPartStride];
+                                                  __builtin_bit_cast(int, wl), s))
+                  : exp2_hw(p[s * kPartStride] - M);
   };
   float a0 = 0.f, a1 = 0.f;
   const int nr = (ns + 4 * kHeadMergeSplits - 1) / (4 * kHeadMergeSplits);
@@ -1755,7 +1767,7 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
     for (int k = 0; k < kHeadMergeSplits; ++k) {
       const int s = 4 * (kHeadMergeSplits * r + k) + w;
       if (s < ns) {
-        const float wgt = exp2_hw(lse_of(s) - M);
+        const float wgt = wgt_of(s);
         a0 = fmaf(wgt, x0[k], a0);
         a1 = fmaf(wgt, x1[k], a1);
       }
@@ -1916,7 +1928,10 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
                          static_cast<const float*>(wpart), st.start_pos,
                          static_cast<const float*>(st.deq), static_cast<const float*>(st.qr));
     };
-    tail ? go(merge_kernel<true>) : go(merge_kernel<false>);
+    if (p.S <= 8)
+      tail ? go(merge_kernel<true, 4>) : go(merge_kernel<false, 4>);
+    else
+      tail ? go(merge_kernel<true, kMergeSplits>) : go(merge_kernel<false, kMergeSplits>);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
