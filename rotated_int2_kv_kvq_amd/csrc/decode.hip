@@ -1499,8 +1499,8 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // so one barrier (the channel sums into LDS) separates the merge from the
 // rotation.
 // kMS: splits per thread and round (two halves: 2 kMS per round): 16, or 4
-// where a tile has at most 8 splits, so that a thread issues no loads that
-// only repeat the last split's (the loads are unconditional, the split index
+// or 8 where a tile has at most 8 or 16 splits, so that a thread issues no
+// loads that only repeat the last split's (the loads are unconditional, the split index
 // clamped).  The sums are the same either way (each half's splits in order).
 constexpr int kMergeSplits = 16;
 
@@ -1704,8 +1704,11 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 // all of its loads issued at once, and the four waves meet in LDS.  Then
 // thread (row j = tid / 2, half) takes 64 columns of R_V row j, loaded at the
 // start, and the two halves add by a DPP step.
-constexpr int kHeadMergeSplits = 16;  // splits per wave and round
+// kHMS: splits per wave and round: 16, or 4 where a head has at most 16
+// splits (no loads that only repeat the last split's).
+constexpr int kHeadMergeSplits = 16;
 
+template <int kHMS>
 __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict__ part,
                                                          const int* __restrict__ ctx_len,
                                                          int max_ctx, int Hq, int Hkv, int spw,
@@ -1730,11 +1733,11 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
   const float* p = part + row * S * kPartStride;
   const int ctx_in = ctx_len[b];
   const float lse_l = p[min(lane, S - 1) * kPartStride];
-  float x0[kHeadMergeSplits], x1[kHeadMergeSplits];
+  float x0[kHMS], x1[kHMS];
   auto load_round = [&](int r) {
 #pragma unroll
-    for (int k = 0; k < kHeadMergeSplits; ++k) {
-      const float* e = p + min(4 * (kHeadMergeSplits * r + k) + w, S - 1) * kPartStride;
+    for (int k = 0; k < kHMS; ++k) {
+      const float* e = p + min(4 * (kHMS * r + k) + w, S - 1) * kPartStride;
       x0[k] = e[4 + lane];
       x1[k] = e[4 + lane + 64];
     }
@@ -1760,12 +1763,12 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
                   : exp2_hw(p[s * kPartStride] - M);
   };
   float a0 = 0.f, a1 = 0.f;
-  const int nr = (ns + 4 * kHeadMergeSplits - 1) / (4 * kHeadMergeSplits);
+  const int nr = (ns + 4 * kHMS - 1) / (4 * kHMS);
   for (int r = 0; r < nr; ++r) {
     if (r > 0) load_round(r);
 #pragma unroll
-    for (int k = 0; k < kHeadMergeSplits; ++k) {
-      const int s = 4 * (kHeadMergeSplits * r + k) + w;
+    for (int k = 0; k < kHMS; ++k) {
+      const int s = 4 * (kHMS * r + k) + w;
       if (s < ns) {
         const float wgt = wgt_of(s);
         a0 = fmaf(wgt, x0[k], a0);
@@ -1919,8 +1922,11 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
   // fewer than 64 query tiles without windows: a workgroup per query head
   const bool per_head = !win && !tail && static_cast<int64_t>(B) * Hkv * p.QG < 64;
   if ((stages & 4) && per_head) {
-    hipLaunchKernelGGL(merge_head_kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len,
-                       max_ctx, Hq, Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len, max_ctx, Hq,
+                         Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
+    };
+    p.S <= 16 ? go(merge_head_kernel<4>) : go(merge_head_kernel<kHeadMergeSplits>);
   } else if (stages & 4) {
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
@@ -1930,6 +1936,8 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
     };
     if (p.S <= 8)
       tail ? go(merge_kernel<true, 4>) : go(merge_kernel<false, 4>);
+    else if (p.S <= 16)
+      tail ? go(merge_kernel<true, 8>) : go(merge_kernel<false, 8>);
     else
       tail ? go(merge_kernel<true, kMergeSplits>) : go(merge_kernel<false, kMergeSplits>);
   }
