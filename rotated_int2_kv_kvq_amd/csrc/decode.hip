@@ -1199,7 +1199,20 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   asm volatile("; q operand " tag                                                              \
                : "+v"(qv0), "+v"(qv1), "+v"(qv2), "+v"(qv3), "+v"(qv4), "+v"(qvs), "+v"(fqy),  \
                  "+v"(fqz))
-  if (nsl >= 2) {
+  // A workgroup of two splits builds its operand in slot 3 of its eight waves
+  // (enough room), so a wave with more than one block sends slice 2 out with
+  // the first two (with one block, whose slices all land at the start, that
+  // was slower: batch 4 8K 12.7 against 12.1 us); otherwise the operand takes
+  // slots 2-3 and slice 2 waits for it.
+  constexpr bool kSlice2First = kSelfQ && kPair > 1;
+  const bool early2 = kSlice2First && nsl > 4;
+  if (early2) {
+    issue(myring, idc[0], idc[1]);
+    issue(myring + kSlotStride, idc[2], idc[3]);
+    issue(myring + 2 * kSlotStride, idc[4], idc[5]);
+    fill_table();
+    KVQ_HOLD_Q("after three slices");
+  } else if (nsl >= 2) {
     issue(myring, idc[0], idc[1]);
     issue(myring + kSlotStride, idc[2], idc[3]);
     fill_table();
@@ -1214,12 +1227,13 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   }
 #undef KVQ_HOLD_Q
   if constexpr (kSelfQ) {
-    // slots 2-3 of every wave: the prologue's scratch, then the operand of
-    // lane L at dwords 20L.. (over the partial products, dead by then), the
-    // per-head group sums after the scratch
-    uint8_t* free_lds = &ring[2][0][0];
-    static_assert(sizeof(QScratch) + kHT * sizeof(float4) <= 2 * kSlotStride,
-                  "the operand's scratch fits in slots 2-3");
+    // slots 2-3 (slot 3 with two splits) of every wave: the prologue's
+    // scratch, then the operand of lane L at dwords 20L.. (over the partial
+    // products, dead by then), the per-head group sums after the scratch
+    uint8_t* free_lds = &ring[kSlice2First ? 3 : 2][0][0];
+    static_assert(sizeof(QScratch) + kHT * sizeof(float4) <=
+                      (kSlice2First ? 1 : 2) * kSlotStride,
+                  "the operand's scratch fits in the free slots");
     static_assert(offsetof(QScratch, red) + 64 * kQaLds * 4 <= offsetof(QScratch, dig),
                   "the operand overwrites only the partial products");
     QScratch& ls = *reinterpret_cast<QScratch*>(free_lds);
@@ -1241,9 +1255,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     fqy = qf_s[hl].y;
     fqz = qf_s[hl].z;
   }
-  // the id table is complete (and the operand read before slots 2-3 refill)
+  // the id table is complete (and the operand read before its slots refill)
   __syncthreads();
-  if (nsl >= 3) issue(myring + 2 * kSlotStride, idc[4], idc[5]);
+  if (!early2 && nsl >= 3) issue(myring + 2 * kSlotStride, idc[4], idc[5]);
 
   auto op6 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
     return v8i{static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
