@@ -27,8 +27,8 @@
 //      split into six 4-bit digits, each digit b an FP8 byte worth b*2^-9.
 //      Digits and codes are short enough that the MFMA sums are exact before
 //      the fp32 accumulation.
-//      The four waves of a workgroup combine their (max, sum, output) in LDS;
-//      each workgroup writes one partial per query head.
+//      The four waves of a split combine their (max, sum, output) in LDS;
+//      each split writes one partial per query head.
 //   3. merge: log-sum-exp merge of the partials and the inverse value
 //      rotation o = o_r * R_V^T.  (A separate launch: merging inside the scan
 //      through a last-workgroup counter needs device-scope release/acquire,
@@ -915,13 +915,15 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
   }
 }
 
-// 1-D grid of n_win + S * Hkv * QG * B workgroups of 256 threads.  With BF16
-// windows (kWin; n_win = 0 otherwise) the first n_win = Hkv * QG * B
-// workgroups each score the window of one (query tile, sequence) and write its
-// partial to wpart (q: the raw queries, bf16 when q_bf16); they are dispatched
-// first and run beside the splits.  The rest are the splits: split x of a
-// query tile covers body pages [x*spw, (x+1)*spw) (after the sink pages with
-// windows), cut into 8-page blocks dealt to the four waves in turn.  Group 128 fits in
+// 1-D grid of n_win + S * Hkv * QG * B workgroups of 256 threads (or, where a
+// workgroup takes two splits, see split_waves, ceil(S / 2) * Hkv * QG * B of
+// 512), then the decode step's append workgroups.  With BF16 windows (kWin;
+// n_win = 0 otherwise) the first n_win = Hkv * QG * B workgroups each score
+// the window of one (query tile, sequence) and write its partial to wpart (q:
+// the raw queries, bf16 when q_bf16); they are dispatched first and run beside
+// the splits.  The rest are the splits: split x of a query tile covers body
+// pages [x*spw, (x+1)*spw) (after the sink pages with windows), cut into
+// 8-page blocks dealt to the split's four waves in turn.  Group 128 fits in
 // 128 VGPRs (four waves per SIMD); group 64, with a third q.K operand and a
 // second value group, gets up to 168 (three waves per SIMD) rather than spill
 // inside the loop (a spill reload waits for every outstanding DMA).  kWide
@@ -929,9 +931,9 @@ __device__ __forceinline__ void block_pv(ScanState& st, const float (&p)[8],
 //
 // kSelfQ: every split workgroup builds its query operand itself (from q and
 // rot_k, with the prologue's arithmetic, so bit for bit the same operand)
-// while its first slices are in flight, in the ring slots 2-3 that the loop
-// has not reached yet; otherwise the operand comes from qa/qf, written by the
-// prologue (or the fused step's preparation) launch.
+// while its first slices are in flight, in ring slots the loop has not
+// reached yet (2-3, or 3 with eight waves); otherwise the operand comes from
+// qa/qf, written by the prologue (or the fused step's preparation) launch.
 // The decode step's single-token append run in the scan launch (see
 // split_kernel): the new tokens, and where the scan leaves what the merge
 // needs to add them.  n_app == 0: no step.
