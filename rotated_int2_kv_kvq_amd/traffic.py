@@ -12,8 +12,9 @@ algorithmic bytes the launch must move.
     python -m rotated_int2_kv_kvq_amd.traffic --fetch-csv F --write-csv W \\
         --bench-json B --copy-bytes N --out profiles/<name>.json
 
-The result records a hash of the kernel's sources; bench.py reports the
-traffic only while the sources still hash the same.
+The result records a hash of the kernel's sources (code only, comments
+left out); bench.py reports the traffic only while the sources still hash
+the same.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/decode.hip", "csrc/append_one.h", "csrc/kvq_common.h",
@@ -29,11 +31,20 @@ KERNEL_SOURCES = ("csrc/decode.hip", "csrc/append_one.h", "csrc/kvq_common.h",
 COPY_KERNEL = "neg_kernel"
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and blank-line or indentation differences,
+    so that editing a comment leaves the hash (and the recorded traffic) as it
+    was.  String literals in these sources hold no comment markers."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.strip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        with open(os.path.join(PKG, rel), encoding="utf-8") as f:
+            h.update(rel.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -87,3 +87,12 @@ def test_traffic_summary_filters_kernel_and_grid(tmp_path):
     res_all = traffic.summarize(str(fetch), str(write_), 2048, 1000.0,
                                 "split_kernel<1, false, false, true>")
     assert res_all["dispatches"]["fetch"] == 3
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The recorded traffic stays valid across comment edits, not code edits."""
+    from rotated_int2_kv_kvq_amd.traffic import _code_only
+
+    base = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    assert _code_only(base) == _code_only("/* doc */\nint f(int x) {\n\n    return x + 1;\n}\n")
+    assert _code_only(base) != _code_only(base.replace("x + 1", "x + 2"))
