@@ -214,6 +214,40 @@ def test_gqa_ratios(hg):
     assert err <= TIGHT
 
 
+def test_two_split_workgroups_ragged():
+    """Where the scan builds its operand at group 128, a workgroup takes two
+    consecutive splits of a tile.  A ragged batch whose sequences have 1 to 8
+    splits (so pairs with an idle second half, and pairs past a sequence's
+    count) matches the oracle, and the staged form (prologue launch, one split
+    per workgroup) bit for bit."""
+    import rotated_int2_kv_kvq_amd as kvq
+    w = scaled(W1, batch=6, ctx_min=1000, ctx_max=1000)
+    say("[pairs] ragged, split_pages 8")
+    case = new_case(w, keep_initial=False)
+    fill_context(case)
+    q = query(case)
+    ctx = np.array([1, 100, 300, 517, 1000, 37], np.int32)
+    max_ctx = int(ctx.max())
+    plan = kvq.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx, split_pages=8)
+    assert plan["operand_in_scan"] and plan["num_splits"] == 8
+    out = decode(case, q, ctx=ctx, split_pages=8)
+    pairs = [(b, hq) for b in range(w.batch) for hq in range(0, w.num_q_heads, 3)]
+    ref = oracle_decode(case, q, pairs, ctx=ctx)
+    err = max(attention_error(out[b, hq].cpu().numpy(), ref[(b, hq)]) for (b, hq) in pairs)
+    say(f"  max rel err {err:.3e}")
+    assert err <= TIGHT
+    ctx_t = torch.from_numpy(ctx).to(case.device)
+    ws = torch.empty(kvq.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, max_ctx,
+                                                split_pages=8),
+                     dtype=torch.uint8, device=case.device)
+    staged = torch.full_like(out, float("nan"))
+    for st in (kvq.STAGE_PREPARE, kvq.STAGE_SPLITS, kvq.STAGE_MERGE):
+        kvq.decode(case.pages, case.table, ctx_t, max_ctx, q, case.rk, case.rv, w.group,
+                   case.sm_scale, out=staged, workspace=ws, stages=st, split_pages=8)
+    torch.cuda.synchronize()
+    assert torch.equal(staged, out)
+
+
 # (workload, split pages, whether the whole call builds the operand in the scan)
 STAGED = {
     "cfg1_b4_ctx1000": (SMALL["cfg1_b4_ctx1000"], 0, True),
