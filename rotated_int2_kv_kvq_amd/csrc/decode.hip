@@ -114,6 +114,34 @@ __host__ __device__ inline int num_splits(int n_pages, int spw) {
   return max(1, (n_pages + spw / 2) / spw);
 }
 
+// Division by a divisor fixed for the launch as a multiply and a shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994): for 1 <= d <= 2^31 take l = ceil(log2 d),
+// s = 31 + l and m = ceil(2^s / d), which lies in [2^31, 2^32).  With
+// e = m d - 2^s in [0, d), n m / 2^s = n / d + n e / (d 2^s), and for
+// 0 <= n < 2^31 the second term is below 1/d, so the floor is n / d.  The
+// host computes (m, s); in a kernel the quotient of a uniform n is three
+// scalar instructions instead of the integer division's reciprocal sequence,
+// whose vector-to-scalar round trips make up much of a workgroup's start.
+struct FastDiv {
+  uint32_t m, s;
+  __device__ __forceinline__ int div(int n) const {
+    return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * m) >> s);
+  }
+};
+inline FastDiv fast_div(int d) {
+  uint32_t l = 0;
+  while ((1ull << l) < static_cast<uint64_t>(d)) ++l;
+  const uint64_t sh = 31 + l;
+  return FastDiv{static_cast<uint32_t>(((1ull << sh) + d - 1) / static_cast<uint64_t>(d)),
+                 static_cast<uint32_t>(sh)};
+}
+// num_splits of a non-negative page count with spw as a FastDiv
+__device__ __forceinline__ int num_splits_fd(int n_pages, int spw, FastDiv fspw) {
+  if (n_pages <= 0) return 0;
+  return max(1, fspw.div(n_pages + spw / 2));
+}
+
 // --------------------------------------------------------------------------- prologue
 // grid (Hkv * QG, B), block 256: wave w rotates query head 4*qg + w of KV head
 // h; then 64 threads pack the A operands lane by lane.
@@ -400,8 +428,7 @@ struct QLoads {
 template <int G>
 __device__ __forceinline__ void prologue_load(int h, int qg, int b, const void* __restrict__ q,
                                               bool q_bf16, const float* __restrict__ rot_k, int Hq,
-                                              int Hkv, QLoads& L) {
-  const int Hg = Hq / Hkv;
+                                              int Hg, QLoads& L) {
   const int tid = threadIdx.x;
   const bool act = tid < 256;
   const int lane = tid & 63;
@@ -488,7 +515,7 @@ __device__ __forceinline__ void prologue_compute(int h, int qg, int b, const voi
                                                  uint32_t* qa_tile, int lane_stride,
                                                  int scale_off, float4* qf_tile) {
   QLoads L;
-  prologue_load<G>(h, qg, b, q, q_bf16, rot_k, Hq, Hkv, L);
+  prologue_load<G>(h, qg, b, q, q_bf16, rot_k, Hq, Hq / Hkv, L);
   prologue_finish<G>(L, rot_k == nullptr, qscale, ls, qa_tile, lane_stride, scale_off, qf_tile);
 }
 
@@ -962,6 +989,13 @@ __host__ __device__ constexpr int split_waves(int G, bool win, bool self_q) {
   return (self_q && !win && G == 1) ? 8 : 4;
 }
 
+// The scan launch's divisors: y = Hkv * QG (query tiles of a sequence), sp
+// (split workgroups of a tile), qg = QG, hkv = Hkv, spw; hg = Hq / Hkv.
+struct ScanDivs {
+  FastDiv y, sp, qg, hkv, spw;
+  int hg;
+};
+
 template <int G, bool kWide, bool kWin, bool kSelfQ>
 __global__ __launch_bounds__(64 * split_waves(G, kWin, kSelfQ))
 __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
@@ -971,7 +1005,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
              const float4* __restrict__ qf, float* __restrict__ part, int S,
              const uint16_t* __restrict__ wstore, int n_win, const void* __restrict__ q,
              int q_bf16, const float* __restrict__ mu, float qscale, float* __restrict__ wpart,
-             const float* __restrict__ rot_k, StepTail step) {
+             const float* __restrict__ rot_k, StepTail step, ScanDivs dv) {
   constexpr int PB = page_bytes_for_groups(G);
   constexpr int kSlot = 2 * PB;
   constexpr int kW = split_waves(G, kWin, kSelfQ);  // waves
@@ -992,9 +1026,9 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     static_assert(sizeof(ring) >= (kHT * kHeadDim + kWinLds) * sizeof(float),
                   "window scratch lives in the ring");
     float(*qin)[kHeadDim] = reinterpret_cast<float(*)[kHeadDim]>(&ring[0][0][0]);
-    const int hy = blockIdx.x % Y, b = blockIdx.x / Y;
-    const int h = hy / QG, qg = hy % QG;
-    const int Hg = Hq / Hkv;
+    const int b = dv.y.div(blockIdx.x), hy = blockIdx.x - b * Y;
+    const int h = dv.qg.div(hy), qg = hy - h * QG;
+    const int Hg = dv.hg;
     const int nh = min(kHT, Hg - qg * kHT);
     const int u = threadIdx.x >> 6, c = threadIdx.x & 63;
     const size_t qrow =
@@ -1036,7 +1070,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int lin = static_cast<int>(blockIdx.x) - n_win;
   if constexpr (kSelfQ && !kWin) {
     if (lin >= n_wg) {
-      const int a = lin - n_wg, hb = a / Hkv, ha = a % Hkv;
+      const int a = lin - n_wg, hb = dv.hkv.div(a), ha = a - hb * Hkv;
       float* scratch = reinterpret_cast<float*>(&ring[0][0][0]);
       float* dq = step.deq + (static_cast<size_t>(hb) * Hkv + ha) * kDeqStride;
       const int pos = step.start_pos[hb];
@@ -1063,12 +1097,14 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   }
   const int xcd = lin & 7;
   const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
-  const int hy = job % Y;
   const int SP = (S + kPair - 1) / kPair;  // workgroups per query tile
-  const int wgp = (job / Y) % SP;
-  const int b = job / (SP * Y);
-  const int h = hy / QG;
-  const int qg = hy % QG;
+  const int jy = dv.y.div(job);
+  const int hy = job - jy * Y;
+  const int b = dv.sp.div(jy);
+  const int wgp = jy - b * SP;
+  const int h = dv.qg.div(hy);
+  const int qg = hy - h * QG;
+  const int Hg = dv.hg;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // this wave's split of the workgroup, and its place among the split's four
@@ -1116,7 +1152,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   constexpr bool kEarlyQ = kSelfQ && !kWide && !kWin;
   QLoads qload;
   if constexpr (kEarlyQ)
-    prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qload);
+    prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hg, qload);
   if constexpr (!kSelfQ) {
     const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
     q0 = qap[0];
@@ -1136,7 +1172,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   // (the merge adds the token) and the block holding it takes the masked path
   const int pex = n_app > 0 ? step.start_pos[b] : -1;
   const int n_pages = (hi_tok + kBlock - 1) / kBlock;
-  const int ns_b = num_splits(n_pages - lo_pages, spw);
+  const int ns_b = num_splits_fd(n_pages - lo_pages, spw, dv.spw);
   // a split past the tile's count, or starting past the context, has no pages
   // (the splits of a workgroup are consecutive: if its first has none, neither
   // has the second)
@@ -1241,7 +1277,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     QScratch& ls = *reinterpret_cast<QScratch*>(free_lds);
     uint32_t* qa_s = reinterpret_cast<uint32_t*>(free_lds + offsetof(QScratch, red));
     float4* qf_s = reinterpret_cast<float4*>(free_lds + sizeof(QScratch));
-    if constexpr (!kEarlyQ) prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hkv, qload);
+    if constexpr (!kEarlyQ) prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hg, qload);
     prologue_finish<G>(qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s,
                        (n_app > 0 && wgp == 0) ? step.qr + hgi * kHT * kHeadDim : nullptr);
     __syncthreads();  // the operand is packed
@@ -1475,7 +1511,6 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   const int cc = threadIdx.x & 63;
   const int w0 = 4 * half;
   const int hloc = qg * kHT + ch;
-  const int Hg = Hq / Hkv;
   const int nh = min(kHT, Hg - qg * kHT);
   if (has && ch < nh) {
     float M = kNegBig;
@@ -1913,6 +1948,8 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
   if ((p.S > 0 || win) && (stages & 2)) {
     const int nw = split_waves(G, win != nullptr, self_q);
     const int sp = (p.S + nw / 4 - 1) / (nw / 4);  // split workgroups per query tile
+    const ScanDivs dv{fast_div(Hkv * p.QG), fast_div(std::max(sp, 1)), fast_div(p.QG),
+                      fast_div(Hkv), fast_div(std::max(p.spw, 1)), Hq / Hkv};
     const dim3 g2(n_win + sp * Hkv * p.QG * B + st.n_app);
     // one buffer descriptor spans the cache when its byte size fits 32 bits
     const bool wide = static_cast<uint64_t>(num_blocks) * Hkv * page_bytes_for_groups(G) >
@@ -1920,7 +1957,7 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, g2, dim3(64 * nw), 0, stream, pages, num_blocks, Hkv,
                          block_table, max_blocks, ctx_len, max_ctx, Hq, p.QG, p.spw, qa, qf, part,
-                         p.S, win, n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, st);
+                         p.S, win, n_win, q, q_bf16 ? 1 : 0, mu, qscale, wpart, rot_k, st, dv);
     };
     auto pick = [&](auto g, auto wd) {
       constexpr int GG = decltype(g)::value;
