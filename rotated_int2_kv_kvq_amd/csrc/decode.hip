@@ -996,6 +996,15 @@ struct ScanDivs {
   int hg;
 };
 
+// The merge launch's divisors: qg = QG, spw; hg = Hq / Hkv.  (The per-head
+// merge keeps its one division: there the compiler fetched such constants
+// with a second kernel-argument load behind a branch, a round trip longer
+// than the division.)
+struct MergeDivs {
+  FastDiv qg, spw;
+  int hg;
+};
+
 template <int G, bool kWide, bool kWin, bool kSelfQ>
 __global__ __launch_bounds__(64 * split_waves(G, kWin, kSelfQ))
 __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 3, 4))) void
@@ -1569,14 +1578,15 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
                                                      const float* __restrict__ wpart,
                                                      const int* __restrict__ new_pos,
                                                      const float* __restrict__ deq,
-                                                     const float* __restrict__ qr) {
+                                                     const float* __restrict__ qr,
+                                                     MergeDivs md) {
   __shared__ __attribute__((aligned(16))) float osum[kHT][kHeadDim];  // both halves
   __shared__ float hinv[kHT];  // 1 / (weight sum) per head
   __shared__ float hwin[kHT];  // the window partial's share of each head's output
-  const int h = blockIdx.x / QG;
-  const int qg = blockIdx.x % QG;
+  const int h = md.qg.div(blockIdx.x);
+  const int qg = blockIdx.x - h * QG;
   const int b = blockIdx.y;
-  const int Hg = Hq / Hkv;
+  const int Hg = md.hg;
   const int nh = min(kHT, Hg - qg * kHT);
   const int tid = threadIdx.x;
   const int j = tid >> 3, part8 = tid & 7;
@@ -1636,7 +1646,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
   // with BF16 windows (wpart != null) the splits cover the body only
   const int lo_pages = wpart ? kSink / kBlock : 0;
   const int hi_tok = wpart ? body_end(ctx) : ctx;
-  const int ns = num_splits((hi_tok + kBlock - 1) / kBlock - lo_pages, spw);
+  const int ns = num_splits_fd((hi_tok + kBlock - 1) / kBlock - lo_pages, spw, md.spw);
   if (ns == 0) {  // no body: the window's output, or zero for an empty context
     if (half == 0 && u < nh) {
       const size_t row = row0 + u;
@@ -1972,6 +1982,7 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
     };
     G == 2 ? pick_w(Const<int, 2>{}) : pick_w(Const<int, 1>{});
   }
+  const MergeDivs mdv{fast_div(std::max(p.QG, 1)), fast_div(std::max(p.spw, 1)), Hq / Hkv};
   // fewer than 64 query tiles without windows: a workgroup per query head
   const bool per_head = !win && !tail && static_cast<int64_t>(B) * Hkv * p.QG < 64;
   if ((stages & 4) && per_head) {
@@ -1985,7 +1996,7 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
       hipLaunchKernelGGL(kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
                          max_ctx, Hq, Hkv, p.QG, p.spw, p.S ? p.S : 1, rot_v, out,
                          static_cast<const float*>(wpart), st.start_pos,
-                         static_cast<const float*>(st.deq), static_cast<const float*>(st.qr));
+                         static_cast<const float*>(st.deq), static_cast<const float*>(st.qr), mdv);
     };
     if (p.S <= 8)
       tail ? go(merge_kernel<true, 4>) : go(merge_kernel<false, 4>);
