@@ -191,9 +191,9 @@ __device__ __forceinline__ void append_one_body(
 
 // 256 threads (a thread per rotated channel, the quarters in turn, the next
 // quarter's column loads in flight while one is summed); the token goes to
-// position pos.  Threads 256 and up of a larger workgroup repeat the first
-// 256's loads and arithmetic (the same values to the same LDS words) and
-// store nothing.  scratch: 264 floats of LDS that the caller lends (the
+// position pos.  Threads 256 and up of a larger workgroup write the first
+// 256's inputs again (the same values to the same LDS words), skip the
+// rotation's loads, pass the barriers and store nothing.  scratch: 264 floats of LDS that the caller lends (the
 // token's inputs and the group reduction).  deq as for append_one_store.
 template <bool kBf16>
 __device__ __forceinline__ void append_one_256(
@@ -209,7 +209,7 @@ __device__ __forceinline__ void append_one_256(
   OneDst D;
   append_one_locate(h, b, pages, num_blocks, Hkv, G, block_table, max_blocks, pos, D);
   const float* Rm = mat ? rot_v : rot_k;
-  const bool ident = Rm == nullptr;
+  const bool ident = Rm == nullptr || tid >= 256;  // (per wave)
   const float* R = ident ? nullptr : Rm + static_cast<size_t>(h) * kHeadDim * kHeadDim + j;
   float rc[2][32];
   if (!ident) {

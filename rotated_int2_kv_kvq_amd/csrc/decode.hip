@@ -184,17 +184,23 @@ __device__ __forceinline__ void prologue_digits(float qscale,
   const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
   const float s0 = wave_sum(r0), s1 = wave_sum(r1);
   // |x| < 2^e: |x| / 2^e to 32 fraction bits, rounded to nearest; digit d
-  // (0 = most significant) as the FP6 field sign | nibble
+  // (0 = most significant) as the FP6 field sign | nibble, the eight fields
+  // of a channel as bytes d = 0..7.  Within a register: the four nibbles of
+  // each half of W spread to the four bytes (lowest nibble to byte 0), the
+  // bytes reversed (digit 0 is the top nibble), and a nonzero byte b (b + 15
+  // reaches bit 4, b <= 15 carries no further) given the sign bit 0x20.
   const int e = min(max(exp_above(amax), -100), 100);
   auto digits = [&](float x, int ch) {
     const uint32_t W =
         static_cast<uint32_t>(fminf(rintf(ldexpf(fabsf(x), 32 - e)), 4294967040.0f));
-    const uint32_t sg = x < 0.f ? 0x20u : 0u;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t nib = (W >> (28 - 4 * d)) & 15u;
-      dig[hl][ch][d] = static_cast<uint8_t>(nib ? (nib | sg) : 0u);
-    }
+    const uint32_t sg = x < 0.f ? ~0u : 0u;
+    auto fields4 = [&](uint32_t t) {  // t: 16 bits, digits 4k..4k+3 from the top
+      uint32_t v = (t | (t << 8)) & 0x00FF00FFu;
+      v = __builtin_bswap32((v | (v << 4)) & 0x0F0F0F0Fu);
+      return v | ((((v + 0x0F0F0F0Fu) & 0x10101010u) << 1) & sg);
+    };
+    *reinterpret_cast<uint2*>(&dig[hl][ch][0]) =
+        make_uint2(fields4(W >> 16), fields4(W & 0xffffu));
   };
   digits(r0, lane);
   digits(r1, lane + 64);
@@ -234,21 +240,21 @@ __device__ __forceinline__ void prologue_pack(const uint8_t (&dig)[kHT][kHeadDim
       digit = 4 + (r & 1);
       use = (g >> 1) == ((r >> 1) & 1);
     }
-    uint64_t bits[3] = {0, 0, 0};
+    // field j at bits 6j.. of the operand's six dwords (little-endian)
+    uint32_t bits[6] = {0, 0, 0, 0, 0, 0};
     if (use) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const int ch = 32 * g + 16 * (j >> 4) + ((3 * (j & 15)) & 15);
-        const uint64_t field = dig[head][ch][digit];
+        const uint32_t field = dig[head][ch][digit];
         const int bit = 6 * j;
-        bits[bit >> 6] |= field << (bit & 63);
-        if ((bit & 63) > 58) bits[(bit >> 6) + 1] |= field >> (64 - (bit & 63));
+        bits[bit >> 5] |= field << (bit & 31);
+        if ((bit & 31) > 26) bits[(bit >> 5) + 1] |= field >> (32 - (bit & 31));
       }
     }
     uint32_t* dst = qa_tile + L * lane_stride;
 #pragma unroll
-    for (int d = 0; d < 6; ++d)
-      dst[6 * op + d] = static_cast<uint32_t>(bits[d >> 1] >> (32 * (d & 1)));
+    for (int d = 0; d < 6; ++d) dst[6 * op + d] = bits[d];
     if (op == 0)
       dst[scale_off] =
           static_cast<uint32_t>(min(max(kScaleOne + qe[head] + 2 - 4 * (r & 3), 1), 254));
