@@ -431,7 +431,11 @@ struct QLoads {
 
 // The loads of query tile (h, qg) of sequence b (threads 0-255; further
 // threads load nothing).  rot_k null: the keys were not rotated, q_r = q.
-template <int G>
+// kEight: a workgroup of eight or more waves splits the products over eight
+// of them: wave w takes rows 32 (w % 4).. of R_K at the one column
+// 64 (w / 4) + lane (in L.r[i].x), so each wave loads and multiplies half as
+// much; the sums are the same, in the same order.
+template <int G, bool kEight = false>
 __device__ __forceinline__ void prologue_load(int h, int qg, int b, const void* __restrict__ q,
                                               bool q_bf16, const float* __restrict__ rot_k, int Hq,
                                               int Hg, QLoads& L) {
@@ -440,7 +444,14 @@ __device__ __forceinline__ void prologue_load(int h, int qg, int b, const void* 
   const int lane = tid & 63;
   const int wv = (tid >> 6) & 3;
   const int nh = min(kHT, Hg - qg * kHT);
-  if (act && rot_k != nullptr) {
+  if constexpr (kEight) {
+    if (tid < 512 && rot_k != nullptr) {
+      const float* R = rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim +
+                       32 * wv * kHeadDim + 64 * ((tid >> 8) & 1) + lane;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) L.r[i].x = R[i * kHeadDim];
+    }
+  } else if (act && rot_k != nullptr) {
     const float2* R = reinterpret_cast<const float2*>(
         rot_k + static_cast<size_t>(h) * kHeadDim * kHeadDim + 32 * wv * kHeadDim + 2 * lane);
 #pragma unroll
@@ -464,14 +475,15 @@ __device__ __forceinline__ void prologue_load(int h, int qg, int b, const void* 
   }
 }
 
-// The operand from the loads: threads 0-255 do the work; further threads of
-// a larger workgroup only pass the barriers (the fused decode step runs it in
-// 1024-thread workgroups).  q.R_K as a split-K product (quarter wv of the
-// input channels, output channels 2 lane and 2 lane + 1, the four heads in
-// one pass).  The A operands of lane L go to qa_tile + L * lane_stride (dwords
+// The operand from the loads: threads 0-255 do the work (with kEight, the
+// products: threads 0-511); further threads of a larger workgroup only pass
+// the barriers (the fused decode step runs it in 1024-thread workgroups).
+// q.R_K as a split-K product (quarter wv of the input channels, output
+// channels 2 lane and 2 lane + 1, or with kEight channel 64 (w / 4) + lane,
+// the four heads in one pass).  The A operands of lane L go to qa_tile + L * lane_stride (dwords
 // 0-17, row scales at scale_off and scale_off + 1), the per-head group sums
 // to qf_tile[0..3].
-template <int G>
+template <int G, bool kEight = false>
 __device__ __forceinline__ void prologue_finish(const QLoads& L, bool ident, float qscale,
                                                 QScratch& ls, uint32_t* qa_tile, int lane_stride,
                                                 int scale_off, float4* qf_tile,
@@ -492,6 +504,15 @@ __device__ __forceinline__ void prologue_finish(const QLoads& L, bool ident, flo
     for (int hh = 0; hh < kHT; ++hh) {
       ls.red[wv][hh][lane] = (lane >> 5) == wv ? ls.qin[hh][lane] : 0.f;
       ls.red[wv][hh][lane + 64] = ((lane + 64) >> 5) == wv ? ls.qin[hh][lane + 64] : 0.f;
+    }
+  } else if (kEight && !ident && tid < 512) {
+    const int c = 64 * ((tid >> 8) & 1) + lane;
+#pragma unroll
+    for (int hh = 0; hh < kHT; ++hh) {
+      float a0 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) a0 = fmaf(ls.qin[hh][32 * wv + i], L.r[i].x, a0);
+      ls.red[wv][hh][c] = a0;
     }
   } else if (act) {
 #pragma unroll
@@ -1167,7 +1188,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   constexpr bool kEarlyQ = kSelfQ && !kWide && !kWin;
   QLoads qload;
   if constexpr (kEarlyQ)
-    prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hg, qload);
+    prologue_load<G, (kPair > 1)>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hg, qload);
   if constexpr (!kSelfQ) {
     const uint4* qap = reinterpret_cast<const uint4*>(qa + (hgi * 64 + lane) * kQaDwords);
     q0 = qap[0];
@@ -1292,9 +1313,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     QScratch& ls = *reinterpret_cast<QScratch*>(free_lds);
     uint32_t* qa_s = reinterpret_cast<uint32_t*>(free_lds + offsetof(QScratch, red));
     float4* qf_s = reinterpret_cast<float4*>(free_lds + sizeof(QScratch));
-    if constexpr (!kEarlyQ) prologue_load<G>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hg, qload);
-    prologue_finish<G>(qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s,
-                       (n_app > 0 && wgp == 0) ? step.qr + hgi * kHT * kHeadDim : nullptr);
+    if constexpr (!kEarlyQ)
+      prologue_load<G, (kPair > 1)>(h, qg, b, q, q_bf16 != 0, rot_k, Hq, Hg, qload);
+    prologue_finish<G, (kPair > 1)>(
+        qload, rot_k == nullptr, qscale, ls, qa_s, kQaLds, kQaLdsScale, qf_s,
+        (n_app > 0 && wgp == 0) ? step.qr + hgi * kHT * kHeadDim : nullptr);
     __syncthreads();  // the operand is packed
     const uint32_t* mine = qa_s + lane * kQaLds;
     qv0 = u32x4{mine[0], mine[1], mine[2], mine[3]};
