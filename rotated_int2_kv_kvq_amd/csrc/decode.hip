@@ -1795,7 +1795,9 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 // thread (row j = tid / 2, half) takes 64 columns of R_V row j, loaded at the
 // start, and the two halves add by a DPP step.
 // kHMS: splits per wave and round: 16, or 4 where a head has at most 16
-// splits (no loads that only repeat the last split's).
+// splits (no loads that only repeat the last split's), or 32 where it has
+// 65-128: then every load, the second 64 splits' lse included, is issued
+// before the context length is known.
 constexpr int kHeadMergeSplits = 16;
 
 template <int kHMS>
@@ -1823,6 +1825,8 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
   const float* p = part + row * S * kPartStride;
   const int ctx_in = ctx_len[b];
   const float lse_l = p[min(lane, S - 1) * kPartStride];
+  constexpr bool kLse2 = kHMS == 32;  // lane l also holds split l + 64's lse
+  const float lse_h = kLse2 ? p[min(lane + 64, S - 1) * kPartStride] : 0.f;
   float x0[kHMS], x1[kHMS];
   auto load_round = [&](int r) {
 #pragma unroll
@@ -1840,17 +1844,24 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* __restrict
     return;
   }
   float M = lane < ns ? lse_l : -INFINITY;
-  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
+  if (kLse2 && lane + 64 < ns) M = fmaxf(M, lse_h);
+  for (int s = lane + (kLse2 ? 128 : 64); s < ns; s += 64) M = fmaxf(M, p[s * kPartStride]);
   M = wave_max(M);
   const float wl = lane < ns ? exp2_hw(lse_l - M) : 0.f;  // the weight of split `lane`
-  float W = wl;
-  for (int s = lane + 64; s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
+  const float wh = kLse2 && lane + 64 < ns ? exp2_hw(lse_h - M) : 0.f;  // of split lane + 64
+  float W = wl + wh;
+  for (int s = lane + (kLse2 ? 128 : 64); s < ns; s += 64) W += exp2_hw(p[s * kPartStride] - M);
   W = wave_sum(W);
-  // this wave's splits; the weight of split s < 64 is lane s's wl
+  // this wave's splits; the weight of split s < 64 is lane s's wl (s < 128:
+  // lane s - 64's wh)
   auto wgt_of = [&](int s) {
-    return s < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                  __builtin_bit_cast(int, wl), s))
-                  : exp2_hw(p[s * kPartStride] - M);
+    if (s < 64)
+      return __builtin_bit_cast(float,
+                                __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
+    if (kLse2 && s < 128)
+      return __builtin_bit_cast(float,
+                                __builtin_amdgcn_readlane(__builtin_bit_cast(int, wh), s - 64));
+    return exp2_hw(p[s * kPartStride] - M);
   };
   float a0 = 0.f, a1 = 0.f;
   const int nr = (ns + 4 * kHMS - 1) / (4 * kHMS);
@@ -2019,7 +2030,12 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
       hipLaunchKernelGGL(kernel, dim3(Hq, B), dim3(256), 0, stream, part, ctx_len, max_ctx, Hq,
                          Hkv, p.spw, p.S ? p.S : 1, rot_v, out);
     };
-    p.S <= 16 ? go(merge_head_kernel<4>) : go(merge_head_kernel<kHeadMergeSplits>);
+    if (p.S <= 16)
+      go(merge_head_kernel<4>);
+    else if (p.S <= 64 || p.S > 128)
+      go(merge_head_kernel<kHeadMergeSplits>);
+    else
+      go(merge_head_kernel<32>);
   } else if (stages & 4) {
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3(Hkv * p.QG, B), dim3(1024), 0, stream, part, ctx_len,
