@@ -143,8 +143,10 @@ __device__ __forceinline__ int num_splits_fd(int n_pages, int spw, FastDiv fspw)
 }
 
 // --------------------------------------------------------------------------- prologue
-// grid (Hkv * QG, B), block 256: wave w rotates query head 4*qg + w of KV head
-// h; then 64 threads pack the A operands lane by lane.
+// grid (Hkv * QG, B), block 512: eight waves form q.R_K of query tile qg of
+// KV head h (a quarter of R_K's rows and half its columns each), four turn
+// the four heads into digits, then 64 threads per operand pack the A
+// operands lane by lane.
 //
 // |x| is fixed-point with 32 fraction bits under 2^e: eight 4-bit digits,
 // digit d (0 = most significant) worth b * 2^(e - 4 - 4d), as the FP6 value
@@ -534,7 +536,8 @@ __device__ __forceinline__ void prologue_finish(const QLoads& L, bool ident, flo
   if (act) prologue_pack<G>(ls.dig, ls.qe, qa_tile, lane_stride, scale_off);
 }
 
-// Both parts back to back.
+// Both parts back to back (the products on eight waves: every workgroup
+// that runs this has at least 512 threads).
 template <int G>
 __device__ __forceinline__ void prologue_compute(int h, int qg, int b, const void* __restrict__ q,
                                                  bool q_bf16, const float* __restrict__ rot_k,
@@ -542,8 +545,9 @@ __device__ __forceinline__ void prologue_compute(int h, int qg, int b, const voi
                                                  uint32_t* qa_tile, int lane_stride,
                                                  int scale_off, float4* qf_tile) {
   QLoads L;
-  prologue_load<G>(h, qg, b, q, q_bf16, rot_k, Hq, Hq / Hkv, L);
-  prologue_finish<G>(L, rot_k == nullptr, qscale, ls, qa_tile, lane_stride, scale_off, qf_tile);
+  prologue_load<G, true>(h, qg, b, q, q_bf16, rot_k, Hq, Hq / Hkv, L);
+  prologue_finish<G, true>(L, rot_k == nullptr, qscale, ls, qa_tile, lane_stride, scale_off,
+                           qf_tile);
 }
 
 // The prologue kernel's view: its own LDS, the operand to the workspace.
@@ -559,7 +563,7 @@ __device__ __forceinline__ void prologue_body(int hx, int b, const void* __restr
 }
 
 template <bool kBf16, int G>
-__global__ __launch_bounds__(256) void prologue_kernel(const void* __restrict__ q,
+__global__ __launch_bounds__(512) void prologue_kernel(const void* __restrict__ q,
                                                        const float* __restrict__ rot_k, int Hq,
                                                        int Hkv, int QG, float qscale,
                                                        uint32_t* __restrict__ qa,
@@ -1979,7 +1983,7 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
   if (p.S > 0 && (stages & 1) && !self_q) {
     const dim3 g1(Hkv * p.QG, B);
     auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, g1, dim3(256), 0, stream, q, rot_k, Hq, Hkv, p.QG, qscale, qa,
+      hipLaunchKernelGGL(kernel, g1, dim3(512), 0, stream, q, rot_k, Hq, Hkv, p.QG, qscale, qa,
                          qf);
     };
     if (q_bf16)
