@@ -431,8 +431,9 @@ struct QLoads {
   float v0, v1;
 };
 
-// The loads of query tile (h, qg) of sequence b (threads 0-255; further
-// threads load nothing).  rot_k null: the keys were not rotated, q_r = q.
+// The loads of query tile (h, qg) of sequence b (threads 0-255, with kEight
+// threads 0-511 for R_K; further threads load nothing).  rot_k null: the
+// keys were not rotated, q_r = q.
 // kEight: a workgroup of eight or more waves splits the products over eight
 // of them: wave w takes rows 32 (w % 4).. of R_K at the one column
 // 64 (w / 4) + lane (in L.r[i].x), so each wave loads and multiplies half as
