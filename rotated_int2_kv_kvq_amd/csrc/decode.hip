@@ -1913,7 +1913,7 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 // Pages per split, from the longest context (the lengths themselves stay on
 // the device).  A large grid takes at least 128 pages per split (four 8-page
 // blocks per wave), below which per-workgroup start-up and the merge of many
-// partials cost more than the extra workgroups bring; above that, about 8192
+// partials cost more than the extra workgroups bring; above that, about 5120
 // workgroups for the longest context in every sequence, in whole 32-page
 // steps, so that a ragged batch (whose actual work may be half of that) still
 // leaves the dispatcher many short workgroups to balance; at most 512 pages.
@@ -1921,12 +1921,13 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 // the launch still has about 512 workgroups: 128 splits of 128 pages would
 // leave half of the 256 CUs idle.  Measured cold on MI355X: 128K context
 // batch 1 and 16K batch 16 are fastest at 128 pages; a batch of 64 with
-// contexts of 1K-32K at 128 (230 us) against 512 (258 us).
+// contexts of 1K-32K (group 64) at 192 pages: whole call 196.6-197.3 us,
+// against 198.2 at 160, 204.5-206.1 at 128 and 258 at 512.
 int choose_split_pages(int B, int Hkv, int QG, int max_ctx) {
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
   const int64_t total = static_cast<int64_t>(B) * Hkv * QG * max_pages;
   const int64_t floor = std::min<int64_t>(128, std::max<int64_t>(32, total / 512 / 8 * 8));
-  int64_t spw = (total / 8192 + 16) / 32 * 32;
+  int64_t spw = (total / 5120 + 16) / 32 * 32;
   if (spw < floor) spw = floor;
   if (spw > 512) spw = 512;
   return static_cast<int>(spw);
