@@ -1593,9 +1593,11 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
 // so one barrier (the channel sums into LDS) separates the merge from the
 // rotation.
 // kMS: splits per thread and round (two halves: 2 kMS per round): 16, or 4
-// or 8 where a tile has at most 8 or 16 splits, so that a thread issues no
-// loads that only repeat the last split's (the loads are unconditional, the split index
-// clamped).  The sums are the same either way (each half's splits in order).
+// where a tile has at most 16 splits (the first two rounds' loads are issued
+// together, and the smaller register count lets two workgroups share a CU),
+// so that a thread issues few loads that only repeat the last split's (the
+// loads are unconditional, the split index clamped).  The sums are the same
+// either way (each half's splits in order).
 constexpr int kMergeSplits = 16;
 
 // kStep: the decode step's new token of (sequence, KV head), left out by the
@@ -2049,10 +2051,8 @@ static int launch_decode_impl(const uint8_t* pages, int64_t num_blocks, int Hkv,
                          static_cast<const float*>(wpart), st.start_pos,
                          static_cast<const float*>(st.deq), static_cast<const float*>(st.qr), mdv);
     };
-    if (p.S <= 8)
+    if (p.S <= 16)
       tail ? go(merge_kernel<true, 4>) : go(merge_kernel<false, 4>);
-    else if (p.S <= 16)
-      tail ? go(merge_kernel<true, 8>) : go(merge_kernel<false, 8>);
     else
       tail ? go(merge_kernel<true, kMergeSplits>) : go(merge_kernel<false, kMergeSplits>);
   }
