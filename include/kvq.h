@@ -292,7 +292,10 @@ int kvq_window_write(void *window, int32_t num_kv_heads, int32_t head_dim, int32
  * kvq_decode_attn_window -- kvq_decode_attn over sinks + INT2 body + recent
  * window (see above).  window and mu (float32 [num_kv_heads][head_dim], the
  * key mean the body was encoded with) are device pointers; the other
- * arguments, the workspace size and the errors are those of kvq_decode_attn.
+ * arguments, the workspace size and the errors are those of kvq_decode_attn,
+ * except that split_pages 0 may take up to half again the automatic split
+ * size, so that the launch's window and split workgroups fit one round of
+ * the GPU (it never needs more workspace than kvq_decode_workspace_bytes).
  */
 int kvq_decode_attn_window(const void *pages, int64_t num_blocks, int32_t num_kv_heads,
                            int32_t head_dim, int32_t group, const int32_t *block_table,
@@ -308,8 +311,9 @@ int kvq_decode_attn_window(const void *pages, int64_t num_blocks, int32_t num_kv
  * sequence b (position p = start_pos[b], with ctx_len[b] = p + 1) enters the
  * recent window; when p >= 320 the token it displaces, position p - 256, is
  * first encoded from its window copy into the INT2 body (as kvq_append would
- * encode it).  Then kvq_decode_attn_window over ctx_len[b] tokens.  Arguments
- * as kvq_append_decode plus the window store (read and written).
+ * encode it).  Then kvq_decode_attn_window over ctx_len[b] tokens (its
+ * split_pages rule included).  Arguments as kvq_append_decode plus the window
+ * store (read and written).
  */
 int kvq_append_decode_window(void *pages, int64_t num_blocks, int32_t num_kv_heads,
                              int32_t head_dim, int32_t group, const int32_t *block_table,

@@ -251,6 +251,7 @@ KVQ_API int kvq_decode_attn_window(const void* pages, int64_t num_blocks, int32_
                               split_pages, &plan);
   if (st != KVQ_OK || batch == 0) return st;
   if (!window || !mu || !aligned(window, 16) || !aligned(mu, 16)) return KVQ_ERR_INVALID_ARG;
+  plan = kvq::make_window_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
   const int rc = kvq::launch_decode(
       static_cast<const uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
       max_blocks_per_seq, ctx_len, max_ctx_len, batch, num_q_heads, q, q_dtype == KVQ_BF16, rot_k,
@@ -280,6 +281,7 @@ KVQ_API int kvq_append_decode_window(void* pages, int64_t num_blocks, int32_t nu
                     rot_k, rot_v, sm_scale, out, workspace, workspace_bytes, split_pages, &plan);
   if (st != KVQ_OK || batch == 0) return st;
   if (!window || !aligned(window, 16)) return KVQ_ERR_INVALID_ARG;
+  plan = kvq::make_window_plan(batch, num_q_heads, num_kv_heads, max_ctx_len, split_pages);
   const int rc = kvq::launch_append_decode(
       static_cast<uint8_t*>(pages), num_blocks, num_kv_heads, head_dim / group, block_table,
       max_blocks_per_seq, start_pos, k, v, kv_dtype == KVQ_BF16, mu, clip_k, clip_v, ctx_len,

@@ -22,6 +22,10 @@ struct DecodePlan {
 
 DecodePlan make_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages);
 
+// The plan of a call with BF16 windows (split_pages 0: a split size that
+// keeps the scan launch within one round of workgroups where it can).
+DecodePlan make_window_plan(int B, int Hq, int Hkv, int max_ctx, int split_pages);
+
 // Whether a call launching the PREPARE and SPLITS stages together builds the
 // query operand inside the split workgroups (no prologue launch).
 bool operand_in_scan(const DecodePlan& p, int Hkv, int B, int stages);
