@@ -1093,12 +1093,15 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
   }
 
   // Workgroups go to the eight XCDs round-robin in launch order, and each XCD
-  // has its own L2.  Renumber the splits so that every XCD takes one contiguous
-  // run of (query group, split) pairs: the splits of a query group then share
-  // one L2 copy of its query operand instead of fetching it once per XCD.
-  // Within the run the query groups of one split come first, so the KV heads
-  // of a sequence start on the same pages together and read neighbouring
-  // slices of each block (the ragged group-64 batch of 64: 224-232 -> 214 us).
+  // has its own L2.  Where the scan builds its operand, renumber the splits so
+  // that every XCD takes one contiguous run of (query group, split) pairs: the
+  // splits of a query tile then share one L2 copy of its R_K and query rows
+  // instead of fetching them once per XCD.  Where the operand comes from the
+  // workspace the splits keep launch order (the ragged group-64 batch of 64:
+  // 188 -> 179 us): neighbouring workgroups, on neighbouring XCDs, then start
+  // on the same sequence's pages together.  Consecutive jobs run over the KV
+  // heads and query groups of one split first, so the KV heads of a sequence
+  // read neighbouring slices of each block.
   // The decode step's appends (kSelfQ without windows: the scan builds its own
   // operand and needs no earlier launch) are the last n_app workgroups, one
   // per (sequence, KV head).  Dispatched after every split, they start as the
@@ -1137,7 +1140,7 @@ split_kernel(const uint8_t* __restrict__ pages, int64_t num_blocks, int Hkv,
     }
   }
   const int xcd = lin & 7;
-  const int job = xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3);
+  const int job = kSelfQ ? xcd * (n_wg >> 3) + min(xcd, n_wg & 7) + (lin >> 3) : lin;
   const int SP = (S + kPair - 1) / kPair;  // workgroups per query tile
   const int jy = dv.y.div(job);
   const int hy = job - jy * Y;
