@@ -88,7 +88,7 @@ def cache_bytes_per_token_head(group: int) -> int:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
@@ -575,7 +575,7 @@ def bits_per_element(group: int, head_dim: int = 128) -> float:
 
 def pages_context(w, ctx0, per_tok_head, prefill):
     """The pages' own figures beside this measurement (none is on MI355X and
-    none is a target), and this build's counterparts."""
+    none is a target), and this library's counterparts."""
     import numpy as np
     n = int(np.max(ctx0))
     sink, recent = 64, 256
@@ -598,7 +598,7 @@ def pages_context(w, ctx0, per_tok_head, prefill):
             {"figure": "effective bits per cache element", "value": 2.32, "method": "OptR",
              "source": "same review, 'The reading' and 'Core claim'"},
         ],
-        "this_build": {
+        "this_library": {
             "bits_per_element": bits_per_element(w.group),
             "memory_reduction_vs_bf16": round(16.0 / bits_per_element(w.group), 3),
             "bits_per_element_with_bf16_windows": round(with_windows, 4),

@@ -50,7 +50,7 @@ def test_bits_and_context_fields():
     figs = {f["figure"]: f["value"] for f in ctx["pages"]}
     assert figs["decode speed-up vs BF16 FlashDecoding-v2"] == "up to 3.0x"
     assert figs["effective bits per cache element"] == 2.32
-    tb = ctx["this_build"]
+    tb = ctx["this_library"]
     assert tb["bits_per_element"] == 2.25 and tb["prefill_overhead_pct"] == {"x": 1.0}
     # 16,064 body tokens at 2.25 bits and 320 window tokens at 16 bits over 16,384
     assert abs(tb["bits_per_element_with_bf16_windows"] - (16064 * 2.25 + 320 * 16) / 16384) < 1e-4
