@@ -1926,8 +1926,9 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 // the launch still has about 512 workgroups: 128 splits of 128 pages would
 // leave half of the 256 CUs idle.  Measured cold on MI355X: 128K context
 // batch 1 and 16K batch 16 are fastest at 128 pages; a batch of 64 with
-// contexts of 1K-32K (group 64) at 192 pages: whole call 196.6-197.3 us,
-// against 198.2 at 160, 204.5-206.1 at 128 and 258 at 512.
+// contexts of 1K-32K (group 64) at 192 pages: whole call 183.9-194.1 us,
+// against 191.1-194.0 at 160, 193.1 at 224, 202.5-206.5 at 128 and 207.7 at
+// 256.
 int choose_split_pages(int B, int Hkv, int QG, int max_ctx) {
   const int64_t max_pages = (static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock;
   const int64_t total = static_cast<int64_t>(B) * Hkv * QG * max_pages;
